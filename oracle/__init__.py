@@ -1,0 +1,17 @@
+"""CPU oracle of the MoE-layer forward: TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its Python binding) never imports, calls or links it, and it shares no code
+with them.
+
+Parity status: every function in ``moe_oracle`` is pinned by
+``tests/test_oracle_pins.py`` (brute force on tiny inputs, library routines
+for the special cases, closed forms and invariants).  No function here is
+"parity unpinned".
+"""
+from .moe_oracle import (  # noqa: F401
+    router_logits, topk_route, expert_histogram, exclusive_scan, stable_scatter,
+    dispatch, gather_rows, silu, swiglu_expert, expert_ffn, combine, forward,
+    forward_tokens,
+)
