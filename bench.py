@@ -1,0 +1,241 @@
+"""Benchmark of one GPU's MoE-layer forward (one JSON line on stdout).
+
+A step is one ``moe_forward`` call on the whole batch: router GEMM, top-k
+gating, dispatch queues, grouped SwiGLU expert FFN with the gather fused into
+its first GEMM, and the gate-weighted combine.  The default workload is the
+Mixtral-shaped layer (T=8192 tokens, d=4096, E=8 experts, top-2, SwiGLU
+width 14336, bf16 storage, fp32 accumulation) with seeded synthetic inputs
+and random weights; inputs are resident in HBM before timing starts.
+
+Besides the step time it measures, with HIP events on the stream the kernels
+run on, the expert-FFN call (the dominant work: 6*k*d*f FLOPs per token),
+the dispatch call with the row gather materialised, and the combine, and it
+times the CPU oracle on a bounded slice of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "MoE layer fwd tokens/s; expert-GEMM TFLOP/s (% MFMA peak); dispatch GB/s"
+FFN_SRC = os.path.join(ROOT, "mixture_experts_layer_exclusive_amd", "csrc", "expert_ffn.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "expert_ffn_traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="mixtral_8x_bf16")
+    ap.add_argument("--cpu-tokens", type=int, default=2048,
+                    help="tokens of the workload the CPU oracle runs for the baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for HBM counter calibration)")
+    return ap.parse_args()
+
+
+def src_sha(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per expert-FFN call from the committed counter summary, or
+    None when the kernel source changed since the counters were taken."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_src_sha") != src_sha(FFN_SRC):
+        return None
+    return rec.get("hbm_bytes_per_call")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(each GPU would run this same layer on its own token shard); use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import moe_inputs as mi
+    import mixture_experts_layer_exclusive_amd as moe
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    spec = mi.WORKLOADS[args.workload]
+    p = spec["problem"]
+    tdt = torch.bfloat16 if p.dtype == "bf16" else torch.float32
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    t_gen = time.perf_counter()
+    L = mi.make_layer(args.workload, seed=0)
+    x, wg, wu, wd = up(L["x"]), up(L["w_gate"]), up(L["w_up"]), up(L["w_down"])
+    wr = up(L["w_router"]) if L["w_router"] is not None else None
+    lg = up(L["logits"]) if L["logits"] is not None else None
+    t_gen = time.perf_counter() - t_gen
+    print(f"# inputs generated and uploaded in {t_gen:.1f} s", file=sys.stderr, flush=True)
+
+    prob = moe.problem(p.T, p.d, p.E, p.k, p.f, tdt)
+    ws = torch.empty(moe.workspace_size(prob, 3), dtype=torch.uint8, device=dev)
+    y = torch.empty(p.T, p.d, dtype=tdt, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        moe.forward(x, wg, wu, wd, p.k, w_router=wr, logits=lg, ws=ws, y=y)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    ms_step_ev = ev0.elapsed_time(ev1) / args.steps
+    tokens_s = p.T / (ms_step / 1e3)
+    print(f"# forward: {ms_step:.3f} ms/step wall, {ms_step_ev:.3f} ms/step events",
+          file=sys.stderr, flush=True)
+
+    # ---- per-call timings with HIP events on the launch stream ----
+    _, inter = moe.forward(x, wg, wu, wd, p.k, w_router=wr, logits=lg, intermediates=True)
+    torch.cuda.synchronize()
+    ids, gates = inter["topk_ids"], inter["topk_gates"]
+    offsets, sa, apos = inter["offsets"], inter["sorted_assign"], inter["assign_pos"]
+    n = p.T * p.k
+    ffn_ws = torch.empty(moe.workspace_size(prob, 2), dtype=torch.uint8, device=dev)
+    disp_ws = torch.empty(max(256, moe.workspace_size(prob, 1)), dtype=torch.uint8, device=dev)
+    y_perm = torch.empty(n, p.d, dtype=tdt, device=dev)
+    x_perm = torch.empty(n, p.d, dtype=tdt, device=dev)
+    disp_out = dict(counts=torch.empty_like(inter["counts"]), offsets=torch.empty_like(offsets),
+                    sorted_assign=torch.empty_like(sa), assign_pos=torch.empty_like(apos),
+                    x_perm=x_perm)
+    y2 = torch.empty_like(y)
+
+    def timed(fn, reps):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps  # ms
+
+    reps = max(5, args.steps)
+    ms_ffn = timed(lambda: moe.expert_ffn(offsets, wg, wu, wd, p.k, p.T, x=x, sorted_assign=sa,
+                                          ws=ffn_ws, y_perm=y_perm), reps)
+    ms_disp = timed(lambda: moe.dispatch(ids, p.E, x=x, with_x_perm=True, ws=disp_ws, out=disp_out), reps)
+    ms_comb = timed(lambda: moe.combine(y_perm, apos, gates, y=y2), reps)
+    if lg is None:
+        lo = torch.empty(p.T, p.E, dtype=torch.float32, device=dev)
+        ms_route = timed(lambda: moe.route(p.k, x=x, w_router=wr, ids=ids, gates=gates, logits_out=lo), reps)
+    else:
+        ms_route = timed(lambda: moe.route(p.k, logits=lg, ids=ids, gates=gates), reps)
+
+    s = 2 if p.dtype == "bf16" else 4
+    ffn_flops = 6.0 * p.T * p.k * p.d * p.f
+    ffn_tflops = ffn_flops / (ms_ffn * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if p.dtype == "bf16" else PEAK_F32_TFLOPS
+    disp_bytes = (1 + p.k) * p.T * p.d * s + 12 * n
+    comb_bytes = (p.k + 1) * p.T * p.d * s + 8 * n
+    disp_gbs = disp_bytes / (ms_disp * 1e-3) / 1e9
+    comb_gbs = comb_bytes / (ms_comb * 1e-3) / 1e9
+
+    counts = inter["counts"].cpu().numpy()
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    # ---- CPU oracle baseline on a bounded slice of the same workload ----
+    cpu = None
+    if not args.no_cpu_baseline:
+        del x_perm, y_perm, ffn_ws, disp_ws
+        import oracle
+        from threadpoolctl import threadpool_info
+        S = min(args.cpu_tokens, p.T)
+        f32 = lambda a: mi.as_f32(a, p.dtype)  # noqa: E731
+        xs = f32(L["x"][:S])
+        wgs, wus, wds = f32(L["w_gate"]), f32(L["w_up"]), f32(L["w_down"])
+        tc = time.perf_counter()
+        if L["logits"] is not None:
+            oracle.forward(xs, p.k, wgs, wus, wds, logits=L["logits"][:S])
+        else:
+            oracle.forward(xs, p.k, wgs, wus, wds, w_router=f32(L["w_router"]))
+        tc = time.perf_counter() - tc
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        cpu = {"value": round(S / tc, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "sample": f"first {S} of {p.T} tokens, whole layer (router GEMM, top-k, queues, "
+                         f"SwiGLU FFN, combine) in float64 numpy; {tc:.1f} s"}
+
+    traffic = measured_traffic()
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if p.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) activations, N(0,1/sqrt(d)) expert weights, "
+                "N(0,0.02) router; random weights, no checkpoint)",
+        "config": {"workload": args.workload, "tokens": p.T, "d": p.d, "experts": p.E,
+                   "top_k": p.k, "ffn_width": p.f, "parallelism": "single GPU"},
+        "roofline": {"kernel": "expert FFN call (grouped GEMM1 gate/up+SwiGLU, grouped GEMM2 down)",
+                     "bound": "mfma", "achieved": round(ffn_tflops, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(ffn_tflops / peak, 4),
+                     "traffic": traffic, "ms_per_launch": round(ms_ffn, 4),
+                     "flops_per_launch": ffn_flops},
+        "expert_gemm_tflops": round(ffn_tflops, 2),
+        "expert_gemm_frac_mfma_peak": round(ffn_tflops / peak, 4),
+        "dispatch_gbs": round(disp_gbs, 1),
+        "dispatch_frac_hbm_peak": round(disp_gbs / PEAK_HBM_GBS, 4),
+        "combine_gbs": round(comb_gbs, 1),
+        "combine_frac_hbm_peak": round(comb_gbs / PEAK_HBM_GBS, 4),
+        "stage_ms": {"route": round(ms_route, 4), "dispatch_with_x_perm": round(ms_disp, 4),
+                     "expert_ffn": round(ms_ffn, 4), "combine": round(ms_comb, 4)},
+        "expert_counts": {"min": int(counts.min()), "max": int(counts.max()),
+                          "empty": int((counts == 0).sum())},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,199 @@
+/*
+ * moe.h -- C ABI of one GPU's MoE-layer forward on MI355X (gfx950).
+ *
+ * The layer: a router GEMM and static top-k softmax gating pick k of E
+ * experts per token; compact per-expert dispatch queues are built by a
+ * counting sort (histogram, exclusive scan, stable scatter), so that no
+ * dense token-by-expert matrix is ever formed; each expert runs a bias-free
+ * SwiGLU feed-forward over its queue; a gate-weighted combine returns the
+ * results to token order.
+ *
+ * Sources (summaries of three papers; they give the structure, not the
+ * formulas):
+ *   - MoEBlaze summary (euno.news, "MoEBlaze: breaking the memory wall for
+ *     efficient MoE training on modern GPUs"), Methodology item 1
+ *     (data-structure-based dispatch through per-expert queues built during
+ *     the forward pass and dropped after it), Methodology item 2 (dispatch
+ *     and reverse dispatch fused around the expert FFN), Limitations (static
+ *     top-k routing).
+ *   - Piper technical summary (gist.science, Dutch), section 1 (problem
+ *     statement): tall-and-skinny expert GEMMs and skewed expert loads.
+ *   - DisagMoE technical summary (gist.science, Korean), section 2.2
+ *     (AF-Pipe): k, the number of experts per token.
+ *
+ * Conventions shared by every entry point
+ *   - Sizes: T tokens, hidden size d, E experts, k experts per token, SwiGLU
+ *     width f.  An assignment is a = t*k + j (token t, slot j < k).
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller; arrays
+ *     are dense and row-major.  Weights use the [out, in] layout, so every
+ *     GEMM operand is contiguous along its reduction dimension:
+ *       x [T, d], w_router [E, d], w_gate [E, f, d], w_up [E, f, d],
+ *       w_down [E, d, f], y [T, d], x_perm / y_perm [T*k, d].
+ *     x, weights, x_perm, y_perm and y have the problem's dtype; logits and
+ *     gates are float32; ids, counts, offsets and permutations are int32.
+ *   - Device pointers must be 16-byte aligned.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  All work is
+ *     enqueued on it; no entry point synchronises, allocates or frees, and
+ *     the library keeps no mutable global state, so calls on different
+ *     streams with different buffers may run concurrently.
+ *   - Workspace `ws` (device, >= the size from moe_workspace_size) is
+ *     scratch whose contents are undefined before and after the call; it
+ *     must not be shared by calls that may overlap.
+ *   - Status is returned synchronously.  All argument checks happen before
+ *     any HIP call: MOE_ERR_INVALID_ARGUMENT (NULL required pointer, T < 0,
+ *     d/E/k/f < 1, k > E, unknown dtype), MOE_ERR_UNSUPPORTED (outside the
+ *     documented limits below, or a misaligned pointer),
+ *     MOE_ERR_WORKSPACE_TOO_SMALL.  T == 0 is a valid no-op.  A failed
+ *     kernel launch returns MOE_ERR_HIP; faults during execution surface on
+ *     the stream.  Logits must be finite (not checked).
+ *   - Limits: 1 <= E <= MOE_MAX_EXPERTS, 1 <= k <= min(E, MOE_MAX_TOPK),
+ *     T*k <= 2^31 - 1; bf16 needs d and f to be multiples of 64.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_MAX_EXPERTS 256
+#define MOE_MAX_TOPK 32
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARGUMENT = 1,
+    MOE_ERR_UNSUPPORTED = 2,
+    MOE_ERR_WORKSPACE_TOO_SMALL = 3,
+    MOE_ERR_HIP = 4
+} moe_status_t;
+
+typedef enum {
+    MOE_DTYPE_F32 = 0,  /* float32 storage and arithmetic throughout */
+    MOE_DTYPE_BF16 = 1  /* bf16 storage, bf16 MFMA products, fp32 accumulate */
+} moe_dtype_t;
+
+/* Which call a workspace size is asked for. */
+typedef enum {
+    MOE_OP_DISPATCH = 1,
+    MOE_OP_EXPERT_FFN = 2,
+    MOE_OP_FORWARD = 3
+} moe_op_t;
+
+/* The problem statement: T tokens, hidden size d, E experts, top-k, SwiGLU
+ * width f, storage dtype (a moe_dtype_t value). */
+typedef struct {
+    int64_t T;
+    int32_t d;
+    int32_t E;
+    int32_t k;
+    int32_t f;
+    int32_t dtype;
+} moe_problem_t;
+
+/* Optional outputs of moe_forward.  Any field may be NULL; a NULL field is
+ * kept in the workspace instead.  Shapes as in moe_route / moe_dispatch. */
+typedef struct {
+    float* logits;           /* [T, E] router logits (not written when logits_in is given) */
+    int32_t* topk_ids;       /* [T, k] */
+    float* topk_gates;       /* [T, k] */
+    int32_t* counts;         /* [E] */
+    int32_t* offsets;        /* [E + 1] */
+    int32_t* sorted_assign;  /* [T*k] */
+    int32_t* assign_pos;     /* [T*k] */
+} moe_forward_outputs_t;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* moe_status_string(int32_t status);
+
+/* Library ABI version (bumped when a signature changes). */
+int32_t moe_abi_version(void);
+
+/* Bytes of device workspace `op` needs for problem `p` (0 is possible).
+ * Host only; no HIP call. */
+moe_status_t moe_workspace_size(const moe_problem_t* p, int32_t op, size_t* bytes);
+
+/*
+ * moe_route -- router GEMM and static top-k gating.
+ * The router picks a few experts for every token (Piper, Japanese
+ * explainer, opening section); the policy is static top-k (MoEBlaze
+ * summary, Limitations).
+ *   logits[t, e] = sum_c x[t, c] * w_router[e, c]   (fp32 accumulate)
+ *   topk_ids[t, j]: the k largest logits of token t in descending order,
+ *     equal logits broken toward the lower expert id (-0.0 == +0.0).
+ *   topk_gates[t, j] = exp(l_j - l_0) / sum_i exp(l_i - l_0) over the k
+ *     chosen logits (softmax renormalised over the chosen experts), fp32.
+ * If logits_in [T, E] is non-NULL the router GEMM is skipped and x,
+ * w_router and logits_out may be NULL (logits_out is ignored).  Otherwise x,
+ * w_router and logits_out [T, E] are required and logits_out receives the
+ * router logits that the selection then reads.  The selection is exact on
+ * the fp32 logits, so ids are reproducible bit for bit from the same logits.
+ */
+moe_status_t moe_route(const moe_problem_t* p, const void* x, const void* w_router,
+                       const float* logits_in, float* logits_out,
+                       int32_t* topk_ids, float* topk_gates, void* stream);
+
+/*
+ * moe_dispatch -- the dispatch queues (MoEBlaze summary, Methodology 1): a
+ * stable counting sort of the assignments a = t*k + j by expert id.
+ *   counts[e] = #{a : topk_ids[a] == e}
+ *   offsets[0] = 0, offsets[e + 1] = offsets[e] + counts[e]
+ *   sorted_assign[pos] = a, assign_pos[a] = pos, where the queue of expert e
+ *     is positions [offsets[e], offsets[e+1]) in ascending a (stable).
+ *   x_perm[pos, :] = x[sorted_assign[pos] / k, :] (bitwise row copy), only
+ *     when x_perm is non-NULL (x is then required).
+ * Workspace: moe_workspace_size(p, MOE_OP_DISPATCH).  All outputs are
+ * bit-exact functions of topk_ids.
+ */
+moe_status_t moe_dispatch(const moe_problem_t* p, const int32_t* topk_ids, const void* x,
+                          int32_t* counts, int32_t* offsets,
+                          int32_t* sorted_assign, int32_t* assign_pos, void* x_perm,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_expert_ffn -- grouped SwiGLU expert FFN over the queues (the
+ * tall-and-skinny expert GEMMs of the Piper summary, section 1):
+ *   for every expert e and queue row pos in [offsets[e], offsets[e+1]):
+ *     row = x_perm[pos] if x_perm != NULL, else x[sorted_assign[pos] / k]
+ *     h = silu(w_gate[e] row) * (w_up[e] row),  silu(u) = u / (1 + e^-u)
+ *     y_perm[pos] = w_down[e] h
+ * With x_perm == NULL the row gather is fused into the first GEMM's operand
+ * loads (MoEBlaze summary, Methodology 2); then x and sorted_assign are
+ * required.  bf16: products on bf16 MFMA with fp32 accumulation, h rounded
+ * to bf16 between the two GEMMs, y_perm rounded to bf16.  f32: fp32 FMA.
+ * Workspace: moe_workspace_size(p, MOE_OP_EXPERT_FFN) (holds h).
+ */
+moe_status_t moe_expert_ffn(const moe_problem_t* p, const void* x_perm, const void* x,
+                            const int32_t* sorted_assign, const int32_t* offsets,
+                            const void* w_gate, const void* w_up, const void* w_down,
+                            void* y_perm, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_combine -- gate-weighted reverse dispatch (MoEBlaze summary,
+ * Methodology 2):
+ *   y[t, :] = sum_j topk_gates[t, j] * y_perm[assign_pos[t*k + j], :]
+ * fp32 accumulation in ascending j, one rounding to the dtype per element;
+ * every y row is written exactly once (deterministic).
+ */
+moe_status_t moe_combine(const moe_problem_t* p, const void* y_perm, const int32_t* assign_pos,
+                         const float* topk_gates, void* y, void* stream);
+
+/*
+ * moe_forward -- the whole layer on one stream with no host
+ * synchronisation: moe_route, moe_dispatch (queues only), moe_expert_ffn
+ * with the gather fused, moe_combine.  logits_in (optional, [T, E]) skips
+ * the router GEMM; otherwise x and w_router are used.  `out` (optional)
+ * exposes intermediates.  Workspace: moe_workspace_size(p, MOE_OP_FORWARD).
+ */
+moe_status_t moe_forward(const moe_problem_t* p, const void* x, const void* w_router,
+                         const float* logits_in, const void* w_gate, const void* w_up,
+                         const void* w_down, void* y, const moe_forward_outputs_t* out,
+                         void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,75 @@
+// Gate-weighted combine (reverse dispatch; MoEBlaze summary, Methodology 2):
+//   y[t, :] = sum_j gates[t, j] * y_perm[assign_pos[t*k + j], :]
+// One workgroup per token; each thread owns 16-byte column chunks, reads the
+// k expert rows of its token and accumulates in fp32 in ascending j, then
+// rounds once.  Every y row is written exactly once, so the result does not
+// depend on scheduling.
+#include "device_util.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+__global__ __launch_bounds__(256) void combine_bf16_kernel(const uint4* __restrict__ y_perm,
+                                                          const int32_t* __restrict__ assign_pos,
+                                                          const float* __restrict__ gates, int k,
+                                                          int chunks_per_row,
+                                                          uint4* __restrict__ y) {
+    const int64_t t = blockIdx.x;
+    for (int c = threadIdx.x; c < chunks_per_row; c += 256) {
+        float acc[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+        for (int j = 0; j < k; ++j) {
+            const int pos = assign_pos[t * k + j];
+            if (pos < 0) continue;
+            const float g = gates[t * k + j];
+            const uint4 v = load_nt(y_perm + static_cast<int64_t>(pos) * chunks_per_row + c);
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc[2 * i] = fmaf(g, lo_bf16(w[i]), acc[2 * i]);
+                acc[2 * i + 1] = fmaf(g, hi_bf16(w[i]), acc[2 * i + 1]);
+            }
+        }
+        uint4 o;
+        o.x = pack_bf16x2(acc[0], acc[1]);
+        o.y = pack_bf16x2(acc[2], acc[3]);
+        o.z = pack_bf16x2(acc[4], acc[5]);
+        o.w = pack_bf16x2(acc[6], acc[7]);
+        y[t * chunks_per_row + c] = o;
+    }
+}
+
+__global__ __launch_bounds__(256) void combine_f32_kernel(const float* __restrict__ y_perm,
+                                                         const int32_t* __restrict__ assign_pos,
+                                                         const float* __restrict__ gates, int k,
+                                                         int d, float* __restrict__ y) {
+    const int64_t t = blockIdx.x;
+    for (int c = threadIdx.x; c < d; c += 256) {
+        float acc = 0.f;
+        for (int j = 0; j < k; ++j) {
+            const int pos = assign_pos[t * k + j];
+            if (pos < 0) continue;
+            acc = fmaf(gates[t * k + j], y_perm[static_cast<int64_t>(pos) * d + c], acc);
+        }
+        y[t * d + c] = acc;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const moe_problem_t& p, const void* y_perm, const int32_t* assign_pos,
+                          const float* gates, void* y, hipStream_t s) {
+    const unsigned grid = static_cast<unsigned>(p.T);
+    if (p.dtype == MOE_DTYPE_BF16)
+        combine_bf16_kernel<<<grid, 256, 0, s>>>(static_cast<const uint4*>(y_perm), assign_pos,
+                                                 gates, p.k, p.d / 8, static_cast<uint4*>(y));
+    else
+        combine_f32_kernel<<<grid, 256, 0, s>>>(static_cast<const float*>(y_perm), assign_pos, gates,
+                                                p.k, p.d, static_cast<float*>(y));
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,52 @@
+// Device helpers shared by the kernels: bf16 conversion and wave-level
+// primitives for 64-lane CDNA wavefronts.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef uint16_t bf16_t;  // bf16 bit pattern in memory
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round to nearest, ties to even (NaN stays a quiet NaN).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<bf16_t>(u >> 16);
+}
+
+// Two bf16 packed into one 32-bit word, element 0 in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ int lane_id() { return static_cast<int>(threadIdx.x & 63); }
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+    const int l = lane_id();
+    return (l == 0) ? 0ull : (~0ull >> (64 - l));
+}
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Streaming (non-temporal) loads for data read exactly once.
+template <typename T>
+__device__ __forceinline__ T load_nt(const T* p) {
+    return __builtin_nontemporal_load(p);
+}
+template <>
+__device__ __forceinline__ uint4 load_nt<uint4>(const uint4* p) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+}  // namespace moe

@@ -1,0 +1,272 @@
+// C-ABI entry points: argument validation (pure host code, before any HIP
+// call), workspace carving and kernel launches on the caller's stream.
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "moe.h"
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr int32_t kAbiVersion = 1;
+constexpr size_t kAlign = 256;
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+size_t elem_bytes(const moe_problem_t& p) { return p.dtype == MOE_DTYPE_F32 ? 4 : 2; }
+
+// Checks the problem statement itself.
+moe_status_t check_problem(const moe_problem_t* p) {
+    if (p == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+    if (p->T < 0 || p->d < 1 || p->E < 1 || p->k < 1 || p->f < 1) return MOE_ERR_INVALID_ARGUMENT;
+    if (p->k > p->E) return MOE_ERR_INVALID_ARGUMENT;
+    if (p->dtype != MOE_DTYPE_F32 && p->dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARGUMENT;
+    if (p->E > MOE_MAX_EXPERTS || p->k > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
+    if (p->T > INT32_MAX / p->k) return MOE_ERR_UNSUPPORTED;
+    if (p->dtype == MOE_DTYPE_BF16 && (p->d % 64 != 0 || p->f % 64 != 0)) return MOE_ERR_UNSUPPORTED;
+    if (expert_ffn_grid_bound(*p) > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+// A required device pointer: present and 16-byte aligned.
+moe_status_t need(const void* ptr) {
+    if (ptr == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+    return aligned16(ptr) ? MOE_OK : MOE_ERR_UNSUPPORTED;
+}
+
+// An optional device pointer: NULL, or 16-byte aligned.
+moe_status_t optional(const void* ptr) {
+    return (ptr == nullptr || aligned16(ptr)) ? MOE_OK : MOE_ERR_UNSUPPORTED;
+}
+
+#define MOE_TRY(expr)                              \
+    do {                                           \
+        const moe_status_t st_ = (expr);           \
+        if (st_ != MOE_OK) return st_;             \
+    } while (0)
+
+#define MOE_LAUNCH(expr)                           \
+    do {                                           \
+        if ((expr) != hipSuccess) return MOE_ERR_HIP; \
+    } while (0)
+
+// Sequential carving of a workspace into 256-byte aligned pieces.
+struct Carver {
+    uintptr_t base;
+    size_t used = 0;
+    explicit Carver(void* b) : base(reinterpret_cast<uintptr_t>(b)) {}
+    template <typename T>
+    T* take(size_t bytes) {
+        T* r = reinterpret_cast<T*>(base + used);
+        used = align_up(used + bytes, kAlign);
+        return r;
+    }
+};
+
+size_t dispatch_ws(const moe_problem_t& p) {
+    const int64_t n = p.T * p.k;
+    return align_up(static_cast<size_t>(dispatch_blocks(n)) * p.E * 4, kAlign);
+}
+
+size_t ffn_ws(const moe_problem_t& p) {
+    return align_up(static_cast<size_t>(p.T) * p.k * p.f * elem_bytes(p), kAlign);
+}
+
+size_t forward_ws(const moe_problem_t& p) {
+    const size_t n = static_cast<size_t>(p.T) * p.k;
+    size_t b = 0;
+    b += align_up(static_cast<size_t>(p.T) * p.E * 4, kAlign);  // logits
+    b += align_up(n * 4, kAlign) * 4;                           // ids, gates, sorted_assign, assign_pos
+    b += align_up(static_cast<size_t>(p.E) * 4, kAlign);       // counts
+    b += align_up(static_cast<size_t>(p.E + 1) * 4, kAlign);   // offsets
+    b += dispatch_ws(p);                                        // block counts
+    b += ffn_ws(p);                                             // h
+    b += align_up(n * p.d * elem_bytes(p), kAlign);             // y_perm
+    return b;
+}
+
+void clear_hip_error() { (void)hipGetLastError(); }
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int32_t status) {
+    switch (status) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_ERR_INVALID_ARGUMENT: return "MOE_ERR_INVALID_ARGUMENT";
+        case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+        case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
+        case MOE_ERR_HIP: return "MOE_ERR_HIP";
+        default: return "MOE_ERR_UNKNOWN";
+    }
+}
+
+int32_t moe_abi_version(void) { return kAbiVersion; }
+
+moe_status_t moe_workspace_size(const moe_problem_t* p, int32_t op, size_t* bytes) {
+    if (bytes == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+    MOE_TRY(check_problem(p));
+    switch (op) {
+        case MOE_OP_DISPATCH: *bytes = dispatch_ws(*p); break;
+        case MOE_OP_EXPERT_FFN: *bytes = ffn_ws(*p); break;
+        case MOE_OP_FORWARD: *bytes = forward_ws(*p); break;
+        default: return MOE_ERR_INVALID_ARGUMENT;
+    }
+    return MOE_OK;
+}
+
+moe_status_t moe_route(const moe_problem_t* p, const void* x, const void* w_router,
+                       const float* logits_in, float* logits_out, int32_t* topk_ids,
+                       float* topk_gates, void* stream) {
+    MOE_TRY(check_problem(p));
+    if (p->T == 0) return MOE_OK;
+    if (logits_in != nullptr) {
+        MOE_TRY(need(logits_in));
+    } else {
+        // the router GEMM writes its logits to logits_out, then top-k reads them
+        MOE_TRY(need(x));
+        MOE_TRY(need(w_router));
+        MOE_TRY(need(logits_out));
+    }
+    MOE_TRY(need(topk_ids));
+    MOE_TRY(need(topk_gates));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    clear_hip_error();
+    const float* l = logits_in;
+    if (l == nullptr) {
+        MOE_LAUNCH(launch_router_logits(*p, x, w_router, logits_out, s));
+        l = logits_out;
+    }
+    MOE_LAUNCH(launch_route_topk(*p, l, topk_ids, topk_gates, s));
+    return MOE_OK;
+}
+
+moe_status_t moe_dispatch(const moe_problem_t* p, const int32_t* topk_ids, const void* x,
+                          int32_t* counts, int32_t* offsets, int32_t* sorted_assign,
+                          int32_t* assign_pos, void* x_perm, void* ws, size_t ws_bytes,
+                          void* stream) {
+    MOE_TRY(check_problem(p));
+    if (p->T == 0) return MOE_OK;
+    MOE_TRY(need(topk_ids));
+    MOE_TRY(need(counts));
+    MOE_TRY(need(offsets));
+    MOE_TRY(need(sorted_assign));
+    MOE_TRY(need(assign_pos));
+    MOE_TRY(optional(x_perm));
+    if (x_perm != nullptr) MOE_TRY(need(x));
+    MOE_TRY(need(ws));
+    if (ws_bytes < dispatch_ws(*p)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    clear_hip_error();
+    MOE_LAUNCH(launch_dispatch_queues(*p, topk_ids, counts, offsets, sorted_assign, assign_pos,
+                                      static_cast<int32_t*>(ws), s));
+    if (x_perm != nullptr) MOE_LAUNCH(launch_gather_rows(*p, x, sorted_assign, offsets, x_perm, s));
+    return MOE_OK;
+}
+
+moe_status_t moe_expert_ffn(const moe_problem_t* p, const void* x_perm, const void* x,
+                            const int32_t* sorted_assign, const int32_t* offsets,
+                            const void* w_gate, const void* w_up, const void* w_down,
+                            void* y_perm, void* ws, size_t ws_bytes, void* stream) {
+    MOE_TRY(check_problem(p));
+    if (p->T == 0) return MOE_OK;
+    if (x_perm != nullptr) {
+        MOE_TRY(need(x_perm));
+    } else {
+        MOE_TRY(need(x));
+        MOE_TRY(need(sorted_assign));
+    }
+    MOE_TRY(need(offsets));
+    MOE_TRY(need(w_gate));
+    MOE_TRY(need(w_up));
+    MOE_TRY(need(w_down));
+    MOE_TRY(need(y_perm));
+    MOE_TRY(need(ws));
+    if (ws_bytes < ffn_ws(*p)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    clear_hip_error();
+    MOE_LAUNCH(launch_expert_ffn(*p, x_perm, x, sorted_assign, offsets, w_gate, w_up, w_down, ws,
+                                 y_perm, s));
+    return MOE_OK;
+}
+
+moe_status_t moe_combine(const moe_problem_t* p, const void* y_perm, const int32_t* assign_pos,
+                         const float* topk_gates, void* y, void* stream) {
+    MOE_TRY(check_problem(p));
+    if (p->T == 0) return MOE_OK;
+    MOE_TRY(need(y_perm));
+    MOE_TRY(need(assign_pos));
+    MOE_TRY(need(topk_gates));
+    MOE_TRY(need(y));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    clear_hip_error();
+    MOE_LAUNCH(launch_combine(*p, y_perm, assign_pos, topk_gates, y, s));
+    return MOE_OK;
+}
+
+moe_status_t moe_forward(const moe_problem_t* p, const void* x, const void* w_router,
+                         const float* logits_in, const void* w_gate, const void* w_up,
+                         const void* w_down, void* y, const moe_forward_outputs_t* out, void* ws,
+                         size_t ws_bytes, void* stream) {
+    MOE_TRY(check_problem(p));
+    if (p->T == 0) return MOE_OK;
+    MOE_TRY(need(x));
+    if (logits_in != nullptr) MOE_TRY(need(logits_in));
+    else MOE_TRY(need(w_router));
+    MOE_TRY(need(w_gate));
+    MOE_TRY(need(w_up));
+    MOE_TRY(need(w_down));
+    MOE_TRY(need(y));
+    moe_forward_outputs_t o = {};
+    if (out != nullptr) {
+        o = *out;
+        MOE_TRY(optional(o.logits));
+        MOE_TRY(optional(o.topk_ids));
+        MOE_TRY(optional(o.topk_gates));
+        MOE_TRY(optional(o.counts));
+        MOE_TRY(optional(o.offsets));
+        MOE_TRY(optional(o.sorted_assign));
+        MOE_TRY(optional(o.assign_pos));
+    }
+    MOE_TRY(need(ws));
+    if (ws_bytes < forward_ws(*p)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+
+    const size_t n = static_cast<size_t>(p->T) * p->k;
+    Carver c(ws);
+    float* logits = c.take<float>(static_cast<size_t>(p->T) * p->E * 4);
+    int32_t* ids = c.take<int32_t>(n * 4);
+    float* gates = c.take<float>(n * 4);
+    int32_t* sa = c.take<int32_t>(n * 4);
+    int32_t* ap = c.take<int32_t>(n * 4);
+    int32_t* counts = c.take<int32_t>(static_cast<size_t>(p->E) * 4);
+    int32_t* offsets = c.take<int32_t>(static_cast<size_t>(p->E + 1) * 4);
+    int32_t* bc = c.take<int32_t>(dispatch_ws(*p));
+    void* h = c.take<char>(ffn_ws(*p));
+    void* y_perm = c.take<char>(n * p->d * elem_bytes(*p));
+    if (o.logits) logits = o.logits;
+    if (o.topk_ids) ids = o.topk_ids;
+    if (o.topk_gates) gates = o.topk_gates;
+    if (o.sorted_assign) sa = o.sorted_assign;
+    if (o.assign_pos) ap = o.assign_pos;
+    if (o.counts) counts = o.counts;
+    if (o.offsets) offsets = o.offsets;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    clear_hip_error();
+    const float* l = logits_in;
+    if (l == nullptr) {
+        MOE_LAUNCH(launch_router_logits(*p, x, w_router, logits, s));
+        l = logits;
+    }
+    MOE_LAUNCH(launch_route_topk(*p, l, ids, gates, s));
+    MOE_LAUNCH(launch_dispatch_queues(*p, ids, counts, offsets, sa, ap, bc, s));
+    MOE_LAUNCH(launch_expert_ffn(*p, nullptr, x, sa, offsets, w_gate, w_up, w_down, h, y_perm, s));
+    MOE_LAUNCH(launch_combine(*p, y_perm, ap, gates, y, s));
+    return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,62 @@
+// Internal declarations of the MoE-layer HIP library (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+// ---- tuning constants --------------------------------------------------------
+
+// Assignments handled by one workgroup of the histogram and scatter kernels.
+constexpr int kDispatchChunk = 2048;
+
+// bf16 grouped GEMM: rows of the queue per tile, reduction step, columns.
+constexpr int kBM = 128;
+constexpr int kBK = 64;
+constexpr int kGateUpCols = 128;  // f-columns per GEMM1 tile (gate and up each)
+constexpr int kDownCols = 256;    // output columns per GEMM2 tile
+
+// f32 grouped GEMM tile.
+constexpr int kF32BM = 64;
+constexpr int kF32BN = 64;
+
+// ---- small host helpers ------------------------------------------------------
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+inline int64_t dispatch_blocks(int64_t n_assign) { return ceil_div(n_assign, kDispatchChunk); }
+
+// Upper bound of sum_e ceil(count_e / bm) over any routing of n rows to E experts.
+inline int64_t max_m_tiles(int64_t n_rows, int E, int bm) { return n_rows / bm + E; }
+
+// Largest 1-D grid the expert FFN launches for problem p (validated against
+// the hardware limit before any launch).
+int64_t expert_ffn_grid_bound(const moe_problem_t& p);
+
+// ---- launchers (return the launch status) ------------------------------------
+
+hipError_t launch_router_logits(const moe_problem_t& p, const void* x, const void* w_router,
+                                float* logits, hipStream_t s);
+hipError_t launch_route_topk(const moe_problem_t& p, const float* logits, int32_t* ids,
+                             float* gates, hipStream_t s);
+
+hipError_t launch_dispatch_queues(const moe_problem_t& p, const int32_t* ids, int32_t* counts,
+                                  int32_t* offsets, int32_t* sorted_assign, int32_t* assign_pos,
+                                  int32_t* block_counts, hipStream_t s);
+hipError_t launch_gather_rows(const moe_problem_t& p, const void* x, const int32_t* sorted_assign,
+                              const int32_t* offsets, void* x_perm, hipStream_t s);
+
+hipError_t launch_expert_ffn(const moe_problem_t& p, const void* x_perm, const void* x,
+                             const int32_t* sorted_assign, const int32_t* offsets,
+                             const void* w_gate, const void* w_up, const void* w_down,
+                             void* h, void* y_perm, hipStream_t s);
+
+hipError_t launch_combine(const moe_problem_t& p, const void* y_perm, const int32_t* assign_pos,
+                          const float* gates, void* y, hipStream_t s);
+
+}  // namespace moe

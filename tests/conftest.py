@@ -23,3 +23,12 @@ def gpu_available() -> bool:
 @pytest.fixture(scope="session")
 def root():
     return ROOT
+
+
+def pytest_collection_modifyitems(config, items):
+    if gpu_available():
+        return
+    skip = pytest.mark.skip(reason="no GPU in this process")
+    for item in items:
+        if "gpu" in item.keywords:
+            item.add_marker(skip)

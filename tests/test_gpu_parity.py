@@ -1,0 +1,362 @@
+"""Parity of the HIP path against the CPU oracle, element by element.
+
+* Routing and dispatch are bit-exact when both sides route from the same
+  supplied fp32 logits (ids, counts, offsets, sorted_assign, assign_pos,
+  x_perm); gates within 1e-6.
+* Router logits within max|dl| / max|l| <= 1e-5.
+* Expert FFN, combine and the whole layer within max|dy| / max|y_ref| <=
+  1e-5 (fp32) and 1e-2 (bf16), with the oracle in float64.
+* With the router on the GPU, GPU and oracle logits differ by rounding, so a
+  token whose k-th and (k+1)-th oracle logits lie closer than twice that
+  difference may legitimately pick another expert: such tokens are checked
+  for a valid choice instead of an identical one.
+* Full-size workloads run in the benchmark's launch configuration and are
+  checked on a seeded token sample the oracle computes one token at a time,
+  plus properties that hold at any size.
+Outputs are poisoned before each call so that an unwritten element fails.
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+import oracle as O
+import mixture_experts_layer_exclusive_amd as moe
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TOL = {"f32": 1e-5, "bf16": 1e-2}
+
+
+def dev(a, dtype=None):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(DEV)
+    return torch.from_numpy(a).to(DEV)
+
+
+def host(t):
+    if t.dtype == torch.bfloat16:
+        return t.float().cpu().numpy()
+    return t.cpu().numpy()
+
+
+def poison_i32(*shape):
+    return torch.full(shape, -7, dtype=torch.int32, device=DEV)
+
+
+def poison_f32(*shape):
+    return torch.full(shape, float("nan"), dtype=torch.float32, device=DEV)
+
+
+def poison(shape, dtype):
+    return torch.full(shape, float("nan"), dtype=dtype, device=DEV)
+
+
+def rel(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape
+    assert np.all(np.isfinite(got)), "non-finite output"
+    return float(np.max(np.abs(got - ref)) / max(np.max(np.abs(ref)), 1e-30))
+
+
+def logits_for(p, kind, seed=0):
+    if kind == "gauss":
+        return mi.make_gaussian_logits(p, seed)
+    if kind == "zipf":
+        return mi.make_zipf_logits(p, seed)
+    if kind == "ties":
+        return mi.make_tie_logits(p, seed)
+    raise ValueError(kind)
+
+
+def f32_of(a, dtype):
+    return mi.as_f32(a, dtype)
+
+
+# --------------------------------------------------------------------------
+# routing and dispatch: bit-exact on supplied logits
+# --------------------------------------------------------------------------
+
+ROUTE_CASES = [
+    (256, 8, 2, "gauss"), (8192, 8, 2, "gauss"), (16384, 64, 6, "gauss"),
+    (32768, 128, 8, "gauss"), (65536, 128, 8, "zipf"), (4099, 128, 8, "ties"),
+    (1000, 256, 32, "gauss"), (333, 3, 3, "ties"), (17, 1, 1, "gauss"), (1, 64, 5, "gauss"),
+    (777, 65, 7, "ties"), (2049, 200, 4, "zipf"),
+]
+
+
+@pytest.mark.parametrize("T,E,k,kind", ROUTE_CASES)
+def test_route_and_dispatch_bit_exact(T, E, k, kind):
+    print(f"route/dispatch T={T} E={E} k={k} {kind}", flush=True)
+    p = mi.Problem(T, 64, E, k, 64, "bf16")
+    l = logits_for(p, kind, seed=T + E)
+    ids_ref, g_ref = O.topk_route(l, k)
+    ids = poison_i32(T, k)
+    gates = poison_f32(T, k)
+    moe.route(k, logits=dev(l), ids=ids, gates=gates)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(ids), ids_ref)
+    assert np.max(np.abs(host(gates) - g_ref)) <= 1e-6
+
+    q = O.dispatch(ids_ref, E)
+    x = mi.make_x(p, seed=T)
+    out = dict(counts=poison_i32(E), offsets=poison_i32(E + 1), sorted_assign=poison_i32(T * k),
+               assign_pos=poison_i32(T * k), x_perm=poison((T * k, 64), torch.bfloat16))
+    moe.dispatch(dev(ids_ref), E, x=dev(x), with_x_perm=True, out=out)
+    torch.cuda.synchronize()
+    for key in ("counts", "offsets", "sorted_assign", "assign_pos"):
+        assert np.array_equal(host(out[key]), q[key]), key
+    xp = out["x_perm"].view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(xp, O.gather_rows(x, q["sorted_assign"], k))
+
+
+def test_dispatch_f32_rows_and_odd_width():
+    p = mi.Problem(300, 3, 5, 2, 7, "f32")
+    ids_ref, _ = O.topk_route(mi.make_tie_logits(p, 3), 2)
+    q = O.dispatch(ids_ref, 5)
+    x = mi.make_x(p, 3)
+    out = moe.dispatch(dev(ids_ref), 5, x=dev(x), with_x_perm=True,
+                       out=dict(x_perm=poison((600, 3), torch.float32)))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(out["sorted_assign"]), q["sorted_assign"])
+    assert np.array_equal(host(out["x_perm"]).view(np.uint32), O.gather_rows(x, q["sorted_assign"], 2).view(np.uint32))
+
+
+# --------------------------------------------------------------------------
+# router GEMM
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,d,E,dtype", [(256, 128, 8, "f32"), (1000, 4096, 8, "bf16"),
+                                         (777, 2048, 128, "bf16"), (300, 2048, 64, "bf16"),
+                                         (65, 100, 7, "f32"), (129, 192, 256, "bf16")])
+def test_router_logits(T, d, E, dtype):
+    p = mi.Problem(T, d, E, min(2, E), 64, dtype)
+    x = mi.make_x(p, 5)
+    wr = mi.make_router_weight(p, 5)
+    ref = O.router_logits(f32_of(x, dtype), f32_of(wr, dtype))
+    lo = poison_f32(T, E)
+    ids, gates, _ = moe.route(p.k, x=dev(x), w_router=dev(wr), logits_out=lo)
+    torch.cuda.synchronize()
+    assert rel(host(lo), ref) <= 1e-5
+
+
+# --------------------------------------------------------------------------
+# expert FFN and combine, from the oracle's queues
+# --------------------------------------------------------------------------
+
+FFN_CASES = [
+    (2000, 192, 4, 2, 320, "bf16", "gauss"),   # column tails in both GEMMs, many row tiles
+    (300, 256, 8, 2, 384, "bf16", "gauss"),
+    (1500, 512, 16, 4, 256, "bf16", "zipf"),   # skewed: empty and tiny experts
+    (64, 128, 128, 8, 64, "bf16", "gauss"),    # many experts, a few rows each
+    (256, 128, 8, 2, 256, "f32", "gauss"),
+    (200, 100, 6, 3, 70, "f32", "ties"),
+    (1, 64, 8, 2, 64, "bf16", "gauss"),
+]
+
+
+@pytest.mark.parametrize("T,d,E,k,f,dtype,kind", FFN_CASES)
+@pytest.mark.parametrize("fused_gather", [True, False])
+def test_expert_ffn_and_combine(T, d, E, k, f, dtype, kind, fused_gather):
+    print(f"ffn T={T} d={d} E={E} k={k} f={f} {dtype} {kind} fused={fused_gather}", flush=True)
+    p = mi.Problem(T, d, E, k, f, dtype)
+    L = mi.make_layer(p, seed=T + d)
+    x32 = f32_of(L["x"], dtype)
+    wg, wu, wd = (f32_of(L[n], dtype) for n in ("w_gate", "w_up", "w_down"))
+    ids, gates = O.topk_route(logits_for(p, kind, T), k)
+    q = O.dispatch(ids, E)
+    yp_ref = O.expert_ffn(x32, q["sorted_assign"], q["offsets"], k, wg, wu, wd)
+
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    xd = dev(L["x"])
+    sa = dev(q["sorted_assign"])
+    offs = dev(q["offsets"])
+    y_perm = poison((T * k, d), tdt)
+    if fused_gather:
+        moe.expert_ffn(offs, dev(L["w_gate"]), dev(L["w_up"]), dev(L["w_down"]), k, T, x=xd,
+                       sorted_assign=sa, y_perm=y_perm)
+    else:
+        xp = dev(O.gather_rows(L["x"], q["sorted_assign"], k))
+        moe.expert_ffn(offs, dev(L["w_gate"]), dev(L["w_up"]), dev(L["w_down"]), k, T, x_perm=xp,
+                       y_perm=y_perm)
+    torch.cuda.synchronize()
+    assert rel(host(y_perm), yp_ref) <= TOL[dtype]
+
+    # combine from the oracle's expert outputs rounded to the storage dtype
+    yp_in = yp_ref.astype(np.float32)
+    if dtype == "bf16":
+        yp_in = mi.f32_to_bf16_bits(yp_in)
+    y_ref = O.combine(f32_of(yp_in, dtype), q["assign_pos"], gates)
+    y = poison((T, d), tdt)
+    moe.combine(dev(yp_in), dev(q["assign_pos"]), dev(gates), y=y)
+    torch.cuda.synchronize()
+    assert rel(host(y), y_ref) <= (1e-6 if dtype == "f32" else 4e-3)
+
+
+# --------------------------------------------------------------------------
+# the whole layer
+# --------------------------------------------------------------------------
+
+def run_forward(L, logits=None, k=None):
+    p = L["problem"]
+    y, inter = moe.forward(dev(L["x"]), dev(L["w_gate"]), dev(L["w_up"]), dev(L["w_down"]),
+                           k or p.k, w_router=None if logits is not None else dev(L["w_router"]),
+                           logits=None if logits is None else dev(logits), intermediates=True)
+    torch.cuda.synchronize()
+    return y, inter
+
+
+@pytest.mark.parametrize("T,d,E,k,f,dtype,kind", [
+    (600, 256, 8, 2, 512, "bf16", "gauss"), (1000, 128, 64, 6, 192, "bf16", "zipf"),
+    (256, 128, 8, 2, 256, "f32", "ties"), (50, 64, 4, 4, 128, "bf16", "gauss"),
+    (33, 64, 1, 1, 64, "bf16", "gauss"), (1, 128, 128, 8, 64, "bf16", "gauss"),
+])
+def test_forward_supplied_logits(T, d, E, k, f, dtype, kind):
+    print(f"forward logits T={T} d={d} E={E} k={k} f={f} {dtype}", flush=True)
+    p = mi.Problem(T, d, E, k, f, dtype)
+    L = mi.make_layer(p, seed=d + E)
+    l = logits_for(p, kind, seed=f)
+    ref = O.forward(f32_of(L["x"], dtype), k, *(f32_of(L[n], dtype) for n in ("w_gate", "w_up", "w_down")),
+                    logits=l)
+    y, inter = run_forward(L, logits=l)
+    for key, rkey in (("topk_ids", "ids"), ("counts", "counts"), ("offsets", "offsets"),
+                      ("sorted_assign", "sorted_assign"), ("assign_pos", "assign_pos")):
+        assert np.array_equal(host(inter[key]).reshape(ref[rkey].shape), ref[rkey]), key
+    assert np.max(np.abs(host(inter["topk_gates"]) - ref["gates"])) <= 1e-6
+    assert rel(host(y), ref["y"]) <= TOL[dtype]
+
+
+def margins(l, k):
+    """Gap between the k-th and (k+1)-th largest logit per token (inf if k == E)."""
+    s = -np.sort(-l.astype(np.float64), axis=1)
+    if k >= l.shape[1]:
+        return np.full(l.shape[0], np.inf)
+    return s[:, k - 1] - s[:, k]
+
+
+def check_routing_with_router(l_gpu, ids_gpu, l_ref, k):
+    """Router parity, then ids equal wherever the oracle's top-k margin exceeds
+    twice the logit difference; elsewhere the GPU choice must be a valid top-k
+    of the oracle logits within that difference.  Returns the safe-token mask."""
+    assert rel(l_gpu, l_ref) <= 1e-5
+    dl = np.max(np.abs(l_gpu.astype(np.float64) - l_ref), axis=1)
+    ids_ref, _ = O.topk_route(l_ref, k)
+    safe = margins(l_ref, k) > 2 * dl + 1e-12
+    assert np.array_equal(ids_gpu[safe], ids_ref[safe])
+    kth = -np.sort(-l_ref.astype(np.float64), axis=1)[:, k - 1]
+    chosen = np.take_along_axis(l_ref.astype(np.float64), ids_gpu.astype(np.int64), 1)
+    assert np.all(chosen >= kth[:, None] - 2 * dl[:, None] - 1e-12)
+    return safe
+
+
+def test_forward_tiny_f32_with_router():
+    L = mi.make_layer("tiny_f32", seed=0)
+    p = L["problem"]
+    ref = O.forward(L["x"], p.k, L["w_gate"], L["w_up"], L["w_down"], w_router=L["w_router"])
+    y, inter = run_forward(L)
+    safe = check_routing_with_router(host(inter["logits"]), host(inter["topk_ids"]), ref["logits"], p.k)
+    assert safe.mean() > 0.99
+    assert rel(host(y)[safe], ref["y"][safe]) <= 1e-5
+    # run twice: bitwise identical
+    y2, _ = run_forward(L)
+    assert torch.equal(y, y2)
+
+
+def test_identical_experts_give_dense_ffn():
+    p = mi.Problem(512, 256, 8, 2, 384, "bf16")
+    L = mi.make_layer(p, seed=2)
+    for n in ("w_gate", "w_up", "w_down"):
+        L[n] = np.ascontiguousarray(np.repeat(L[n][:1], p.E, 0))
+    dense = O.swiglu_expert(f32_of(L["x"], "bf16"), *(f32_of(L[n][0], "bf16") for n in ("w_gate", "w_up", "w_down")))
+    y, _ = run_forward(L)
+    assert rel(host(y), dense) <= 1e-2
+
+
+def test_forward_twice_is_bitwise_identical():
+    p = mi.Problem(3000, 512, 64, 6, 256, "bf16")
+    L = mi.make_layer(p, seed=4)
+    y1, i1 = run_forward(L)
+    y2, i2 = run_forward(L)
+    assert torch.equal(y1, y2)
+    for key in i1:
+        assert torch.equal(i1[key], i2[key]), key
+
+
+def test_zero_tokens_noop():
+    p = mi.Problem(1, 128, 8, 2, 64, "bf16")
+    L = mi.make_layer(p, seed=1)
+    x = dev(L["x"])[:0]
+    y = moe.forward(x, dev(L["w_gate"]), dev(L["w_up"]), dev(L["w_down"]), 2, w_router=dev(L["w_router"]))
+    torch.cuda.synchronize()
+    assert y.shape == (0, 128)
+
+
+# --------------------------------------------------------------------------
+# full-size workloads, in the benchmark's launch configuration
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["mixtral_8x_bf16", "deepseek_moe_bf16", "qwen3_moe_bf16", "zipf_skewed_bf16"])
+def test_full_size_workload_sampled(name):
+    print(f"full-size {name}: generating inputs", flush=True)
+    L = mi.make_layer(name, seed=0)
+    p = L["problem"]
+    dt = p.dtype
+    sample = mi.sample_tokens(p.T, 48, seed=0)
+    xg = dev(L["x"])
+    wg, wu, wd = dev(L["w_gate"]), dev(L["w_up"]), dev(L["w_down"])
+    wr = dev(L["w_router"]) if L["w_router"] is not None else None
+    lg = dev(L["logits"]) if L["logits"] is not None else None
+    ws = torch.empty(moe.workspace_size(moe.problem(p.T, p.d, p.E, p.k, p.f, torch.bfloat16), 3),
+                     dtype=torch.uint8, device=DEV)
+    y = poison((p.T, p.d), torch.bfloat16)
+    print(f"full-size {name}: forward", flush=True)
+    _, inter = moe.forward(xg, wg, wu, wd, p.k, w_router=wr, logits=lg, intermediates=True, ws=ws, y=y)
+    torch.cuda.synchronize()
+    del xg, wg, wu, wd
+    ids_gpu = host(inter["topk_ids"])
+    yh = host(y)
+    assert np.all(np.isfinite(yh))
+
+    # routing: exact on supplied logits, else the margin protocol over all tokens
+    x32 = f32_of(L["x"], dt)
+    if L["logits"] is not None:
+        l_ref = L["logits"]
+        ids_ref, g_ref = O.topk_route(l_ref, p.k)
+        assert np.array_equal(ids_gpu, ids_ref)
+        assert np.max(np.abs(host(inter["topk_gates"]) - g_ref)) <= 1e-6
+        safe = np.ones(p.T, dtype=bool)
+    else:
+        l_ref = O.router_logits(x32, f32_of(L["w_router"], dt))
+        safe = check_routing_with_router(host(inter["logits"]), ids_gpu, l_ref, p.k)
+        ids_ref, _ = O.topk_route(l_ref, p.k)
+    print(f"full-size {name}: {int((~safe).sum())} near-tie tokens", flush=True)
+    assert (~safe).mean() < 0.01
+
+    # dispatch: bit-exact when routing agrees everywhere, else valid for the GPU's own ids
+    counts = host(inter["counts"])
+    offsets = host(inter["offsets"])
+    sa = host(inter["sorted_assign"])
+    ap = host(inter["assign_pos"])
+    if np.array_equal(ids_gpu, ids_ref):
+        q = O.dispatch(ids_ref, p.E)
+        for key, v in (("counts", counts), ("offsets", offsets), ("sorted_assign", sa), ("assign_pos", ap)):
+            assert np.array_equal(v, q[key]), key
+    else:
+        flat = ids_gpu.reshape(-1)
+        assert counts.sum() == p.T * p.k and offsets[-1] == p.T * p.k
+        assert np.array_equal(np.diff(offsets), counts)
+        assert np.array_equal(ap[sa], np.arange(p.T * p.k))
+        for e in range(p.E):
+            seg = sa[offsets[e]:offsets[e + 1]]
+            assert np.all(flat[seg] == e) and np.all(np.diff(seg) > 0)
+
+    # values on the sampled tokens, one token at a time in the oracle
+    tok = sample[safe[sample]]
+    get = {n: (lambda a: (lambda e: f32_of(a[e], dt)))(L[n]) for n in ("w_gate", "w_up", "w_down")}
+    print(f"full-size {name}: oracle on {len(tok)} sampled tokens", flush=True)
+    ref = O.forward_tokens(tok, x32, l_ref, p.k, get["w_gate"], get["w_up"], get["w_down"])
+    err = rel(yh[tok], ref["y"])
+    print(f"full-size {name}: max|dy|/max|y| on sample = {err:.3e}", flush=True)
+    assert err <= TOL[dt]
