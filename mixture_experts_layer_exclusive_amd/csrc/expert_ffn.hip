@@ -36,6 +36,17 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 constexpr int GROUP_M = 8;
 constexpr int NUM_XCD = 8;
 
+// bf16 GEMM pipeline shape: K slice width, LDS ring depth, slot swizzle.
+#ifndef GEMM_BK
+#define GEMM_BK 64
+#endif
+#ifndef GEMM_STAGES
+#define GEMM_STAGES 2
+#endif
+#ifndef GEMM_SWZ
+#define GEMM_SWZ 0
+#endif
+
 // Per-expert tile prefix in LDS: s_prefix[e] = sum_{e' < e} ceil(rows_e' / bm),
 // s_prefix[E] = total row tiles.  Computed by wave 0.
 __device__ __forceinline__ void build_tile_prefix(const int32_t* __restrict__ offsets, int E, int bm,
@@ -108,58 +119,114 @@ __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.f + 
 // ---------------------------------------------------------------------------
 // bf16 grouped GEMM on MFMA (v_mfma_f32_32x32x16_bf16)
 //
-// Tile: 128 queue rows x 256 B rows (GEMM1: 128 gate rows + the same 128 up
-// rows; GEMM2: 256 W_down rows), K step 64, both operands K-contiguous.
-// 4 waves in 2 x 2; a wave owns 64 rows x 128 B rows = 2 x 4 MFMA blocks of
-// 32 x 32 (in GEMM1, blocks 0-1 are gate and 2-3 the matching up columns, so
-// the SwiGLU pairs sit in the same lane and register).  Operands are staged
-// through double-buffered LDS with rows padded by 16 bytes, which makes the
-// 16-byte fragment reads of 32 consecutive rows conflict-free.
+// Tile: 256 queue rows ("activation rows", A) x 256 weight rows (B): in GEMM1
+// the 256 weight rows are 128 W_gate rows and the same 128 W_up rows, so the
+// tile yields 256 x 128 of h; in GEMM2 they are 256 W_down rows.  Both
+// operands are contiguous along K.
+//
+// 4 waves in 2 x 2.  Wave (wm, wn) owns activation rows wm*128 .. +128 and
+// weight rows (GEMM2) wn*128 .. +128, or (GEMM1) gate rows wn*64 .. +64 plus
+// the matching up rows.  It keeps 4 x 4 accumulators of 32 x 32 (256 fp32
+// per lane).  The MFMA takes the weight fragment as its first operand and the
+// activation fragment as its second, so an accumulator holds C^T: each lane
+// owns one output row and runs of 4 consecutive output columns, which become
+// 8-byte stores, and in GEMM1 the gate and up values of one h element sit in
+// the same lane and register of blocks nb and nb + 2.
+//
+// Operand staging: global_load_lds_dwordx4 copies 16 bytes per lane straight
+// into LDS (no register round trip) into an NSTAGE-deep ring of K slices of
+// width BK.  Each row of a slice is BK/8 16-byte slots, and the slot that
+// holds chunk c of row r is c ^ swz(r), which spreads the 16-byte fragment
+// reads of consecutive rows over all LDS banks.  One barrier per K step: it
+// publishes slice kt and frees the slot that slice kt + NSTAGE - 1 refills.
+// Rows past the end of an expert's queue (or past N) load a clamped valid row
+// and their results are never stored.
 // ---------------------------------------------------------------------------
-constexpr int LDT = kBK + 8;  // padded LDS row, in bf16 elements
-constexpr int B_ROWS = 256;
+typedef uint16_t bf16x4_t __attribute__((ext_vector_type(4)));
 
-template <bool GATEUP, bool GATHER>
-__global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
+template <int BK, int SWZ>
+__device__ __forceinline__ int swz(int r) {
+    // BK = 64: 8 slots per row; BK = 32: 4 slots per row
+    if (BK == 64) return SWZ == 0 ? (r & 7) : ((r >> 1) & 7);
+    return SWZ == 0 ? ((r >> 1) & 3) : ((r >> 2) & 3);
+}
+
+// s_waitcnt with only the vector-memory counter limited (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane i's bytes land
+// at LDS address lds_base + 16 * i.  Issued as inline assembly so that the
+// compiler does not treat every later LDS read as dependent on it; the caller
+// orders it with wait_vmcnt and the workgroup barrier.
+__device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_base) {
+    asm volatile(
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, off"
+        :
+        : "v"(gptr), "s"(lds_base)
+        : "memory");
+}
+
+// Workgroup barrier without a memory fence (the LDS traffic it orders is
+// waited for explicitly); the empty asm statements keep the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void barrier_lds() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+
+template <bool GATEUP, bool GATHER, int BK, int NSTAGE, int SWZ>
+__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void grouped_gemm_bf16_kernel(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ sorted_assign, int topk,
     const int32_t* __restrict__ offsets, int E, const bf16_t* __restrict__ B0,
     const bf16_t* __restrict__ B1, bf16_t* __restrict__ C, int N, int K) {
-    constexpr int BN_OUT = GATEUP ? kGateUpCols : kDownCols;
-    __shared__ __attribute__((aligned(16))) bf16_t sA[2][kBM * LDT];
-    __shared__ __attribute__((aligned(16))) bf16_t sB[2][B_ROWS * LDT];
+    constexpr int TM = 256;                 // activation rows (and weight rows) per tile
+    constexpr int BN_OUT = GATEUP ? 128 : 256;
+    constexpr int CH = BK / 8;              // 16-byte chunks per row
+    constexpr int RPI = 64 / CH;            // rows per load instruction
+    constexpr int LPW = 64 / RPI;           // load instructions per wave per operand
+    constexpr int SLICE = TM * BK;          // bf16 elements per operand slice
+    __shared__ __attribute__((aligned(1024))) bf16_t sA[NSTAGE][SLICE];
+    __shared__ __attribute__((aligned(1024))) bf16_t sB[NSTAGE][SLICE];
     __shared__ int s_prefix[MOE_MAX_EXPERTS + 1];
 
-    build_tile_prefix(offsets, E, kBM, s_prefix);
+    build_tile_prefix(offsets, E, TM, s_prefix);
     const int n_tiles = (N + BN_OUT - 1) / BN_OUT;
     Tile tile;
-    if (!find_tile(offsets, E, kBM, n_tiles, s_prefix, tile)) return;
+    if (!find_tile(offsets, E, TM, n_tiles, s_prefix, tile)) return;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wm = wave >> 1;
     const int wn = wave & 1;
-    const int cc = tid & 7;         // 16-byte column chunk this thread loads
-    const int rbase = tid >> 3;     // first row this thread loads (then +32, +64, ...)
     const int n0 = tile.nt * BN_OUT;
     const int64_t NK = static_cast<int64_t>(N) * K;
 
-    // global source rows of this thread's A and B chunks
-    const bf16_t* a_src[4];
-    bool a_ok[4];
+    // Per-lane global sources: wave w fills tile rows w*64 .. w*64+63 of both
+    // operands; load j covers rows w*64 + j*RPI .. +RPI, lane -> (row, slot).
+    const int lrow = lane / CH;
+    const int lslot = lane % CH;
+    const bf16_t* a_src[LPW];
+    const bf16_t* b_src[LPW];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int pos = tile.row0 + rbase + 32 * i;
-        a_ok[i] = pos < tile.row1;
-        int64_t row = pos;
-        if (GATHER) row = a_ok[i] ? sorted_assign[pos] / topk : 0;
-        a_src[i] = A + (a_ok[i] ? row : 0) * K + cc * 8;
-    }
-    const bf16_t* b_src[8];
-    bool b_ok[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int r = rbase + 32 * i;
+    for (int j = 0; j < LPW; ++j) {
+        const int r = wave * 64 + j * RPI + lrow;       // tile row 0..255
+        const int chunk = lslot ^ swz<BK, SWZ>(r);      // global chunk for this LDS slot
+        int pos = tile.row0 + r;
+        if (pos >= tile.row1) pos = tile.row1 - 1;
+        const int64_t arow = GATHER ? static_cast<int64_t>(sorted_assign[pos] / topk) : pos;
+        a_src[j] = A + arow * K + chunk * 8;
         int n;
         const bf16_t* base;
         if (GATEUP) {
@@ -169,96 +236,137 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
             n = n0 + r;
             base = B0 + tile.e * NK;
         }
-        b_ok[i] = n < N;
-        b_src[i] = base + static_cast<int64_t>(b_ok[i] ? n : 0) * K + cc * 8;
+        if (n >= N) n = N - 1;
+        b_src[j] = base + static_cast<int64_t>(n) * K + chunk * 8;
     }
 
-    uint4 ra[4], rb[8];
-    const uint4 zero = make_uint4(0, 0, 0, 0);
-    auto gload = [&](int k0) {
+    const uint32_t lds_a0 = __builtin_amdgcn_readfirstlane(lds_addr(&sA[0][wave * 64 * BK]));
+    const uint32_t lds_b0 = __builtin_amdgcn_readfirstlane(lds_addr(&sB[0][wave * 64 * BK]));
+    auto load_slice = [&](int kt) {
+        const uint32_t boff = static_cast<uint32_t>((kt % NSTAGE) * SLICE * 2);
+        const int k0 = kt * BK;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            ra[i] = a_ok[i] ? *reinterpret_cast<const uint4*>(a_src[i] + k0) : zero;
+        for (int j = 0; j < LPW; ++j)
+            lds_dma16(a_src[j] + k0, lds_a0 + boff + j * RPI * BK * 2);
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            rb[i] = b_ok[i] ? *reinterpret_cast<const uint4*>(b_src[i] + k0) : zero;
-    };
-    auto lstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<uint4*>(&sA[buf][(rbase + 32 * i) * LDT + cc * 8]) = ra[i];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            *reinterpret_cast<uint4*>(&sB[buf][(rbase + 32 * i) * LDT + cc * 8]) = rb[i];
+        for (int j = 0; j < LPW; ++j)
+            lds_dma16(b_src[j] + k0, lds_b0 + boff + j * RPI * BK * 2);
     };
 
-    f32x16_t acc[2][4];
+    f32x16_t acc[4][4];
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+    for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int n = 0; n < 4; ++n)
+        for (int b = 0; b < 4; ++b)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[m][n][r] = 0.f;
+            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-    // LDS rows this lane reads for its fragments
-    const int a_row0 = wm * 64 + (lane & 31);
-    int b_row[4];
+    // fragment rows this lane reads
+    int brow[4], arow_l[4];
 #pragma unroll
-    for (int n = 0; n < 4; ++n)
-        b_row[n] = GATEUP ? ((n >> 1) * 128 + wn * 64 + (n & 1) * 32 + (lane & 31))
-                          : (wn * 128 + n * 32 + (lane & 31));
-    const int kq = (lane >> 5) * 8;
+    for (int nb = 0; nb < 4; ++nb)
+        brow[nb] = GATEUP ? ((nb >> 1) * 128 + wn * 64 + (nb & 1) * 32 + (lane & 31))
+                          : (wn * 128 + nb * 32 + (lane & 31));
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) arow_l[mb] = wm * 128 + mb * 32 + (lane & 31);
+    const int khalf = lane >> 5;
 
-    const int nk = K / kBK;
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) gload((kt + 1) * kBK);
+    const int nk = K / BK;
 #pragma unroll
-        for (int kk = 0; kk < kBK / 16; ++kk) {
-            bf16x8_t af[2], bfr[4];
+    for (int s = 0; s < NSTAGE - 1; ++s)
+        if (s < nk) load_slice(s);
+
+    // LDS element offsets (within a slice) of this lane's fragment rows, per
+    // K step kk of the slice
+    constexpr int KS = BK / 16;
+    int boffs[KS][4], aoffs[KS][4];
 #pragma unroll
-            for (int m = 0; m < 2; ++m)
-                af[m] = *reinterpret_cast<const bf16x8_t*>(&sA[buf][(a_row0 + m * 32) * LDT + kk * 16 + kq]);
+    for (int kk = 0; kk < KS; ++kk) {
+        const int c = kk * 2 + khalf;
 #pragma unroll
-            for (int n = 0; n < 4; ++n)
-                bfr[n] = *reinterpret_cast<const bf16x8_t*>(&sB[buf][b_row[n] * LDT + kk * 16 + kq]);
-#pragma unroll
-            for (int m = 0; m < 2; ++m)
-#pragma unroll
-                for (int n = 0; n < 4; ++n)
-                    acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[m], bfr[n], acc[m][n], 0, 0, 0);
+        for (int i = 0; i < 4; ++i) {
+            boffs[kk][i] = brow[i] * BK + ((c ^ swz<BK, SWZ>(brow[i])) * 8);
+            aoffs[kk][i] = arow_l[i] * BK + ((c ^ swz<BK, SWZ>(arow_l[i])) * 8);
         }
-        if (kt + 1 < nk) lstore(buf ^ 1);
-        __syncthreads();
     }
 
-    // epilogue: lane holds column (lane & 31) and rows 8*(r/4) + 4*(lane/32) + r%4
-    // of every 32 x 32 block
-    const int col_in = lane & 31;
-    const int row_q = (lane >> 5) * 4;
+    for (int kt = 0; kt < nk; ++kt) {
+        if (kt + NSTAGE - 2 < nk) wait_vmcnt<2 * LPW * (NSTAGE - 2)>();
+        else wait_vmcnt<0>();
+        barrier_lds();
+        if (kt + NSTAGE - 1 < nk) load_slice(kt + NSTAGE - 1);
+        const int buf = kt % NSTAGE;
+        const bf16_t* sa = sA[buf];
+        const bf16_t* sb = sB[buf];
+        bf16x8_t bfr[2][4], afr[2][4];
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
+        for (int i = 0; i < 4; ++i) {
+            bfr[0][i] = *reinterpret_cast<const bf16x8_t*>(sb + boffs[0][i]);
+            afr[0][i] = *reinterpret_cast<const bf16x8_t*>(sa + aoffs[0][i]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int pos = tile.row0 + wm * 64 + m * 32 + (r >> 2) * 8 + row_q + (r & 3);
-            if (pos >= tile.row1) continue;
-            bf16_t* crow = C + static_cast<int64_t>(pos) * N;
-            if (GATEUP) {
+        for (int kk = 0; kk < KS; ++kk) {
+            const int cur = kk & 1;
+            if (kk + 1 < KS) {
 #pragma unroll
-                for (int n = 0; n < 2; ++n) {
-                    const int col = n0 + wn * 64 + n * 32 + col_in;
-                    if (col < N) crow[col] = f32_to_bf16(silu_mul(acc[m][n][r], acc[m][n + 2][r]));
-                }
-            } else {
-#pragma unroll
-                for (int n = 0; n < 4; ++n) {
-                    const int col = n0 + wn * 128 + n * 32 + col_in;
-                    if (col < N) crow[col] = f32_to_bf16(acc[m][n][r]);
+                for (int i = 0; i < 4; ++i) {
+                    bfr[cur ^ 1][i] = *reinterpret_cast<const bf16x8_t*>(sb + boffs[kk + 1][i]);
+                    afr[cur ^ 1][i] = *reinterpret_cast<const bf16x8_t*>(sa + aoffs[kk + 1][i]);
                 }
             }
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+                for (int mb = 0; mb < 4; ++mb)
+                    acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[cur][nb], afr[cur][mb],
+                                                                        acc[nb][mb], 0, 0, 0);
+            // spread the next step's 8 fragment reads over this step's 16 MFMAs
+            if (kk + 1 < KS) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    // Epilogue.  Block (nb, mb): lane owns output row m = mb*32 + (lane & 31)
+    // and, for g = 0..3, columns nb*32 + 8g + 4*(lane >> 5) + 0..3 (registers
+    // 4g .. 4g+3).
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+        const int pos = tile.row0 + wm * 128 + mb * 32 + (lane & 31);
+        if (pos >= tile.row1) continue;
+        bf16_t* crow = C + static_cast<int64_t>(pos) * N;
+        if (GATEUP) {
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int col = n0 + wn * 64 + nb * 32 + 8 * g + 4 * khalf;
+                    if (col >= N) continue;
+                    bf16x4_t o;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        o[i] = f32_to_bf16(silu_mul(acc[nb][mb][4 * g + i], acc[nb + 2][mb][4 * g + i]));
+                    *reinterpret_cast<bf16x4_t*>(crow + col) = o;
+                }
+        } else {
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int col = n0 + wn * 128 + nb * 32 + 8 * g + 4 * khalf;
+                    if (col >= N) continue;
+                    bf16x4_t o;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) o[i] = f32_to_bf16(acc[nb][mb][4 * g + i]);
+                    *reinterpret_cast<bf16x4_t*>(crow + col) = o;
+                }
         }
     }
 }
@@ -382,15 +490,15 @@ hipError_t launch_expert_ffn(const moe_problem_t& p, const void* x_perm, const v
         const bf16_t* a = static_cast<const bf16_t*>(gather ? x : x_perm);
         const unsigned g1 = grid_for(n, p.E, kBM, static_cast<int>(ceil_div(p.f, kGateUpCols)));
         if (gather)
-            grouped_gemm_bf16_kernel<true, true><<<g1, 256, 0, s>>>(
+            grouped_gemm_bf16_kernel<true, true, GEMM_BK, GEMM_STAGES, GEMM_SWZ><<<g1, 256, 0, s>>>(
                 a, sorted_assign, p.k, offsets, p.E, static_cast<const bf16_t*>(w_gate),
                 static_cast<const bf16_t*>(w_up), static_cast<bf16_t*>(h), p.f, p.d);
         else
-            grouped_gemm_bf16_kernel<true, false><<<g1, 256, 0, s>>>(
+            grouped_gemm_bf16_kernel<true, false, GEMM_BK, GEMM_STAGES, GEMM_SWZ><<<g1, 256, 0, s>>>(
                 a, sorted_assign, p.k, offsets, p.E, static_cast<const bf16_t*>(w_gate),
                 static_cast<const bf16_t*>(w_up), static_cast<bf16_t*>(h), p.f, p.d);
         const unsigned g2 = grid_for(n, p.E, kBM, static_cast<int>(ceil_div(p.d, kDownCols)));
-        grouped_gemm_bf16_kernel<false, false><<<g2, 256, 0, s>>>(
+        grouped_gemm_bf16_kernel<false, false, GEMM_BK, GEMM_STAGES, GEMM_SWZ><<<g2, 256, 0, s>>>(
             static_cast<const bf16_t*>(h), sorted_assign, p.k, offsets, p.E,
             static_cast<const bf16_t*>(w_down), nullptr, static_cast<bf16_t*>(y_perm), p.d, p.f);
     } else {

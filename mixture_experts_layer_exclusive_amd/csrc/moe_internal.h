@@ -13,9 +13,8 @@ namespace moe {
 // Assignments handled by one workgroup of the histogram and scatter kernels.
 constexpr int kDispatchChunk = 2048;
 
-// bf16 grouped GEMM: rows of the queue per tile, reduction step, columns.
-constexpr int kBM = 128;
-constexpr int kBK = 64;
+// bf16 grouped GEMM: queue rows per tile, output columns per tile.
+constexpr int kBM = 256;
 constexpr int kGateUpCols = 128;  // f-columns per GEMM1 tile (gate and up each)
 constexpr int kDownCols = 256;    // output columns per GEMM2 tile
 
