@@ -39,7 +39,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mixtral_8x_bf16")
-    ap.add_argument("--cpu-tokens", type=int, default=2048,
+    ap.add_argument("--cpu-tokens", type=int, default=8192,
                     help="tokens of the workload the CPU oracle runs for the baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",

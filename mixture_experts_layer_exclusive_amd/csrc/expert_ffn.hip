@@ -33,7 +33,10 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int GROUP_M = 8;
+#ifndef GEMM_GROUP_M
+#define GEMM_GROUP_M 8
+#endif
+constexpr int GROUP_M = GEMM_GROUP_M;
 constexpr int NUM_XCD = 8;
 
 // bf16 GEMM pipeline shape: K slice width, LDS ring depth, slot swizzle.
@@ -44,7 +47,7 @@ constexpr int NUM_XCD = 8;
 #define GEMM_STAGES 2
 #endif
 #ifndef GEMM_SWZ
-#define GEMM_SWZ 0
+#define GEMM_SWZ 1
 #endif
 
 // Per-expert tile prefix in LDS: s_prefix[e] = sum_{e' < e} ceil(rows_e' / bm),
@@ -156,6 +159,13 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// s_waitcnt: vector-memory counter <= N and all LDS reads returned.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
 }
 
 // 16 bytes per lane from global memory straight into LDS: lane i's bytes land
@@ -271,11 +281,6 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     for (int mb = 0; mb < 4; ++mb) arow_l[mb] = wm * 128 + mb * 32 + (lane & 31);
     const int khalf = lane >> 5;
 
-    const int nk = K / BK;
-#pragma unroll
-    for (int s = 0; s < NSTAGE - 1; ++s)
-        if (s < nk) load_slice(s);
-
     // LDS element offsets (within a slice) of this lane's fragment rows, per
     // K step kk of the slice
     constexpr int KS = BK / 16;
@@ -290,49 +295,72 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         }
     }
 
+    const int nk = K / BK;
+    constexpr int PER = 2 * LPW;  // LDS DMA instructions per slice per wave
+    static_assert(KS % 2 == 0, "fragment double buffer needs an even step count");
+
+    // fragments of one K step: 4 weight blocks, 4 activation blocks, two sets
+    bf16x8_t fb[2][4], fa[2][4];
+#define MOE_READ_FRAGS(SB, SA, KK, SLOT)                                               \
+    _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                                 \
+        fb[SLOT][i_] = *reinterpret_cast<const bf16x8_t*>((SB) + boffs[KK][i_]);     \
+        fa[SLOT][i_] = *reinterpret_cast<const bf16x8_t*>((SA) + aoffs[KK][i_]);     \
+    }
+#define MOE_MFMA_STEP(SLOT)                                                            \
+    _Pragma("unroll") for (int nb_ = 0; nb_ < 4; ++nb_)                                \
+    _Pragma("unroll") for (int mb_ = 0; mb_ < 4; ++mb_)                                \
+        acc[nb_][mb_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[SLOT][nb_], fa[SLOT][mb_], \
+                                                                acc[nb_][mb_], 0, 0, 0);
+    // spread 8 LDS fragment reads over 16 MFMAs
+#define MOE_INTERLEAVE()                                                               \
+    _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) {                                 \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                             \
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                             \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                             \
+    }
+
+    // Ring of NSTAGE slices.  Slice kt's barrier sits before its last K step:
+    // by then every fragment of slice kt is in registers, so the barrier both
+    // frees slot kt % NSTAGE for slice kt + NSTAGE and publishes slice kt + 1,
+    // whose first fragments are read while the last MFMAs of slice kt run.
+#pragma unroll
+    for (int s = 0; s < NSTAGE; ++s)
+        if (s < nk) load_slice(s);
+    if (nk >= NSTAGE) wait_vmcnt_lgkm0<PER * (NSTAGE - 1)>();
+    else wait_vmcnt_lgkm0<0>();
+    barrier_lds();
+    MOE_READ_FRAGS(sB[0], sA[0], 0, 0)
+    __builtin_amdgcn_sched_barrier(0);
+
     for (int kt = 0; kt < nk; ++kt) {
-        if (kt + NSTAGE - 2 < nk) wait_vmcnt<2 * LPW * (NSTAGE - 2)>();
-        else wait_vmcnt<0>();
-        barrier_lds();
-        if (kt + NSTAGE - 1 < nk) load_slice(kt + NSTAGE - 1);
         const int buf = kt % NSTAGE;
         const bf16_t* sa = sA[buf];
         const bf16_t* sb = sB[buf];
-        bf16x8_t bfr[2][4], afr[2][4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            bfr[0][i] = *reinterpret_cast<const bf16x8_t*>(sb + boffs[0][i]);
-            afr[0][i] = *reinterpret_cast<const bf16x8_t*>(sa + aoffs[0][i]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
             const int cur = kk & 1;
             if (kk + 1 < KS) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    bfr[cur ^ 1][i] = *reinterpret_cast<const bf16x8_t*>(sb + boffs[kk + 1][i]);
-                    afr[cur ^ 1][i] = *reinterpret_cast<const bf16x8_t*>(sa + aoffs[kk + 1][i]);
+                MOE_READ_FRAGS(sb, sa, kk + 1, cur ^ 1)
+            } else {
+                if (kt + 1 < nk) {
+                    if (kt + NSTAGE <= nk) wait_vmcnt_lgkm0<PER * (NSTAGE - 2)>();
+                    else wait_vmcnt_lgkm0<0>();
+                    barrier_lds();
+                    if (kt + NSTAGE < nk) load_slice(kt + NSTAGE);
                 }
+                // first fragments of the next slice (after the last slice this
+                // reads a stale, in-bounds slot whose values are never used)
+                const int nbuf = (kt + 1) % NSTAGE;
+                MOE_READ_FRAGS(sB[nbuf], sA[nbuf], 0, cur ^ 1)
             }
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-                for (int mb = 0; mb < 4; ++mb)
-                    acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[cur][nb], afr[cur][mb],
-                                                                        acc[nb][mb], 0, 0, 0);
-            // spread the next step's 8 fragment reads over this step's 16 MFMAs
-            if (kk + 1 < KS) {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-                }
-            }
+            MOE_MFMA_STEP(cur)
+            MOE_INTERLEAVE()
             __builtin_amdgcn_sched_barrier(0);
         }
     }
+#undef MOE_READ_FRAGS
+#undef MOE_MFMA_STEP
+#undef MOE_INTERLEAVE
 
     // Epilogue.  Block (nb, mb): lane owns output row m = mb*32 + (lane & 31)
     // and, for g = 0..3, columns nb*32 + 8g + 4*(lane >> 5) + 0..3 (registers

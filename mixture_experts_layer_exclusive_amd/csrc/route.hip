@@ -87,6 +87,92 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const TIn* __restric
     }
 }
 
+// ---- bf16 router GEMM on MFMA ------------------------------------------------
+//
+// A workgroup takes 32 tokens and all experts; its 4 waves split the hidden
+// dimension in four.  Each wave computes logits^T blocks of 32 experts x 32
+// tokens with v_mfma_f32_32x32x16_bf16, loading its fragments straight from
+// global memory (x rows stream from HBM once; the small router weight stays
+// in L2).  The partial sums of the four waves are added in LDS in a fixed
+// order, so the result does not depend on scheduling.  The kernel is bound by
+// the HBM read of x.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+template <int EB>
+__global__ __launch_bounds__(256) void router_logits_mfma_kernel(const bf16_t* __restrict__ x,
+                                                                const bf16_t* __restrict__ w,
+                                                                float* __restrict__ logits,
+                                                                int64_t T, int d, int E) {
+    __shared__ float part[3][EB][16][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * 32;
+    int64_t tok = t0 + (lane & 31);
+    if (tok >= T) tok = T - 1;  // clamped rows compute discarded outputs
+    const int kq = 8 * (lane >> 5);
+    const bf16_t* xr = x + tok * d + kq;
+    const bf16_t* wr[EB];
+#pragma unroll
+    for (int b = 0; b < EB; ++b) {
+        int e = b * 32 + (lane & 31);
+        if (e >= E) e = E - 1;
+        wr[b] = w + static_cast<int64_t>(e) * d + kq;
+    }
+    f32x16_t acc[EB];
+#pragma unroll
+    for (int b = 0; b < EB; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[b][r] = 0.f;
+
+    const int kspan = d / 4;  // multiple of 16
+    const int k1 = (wave + 1) * kspan;
+    int k = wave * kspan;
+    // 8 K steps per round so that 8 x-row loads are in flight per wave
+    for (; k + 128 <= k1; k += 128) {
+        bf16x8_t xf[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) xf[s] = *reinterpret_cast<const bf16x8_t*>(xr + k + 16 * s);
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+#pragma unroll
+            for (int b = 0; b < EB; ++b) {
+                const bf16x8_t wf = *reinterpret_cast<const bf16x8_t*>(wr[b] + k + 16 * s);
+                acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, xf[s], acc[b], 0, 0, 0);
+            }
+    }
+    for (; k < k1; k += 16) {
+        const bf16x8_t xf = *reinterpret_cast<const bf16x8_t*>(xr + k);
+#pragma unroll
+        for (int b = 0; b < EB; ++b) {
+            const bf16x8_t wf = *reinterpret_cast<const bf16x8_t*>(wr[b] + k);
+            acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, xf, acc[b], 0, 0, 0);
+        }
+    }
+    if (wave > 0) {
+#pragma unroll
+        for (int b = 0; b < EB; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) part[wave - 1][b][r][lane] = acc[b][r];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    const int64_t t = t0 + (lane & 31);
+    if (t >= T) return;
+#pragma unroll
+    for (int b = 0; b < EB; ++b) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            // fixed order: wave 0 + wave 1 + wave 2 + wave 3
+            const float v = ((acc[b][r] + part[0][b][r][lane]) + part[1][b][r][lane]) + part[2][b][r][lane];
+            // lane holds token (lane & 31); register r holds expert
+            // b*32 + 8*(r/4) + 4*(lane/32) + r%4
+            const int e = b * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            if (e < E) logits[t * E + e] = v;
+        }
+    }
+}
+
 // ---- top-k selection and gates: one 64-lane wave per token -----------------
 //
 // Lane l holds the logits of experts l, l + 64, ... (EPL of them).  Each of
@@ -163,15 +249,26 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
 
 hipError_t launch_router_logits(const moe_problem_t& p, const void* x, const void* w_router,
                                 float* logits, hipStream_t s) {
-    dim3 grid(static_cast<unsigned>(ceil_div(p.T, RT_M)), static_cast<unsigned>(ceil_div(p.E, RT_N)));
-    if (p.dtype == MOE_DTYPE_F32)
+    if (p.dtype == MOE_DTYPE_F32) {
+        dim3 grid(static_cast<unsigned>(ceil_div(p.T, RT_M)), static_cast<unsigned>(ceil_div(p.E, RT_N)));
         router_logits_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float*>(x),
                                                          static_cast<const float*>(w_router), logits,
                                                          p.T, p.d, p.E);
-    else
-        router_logits_kernel<bf16_t><<<grid, 256, 0, s>>>(static_cast<const bf16_t*>(x),
-                                                          static_cast<const bf16_t*>(w_router),
-                                                          logits, p.T, p.d, p.E);
+        return hipGetLastError();
+    }
+    const unsigned grid = static_cast<unsigned>(ceil_div(p.T, 32));
+    const bf16_t* xb = static_cast<const bf16_t*>(x);
+    const bf16_t* wb = static_cast<const bf16_t*>(w_router);
+    switch (ceil_div(p.E, 32)) {
+        case 1: router_logits_mfma_kernel<1><<<grid, 256, 0, s>>>(xb, wb, logits, p.T, p.d, p.E); break;
+        case 2: router_logits_mfma_kernel<2><<<grid, 256, 0, s>>>(xb, wb, logits, p.T, p.d, p.E); break;
+        case 3: router_logits_mfma_kernel<3><<<grid, 256, 0, s>>>(xb, wb, logits, p.T, p.d, p.E); break;
+        case 4: router_logits_mfma_kernel<4><<<grid, 256, 0, s>>>(xb, wb, logits, p.T, p.d, p.E); break;
+        case 5: router_logits_mfma_kernel<5><<<grid, 256, 0, s>>>(xb, wb, logits, p.T, p.d, p.E); break;
+        case 6: router_logits_mfma_kernel<6><<<grid, 256, 0, s>>>(xb, wb, logits, p.T, p.d, p.E); break;
+        case 7: router_logits_mfma_kernel<7><<<grid, 256, 0, s>>>(xb, wb, logits, p.T, p.d, p.E); break;
+        default: router_logits_mfma_kernel<8><<<grid, 256, 0, s>>>(xb, wb, logits, p.T, p.d, p.E); break;
+    }
     return hipGetLastError();
 }
 
