@@ -117,7 +117,15 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, i
     return true;
 }
 
+// silu(g) * u in fp32 (the fp32 problem: correctly rounded exp and divide).
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.f + expf(-g)) * u; }
+
+// The same for the bf16 problem, whose result is rounded to bf16 (8 bits):
+// hardware exp2 and reciprocal (about 1 ulp of fp32 each) are far below that.
+__device__ __forceinline__ float silu_mul_fast(float g, float u) {
+    const float e = __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
+    return g * u * __builtin_amdgcn_rcpf(1.f + e);
+}
 
 // ---------------------------------------------------------------------------
 // bf16 grouped GEMM on MFMA (v_mfma_f32_32x32x16_bf16)
@@ -297,6 +305,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 
     const int nk = K / BK;
     constexpr int PER = 2 * LPW;  // LDS DMA instructions per slice per wave
+    static_assert(2 * LPW == 16, "the interleaved refill assumes 16 DMAs per slice per wave");
     static_assert(KS % 2 == 0, "fragment double buffer needs an even step count");
 
     // fragments of one K step: 4 weight blocks, 4 activation blocks, two sets
@@ -341,20 +350,40 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             const int cur = kk & 1;
             if (kk + 1 < KS) {
                 MOE_READ_FRAGS(sb, sa, kk + 1, cur ^ 1)
+                MOE_MFMA_STEP(cur)
+                MOE_INTERLEAVE()
             } else {
                 if (kt + 1 < nk) {
                     if (kt + NSTAGE <= nk) wait_vmcnt_lgkm0<PER * (NSTAGE - 2)>();
                     else wait_vmcnt_lgkm0<0>();
                     barrier_lds();
-                    if (kt + NSTAGE < nk) load_slice(kt + NSTAGE);
                 }
-                // first fragments of the next slice (after the last slice this
-                // reads a stale, in-bounds slot whose values are never used)
+                // The last K step of the slice: its 16 MFMAs interleaved with
+                // the refill DMAs of slot kt % NSTAGE (slice kt + NSTAGE) and the
+                // next slice's first fragment reads (after the last slice these
+                // read a stale, in-bounds slot whose values are never used).
+                const bool dma = kt + NSTAGE < nk;
+                const uint32_t boff_ = static_cast<uint32_t>(buf * SLICE * 2);
+                const int k0_ = (kt + NSTAGE) * BK;
                 const int nbuf = (kt + 1) % NSTAGE;
-                MOE_READ_FRAGS(sB[nbuf], sA[nbuf], 0, cur ^ 1)
+                const bf16_t* nsb = sB[nbuf];
+                const bf16_t* nsa = sA[nbuf];
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const int nb_ = q >> 2, mb_ = q & 3;
+                    acc[nb_][mb_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[cur][nb_], fa[cur][mb_],
+                                                                          acc[nb_][mb_], 0, 0, 0);
+                    if (dma) {
+                        if (q < LPW) lds_dma16(a_src[q] + k0_, lds_a0 + boff_ + q * RPI * BK * 2);
+                        else lds_dma16(b_src[q - LPW] + k0_, lds_b0 + boff_ + (q - LPW) * RPI * BK * 2);
+                    }
+                    if (q & 1) {
+                        const int i_ = q >> 1;
+                        if (i_ < 4) fb[cur ^ 1][i_] = *reinterpret_cast<const bf16x8_t*>(nsb + boffs[0][i_]);
+                        else fa[cur ^ 1][i_ - 4] = *reinterpret_cast<const bf16x8_t*>(nsa + aoffs[0][i_ - 4]);
+                    }
+                }
             }
-            MOE_MFMA_STEP(cur)
-            MOE_INTERLEAVE()
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -380,7 +409,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                     bf16x4_t o;
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        o[i] = f32_to_bf16(silu_mul(acc[nb][mb][4 * g + i], acc[nb + 2][mb][4 * g + i]));
+                        o[i] = f32_to_bf16(silu_mul_fast(acc[nb][mb][4 * g + i], acc[nb + 2][mb][4 * g + i]));
                     *reinterpret_cast<bf16x4_t*>(crow + col) = o;
                 }
         } else {
