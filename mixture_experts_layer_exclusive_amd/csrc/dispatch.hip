@@ -6,15 +6,18 @@
 // Three passes over the int32 ids:
 //   1. histogram: workgroup b counts the experts of assignments
 //      [b*C, (b+1)*C) with LDS atomics -> block_counts[e][b] (expert-major);
+//      C is a multiple of 256 chosen so that about 256 workgroups run;
 //   2. scan: one workgroup turns block_counts into an exclusive prefix sum in
 //      expert-major order.  Entry [e][b] becomes the first queue position of
 //      expert e owned by block b; entry [e][0] is offsets[e];
-//   3. scatter: each workgroup walks its chunk again in ascending a, 256
-//      assignments per round.  Within a wave, lanes holding the same expert
-//      are found with log2(E) ballots (one per id bit), the rank is the
-//      popcount of lower peers; ranks across the four waves come from a
-//      per-round LDS table.  Visiting a in ascending order in every level
-//      makes the sort stable.
+//   3. scatter: each wave of a workgroup owns a contiguous part of the
+//      chunk, counts it, takes its first position per expert from the block
+//      base plus the earlier waves' counts, then walks its part in ascending
+//      a, 64 at a time: lanes holding the same expert are found with log2(E)
+//      ballots (one per id bit) and ranked by the popcount of lower peers.
+//      Ascending a at every level makes the sort stable.
+// Up to 4096 assignments the three passes run in one 1024-thread workgroup.
+// The scatter stages its chunk's ids in LDS first (one bulk load).
 // Ids outside [0, E) are skipped (their assign_pos is -1).
 #include "device_util.h"
 #include "moe_internal.h"
@@ -24,19 +27,47 @@ namespace moe {
 namespace {
 
 constexpr int SCAN_THREADS = 1024;
+
+// Bits needed for an expert id.
+__host__ __device__ __forceinline__ int id_bits(int E) {
+    int b = 0;
+    while ((1 << b) < E) ++b;
+    return b;
+}
 constexpr int SCAN_ITEMS = 8;
 
+// Stable ranks of one 64-lane step of a wave's assignments: lanes holding
+// the same expert are found with one ballot per id bit; the rank of a lane
+// is the number of lower lanes in its group, `count` the group size.
+__device__ __forceinline__ void wave_peer_rank(bool ok, int e, int nbits, int& rank, int& count) {
+    uint64_t peers = __ballot(ok);
+    for (int b = 0; b < nbits; ++b) {
+        const bool bit = ok && ((e >> b) & 1);
+        const uint64_t m = __ballot(bit);
+        peers &= bit ? m : ~m;
+    }
+    rank = __popcll(peers & lanemask_lt());
+    count = __popcll(peers);
+}
+
 __global__ __launch_bounds__(256) void dispatch_hist_kernel(const int32_t* __restrict__ ids,
-                                                           int64_t n, int E, int nblk,
+                                                           int64_t n, int64_t chunk, int E, int nblk,
                                                            int32_t* __restrict__ block_counts) {
     __shared__ int h[MOE_MAX_EXPERTS];
     for (int e = threadIdx.x; e < E; e += 256) h[e] = 0;
     __syncthreads();
-    const int64_t a0 = static_cast<int64_t>(blockIdx.x) * kDispatchChunk;
-    const int64_t a1 = (a0 + kDispatchChunk < n) ? a0 + kDispatchChunk : n;
-    for (int64_t a = a0 + threadIdx.x; a < a1; a += 256) {
-        const int e = ids[a];
-        if (static_cast<unsigned>(e) < static_cast<unsigned>(E)) atomicAdd(&h[e], 1);
+    const int64_t a0 = static_cast<int64_t>(blockIdx.x) * chunk;
+    const int64_t a1 = (a0 + chunk < n) ? a0 + chunk : n;
+    const int nbits = id_bits(E);
+    // one LDS atomic per distinct expert of each 64-lane step (no same-address
+    // conflicts inside an instruction)
+    for (int64_t base = a0 + (threadIdx.x & ~63); base < a1; base += 256) {
+        const int64_t a = base + (threadIdx.x & 63);
+        const int e = a < a1 ? ids[a] : -1;
+        const bool ok = a < a1 && static_cast<unsigned>(e) < static_cast<unsigned>(E);
+        int rank, count;
+        wave_peer_rank(ok, e, nbits, rank, count);
+        if (ok && rank == 0) atomicAdd(&h[e], count);
     }
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += 256)
@@ -105,73 +136,166 @@ __global__ __launch_bounds__(SCAN_THREADS) void dispatch_scan_kernel(int32_t* __
     if (tid == 0) offsets[E] = grand;
 }
 
-__global__ __launch_bounds__(256) void dispatch_scatter_kernel(const int32_t* __restrict__ ids,
-                                                              int64_t n, int E, int nbits, int nblk,
-                                                              const int32_t* __restrict__ bases,
-                                                              int32_t* __restrict__ sorted_assign,
-                                                              int32_t* __restrict__ assign_pos) {
-    __shared__ int cursor[MOE_MAX_EXPERTS];
-    __shared__ int wcnt[4][MOE_MAX_EXPERTS];
+// Scatters the assignments [a0, a1) whose experts start at block_base[e]
+// (LDS, E entries) in ascending a; s_ids holds their ids (LDS, staged by the
+// caller).  NW waves: wave w owns the contiguous sub-range w of the chunk,
+// counts it, then walks it 64 at a time with its own LDS cursors, so only two
+// workgroup barriers are needed.
+template <int NW>
+__device__ __forceinline__ void scatter_chunk(const int* s_ids, int64_t a0, int64_t a1,
+                                              int E, int nbits, const int* block_base,
+                                              int (*wcur)[MOE_MAX_EXPERTS],
+                                              int32_t* __restrict__ sorted_assign,
+                                              int32_t* __restrict__ assign_pos) {
     const int tid = threadIdx.x;
+    const int lane = tid & 63;
     const int wave = tid >> 6;
-    for (int e = tid; e < E; e += 256) {
-        cursor[e] = bases[static_cast<int64_t>(e) * nblk + blockIdx.x];
-        wcnt[0][e] = wcnt[1][e] = wcnt[2][e] = wcnt[3][e] = 0;
+    const int64_t span = ((a1 - a0) + NW - 1) / NW;
+    const int64_t w0 = a0 + wave * span;
+    const int64_t w1 = (w0 + span < a1) ? w0 + span : a1;
+    // phase 1: per-wave histograms
+    for (int x = tid; x < NW * E; x += NW * 64) wcur[x / E][x % E] = 0;
+    __syncthreads();
+    for (int64_t base = w0; base < w1; base += 64) {
+        const int64_t a = base + lane;
+        const int e = a < w1 ? s_ids[a - a0] : -1;
+        const bool ok = a < w1 && static_cast<unsigned>(e) < static_cast<unsigned>(E);
+        int rank, count;
+        wave_peer_rank(ok, e, nbits, rank, count);
+        if (ok && rank == 0) atomicAdd(&wcur[wave][e], count);
     }
     __syncthreads();
-    const int64_t a0 = static_cast<int64_t>(blockIdx.x) * kDispatchChunk;
-    const int64_t a1 = (a0 + kDispatchChunk < n) ? a0 + kDispatchChunk : n;
-    for (int64_t base = a0; base < a1; base += 256) {
-        const int64_t a = base + tid;
-        const bool in_range = a < a1;
-        const int e = in_range ? ids[a] : -1;
-        const bool ok = in_range && static_cast<unsigned>(e) < static_cast<unsigned>(E);
-        uint64_t peers = __ballot(ok);
-        for (int b = 0; b < nbits; ++b) {
-            const bool bit = ok && ((e >> b) & 1);
-            const uint64_t m = __ballot(bit);
-            peers &= bit ? m : ~m;
+    // phase 2: each wave's first position per expert
+    for (int e = tid; e < E; e += NW * 64) {
+        int run = block_base[e];
+        for (int w = 0; w < NW; ++w) {
+            const int c = wcur[w][e];
+            wcur[w][e] = run;
+            run += c;
         }
-        const int rank = __popcll(peers & lanemask_lt());
-        if (ok && rank == 0) wcnt[wave][e] = __popcll(peers);
-        __syncthreads();
+    }
+    __syncthreads();
+    // phase 3: ordered walk, wave-private cursors
+    for (int64_t base = w0; base < w1; base += 64) {
+        const int64_t a = base + lane;
+        const bool in_range = a < w1;
+        const int e = in_range ? s_ids[a - a0] : -1;
+        const bool ok = in_range && static_cast<unsigned>(e) < static_cast<unsigned>(E);
+        int rank, count;
+        wave_peer_rank(ok, e, nbits, rank, count);
+        int pos = 0;
+        if (ok) pos = wcur[wave][e] + rank;
+        __builtin_amdgcn_wave_barrier();
+        if (ok && rank == 0) wcur[wave][e] += count;
+        __builtin_amdgcn_wave_barrier();
         if (ok) {
-            int pos = cursor[e] + rank;
-            for (int w = 0; w < wave; ++w) pos += wcnt[w][e];
             sorted_assign[pos] = static_cast<int32_t>(a);
             assign_pos[a] = pos;
         } else if (in_range) {
             assign_pos[a] = -1;
         }
-        __syncthreads();
-        for (int x = tid; x < E; x += 256) {
-            cursor[x] += wcnt[0][x] + wcnt[1][x] + wcnt[2][x] + wcnt[3][x];
-            wcnt[0][x] = wcnt[1][x] = wcnt[2][x] = wcnt[3][x] = 0;
-        }
-        __syncthreads();
     }
 }
 
-// x_perm[pos] = x[sorted_assign[pos] / k] for pos < offsets[E]; one
-// workgroup per queue row, 16-byte words when the row allows it.
-template <typename W>
-__global__ __launch_bounds__(256) void gather_rows_kernel(const W* __restrict__ x,
-                                                         const int32_t* __restrict__ sorted_assign,
-                                                         const int32_t* __restrict__ offsets, int E,
-                                                         int k, int64_t words_per_row,
-                                                         W* __restrict__ x_perm) {
-    const int64_t pos = blockIdx.x;
-    if (pos >= offsets[E]) return;
-    const int64_t tok = sorted_assign[pos] / k;
-    const W* src = x + tok * words_per_row;
-    W* dst = x_perm + pos * words_per_row;
-    for (int64_t i = threadIdx.x; i < words_per_row; i += 256) dst[i] = load_nt(src + i);
+__global__ __launch_bounds__(256) void dispatch_scatter_kernel(const int32_t* __restrict__ ids,
+                                                              int64_t n, int64_t chunk, int E, int nbits,
+                                                              int nblk,
+                                                              const int32_t* __restrict__ bases,
+                                                              int32_t* __restrict__ sorted_assign,
+                                                              int32_t* __restrict__ assign_pos) {
+    __shared__ int block_base[MOE_MAX_EXPERTS];
+    __shared__ int wcur[4][MOE_MAX_EXPERTS];
+    __shared__ int s_ids[kMaxDispatchChunk];
+    for (int e = threadIdx.x; e < E; e += 256)
+        block_base[e] = bases[static_cast<int64_t>(e) * nblk + blockIdx.x];
+    const int64_t a0 = static_cast<int64_t>(blockIdx.x) * chunk;
+    const int64_t a1 = (a0 + chunk < n) ? a0 + chunk : n;
+    for (int64_t a = a0 + threadIdx.x; a < a1; a += 256) s_ids[a - a0] = ids[a];
+    scatter_chunk<4>(s_ids, a0, a1, E, nbits, block_base, wcur, sorted_assign, assign_pos);
 }
 
-int id_bits(int E) {
-    int b = 0;
-    while ((1 << b) < E) ++b;
-    return b;
+// The whole counting sort in one 1024-thread workgroup, for problems small
+// enough that one launch beats three: histogram in LDS, exclusive scan over
+// the experts, then the ordered scatter.
+constexpr int SMALL_SORT_MAX = 4096;
+
+__global__ __launch_bounds__(1024) void dispatch_small_kernel(const int32_t* __restrict__ ids,
+                                                             int64_t n, int E, int nbits,
+                                                             int32_t* __restrict__ counts,
+                                                             int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ sorted_assign,
+                                                             int32_t* __restrict__ assign_pos) {
+    __shared__ int hist[MOE_MAX_EXPERTS];
+    __shared__ int base[MOE_MAX_EXPERTS];
+    __shared__ int wcur[16][MOE_MAX_EXPERTS];
+    __shared__ int s_ids[SMALL_SORT_MAX];
+    const int tid = threadIdx.x;
+    for (int e = tid; e < E; e += 1024) hist[e] = 0;
+    for (int64_t a = tid; a < n; a += 1024) s_ids[a] = ids[a];
+    __syncthreads();
+    for (int64_t base = tid & ~63; base < n; base += 1024) {
+        const int64_t a = base + (tid & 63);
+        const int e = a < n ? s_ids[a] : -1;
+        const bool ok = a < n && static_cast<unsigned>(e) < static_cast<unsigned>(E);
+        int rank, count;
+        wave_peer_rank(ok, e, nbits, rank, count);
+        if (ok && rank == 0) atomicAdd(&hist[e], count);
+    }
+    __syncthreads();
+    if (tid < 64) {
+        // exclusive scan over E <= 256 experts: 4 per lane
+        int c[4], local = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = tid * 4 + i;
+            c[i] = e < E ? hist[e] : 0;
+            local += c[i];
+        }
+        int incl = local;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int o = __shfl_up(incl, off, 64);
+            if (tid >= off) incl += o;
+        }
+        int run = incl - local;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = tid * 4 + i;
+            if (e < E) {
+                base[e] = run;
+                offsets[e] = run;
+                counts[e] = c[i];
+            }
+            run += c[i];
+        }
+        if (tid == 63) offsets[E] = incl;
+    }
+    __syncthreads();
+    scatter_chunk<16>(s_ids, 0, n, E, nbits, base, wcur, sorted_assign, assign_pos);
+}
+
+// Dispatch gather, token-major: every row of x is read once and written to
+// its k queue rows, x_perm[assign_pos[t*k + j]] = x[t] (assignments with no
+// queue position are skipped).  A workgroup copies TPB whole rows; threads
+// stride over (row, word) pairs, so both the reads and the row writes are
+// contiguous.
+template <typename W>
+__global__ __launch_bounds__(256) void gather_rows_kernel(const W* __restrict__ x,
+                                                         const int32_t* __restrict__ assign_pos,
+                                                         int64_t T, int k, int64_t words_per_row,
+                                                         int tpb, W* __restrict__ x_perm) {
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * tpb;
+    const int64_t nt = (t0 + tpb <= T) ? tpb : T - t0;
+    const int64_t total = nt * words_per_row;
+    for (int64_t i = threadIdx.x; i < total; i += 256) {
+        const int64_t t = t0 + i / words_per_row;
+        const int64_t w = i % words_per_row;
+        const W v = load_nt(x + t * words_per_row + w);
+        for (int j = 0; j < k; ++j) {
+            const int pos = assign_pos[t * k + j];
+            if (pos >= 0) x_perm[static_cast<int64_t>(pos) * words_per_row + w] = v;
+        }
+    }
 }
 
 }  // namespace
@@ -180,30 +304,38 @@ hipError_t launch_dispatch_queues(const moe_problem_t& p, const int32_t* ids, in
                                   int32_t* offsets, int32_t* sorted_assign, int32_t* assign_pos,
                                   int32_t* block_counts, hipStream_t s) {
     const int64_t n = p.T * p.k;
+    if (n <= SMALL_SORT_MAX) {
+        dispatch_small_kernel<<<1, 1024, 0, s>>>(ids, n, p.E, id_bits(p.E), counts, offsets,
+                                                 sorted_assign, assign_pos);
+        return hipGetLastError();
+    }
+    const int64_t chunk = dispatch_chunk(n);
     const int nblk = static_cast<int>(dispatch_blocks(n));
-    dispatch_hist_kernel<<<nblk, 256, 0, s>>>(ids, n, p.E, nblk, block_counts);
+    dispatch_hist_kernel<<<nblk, 256, 0, s>>>(ids, n, chunk, p.E, nblk, block_counts);
     dispatch_scan_kernel<<<1, SCAN_THREADS, 0, s>>>(block_counts, p.E, nblk, counts, offsets);
-    dispatch_scatter_kernel<<<nblk, 256, 0, s>>>(ids, n, p.E, id_bits(p.E), nblk, block_counts,
+    dispatch_scatter_kernel<<<nblk, 256, 0, s>>>(ids, n, chunk, p.E, id_bits(p.E), nblk, block_counts,
                                                  sorted_assign, assign_pos);
     return hipGetLastError();
 }
 
-hipError_t launch_gather_rows(const moe_problem_t& p, const void* x, const int32_t* sorted_assign,
-                              const int32_t* offsets, void* x_perm, hipStream_t s) {
-    const int64_t n = p.T * p.k;
+hipError_t launch_gather_rows(const moe_problem_t& p, const void* x, const int32_t* assign_pos,
+                              void* x_perm, hipStream_t s) {
     const int64_t row_bytes = static_cast<int64_t>(p.d) * (p.dtype == MOE_DTYPE_F32 ? 4 : 2);
+    // rows per workgroup: about 8 KB of row data per workgroup
+    const int tpb = static_cast<int>(row_bytes >= 8192 ? 1 : 8192 / row_bytes);
+    const unsigned grid = static_cast<unsigned>(ceil_div(p.T, tpb));
     if (row_bytes % 16 == 0)
-        gather_rows_kernel<uint4><<<static_cast<unsigned>(n), 256, 0, s>>>(
-            static_cast<const uint4*>(x), sorted_assign, offsets, p.E, p.k, row_bytes / 16,
-            static_cast<uint4*>(x_perm));
+        gather_rows_kernel<uint4><<<grid, 256, 0, s>>>(static_cast<const uint4*>(x), assign_pos, p.T,
+                                                      p.k, row_bytes / 16, tpb,
+                                                      static_cast<uint4*>(x_perm));
     else if (row_bytes % 4 == 0)
-        gather_rows_kernel<uint32_t><<<static_cast<unsigned>(n), 256, 0, s>>>(
-            static_cast<const uint32_t*>(x), sorted_assign, offsets, p.E, p.k, row_bytes / 4,
-            static_cast<uint32_t*>(x_perm));
+        gather_rows_kernel<uint32_t><<<grid, 256, 0, s>>>(static_cast<const uint32_t*>(x), assign_pos,
+                                                         p.T, p.k, row_bytes / 4, tpb,
+                                                         static_cast<uint32_t*>(x_perm));
     else
-        gather_rows_kernel<uint16_t><<<static_cast<unsigned>(n), 256, 0, s>>>(
-            static_cast<const uint16_t*>(x), sorted_assign, offsets, p.E, p.k, row_bytes / 2,
-            static_cast<uint16_t*>(x_perm));
+        gather_rows_kernel<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(x), assign_pos,
+                                                         p.T, p.k, row_bytes / 2, tpb,
+                                                         static_cast<uint16_t*>(x_perm));
     return hipGetLastError();
 }
 

@@ -164,7 +164,7 @@ moe_status_t moe_dispatch(const moe_problem_t* p, const int32_t* topk_ids, const
     clear_hip_error();
     MOE_LAUNCH(launch_dispatch_queues(*p, topk_ids, counts, offsets, sorted_assign, assign_pos,
                                       static_cast<int32_t*>(ws), s));
-    if (x_perm != nullptr) MOE_LAUNCH(launch_gather_rows(*p, x, sorted_assign, offsets, x_perm, s));
+    if (x_perm != nullptr) MOE_LAUNCH(launch_gather_rows(*p, x, assign_pos, x_perm, s));
     return MOE_OK;
 }
 

@@ -10,8 +10,6 @@ namespace moe {
 
 // ---- tuning constants --------------------------------------------------------
 
-// Assignments handled by one workgroup of the histogram and scatter kernels.
-constexpr int kDispatchChunk = 2048;
 
 // bf16 grouped GEMM: queue rows per tile, output columns per tile.
 constexpr int kBM = 256;
@@ -28,7 +26,15 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-inline int64_t dispatch_blocks(int64_t n_assign) { return ceil_div(n_assign, kDispatchChunk); }
+// Assignments per workgroup of the histogram and scatter kernels: a multiple
+// of 256 sized so that about 256 workgroups (one per CU) share the work, at
+// most kMaxDispatchChunk (the scatter stages its chunk's ids in LDS).
+constexpr int kMaxDispatchChunk = 8192;
+inline int64_t dispatch_chunk(int64_t n_assign) {
+    const int64_t c = ceil_div(ceil_div(n_assign, 256), 256) * 256;
+    return c < 256 ? 256 : (c > kMaxDispatchChunk ? kMaxDispatchChunk : c);
+}
+inline int64_t dispatch_blocks(int64_t n_assign) { return ceil_div(n_assign, dispatch_chunk(n_assign)); }
 
 // Upper bound of sum_e ceil(count_e / bm) over any routing of n rows to E experts.
 inline int64_t max_m_tiles(int64_t n_rows, int E, int bm) { return n_rows / bm + E; }
@@ -47,8 +53,8 @@ hipError_t launch_route_topk(const moe_problem_t& p, const float* logits, int32_
 hipError_t launch_dispatch_queues(const moe_problem_t& p, const int32_t* ids, int32_t* counts,
                                   int32_t* offsets, int32_t* sorted_assign, int32_t* assign_pos,
                                   int32_t* block_counts, hipStream_t s);
-hipError_t launch_gather_rows(const moe_problem_t& p, const void* x, const int32_t* sorted_assign,
-                              const int32_t* offsets, void* x_perm, hipStream_t s);
+hipError_t launch_gather_rows(const moe_problem_t& p, const void* x, const int32_t* assign_pos,
+                              void* x_perm, hipStream_t s);
 
 hipError_t launch_expert_ffn(const moe_problem_t& p, const void* x_perm, const void* x,
                              const int32_t* sorted_assign, const int32_t* offsets,

@@ -151,11 +151,11 @@ def test_zero_tokens_is_a_noop(lib):
 
 def test_workspace_has_no_dense_routing_matrix(lib):
     # The dispatch queues replace a dense token-by-expert matrix: the dispatch
-    # workspace holds per-block expert counts only, E * ceil(T*k / 2048) ints.
+    # workspace holds per-block expert counts only (about 256 blocks).
     for T, d, E, k, f in [(65536, 2048, 128, 8, 768), (8192, 4096, 8, 2, 14336), (16384, 2048, 64, 6, 1408)]:
         p = prob(T, d, E, k, f)
         _, nd = ws_size(lib, p, L.MOE_OP_DISPATCH)
-        assert nd <= E * ((T * k + 2047) // 2048) * 4 + 256
+        assert nd <= E * 256 * 4 + 256  # at most 256 blocks
         assert nd * 16 < T * E * 4
         # forward: logits, ids/gates/permutations, counts, h and y_perm only
         _, nw = ws_size(lib, p, L.MOE_OP_FORWARD)
