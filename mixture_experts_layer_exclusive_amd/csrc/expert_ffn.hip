@@ -260,15 +260,19 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 
     const uint32_t lds_a0 = __builtin_amdgcn_readfirstlane(lds_addr(&sA[0][wave * 64 * BK]));
     const uint32_t lds_b0 = __builtin_amdgcn_readfirstlane(lds_addr(&sB[0][wave * 64 * BK]));
+    // Load q of a slice (q < 2 * LPW).  GEMM1 issues its activation rows
+    // first and GEMM2 its weight rows first, the order that measured faster
+    // for each (a few percent: the loads of a slice queue behind each other).
+    auto dma = [&](int q, int k0, uint32_t boff) {
+        const bool a_op = GATEUP ? q < LPW : q >= LPW;
+        const int j = q < LPW ? q : q - LPW;
+        if (a_op) lds_dma16(a_src[j] + k0, lds_a0 + boff + j * RPI * BK * 2);
+        else lds_dma16(b_src[j] + k0, lds_b0 + boff + j * RPI * BK * 2);
+    };
     auto load_slice = [&](int kt) {
         const uint32_t boff = static_cast<uint32_t>((kt % NSTAGE) * SLICE * 2);
-        const int k0 = kt * BK;
 #pragma unroll
-        for (int j = 0; j < LPW; ++j)
-            lds_dma16(a_src[j] + k0, lds_a0 + boff + j * RPI * BK * 2);
-#pragma unroll
-        for (int j = 0; j < LPW; ++j)
-            lds_dma16(b_src[j] + k0, lds_b0 + boff + j * RPI * BK * 2);
+        for (int q = 0; q < 2 * LPW; ++q) dma(q, kt * BK, boff);
     };
 
     f32x16_t acc[4][4];
@@ -362,7 +366,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                 // the refill DMAs of slot kt % NSTAGE (slice kt + NSTAGE) and the
                 // next slice's first fragment reads (after the last slice these
                 // read a stale, in-bounds slot whose values are never used).
-                const bool dma = kt + NSTAGE < nk;
+                const bool refill = kt + NSTAGE < nk;
                 const uint32_t boff_ = static_cast<uint32_t>(buf * SLICE * 2);
                 const int k0_ = (kt + NSTAGE) * BK;
                 const int nbuf = (kt + 1) % NSTAGE;
@@ -373,10 +377,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                     const int nb_ = q >> 2, mb_ = q & 3;
                     acc[nb_][mb_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[cur][nb_], fa[cur][mb_],
                                                                           acc[nb_][mb_], 0, 0, 0);
-                    if (dma) {
-                        if (q < LPW) lds_dma16(a_src[q] + k0_, lds_a0 + boff_ + q * RPI * BK * 2);
-                        else lds_dma16(b_src[q - LPW] + k0_, lds_b0 + boff_ + (q - LPW) * RPI * BK * 2);
-                    }
+                    if (refill) dma(q, k0_, boff_);
                     if (q & 1) {
                         const int i_ = q >> 1;
                         if (i_ < 4) fb[cur ^ 1][i_] = *reinterpret_cast<const bf16x8_t*>(nsb + boffs[0][i_]);
