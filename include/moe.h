@@ -47,7 +47,8 @@
  *     kernel launch returns MOE_ERR_HIP; faults during execution surface on
  *     the stream.  Logits must be finite (not checked).
  *   - Limits: 1 <= E <= MOE_MAX_EXPERTS, 1 <= k <= min(E, MOE_MAX_TOPK),
- *     T*k <= 2^31 - 1; bf16 needs d and f to be multiples of 64.
+ *     T*k <= 2^31 - 1; bf16 needs d and f to be multiples of 64 and
+ *     d*f <= 2^31 - 1 (one expert's weight matrix below 4 GiB).
  */
 #ifndef MOE_H
 #define MOE_H

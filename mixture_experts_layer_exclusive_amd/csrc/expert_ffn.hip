@@ -39,17 +39,6 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 constexpr int GROUP_M = GEMM_GROUP_M;
 constexpr int NUM_XCD = 8;
 
-// bf16 GEMM pipeline shape: K slice width, LDS ring depth, slot swizzle.
-#ifndef GEMM_BK
-#define GEMM_BK 64
-#endif
-#ifndef GEMM_STAGES
-#define GEMM_STAGES 2
-#endif
-#ifndef GEMM_SWZ
-#define GEMM_SWZ 1
-#endif
-
 // Per-expert tile prefix in LDS: s_prefix[e] = sum_{e' < e} ceil(rows_e' / bm),
 // s_prefix[E] = total row tiles.  Computed by wave 0.
 __device__ __forceinline__ void build_tile_prefix(const int32_t* __restrict__ offsets, int E, int bm,
@@ -145,22 +134,22 @@ __device__ __forceinline__ float silu_mul_fast(float g, float u) {
 // the same lane and register of blocks nb and nb + 2.
 //
 // Operand staging: global_load_lds_dwordx4 copies 16 bytes per lane straight
-// into LDS (no register round trip) into an NSTAGE-deep ring of K slices of
-// width BK.  Each row of a slice is BK/8 16-byte slots, and the slot that
-// holds chunk c of row r is c ^ swz(r), which spreads the 16-byte fragment
-// reads of consecutive rows over all LDS banks.  One barrier per K step: it
-// publishes slice kt and frees the slot that slice kt + NSTAGE - 1 refills.
+// into LDS (no register round trip), into a ring of two K slices of 64
+// columns: one 128-byte line per row and slice.  Each row of a slice is 8
+// 16-byte slots, and the slot that holds chunk c of row r is c ^ ((r >> 1) &
+// 7), which spreads the 16-byte fragment reads of 16 consecutive rows over
+// all LDS banks.  A slice's fragments (4 K steps x 8 blocks) are read into
+// registers at its start, so its LDS stage is free after the first K step and
+// the next-but-one slice's loads go out spread over the other three K steps:
+// an LDS-bound load is a vector-memory instruction that the wave issues in
+// order with its MFMAs, and a burst of them stalls the MFMAs behind it.
 // Rows past the end of an expert's queue (or past N) load a clamped valid row
 // and their results are never stored.
 // ---------------------------------------------------------------------------
 typedef uint16_t bf16x4_t __attribute__((ext_vector_type(4)));
 
-template <int BK, int SWZ>
-__device__ __forceinline__ int swz(int r) {
-    // BK = 64: 8 slots per row; BK = 32: 4 slots per row
-    if (BK == 64) return SWZ == 0 ? (r & 7) : ((r >> 1) & 7);
-    return SWZ == 0 ? ((r >> 1) & 3) : ((r >> 2) & 3);
-}
+// LDS slot of chunk c of tile row r: c ^ slot_swizzle(r).
+__device__ __forceinline__ int slot_swizzle(int r) { return (r >> 1) & 7; }
 
 // s_waitcnt with only the vector-memory counter limited (gfx9 encoding).
 template <int N>
@@ -169,7 +158,8 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// s_waitcnt: vector-memory counter <= N and all LDS reads returned.
+// s_waitcnt: vector-memory counter <= N and all LDS reads returned
+// (N = 63: LDS reads only).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt_lgkm0() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -190,6 +180,18 @@ __device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_base) {
         : "memory");
 }
 
+// The same from a wave-uniform base address plus a 32-bit per-lane byte
+// offset (the scalar-base form of the load).
+__device__ __forceinline__ void lds_dma16_s(const void* sbase, uint32_t voff, uint32_t lds_base) {
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, %1"
+        :
+        : "v"(voff), "s"(sbase), "s"(lds_base)
+        : "memory");
+}
+
 // Workgroup barrier without a memory fence (the LDS traffic it orders is
 // waited for explicitly); the empty asm statements keep the compiler from
 // moving memory accesses across it.
@@ -203,76 +205,106 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
 }
 
-template <bool GATEUP, bool GATHER, int BK, int NSTAGE, int SWZ>
+// A pointer that is wave-uniform but not provably so to the compiler, moved
+// to scalar registers.
+template <typename T>
+__device__ __forceinline__ const T* uniform_ptr(const T* p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+    return reinterpret_cast<const T*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+template <bool GATEUP, bool GATHER>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void grouped_gemm_bf16_kernel(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ sorted_assign, int topk,
     const int32_t* __restrict__ offsets, int E, const bf16_t* __restrict__ B0,
     const bf16_t* __restrict__ B1, bf16_t* __restrict__ C, int N, int K) {
-    constexpr int TM = 256;                 // activation rows (and weight rows) per tile
-    constexpr int BN_OUT = GATEUP ? 128 : 256;
-    constexpr int CH = BK / 8;              // 16-byte chunks per row
-    constexpr int RPI = 64 / CH;            // rows per load instruction
-    constexpr int LPW = 64 / RPI;           // load instructions per wave per operand
-    constexpr int SLICE = TM * BK;          // bf16 elements per operand slice
-    __shared__ __attribute__((aligned(1024))) bf16_t sA[NSTAGE][SLICE];
-    __shared__ __attribute__((aligned(1024))) bf16_t sB[NSTAGE][SLICE];
-    __shared__ int s_prefix[MOE_MAX_EXPERTS + 1];
+    constexpr int TM = 256;                  // activation rows per tile
+    constexpr int TN = 256;                  // weight rows per tile
+    constexpr int BK = 64;                   // K slice width (one 128-byte line per row)
+    constexpr int BN_OUT = GATEUP ? TN / 2 : TN;
+    constexpr int LA = TM / 32;              // activation loads per wave per slice (8 rows each)
+    constexpr int LB = TN / 32;              // weight loads per wave per slice
+    constexpr int NL = LA + LB;
+    constexpr int ROWB = BK * 2;             // bytes per row of a slice
+    constexpr int SA_BYTES = TM * ROWB;
+    constexpr int STAGE_BYTES = (TM + TN) * ROWB;
+    constexpr int NR = 8;                    // fragment reads per K step (4 activation, 4 weight)
+    constexpr int NM = 16;                   // MFMAs per K step
+    constexpr int KS = BK / 16;              // K steps per slice
+    // GEMM1 issues its activation loads first, GEMM2 its weight loads first
+    // (the order that measured faster for each).
+    constexpr bool A_FIRST = GATEUP;
+    static_assert(2 * STAGE_BYTES <= 160 * 1024, "two stages must fit the 160 KB of LDS");
+    static_assert(KS == 4 && (KS - 1) * NR == NM + NR, "the step schedule below assumes 4 K steps");
+    static_assert(3 * NL <= (KS - 1) * NM, "the refill spreads one load per 3 MFMAs");
+    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE_BYTES];
+    // The tile prefix table lives in stage 0 until the first load.
+    int* const s_prefix = reinterpret_cast<int*>(smem);
 
     build_tile_prefix(offsets, E, TM, s_prefix);
     const int n_tiles = (N + BN_OUT - 1) / BN_OUT;
     Tile tile;
     if (!find_tile(offsets, E, TM, n_tiles, s_prefix, tile)) return;
+    __syncthreads();  // every lookup is done before the loads overwrite the table
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1;
     const int wn = wave & 1;
     const int n0 = tile.nt * BN_OUT;
-    const int64_t NK = static_cast<int64_t>(N) * K;
+    const int lrow = lane >> 3;
+    const int lslot = lane & 7;
 
-    // Per-lane global sources: wave w fills tile rows w*64 .. w*64+63 of both
-    // operands; load j covers rows w*64 + j*RPI .. +RPI, lane -> (row, slot).
-    const int lrow = lane / CH;
-    const int lslot = lane % CH;
-    const bf16_t* a_src[LPW];
-    const bf16_t* b_src[LPW];
+    // Loads: wave w fills activation rows w*64 .. +64 and weight rows
+    // w*64 .. +64 of a stage; load j covers 8 rows, lane -> (row lrow, LDS
+    // slot lslot), and the slot receives global chunk lslot ^ swizzle(row).
+    // Gathered activation rows use 64-bit addresses; the others a uniform
+    // base and 32-bit byte offsets (one expert's weights stay below 4 GiB).
+    const bf16_t* a_src[GATHER ? LA : 1];
+    uint32_t a_off[GATHER ? 1 : LA];
+    const bf16_t* const a_base = uniform_ptr(A + static_cast<int64_t>(tile.row0) * K);
 #pragma unroll
-    for (int j = 0; j < LPW; ++j) {
-        const int r = wave * 64 + j * RPI + lrow;       // tile row 0..255
-        const int chunk = lslot ^ swz<BK, SWZ>(r);      // global chunk for this LDS slot
+    for (int j = 0; j < LA; ++j) {
+        const int r = wave * 64 + j * 8 + lrow;
+        const int chunk = lslot ^ slot_swizzle(r);
         int pos = tile.row0 + r;
         if (pos >= tile.row1) pos = tile.row1 - 1;
-        const int64_t arow = GATHER ? static_cast<int64_t>(sorted_assign[pos] / topk) : pos;
-        a_src[j] = A + arow * K + chunk * 8;
-        int n;
-        const bf16_t* base;
-        if (GATEUP) {
-            n = n0 + (r & 127);
-            base = (r < 128 ? B0 : B1) + tile.e * NK;
-        } else {
-            n = n0 + r;
-            base = B0 + tile.e * NK;
-        }
-        if (n >= N) n = N - 1;
-        b_src[j] = base + static_cast<int64_t>(n) * K + chunk * 8;
+        if (GATHER)
+            a_src[GATHER ? j : 0] = A + static_cast<int64_t>(sorted_assign[pos] / topk) * K + chunk * 8;
+        else
+            a_off[GATHER ? 0 : j] = (static_cast<uint32_t>(pos - tile.row0) * K + chunk * 8) * 2u;
     }
-
-    const uint32_t lds_a0 = __builtin_amdgcn_readfirstlane(lds_addr(&sA[0][wave * 64 * BK]));
-    const uint32_t lds_b0 = __builtin_amdgcn_readfirstlane(lds_addr(&sB[0][wave * 64 * BK]));
-    // Load q of a slice (q < 2 * LPW).  GEMM1 issues its activation rows
-    // first and GEMM2 its weight rows first, the order that measured faster
-    // for each (a few percent: the loads of a slice queue behind each other).
-    auto dma = [&](int q, int k0, uint32_t boff) {
-        const bool a_op = GATEUP ? q < LPW : q >= LPW;
-        const int j = q < LPW ? q : q - LPW;
-        if (a_op) lds_dma16(a_src[j] + k0, lds_a0 + boff + j * RPI * BK * 2);
-        else lds_dma16(b_src[j] + k0, lds_b0 + boff + j * RPI * BK * 2);
-    };
-    auto load_slice = [&](int kt) {
-        const uint32_t boff = static_cast<uint32_t>((kt % NSTAGE) * SLICE * 2);
+    // In GEMM1 the first 128 weight rows are gate rows and the rest up rows,
+    // so each wave's rows come from one matrix.
+    const int rb0 = wave * (TN / 4);
+    const bf16_t* const b_base =
+        uniform_ptr((GATEUP && rb0 >= TN / 2 ? B1 : B0) + static_cast<int64_t>(tile.e) * N * K);
+    uint32_t b_off[LB];
 #pragma unroll
-        for (int q = 0; q < 2 * LPW; ++q) dma(q, kt * BK, boff);
+    for (int j = 0; j < LB; ++j) {
+        const int r = rb0 + j * 8 + lrow;
+        const int chunk = lslot ^ slot_swizzle(r);
+        int n = n0 + (GATEUP && r >= TN / 2 ? r - TN / 2 : r);
+        if (n >= N) n = N - 1;
+        b_off[j] = (static_cast<uint32_t>(n) * K + chunk * 8) * 2u;
+    }
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+    const uint32_t lds_a = lds0 + wave * 64 * ROWB;
+    const uint32_t lds_b = lds0 + SA_BYTES + rb0 * ROWB;
+    // load q (< NL) of slice kt
+    auto dma = [&](int q, int kt) {
+        const uint32_t so = static_cast<uint32_t>((kt & 1) * STAGE_BYTES);
+        const bool a_op = A_FIRST ? q < LA : q >= LB;
+        const int j = a_op ? (A_FIRST ? q : q - LB) : (A_FIRST ? q - LA : q);
+        if (a_op) {
+            if (GATHER) lds_dma16(a_src[GATHER ? j : 0] + kt * BK, lds_a + so + j * 8 * ROWB);
+            else lds_dma16_s(a_base + kt * BK, a_off[GATHER ? 0 : j], lds_a + so + j * 8 * ROWB);
+        } else {
+            lds_dma16_s(b_base + kt * BK, b_off[j], lds_b + so + j * 8 * ROWB);
+        }
     };
 
     f32x16_t acc[4][4];
@@ -283,121 +315,122 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-    // fragment rows this lane reads
-    int brow[4], arow_l[4];
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-        brow[nb] = GATEUP ? ((nb >> 1) * 128 + wn * 64 + (nb & 1) * 32 + (lane & 31))
-                          : (wn * 128 + nb * 32 + (lane & 31));
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) arow_l[mb] = wm * 128 + mb * 32 + (lane & 31);
+    // Fragment reads.  A 32-row block starts at a multiple of 32 rows, so the
+    // slot swizzle of the lane's row (lane & 31 within the block) is the same
+    // in every block: one byte offset per K step serves all blocks.
     const int khalf = lane >> 5;
-
-    // LDS element offsets (within a slice) of this lane's fragment rows, per
-    // K step kk of the slice
-    constexpr int KS = BK / 16;
-    int boffs[KS][4], aoffs[KS][4];
+    const int l32 = lane & 31;
+    uint32_t foff[KS];
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-        const int c = kk * 2 + khalf;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            boffs[kk][i] = brow[i] * BK + ((c ^ swz<BK, SWZ>(brow[i])) * 8);
-            aoffs[kk][i] = arow_l[i] * BK + ((c ^ swz<BK, SWZ>(arow_l[i])) * 8);
-        }
-    }
+    for (int kk = 0; kk < KS; ++kk) foff[kk] = l32 * ROWB + (((2 * kk + khalf) ^ slot_swizzle(l32)) * 16);
+    const char* const sa_w = smem + wm * 128 * ROWB;
+    const char* const sb_w = smem + SA_BYTES;
+    auto b_row0 = [&](int nb) {
+        if (GATEUP) return (nb >> 1) * (TN / 2) + wn * (TN / 4) + (nb & 1) * 32;
+        return wn * (TN / 2) + nb * 32;
+    };
 
     const int nk = K / BK;
-    constexpr int PER = 2 * LPW;  // LDS DMA instructions per slice per wave
-    static_assert(2 * LPW == 16, "the interleaved refill assumes 16 DMAs per slice per wave");
-    static_assert(KS % 2 == 0, "fragment double buffer needs an even step count");
+    // All fragments of one slice: step kk's activation blocks f[kk][0..3] and
+    // weight blocks f[kk][4..7].
+    bf16x8_t f[KS][NR];
+    auto read_frag = [&](int kk, int i, uint32_t so) {
+        if (i < 4)
+            f[kk][i] = *reinterpret_cast<const bf16x8_t*>(sa_w + so + i * 32 * ROWB + foff[kk]);
+        else
+            f[kk][i] = *reinterpret_cast<const bf16x8_t*>(sb_w + so + b_row0(i - 4) * ROWB + foff[kk]);
+    };
+#define MOE_MFMA(KK, Q)                                                                         \
+    acc[(Q) / 4][(Q) % 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                           \
+        f[KK][4 + (Q) / 4], f[KK][(Q) % 4], acc[(Q) / 4][(Q) % 4], 0, 0, 0)
 
-    // fragments of one K step: 4 weight blocks, 4 activation blocks, two sets
-    bf16x8_t fb[2][4], fa[2][4];
-#define MOE_READ_FRAGS(SB, SA, KK, SLOT)                                               \
-    _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                                 \
-        fb[SLOT][i_] = *reinterpret_cast<const bf16x8_t*>((SB) + boffs[KK][i_]);     \
-        fa[SLOT][i_] = *reinterpret_cast<const bf16x8_t*>((SA) + aoffs[KK][i_]);     \
-    }
-#define MOE_MFMA_STEP(SLOT)                                                            \
-    _Pragma("unroll") for (int nb_ = 0; nb_ < 4; ++nb_)                                \
-    _Pragma("unroll") for (int mb_ = 0; mb_ < 4; ++mb_)                                \
-        acc[nb_][mb_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[SLOT][nb_], fa[SLOT][mb_], \
-                                                                acc[nb_][mb_], 0, 0, 0);
-    // spread 8 LDS fragment reads over 16 MFMAs
-#define MOE_INTERLEAVE()                                                               \
-    _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) {                                 \
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                             \
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                             \
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                             \
-    }
-
-    // Ring of NSTAGE slices.  Slice kt's barrier sits before its last K step:
-    // by then every fragment of slice kt is in registers, so the barrier both
-    // frees slot kt % NSTAGE for slice kt + NSTAGE and publishes slice kt + 1,
-    // whose first fragments are read while the last MFMAs of slice kt run.
+    // Per slice kt (stage kt & 1):
+    //   step 0: its MFMAs, with the reads of steps 1..3; then every wave has
+    //           read the stage, and a barrier frees it;
+    //   steps 1..3: MFMAs, with the loads of slice kt + 2 into the freed
+    //           stage spread one per 3 MFMAs (almost two slices to land);
+    //           before step 3, the wait for slice kt + 1 and the barrier that
+    //           publishes it;
+    //   step 3 also reads slice kt + 1's step-0 fragments.
+    // Loads complete in issue order, so each wait leaves pending exactly the
+    // loads of slice kt + 2 issued before it.
+    auto refill = [&](int step, int q, int kt) {  // MFMA q of step 1..3
+        const int p = (step - 1) * NM + q;
+        if (p % 3 == 0 && p / 3 < NL) dma(p / 3, kt + 2);
+    };
+    constexpr int BEFORE3 = (2 * NM + 2) / 3 < NL ? (2 * NM + 2) / 3 : NL;  // loads issued in steps 1..2
 #pragma unroll
-    for (int s = 0; s < NSTAGE; ++s)
-        if (s < nk) load_slice(s);
-    if (nk >= NSTAGE) wait_vmcnt_lgkm0<PER * (NSTAGE - 1)>();
-    else wait_vmcnt_lgkm0<0>();
+    for (int q = 0; q < NL; ++q) dma(q, 0);
+    if (nk > 1) {
+#pragma unroll
+        for (int q = 0; q < NL; ++q) dma(q, 1);
+        wait_vmcnt_lgkm0<NL>();
+    } else {
+        wait_vmcnt_lgkm0<0>();
+    }
     barrier_lds();
-    MOE_READ_FRAGS(sB[0], sA[0], 0, 0)
+#pragma unroll
+    for (int i = 0; i < NR; ++i) read_frag(0, i, 0);
     __builtin_amdgcn_sched_barrier(0);
 
     for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt % NSTAGE;
-        const bf16_t* sa = sA[buf];
-        const bf16_t* sb = sB[buf];
+        const uint32_t so = static_cast<uint32_t>((kt & 1) * STAGE_BYTES);
+        const uint32_t nso = static_cast<uint32_t>(((kt + 1) & 1) * STAGE_BYTES);
+        const bool more = kt + 2 < nk;
+        // step 0: 24 reads over 16 MFMAs
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-            const int cur = kk & 1;
-            if (kk + 1 < KS) {
-                MOE_READ_FRAGS(sb, sa, kk + 1, cur ^ 1)
-                MOE_MFMA_STEP(cur)
-                MOE_INTERLEAVE()
-            } else {
-                if (kt + 1 < nk) {
-                    if (kt + NSTAGE <= nk) wait_vmcnt_lgkm0<PER * (NSTAGE - 2)>();
-                    else wait_vmcnt_lgkm0<0>();
-                    barrier_lds();
-                }
-                // The last K step of the slice: its 16 MFMAs interleaved with
-                // the refill DMAs of slot kt % NSTAGE (slice kt + NSTAGE) and the
-                // next slice's first fragment reads (after the last slice these
-                // read a stale, in-bounds slot whose values are never used).
-                const bool refill = kt + NSTAGE < nk;
-                const uint32_t boff_ = static_cast<uint32_t>(buf * SLICE * 2);
-                const int k0_ = (kt + NSTAGE) * BK;
-                const int nbuf = (kt + 1) % NSTAGE;
-                const bf16_t* nsb = sB[nbuf];
-                const bf16_t* nsa = sA[nbuf];
+        for (int kk = 1; kk < KS; ++kk)
 #pragma unroll
-                for (int q = 0; q < 16; ++q) {
-                    const int nb_ = q >> 2, mb_ = q & 3;
-                    acc[nb_][mb_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[cur][nb_], fa[cur][mb_],
-                                                                          acc[nb_][mb_], 0, 0, 0);
-                    if (refill) dma(q, k0_, boff_);
-                    if (q & 1) {
-                        const int i_ = q >> 1;
-                        if (i_ < 4) fb[cur ^ 1][i_] = *reinterpret_cast<const bf16x8_t*>(nsb + boffs[0][i_]);
-                        else fa[cur ^ 1][i_ - 4] = *reinterpret_cast<const bf16x8_t*>(nsa + aoffs[0][i_ - 4]);
-                    }
-                }
+            for (int i = 0; i < NR; ++i) read_frag(kk, i, so);
+#pragma unroll
+        for (int q = 0; q < NM; ++q) MOE_MFMA(0, q);
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+#pragma unroll
+        for (int i = NR; i < NM; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt_lgkm0<63>();
+        barrier_lds();
+        // steps 1 and 2
+#pragma unroll
+        for (int step = 1; step <= 2; ++step) {
+#pragma unroll
+            for (int q = 0; q < NM; ++q) {
+                if (step == 1) MOE_MFMA(1, q);
+                else MOE_MFMA(2, q);
+                if (more) refill(step, q, kt);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+        if (kt + 1 < nk) {
+            if (more) wait_vmcnt<BEFORE3>();
+            else wait_vmcnt<0>();
+            barrier_lds();
+        }
+        // step 3 (after the last slice the reads fetch a stale, in-bounds
+        // stage whose values are never used)
+#pragma unroll
+        for (int q = 0; q < NM; ++q) {
+            MOE_MFMA(3, q);
+            if (more) refill(3, q, kt);
+            if ((q & 1) && (q >> 1) < NR) read_frag(0, q >> 1, nso);
+        }
+        __builtin_amdgcn_sched_barrier(0);
     }
-#undef MOE_READ_FRAGS
-#undef MOE_MFMA_STEP
-#undef MOE_INTERLEAVE
+#undef MOE_MFMA
 
     // Epilogue.  Block (nb, mb): lane owns output row m = mb*32 + (lane & 31)
-    // and, for g = 0..3, columns nb*32 + 8g + 4*(lane >> 5) + 0..3 (registers
-    // 4g .. 4g+3).
+    // and, for g = 0..3, columns 8g + 4*(lane >> 5) + 0..3 of the block
+    // (registers 4g .. 4g+3).
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
-        const int pos = tile.row0 + wm * 128 + mb * 32 + (lane & 31);
+        const int pos = tile.row0 + wm * 128 + mb * 32 + l32;
         if (pos >= tile.row1) continue;
         bf16_t* crow = C + static_cast<int64_t>(pos) * N;
         if (GATEUP) {
@@ -548,15 +581,15 @@ hipError_t launch_expert_ffn(const moe_problem_t& p, const void* x_perm, const v
         const bf16_t* a = static_cast<const bf16_t*>(gather ? x : x_perm);
         const unsigned g1 = grid_for(n, p.E, kBM, static_cast<int>(ceil_div(p.f, kGateUpCols)));
         if (gather)
-            grouped_gemm_bf16_kernel<true, true, GEMM_BK, GEMM_STAGES, GEMM_SWZ><<<g1, 256, 0, s>>>(
+            grouped_gemm_bf16_kernel<true, true><<<g1, 256, 0, s>>>(
                 a, sorted_assign, p.k, offsets, p.E, static_cast<const bf16_t*>(w_gate),
                 static_cast<const bf16_t*>(w_up), static_cast<bf16_t*>(h), p.f, p.d);
         else
-            grouped_gemm_bf16_kernel<true, false, GEMM_BK, GEMM_STAGES, GEMM_SWZ><<<g1, 256, 0, s>>>(
+            grouped_gemm_bf16_kernel<true, false><<<g1, 256, 0, s>>>(
                 a, sorted_assign, p.k, offsets, p.E, static_cast<const bf16_t*>(w_gate),
                 static_cast<const bf16_t*>(w_up), static_cast<bf16_t*>(h), p.f, p.d);
         const unsigned g2 = grid_for(n, p.E, kBM, static_cast<int>(ceil_div(p.d, kDownCols)));
-        grouped_gemm_bf16_kernel<false, false, GEMM_BK, GEMM_STAGES, GEMM_SWZ><<<g2, 256, 0, s>>>(
+        grouped_gemm_bf16_kernel<false, false><<<g2, 256, 0, s>>>(
             static_cast<const bf16_t*>(h), sorted_assign, p.k, offsets, p.E,
             static_cast<const bf16_t*>(w_down), nullptr, static_cast<bf16_t*>(y_perm), p.d, p.f);
     } else {

@@ -27,6 +27,8 @@ moe_status_t check_problem(const moe_problem_t* p) {
     if (p->E > MOE_MAX_EXPERTS || p->k > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
     if (p->T > INT32_MAX / p->k) return MOE_ERR_UNSUPPORTED;
     if (p->dtype == MOE_DTYPE_BF16 && (p->d % 64 != 0 || p->f % 64 != 0)) return MOE_ERR_UNSUPPORTED;
+    // the bf16 GEMMs address one expert's weight matrix with 32-bit byte offsets
+    if (p->dtype == MOE_DTYPE_BF16 && static_cast<int64_t>(p->d) * p->f > INT32_MAX) return MOE_ERR_UNSUPPORTED;
     if (expert_ffn_grid_bound(*p) > INT32_MAX) return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }

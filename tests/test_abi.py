@@ -77,6 +77,7 @@ def ws_size(lib, p, op):
     (dict(d=100), L.MOE_ERR_UNSUPPORTED),           # bf16 needs d % 64 == 0
     (dict(f=96), L.MOE_ERR_UNSUPPORTED),
     (dict(T=2 ** 30, k=2), L.MOE_ERR_UNSUPPORTED),  # T*k >= 2^31
+    (dict(d=65536, f=32768), L.MOE_ERR_UNSUPPORTED),  # bf16 d*f >= 2^31
 ])
 def test_problem_validation(lib, bad, status):
     p = prob(**bad)
