@@ -215,7 +215,7 @@ __device__ __forceinline__ const T* uniform_ptr(const T* p) {
     return reinterpret_cast<const T*>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
-template <bool GATEUP, bool GATHER>
+template <bool GATEUP, bool GATHER, bool WIDE>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void grouped_gemm_bf16_kernel(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ sorted_assign, int topk,
     const int32_t* __restrict__ offsets, int E, const bf16_t* __restrict__ B0,
@@ -261,21 +261,26 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // Loads: wave w fills activation rows w*64 .. +64 and weight rows
     // w*64 .. +64 of a stage; load j covers 8 rows, lane -> (row lrow, LDS
     // slot lslot), and the slot receives global chunk lslot ^ swizzle(row).
-    // Gathered activation rows use 64-bit addresses; the others a uniform
-    // base and 32-bit byte offsets (one expert's weights stay below 4 GiB).
-    const bf16_t* a_src[GATHER ? LA : 1];
-    uint32_t a_off[GATHER ? 1 : LA];
-    const bf16_t* const a_base = uniform_ptr(A + static_cast<int64_t>(tile.row0) * K);
+    // Operand rows are addressed as a uniform base plus 32-bit byte offsets
+    // (one expert's weights stay below 4 GiB), except gathered activation
+    // rows of an x of 2^31 elements or more (WIDE), which take 64-bit
+    // addresses.
+    static_assert(GATHER || !WIDE, "only gathered rows need 64-bit addresses");
+    const bf16_t* a_src[WIDE ? LA : 1];
+    uint32_t a_off[WIDE ? 1 : LA];
+    const bf16_t* const a_base = uniform_ptr(GATHER ? A : A + static_cast<int64_t>(tile.row0) * K);
 #pragma unroll
     for (int j = 0; j < LA; ++j) {
         const int r = wave * 64 + j * 8 + lrow;
         const int chunk = lslot ^ slot_swizzle(r);
         int pos = tile.row0 + r;
         if (pos >= tile.row1) pos = tile.row1 - 1;
-        if (GATHER)
-            a_src[GATHER ? j : 0] = A + static_cast<int64_t>(sorted_assign[pos] / topk) * K + chunk * 8;
+        if (WIDE)
+            a_src[WIDE ? j : 0] = A + static_cast<int64_t>(sorted_assign[pos] / topk) * K + chunk * 8;
+        else if (GATHER)
+            a_off[WIDE ? 0 : j] = (static_cast<uint32_t>(sorted_assign[pos] / topk) * K + chunk * 8) * 2u;
         else
-            a_off[GATHER ? 0 : j] = (static_cast<uint32_t>(pos - tile.row0) * K + chunk * 8) * 2u;
+            a_off[WIDE ? 0 : j] = (static_cast<uint32_t>(pos - tile.row0) * K + chunk * 8) * 2u;
     }
     // In GEMM1 the first 128 weight rows are gate rows and the rest up rows,
     // so each wave's rows come from one matrix.
@@ -300,8 +305,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         const bool a_op = A_FIRST ? q < LA : q >= LB;
         const int j = a_op ? (A_FIRST ? q : q - LB) : (A_FIRST ? q - LA : q);
         if (a_op) {
-            if (GATHER) lds_dma16(a_src[GATHER ? j : 0] + kt * BK, lds_a + so + j * 8 * ROWB);
-            else lds_dma16_s(a_base + kt * BK, a_off[GATHER ? 0 : j], lds_a + so + j * 8 * ROWB);
+            if (WIDE) lds_dma16(a_src[WIDE ? j : 0] + kt * BK, lds_a + so + j * 8 * ROWB);
+            else lds_dma16_s(a_base + kt * BK, a_off[WIDE ? 0 : j], lds_a + so + j * 8 * ROWB);
         } else {
             lds_dma16_s(b_base + kt * BK, b_off[j], lds_b + so + j * 8 * ROWB);
         }
@@ -580,16 +585,20 @@ hipError_t launch_expert_ffn(const moe_problem_t& p, const void* x_perm, const v
     if (p.dtype == MOE_DTYPE_BF16) {
         const bf16_t* a = static_cast<const bf16_t*>(gather ? x : x_perm);
         const unsigned g1 = grid_for(n, p.E, kBM, static_cast<int>(ceil_div(p.f, kGateUpCols)));
-        if (gather)
-            grouped_gemm_bf16_kernel<true, true><<<g1, 256, 0, s>>>(
+        if (gather && p.T * p.d >= (int64_t{1} << 31))
+            grouped_gemm_bf16_kernel<true, true, true><<<g1, 256, 0, s>>>(
+                a, sorted_assign, p.k, offsets, p.E, static_cast<const bf16_t*>(w_gate),
+                static_cast<const bf16_t*>(w_up), static_cast<bf16_t*>(h), p.f, p.d);
+        else if (gather)
+            grouped_gemm_bf16_kernel<true, true, false><<<g1, 256, 0, s>>>(
                 a, sorted_assign, p.k, offsets, p.E, static_cast<const bf16_t*>(w_gate),
                 static_cast<const bf16_t*>(w_up), static_cast<bf16_t*>(h), p.f, p.d);
         else
-            grouped_gemm_bf16_kernel<true, false><<<g1, 256, 0, s>>>(
+            grouped_gemm_bf16_kernel<true, false, false><<<g1, 256, 0, s>>>(
                 a, sorted_assign, p.k, offsets, p.E, static_cast<const bf16_t*>(w_gate),
                 static_cast<const bf16_t*>(w_up), static_cast<bf16_t*>(h), p.f, p.d);
         const unsigned g2 = grid_for(n, p.E, kBM, static_cast<int>(ceil_div(p.d, kDownCols)));
-        grouped_gemm_bf16_kernel<false, false><<<g2, 256, 0, s>>>(
+        grouped_gemm_bf16_kernel<false, false, false><<<g2, 256, 0, s>>>(
             static_cast<const bf16_t*>(h), sorted_assign, p.k, offsets, p.E,
             static_cast<const bf16_t*>(w_down), nullptr, static_cast<bf16_t*>(y_perm), p.d, p.f);
     } else {

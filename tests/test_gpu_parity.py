@@ -195,6 +195,38 @@ def test_expert_ffn_and_combine(T, d, E, k, f, dtype, kind, fused_gather):
     assert rel(host(y), y_ref) <= (1e-6 if dtype == "f32" else 4e-3)
 
 
+def test_expert_ffn_gather_from_x_beyond_4gib():
+    # x with 2^31 or more elements: the fused gather addresses its rows with
+    # 64-bit offsets.  x repeats a seeded block of R rows, so the oracle
+    # knows every row; the sample includes tokens past the 4 GiB mark.
+    T, d, E, k, f, R = (1 << 31) // 4096 + 256, 4096, 4, 1, 64, 4096
+    print(f"ffn beyond 4 GiB: T={T} d={d} E={E} k={k} f={f}", flush=True)
+    p = mi.Problem(T, d, E, k, f, "bf16")
+    block = mi.make_x(mi.Problem(R, d, E, k, f, "bf16"), seed=5)
+    W = dict(zip(("w_gate", "w_up", "w_down"), mi.make_expert_weights(p, seed=5)))
+    ids, _ = O.topk_route(mi.make_gaussian_logits(p, 5), k)
+    q = O.dispatch(ids, E)
+    xb = dev(block)
+    x = xb.repeat((T + R - 1) // R, 1)[:T].contiguous()
+    del xb
+    y_perm = poison((T * k, d), torch.bfloat16)
+    moe.expert_ffn(dev(q["offsets"]), dev(W["w_gate"]), dev(W["w_up"]), dev(W["w_down"]), k, T, x=x,
+                   sorted_assign=dev(q["sorted_assign"]), y_perm=y_perm)
+    torch.cuda.synchronize()
+    del x
+    tok = np.unique(np.concatenate([[0, R - 1, T // 2, T - 256, T - 1],
+                                    mi.sample_tokens(T, 24, seed=5)]))
+    assert tok.max() * d >= (1 << 31)
+    wf = {n: f32_of(W[n], "bf16") for n in W}
+    x32 = f32_of(block, "bf16")
+    for t in tok:
+        for j in range(k):
+            e = int(ids[t, j])
+            ref = O.swiglu_expert(x32[t % R][None], wf["w_gate"][e], wf["w_up"][e], wf["w_down"][e])[0]
+            pos = int(q["assign_pos"][t * k + j])
+            assert rel(host(y_perm[pos]), ref) <= TOL["bf16"], (t, j)
+
+
 # --------------------------------------------------------------------------
 # the whole layer
 # --------------------------------------------------------------------------
