@@ -22,6 +22,7 @@
 // tile, so the weight tile and the activation tiles a workgroup needs are
 // mostly already in its XCD's L2.
 #include <algorithm>
+#include <atomic>
 
 #include "device_util.h"
 #include "moe_internal.h"
@@ -78,22 +79,17 @@ struct Tile {
     int nt;      // column tile
 };
 
-// Maps this workgroup to a (row tile, column tile) pair; false when it has
-// no work.
-__device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, int E, int bm,
-                                          int n_tiles, const int* s_prefix, Tile& t) {
+// Row tile and column tile of position pid in the tile order: groups of
+// GROUP_M row tiles, each group walked column tile by column tile.
+__device__ __forceinline__ Tile tile_of(int pid, const int32_t* __restrict__ offsets, int E, int bm,
+                                        int n_tiles, const int* s_prefix) {
     const int total_m = s_prefix[E];
-    const int total = total_m * n_tiles;
-    const int hw = blockIdx.x;
-    const int per_xcd = (total + NUM_XCD - 1) / NUM_XCD;
-    if (hw >= per_xcd * NUM_XCD) return false;
-    const int pid = (hw % NUM_XCD) * per_xcd + hw / NUM_XCD;
-    if (pid >= total) return false;
     const int group = pid / (GROUP_M * n_tiles);
     const int first_m = group * GROUP_M;
     const int gsz = min(GROUP_M, total_m - first_m);
     const int local = pid - group * GROUP_M * n_tiles;
     const int mt = first_m + local % gsz;
+    Tile t;
     t.nt = local / gsz;
     int lo = 0, hi = E;
     while (hi - lo > 1) {
@@ -103,6 +99,70 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, i
     t.e = lo;
     t.row0 = offsets[lo] + (mt - s_prefix[lo]) * bm;
     t.row1 = min(t.row0 + bm, offsets[lo + 1]);
+    return t;
+}
+
+// Split-K plan: the first `full` tiles of the order (a multiple of `slots`,
+// the workgroups resident at once) run whole; when the rest would leave most
+// workgroup slots idle in a last wave, each of them runs as S K ranges.
+// slots = 0: no split.
+struct SplitPlan {
+    int total, full, S;
+};
+__device__ __forceinline__ SplitPlan split_plan(int total, int slots, int nk) {
+    SplitPlan sp{total, total, 1};
+    if (slots > 0) {
+        const int r = total % slots;
+        const int S = r > 0 ? min(slots / r, min(kSplitMax, nk / kSplitMinSlices)) : 1;
+        if (S >= 2) {
+            sp.full = total - r;
+            sp.S = S;
+        }
+    }
+    return sp;
+}
+
+// This workgroup's work: a whole tile (j = -1, K slices [0, nk)) or K slices
+// [kb, kb + nkl) of split tile number j / S of the tail, whose partial sums
+// go to slot j.  The workgroup id is remapped so that each XCD (workgroups
+// are dealt to the 8 XCDs round-robin) walks one contiguous range of the
+// whole tiles; the split work comes after every whole tile.
+struct Work {
+    Tile t;
+    int kb, nkl, j;
+};
+__device__ __forceinline__ bool find_work(const int32_t* __restrict__ offsets, int E, int bm,
+                                          int n_tiles, const int* s_prefix, int nk, int slots,
+                                          Work& w) {
+    const SplitPlan sp = split_plan(s_prefix[E] * n_tiles, slots, nk);
+    const int hw = blockIdx.x;
+    const int per_xcd = (sp.full + NUM_XCD - 1) / NUM_XCD;
+    int pid;
+    if (hw < per_xcd * NUM_XCD) {
+        pid = (hw % NUM_XCD) * per_xcd + hw / NUM_XCD;
+        if (pid >= sp.full) return false;
+        w.kb = 0;
+        w.nkl = nk;
+        w.j = -1;
+    } else {
+        const int j = hw - per_xcd * NUM_XCD;
+        if (j >= (sp.total - sp.full) * sp.S) return false;
+        pid = sp.full + j / sp.S;
+        const int part = j % sp.S;
+        w.kb = part * nk / sp.S;
+        w.nkl = (part + 1) * nk / sp.S - w.kb;
+        w.j = j;
+    }
+    w.t = tile_of(pid, offsets, E, bm, n_tiles, s_prefix);
+    return true;
+}
+
+// This workgroup's whole tile (no split); false when it has no work.
+__device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, int E, int bm,
+                                          int n_tiles, const int* s_prefix, Tile& t) {
+    Work w;
+    if (!find_work(offsets, E, bm, n_tiles, s_prefix, 1, 0, w)) return false;
+    t = w.t;
     return true;
 }
 
@@ -219,7 +279,8 @@ template <bool GATEUP, bool GATHER, bool WIDE>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void grouped_gemm_bf16_kernel(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ sorted_assign, int topk,
     const int32_t* __restrict__ offsets, int E, const bf16_t* __restrict__ B0,
-    const bf16_t* __restrict__ B1, bf16_t* __restrict__ C, int N, int K) {
+    const bf16_t* __restrict__ B1, bf16_t* __restrict__ C, int N, int K, int slots,
+    float* __restrict__ part) {
     constexpr int TM = 256;                  // activation rows per tile
     constexpr int TN = 256;                  // weight rows per tile
     constexpr int BK = 64;                   // K slice width (one 128-byte line per row)
@@ -245,8 +306,10 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 
     build_tile_prefix(offsets, E, TM, s_prefix);
     const int n_tiles = (N + BN_OUT - 1) / BN_OUT;
-    Tile tile;
-    if (!find_tile(offsets, E, TM, n_tiles, s_prefix, tile)) return;
+    Work work;
+    // (GEMM1 never splits: its epilogue is not linear in the partial sums)
+    if (!find_work(offsets, E, TM, n_tiles, s_prefix, K / BK, GATEUP ? 0 : slots, work)) return;
+    const Tile tile = work.t;
     __syncthreads();  // every lookup is done before the loads overwrite the table
 
     const int tid = threadIdx.x;
@@ -268,7 +331,9 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     static_assert(GATHER || !WIDE, "only gathered rows need 64-bit addresses");
     const bf16_t* a_src[WIDE ? LA : 1];
     uint32_t a_off[WIDE ? 1 : LA];
-    const bf16_t* const a_base = uniform_ptr(GATHER ? A : A + static_cast<int64_t>(tile.row0) * K);
+    // (the K range [work.kb, work.kb + work.nkl) of 64-column slices is folded into the bases)
+    const bf16_t* const a_base =
+        uniform_ptr((GATHER ? A : A + static_cast<int64_t>(tile.row0) * K) + work.kb * BK);
 #pragma unroll
     for (int j = 0; j < LA; ++j) {
         const int r = wave * 64 + j * 8 + lrow;
@@ -276,7 +341,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         int pos = tile.row0 + r;
         if (pos >= tile.row1) pos = tile.row1 - 1;
         if (WIDE)
-            a_src[WIDE ? j : 0] = A + static_cast<int64_t>(sorted_assign[pos] / topk) * K + chunk * 8;
+            a_src[WIDE ? j : 0] = A + static_cast<int64_t>(sorted_assign[pos] / topk) * K + work.kb * BK + chunk * 8;
         else if (GATHER)
             a_off[WIDE ? 0 : j] = (static_cast<uint32_t>(sorted_assign[pos] / topk) * K + chunk * 8) * 2u;
         else
@@ -286,7 +351,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // so each wave's rows come from one matrix.
     const int rb0 = wave * (TN / 4);
     const bf16_t* const b_base =
-        uniform_ptr((GATEUP && rb0 >= TN / 2 ? B1 : B0) + static_cast<int64_t>(tile.e) * N * K);
+        uniform_ptr((GATEUP && rb0 >= TN / 2 ? B1 : B0) + static_cast<int64_t>(tile.e) * N * K + work.kb * BK);
     uint32_t b_off[LB];
 #pragma unroll
     for (int j = 0; j < LB; ++j) {
@@ -335,7 +400,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         return wn * (TN / 2) + nb * 32;
     };
 
-    const int nk = K / BK;
+    const int nk = work.nkl;
     // All fragments of one slice: step kk's activation blocks f[kk][0..3] and
     // weight blocks f[kk][4..7].
     bf16x8_t f[KS][NR];
@@ -430,6 +495,19 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     }
 #undef MOE_MFMA
 
+    // A split K range: the fp32 partial sums go to slot work.j, register by
+    // register (register r of thread t at (j * 256 + r) * 256 + t).
+    if (!GATEUP && work.j >= 0) {
+        float* const dst = const_cast<float*>(uniform_ptr(part + static_cast<int64_t>(work.j) * 256 * 256));
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) dst[((nb * 4 + mb) * 16 + i) * 256 + tid] = acc[nb][mb][i];
+        return;
+    }
+
     // Epilogue.  Block (nb, mb): lane owns output row m = mb*32 + (lane & 31)
     // and, for g = 0..3, columns 8g + 4*(lane >> 5) + 0..3 of the block
     // (registers 4g .. 4g+3).
@@ -464,6 +542,50 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                     *reinterpret_cast<bf16x4_t*>(crow + col) = o;
                 }
         }
+    }
+}
+
+// Split-K reduction of the down projection's tail: 16 workgroups per split
+// tile t, one per 32 x 32 accumulator block (nb, mb) of each wave, sum the S
+// partial tiles in a fixed order (so the result does not depend on
+// scheduling) and store the block as the GEMM2 epilogue would.
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ part,
+                                                           const int32_t* __restrict__ offsets, int E,
+                                                           int N, int nk, int slots,
+                                                           bf16_t* __restrict__ C) {
+    __shared__ int s_prefix[MOE_MAX_EXPERTS + 1];
+    build_tile_prefix(offsets, E, kBM, s_prefix);
+    const int n_tiles = (N + kDownCols - 1) / kDownCols;
+    const SplitPlan sp = split_plan(s_prefix[E] * n_tiles, slots, nk);
+    const int t = blockIdx.x >> 4;
+    if (t >= sp.total - sp.full) return;
+    const int nb = (blockIdx.x >> 2) & 3;
+    const int mb = blockIdx.x & 3;
+    const Tile tile = tile_of(sp.full + t, offsets, E, kBM, n_tiles, s_prefix);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int pos = tile.row0 + (wave >> 1) * 128 + mb * 32 + (lane & 31);
+    if (pos >= tile.row1) return;
+    const int r0 = (nb * 4 + mb) * 16;
+    const float* src = part + (static_cast<int64_t>(t) * sp.S * 256 + r0) * 256 + tid;
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = src[i * 256];
+    for (int sidx = 1; sidx < sp.S; ++sidx) {
+        const float* ps = src + static_cast<int64_t>(sidx) * 256 * 256;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] += ps[i * 256];
+    }
+    bf16_t* crow = C + static_cast<int64_t>(pos) * N;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const int col = tile.nt * kDownCols + (wave & 1) * 128 + nb * 32 + 8 * g + 4 * (lane >> 5);
+        if (col >= N) continue;
+        bf16x4_t o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = f32_to_bf16(v[4 * g + i]);
+        *reinterpret_cast<bf16x4_t*>(crow + col) = o;
     }
 }
 
@@ -570,37 +692,61 @@ int64_t expert_ffn_grid_bound(const moe_problem_t& p) {
     const int64_t n = p.T * p.k;
     if (p.dtype == MOE_DTYPE_BF16) {
         const int64_t m = max_m_tiles(n, p.E, kBM);
-        return m * std::max(ceil_div(p.f, kGateUpCols), ceil_div(p.d, kDownCols)) + NUM_XCD;
+        return m * std::max(ceil_div(p.f, kGateUpCols), ceil_div(p.d, kDownCols)) + NUM_XCD + kSplitWGs;
     }
     const int64_t m = max_m_tiles(n, p.E, kF32BM);
     return m * std::max(ceil_div(p.f, kF32BN), ceil_div(p.d, kF32BN)) + NUM_XCD;
 }
 
+// Workgroups of the bf16 GEMM that run at once on the current device: one
+// per CU (each takes 160 KB of LDS), at most kSplitWGs; 0 if unknown.
+int resident_slots() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            return 0;
+        v = std::min(cus, kSplitWGs);
+        cache[dev].store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
 hipError_t launch_expert_ffn(const moe_problem_t& p, const void* x_perm, const void* x,
                              const int32_t* sorted_assign, const int32_t* offsets,
                              const void* w_gate, const void* w_up, const void* w_down,
-                             void* h, void* y_perm, hipStream_t s) {
+                             void* ffn_ws, void* y_perm, hipStream_t s) {
     const int64_t n = p.T * p.k;
     const bool gather = (x_perm == nullptr);
+    void* h = ffn_ws;
     if (p.dtype == MOE_DTYPE_BF16) {
         const bf16_t* a = static_cast<const bf16_t*>(gather ? x : x_perm);
         const unsigned g1 = grid_for(n, p.E, kBM, static_cast<int>(ceil_div(p.f, kGateUpCols)));
         if (gather && p.T * p.d >= (int64_t{1} << 31))
             grouped_gemm_bf16_kernel<true, true, true><<<g1, 256, 0, s>>>(
                 a, sorted_assign, p.k, offsets, p.E, static_cast<const bf16_t*>(w_gate),
-                static_cast<const bf16_t*>(w_up), static_cast<bf16_t*>(h), p.f, p.d);
+                static_cast<const bf16_t*>(w_up), static_cast<bf16_t*>(h), p.f, p.d, 0, nullptr);
         else if (gather)
             grouped_gemm_bf16_kernel<true, true, false><<<g1, 256, 0, s>>>(
                 a, sorted_assign, p.k, offsets, p.E, static_cast<const bf16_t*>(w_gate),
-                static_cast<const bf16_t*>(w_up), static_cast<bf16_t*>(h), p.f, p.d);
+                static_cast<const bf16_t*>(w_up), static_cast<bf16_t*>(h), p.f, p.d, 0, nullptr);
         else
             grouped_gemm_bf16_kernel<true, false, false><<<g1, 256, 0, s>>>(
                 a, sorted_assign, p.k, offsets, p.E, static_cast<const bf16_t*>(w_gate),
-                static_cast<const bf16_t*>(w_up), static_cast<bf16_t*>(h), p.f, p.d);
+                static_cast<const bf16_t*>(w_up), static_cast<bf16_t*>(h), p.f, p.d, 0, nullptr);
         const unsigned g2 = grid_for(n, p.E, kBM, static_cast<int>(ceil_div(p.d, kDownCols)));
-        grouped_gemm_bf16_kernel<false, false, false><<<g2, 256, 0, s>>>(
+        const int slots = ffn_can_split(p) ? resident_slots() : 0;
+        float* part = slots > 0 ? reinterpret_cast<float*>(static_cast<char*>(ffn_ws) + ffn_h_bytes(p)) : nullptr;
+        grouped_gemm_bf16_kernel<false, false, false><<<g2 + (slots > 0 ? kSplitWGs : 0), 256, 0, s>>>(
             static_cast<const bf16_t*>(h), sorted_assign, p.k, offsets, p.E,
-            static_cast<const bf16_t*>(w_down), nullptr, static_cast<bf16_t*>(y_perm), p.d, p.f);
+            static_cast<const bf16_t*>(w_down), nullptr, static_cast<bf16_t*>(y_perm), p.d, p.f, slots,
+            part);
+        if (slots > 0)
+            split_reduce_kernel<<<kSplitWGs * 16, 256, 0, s>>>(part, offsets, p.E, p.d, p.f / 64, slots,
+                                                          static_cast<bf16_t*>(y_perm));
     } else {
         const float* a = static_cast<const float*>(gather ? x : x_perm);
         const unsigned g1 = grid_for(n, p.E, kF32BM, static_cast<int>(ceil_div(p.f, kF32BN)));

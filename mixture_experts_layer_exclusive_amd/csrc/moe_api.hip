@@ -73,9 +73,7 @@ size_t dispatch_ws(const moe_problem_t& p) {
     return align_up(static_cast<size_t>(dispatch_blocks(n)) * p.E * 4, kAlign);
 }
 
-size_t ffn_ws(const moe_problem_t& p) {
-    return align_up(static_cast<size_t>(p.T) * p.k * p.f * elem_bytes(p), kAlign);
-}
+size_t ffn_ws(const moe_problem_t& p) { return ffn_h_bytes(p) + ffn_split_bytes(p); }
 
 size_t forward_ws(const moe_problem_t& p) {
     const size_t n = static_cast<size_t>(p.T) * p.k;
@@ -85,7 +83,7 @@ size_t forward_ws(const moe_problem_t& p) {
     b += align_up(static_cast<size_t>(p.E) * 4, kAlign);       // counts
     b += align_up(static_cast<size_t>(p.E + 1) * 4, kAlign);   // offsets
     b += dispatch_ws(p);                                        // block counts
-    b += ffn_ws(p);                                             // h
+    b += ffn_ws(p);                                             // h, split-K partials
     b += align_up(n * p.d * elem_bytes(p), kAlign);             // y_perm
     return b;
 }

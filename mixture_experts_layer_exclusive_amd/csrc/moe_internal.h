@@ -20,11 +20,31 @@ constexpr int kDownCols = 256;    // output columns per GEMM2 tile
 constexpr int kF32BM = 64;
 constexpr int kF32BN = 64;
 
+// Split-K of the down projection's last partial wave (bf16): the tiles that
+// would leave most CUs idle in a last wave are each cut into S K ranges
+// (2 <= S <= kSplitMax, at least kSplitMinSlices 64-wide K slices each) and
+// reduced by a second kernel.  The workspace holds kSplitWGs partial tiles.
+constexpr int kSplitWGs = 256;
+constexpr int kSplitMax = 8;
+constexpr int kSplitMinSlices = 8;
+
 // ---- small host helpers ------------------------------------------------------
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Expert-FFN workspace: h [T*k, f], then (bf16, when the down projection can
+// split) the fp32 partial tiles of the split-K tail.
+inline size_t ffn_h_bytes(const moe_problem_t& p) {
+    return align_up(static_cast<size_t>(p.T) * p.k * p.f * (p.dtype == MOE_DTYPE_F32 ? 4 : 2), 256);
+}
+inline bool ffn_can_split(const moe_problem_t& p) {
+    return p.dtype == MOE_DTYPE_BF16 && p.f / 64 >= 2 * kSplitMinSlices;
+}
+inline size_t ffn_split_bytes(const moe_problem_t& p) {
+    return ffn_can_split(p) ? static_cast<size_t>(kSplitWGs) * kBM * kDownCols * 4 : 0;
+}
 
 // Assignments per workgroup of the histogram and scatter kernels: a multiple
 // of 256 sized so that about 256 workgroups (one per CU) share the work, at
@@ -59,7 +79,7 @@ hipError_t launch_gather_rows(const moe_problem_t& p, const void* x, const int32
 hipError_t launch_expert_ffn(const moe_problem_t& p, const void* x_perm, const void* x,
                              const int32_t* sorted_assign, const int32_t* offsets,
                              const void* w_gate, const void* w_up, const void* w_down,
-                             void* h, void* y_perm, hipStream_t s);
+                             void* ffn_ws, void* y_perm, hipStream_t s);
 
 hipError_t launch_combine(const moe_problem_t& p, const void* y_perm, const int32_t* assign_pos,
                           const float* gates, void* y, hipStream_t s);

@@ -158,8 +158,13 @@ def test_workspace_has_no_dense_routing_matrix(lib):
         _, nd = ws_size(lib, p, L.MOE_OP_DISPATCH)
         assert nd <= E * 256 * 4 + 256  # at most 256 blocks
         assert nd * 16 < T * E * 4
-        # forward: logits, ids/gates/permutations, counts, h and y_perm only
+        # forward: logits, ids/gates/permutations, counts, h, y_perm and the
+        # split-K partial tiles of the down projection (256 tiles of 256 x 256
+        # fp32) only
         _, nw = ws_size(lib, p, L.MOE_OP_FORWARD)
         s = 2
-        expect = T * E * 4 + 4 * T * k * 4 + T * k * f * s + T * k * d * s + nd
+        split = 256 * 256 * 256 * 4 if f >= 1024 else 0
+        expect = T * E * 4 + 4 * T * k * 4 + T * k * f * s + T * k * d * s + nd + split
         assert expect <= nw <= expect + 16 * 256
+        _, nf = ws_size(lib, p, L.MOE_OP_EXPERT_FFN)
+        assert T * k * f * s + split <= nf <= T * k * f * s + split + 256

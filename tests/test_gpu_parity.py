@@ -154,6 +154,8 @@ FFN_CASES = [
     (256, 128, 8, 2, 256, "f32", "gauss"),
     (200, 100, 6, 3, 70, "f32", "ties"),
     (1, 64, 8, 2, 64, "bf16", "gauss"),
+    (1024, 256, 4, 2, 2048, "bf16", "gauss"),  # few tiles: the down projection splits K (S = 4)
+    (700, 320, 8, 2, 1088, "bf16", "gauss"),   # uneven split ranges (17 slices), column tail
 ]
 
 
