@@ -206,7 +206,6 @@ __device__ __forceinline__ float silu_mul_fast(float g, float u) {
 // Rows past the end of an expert's queue (or past N) load a clamped valid row
 // and their results are never stored.
 // ---------------------------------------------------------------------------
-typedef uint16_t bf16x4_t __attribute__((ext_vector_type(4)));
 
 // LDS slot of chunk c of tile row r: c ^ slot_swizzle(r).
 __device__ __forceinline__ int slot_swizzle(int r) { return (r >> 1) & 7; }
@@ -523,11 +522,10 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                 for (int g = 0; g < 4; ++g) {
                     const int col = n0 + wn * 64 + nb * 32 + 8 * g + 4 * khalf;
                     if (col >= N) continue;
-                    bf16x4_t o;
+                    float v[4];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        o[i] = f32_to_bf16(silu_mul_fast(acc[nb][mb][4 * g + i], acc[nb + 2][mb][4 * g + i]));
-                    *reinterpret_cast<bf16x4_t*>(crow + col) = o;
+                    for (int i = 0; i < 4; ++i) v[i] = silu_mul_fast(acc[nb][mb][4 * g + i], acc[nb + 2][mb][4 * g + i]);
+                    *reinterpret_cast<uint2*>(crow + col) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
                 }
         } else {
 #pragma unroll
@@ -536,10 +534,9 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                 for (int g = 0; g < 4; ++g) {
                     const int col = n0 + wn * 128 + nb * 32 + 8 * g + 4 * khalf;
                     if (col >= N) continue;
-                    bf16x4_t o;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) o[i] = f32_to_bf16(acc[nb][mb][4 * g + i]);
-                    *reinterpret_cast<bf16x4_t*>(crow + col) = o;
+                    const f32x16_t& a = acc[nb][mb];
+                    *reinterpret_cast<uint2*>(crow + col) =
+                        make_uint2(pack_bf16x2(a[4 * g], a[4 * g + 1]), pack_bf16x2(a[4 * g + 2], a[4 * g + 3]));
                 }
         }
     }
@@ -582,10 +579,8 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
     for (int g = 0; g < 4; ++g) {
         const int col = tile.nt * kDownCols + (wave & 1) * 128 + nb * 32 + 8 * g + 4 * (lane >> 5);
         if (col >= N) continue;
-        bf16x4_t o;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = f32_to_bf16(v[4 * g + i]);
-        *reinterpret_cast<bf16x4_t*>(crow + col) = o;
+        *reinterpret_cast<uint2*>(crow + col) =
+            make_uint2(pack_bf16x2(v[4 * g], v[4 * g + 1]), pack_bf16x2(v[4 * g + 2], v[4 * g + 3]));
     }
 }
 
