@@ -41,33 +41,43 @@ constexpr int GROUP_M = GEMM_GROUP_M;
 constexpr int NUM_XCD = 8;
 
 // Per-expert tile prefix in LDS: s_prefix[e] = sum_{e' < e} ceil(rows_e' / bm),
-// s_prefix[E] = total row tiles.  Computed by wave 0.
+// s_prefix[E] = total row tiles, and a copy of offsets[0..E] in s_off (so
+// that the tile lookups need no second global round trip).  Computed by
+// wave 0.
 __device__ __forceinline__ void build_tile_prefix(const int32_t* __restrict__ offsets, int E, int bm,
-                                                  int* s_prefix) {
+                                                  int* s_prefix, int* s_off) {
     if (threadIdx.x < 64) {
         const int lane = threadIdx.x;
+        // lane owns experts 4*lane .. 4*lane+3; all its loads go out together
+        // (clamped indices, no branches), so this costs one round trip
+        int o[5];
+#pragma unroll
+        for (int i = 0; i < 5; ++i) o[i] = offsets[min(lane * 4 + i, E)];
         int c[4];
         int local = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int e = lane * 4 + i;
-            c[i] = (e < E) ? (offsets[e + 1] - offsets[e] + bm - 1) / bm : 0;
+            c[i] = (lane * 4 + i < E) ? (o[i + 1] - o[i] + bm - 1) / bm : 0;
             local += c[i];
         }
         int incl = local;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
-            const int o = __shfl_up(incl, off, 64);
-            if (lane >= off) incl += o;
+            const int v = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += v;
         }
         int run = incl - local;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int e = lane * 4 + i;
-            if (e < E) s_prefix[e] = run;
+            if (e < E) {
+                s_prefix[e] = run;
+                s_off[e] = o[i];
+            }
             run += c[i];
         }
         if (lane == 63) s_prefix[E] = incl;
+        if (lane == 0) s_off[E] = offsets[E];
     }
     __syncthreads();
 }
@@ -81,8 +91,8 @@ struct Tile {
 
 // Row tile and column tile of position pid in the tile order: groups of
 // GROUP_M row tiles, each group walked column tile by column tile.
-__device__ __forceinline__ Tile tile_of(int pid, const int32_t* __restrict__ offsets, int E, int bm,
-                                        int n_tiles, const int* s_prefix) {
+__device__ __forceinline__ Tile tile_of(int pid, const int* s_off, int E, int bm, int n_tiles,
+                                        const int* s_prefix) {
     const int total_m = s_prefix[E];
     const int group = pid / (GROUP_M * n_tiles);
     const int first_m = group * GROUP_M;
@@ -97,8 +107,8 @@ __device__ __forceinline__ Tile tile_of(int pid, const int32_t* __restrict__ off
         if (s_prefix[mid] <= mt) lo = mid; else hi = mid;
     }
     t.e = lo;
-    t.row0 = offsets[lo] + (mt - s_prefix[lo]) * bm;
-    t.row1 = min(t.row0 + bm, offsets[lo + 1]);
+    t.row0 = s_off[lo] + (mt - s_prefix[lo]) * bm;
+    t.row1 = min(t.row0 + bm, s_off[lo + 1]);
     return t;
 }
 
@@ -131,9 +141,8 @@ struct Work {
     Tile t;
     int kb, nkl, j;
 };
-__device__ __forceinline__ bool find_work(const int32_t* __restrict__ offsets, int E, int bm,
-                                          int n_tiles, const int* s_prefix, int nk, int slots,
-                                          Work& w) {
+__device__ __forceinline__ bool find_work(const int* s_off, int E, int bm, int n_tiles,
+                                          const int* s_prefix, int nk, int slots, Work& w) {
     const SplitPlan sp = split_plan(s_prefix[E] * n_tiles, slots, nk);
     const int hw = blockIdx.x;
     const int per_xcd = (sp.full + NUM_XCD - 1) / NUM_XCD;
@@ -153,15 +162,15 @@ __device__ __forceinline__ bool find_work(const int32_t* __restrict__ offsets, i
         w.nkl = (part + 1) * nk / sp.S - w.kb;
         w.j = j;
     }
-    w.t = tile_of(pid, offsets, E, bm, n_tiles, s_prefix);
+    w.t = tile_of(pid, s_off, E, bm, n_tiles, s_prefix);
     return true;
 }
 
 // This workgroup's whole tile (no split); false when it has no work.
-__device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, int E, int bm,
-                                          int n_tiles, const int* s_prefix, Tile& t) {
+__device__ __forceinline__ bool find_tile(const int* s_off, int E, int bm, int n_tiles,
+                                          const int* s_prefix, Tile& t) {
     Work w;
-    if (!find_work(offsets, E, bm, n_tiles, s_prefix, 1, 0, w)) return false;
+    if (!find_work(s_off, E, bm, n_tiles, s_prefix, 1, 0, w)) return false;
     t = w.t;
     return true;
 }
@@ -300,14 +309,15 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     static_assert(KS == 4 && (KS - 1) * NR == NM + NR, "the step schedule below assumes 4 K steps");
     static_assert(3 * NL <= (KS - 1) * NM, "the refill spreads one load per 3 MFMAs");
     __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE_BYTES];
-    // The tile prefix table lives in stage 0 until the first load.
+    // The tile prefix and offsets tables live in stage 0 until the first load.
     int* const s_prefix = reinterpret_cast<int*>(smem);
+    int* const s_off = s_prefix + MOE_MAX_EXPERTS + 1;
 
-    build_tile_prefix(offsets, E, TM, s_prefix);
+    build_tile_prefix(offsets, E, TM, s_prefix, s_off);
     const int n_tiles = (N + BN_OUT - 1) / BN_OUT;
     Work work;
     // (GEMM1 never splits: its epilogue is not linear in the partial sums)
-    if (!find_work(offsets, E, TM, n_tiles, s_prefix, K / BK, GATEUP ? 0 : slots, work)) return;
+    if (!find_work(s_off, E, TM, n_tiles, s_prefix, K / BK, GATEUP ? 0 : slots, work)) return;
     const Tile tile = work.t;
     __syncthreads();  // every lookup is done before the loads overwrite the table
 
@@ -333,19 +343,24 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // (the K range [work.kb, work.kb + work.nkl) of 64-column slices is folded into the bases)
     const bf16_t* const a_base =
         uniform_ptr((GATHER ? A : A + static_cast<int64_t>(tile.row0) * K) + work.kb * BK);
+    // (gathered rows need a lookup in sorted_assign: called after the first
+    // weight loads are on their way)
+    auto setup_a = [&]() {
 #pragma unroll
-    for (int j = 0; j < LA; ++j) {
-        const int r = wave * 64 + j * 8 + lrow;
-        const int chunk = lslot ^ slot_swizzle(r);
-        int pos = tile.row0 + r;
-        if (pos >= tile.row1) pos = tile.row1 - 1;
-        if (WIDE)
-            a_src[WIDE ? j : 0] = A + static_cast<int64_t>(sorted_assign[pos] / topk) * K + work.kb * BK + chunk * 8;
-        else if (GATHER)
-            a_off[WIDE ? 0 : j] = (static_cast<uint32_t>(sorted_assign[pos] / topk) * K + chunk * 8) * 2u;
-        else
-            a_off[WIDE ? 0 : j] = (static_cast<uint32_t>(pos - tile.row0) * K + chunk * 8) * 2u;
-    }
+        for (int j = 0; j < LA; ++j) {
+            const int r = wave * 64 + j * 8 + lrow;
+            const int chunk = lslot ^ slot_swizzle(r);
+            int pos = tile.row0 + r;
+            if (pos >= tile.row1) pos = tile.row1 - 1;
+            if (WIDE)
+                a_src[WIDE ? j : 0] =
+                    A + static_cast<int64_t>(sorted_assign[pos] / topk) * K + work.kb * BK + chunk * 8;
+            else if (GATHER)
+                a_off[WIDE ? 0 : j] = (static_cast<uint32_t>(sorted_assign[pos] / topk) * K + chunk * 8) * 2u;
+            else
+                a_off[WIDE ? 0 : j] = (static_cast<uint32_t>(pos - tile.row0) * K + chunk * 8) * 2u;
+        }
+    };
     // In GEMM1 the first 128 weight rows are gate rows and the rest up rows,
     // so each wave's rows come from one matrix.
     const int rb0 = wave * (TN / 4);
@@ -363,17 +378,21 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
     const uint32_t lds_a = lds0 + wave * 64 * ROWB;
     const uint32_t lds_b = lds0 + SA_BYTES + rb0 * ROWB;
-    // load q (< NL) of slice kt
-    auto dma = [&](int q, int kt) {
+    // activation load j (< LA) and weight load j (< LB) of slice kt
+    auto dma_a = [&](int j, int kt) {
         const uint32_t so = static_cast<uint32_t>((kt & 1) * STAGE_BYTES);
+        if (WIDE) lds_dma16(a_src[WIDE ? j : 0] + kt * BK, lds_a + so + j * 8 * ROWB);
+        else lds_dma16_s(a_base + kt * BK, a_off[WIDE ? 0 : j], lds_a + so + j * 8 * ROWB);
+    };
+    auto dma_b = [&](int j, int kt) {
+        const uint32_t so = static_cast<uint32_t>((kt & 1) * STAGE_BYTES);
+        lds_dma16_s(b_base + kt * BK, b_off[j], lds_b + so + j * 8 * ROWB);
+    };
+    // load q (< NL) of slice kt, in the GEMM's load order
+    auto dma = [&](int q, int kt) {
         const bool a_op = A_FIRST ? q < LA : q >= LB;
-        const int j = a_op ? (A_FIRST ? q : q - LB) : (A_FIRST ? q - LA : q);
-        if (a_op) {
-            if (WIDE) lds_dma16(a_src[WIDE ? j : 0] + kt * BK, lds_a + so + j * 8 * ROWB);
-            else lds_dma16_s(a_base + kt * BK, a_off[WIDE ? 0 : j], lds_a + so + j * 8 * ROWB);
-        } else {
-            lds_dma16_s(b_base + kt * BK, b_off[j], lds_b + so + j * 8 * ROWB);
-        }
+        if (a_op) dma_a(A_FIRST ? q : q - LB, kt);
+        else dma_b(A_FIRST ? q - LA : q, kt);
     };
 
     f32x16_t acc[4][4];
@@ -428,12 +447,23 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         if (p % 3 == 0 && p / 3 < NL) dma(p / 3, kt + 2);
     };
     constexpr int BEFORE3 = (2 * NM + 2) / 3 < NL ? (2 * NM + 2) / 3 : NL;  // loads issued in steps 1..2
+    // Prologue: the weight rows of slices 0 and 1 go out first (their
+    // addresses need no lookup), then the activation rows (see above).
+    // Issue order B0 B1 A0 A1: slice 0 has landed when at most the LA loads
+    // of A1 are pending.
 #pragma unroll
-    for (int q = 0; q < NL; ++q) dma(q, 0);
+    for (int j = 0; j < LB; ++j) dma_b(j, 0);
     if (nk > 1) {
 #pragma unroll
-        for (int q = 0; q < NL; ++q) dma(q, 1);
-        wait_vmcnt_lgkm0<NL>();
+        for (int j = 0; j < LB; ++j) dma_b(j, 1);
+    }
+    setup_a();
+#pragma unroll
+    for (int j = 0; j < LA; ++j) dma_a(j, 0);
+    if (nk > 1) {
+#pragma unroll
+        for (int j = 0; j < LA; ++j) dma_a(j, 1);
+        wait_vmcnt_lgkm0<LA>();
     } else {
         wait_vmcnt_lgkm0<0>();
     }
@@ -507,38 +537,54 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         return;
     }
 
-    // Epilogue.  Block (nb, mb): lane owns output row m = mb*32 + (lane & 31)
-    // and, for g = 0..3, columns 8g + 4*(lane >> 5) + 0..3 of the block
-    // (registers 4g .. 4g+3).
+    // Epilogue through LDS.  Block (nb, mb): lane owns tile row wm*128 +
+    // mb*32 + (lane & 31) and, for g = 0..3, the 4 output columns 8g +
+    // 4*(lane >> 5) + 0..3 of the block (registers 4g .. 4g+3).  The ring is
+    // free once every wave has left the loop: the output tile is staged there
+    // row-major, 16-byte chunk ch of row r at chunk ch ^ (r mod CPR), which
+    // spreads the 8-byte writes of 32 rows over the banks, and then written
+    // out in whole 16-byte chunks, consecutive lanes on consecutive chunks of
+    // a row, so that every store instruction covers whole 128-byte lines
+    // (8-byte stores into 32 rows each took 5-12 us per tile, measured).
+    constexpr int OUTC = GATEUP ? TN / 2 : TN;  // output columns of a tile
+    constexpr int CPR = OUTC / 8;               // 16-byte chunks per row
+    constexpr int ROWO = OUTC * 2;              // bytes per staged row
+    static_assert(TM * ROWO <= 2 * STAGE_BYTES, "the staged tile must fit the ring");
+    wait_vmcnt_lgkm0<0>();
+    barrier_lds();
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
-        const int pos = tile.row0 + wm * 128 + mb * 32 + l32;
-        if (pos >= tile.row1) continue;
-        bf16_t* crow = C + static_cast<int64_t>(pos) * N;
-        if (GATEUP) {
+        const int r = wm * 128 + mb * 32 + l32;
+        char* const srow = smem + r * ROWO + khalf * 8;
+        const int sw = r & (CPR - 1);
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
+        for (int nb = 0; nb < (GATEUP ? 2 : 4); ++nb)
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int col = n0 + wn * 64 + nb * 32 + 8 * g + 4 * khalf;
-                    if (col >= N) continue;
+            for (int g = 0; g < 4; ++g) {
+                uint2 o;
+                if (GATEUP) {
                     float v[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) v[i] = silu_mul_fast(acc[nb][mb][4 * g + i], acc[nb + 2][mb][4 * g + i]);
-                    *reinterpret_cast<uint2*>(crow + col) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-                }
-        } else {
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int col = n0 + wn * 128 + nb * 32 + 8 * g + 4 * khalf;
-                    if (col >= N) continue;
+                    o = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                } else {
                     const f32x16_t& a = acc[nb][mb];
-                    *reinterpret_cast<uint2*>(crow + col) =
-                        make_uint2(pack_bf16x2(a[4 * g], a[4 * g + 1]), pack_bf16x2(a[4 * g + 2], a[4 * g + 3]));
+                    o = make_uint2(pack_bf16x2(a[4 * g], a[4 * g + 1]), pack_bf16x2(a[4 * g + 2], a[4 * g + 3]));
                 }
-        }
+                const int ch = (GATEUP ? wn * 8 : wn * 16) + nb * 4 + g;
+                *reinterpret_cast<uint2*>(srow + ((ch ^ sw) * 16)) = o;
+            }
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int idx = tid; idx < TM * CPR; idx += 256) {
+        const int r = idx / CPR;
+        const int ch = idx % CPR;
+        const int pos = tile.row0 + r;
+        const int col = n0 + ch * 8;
+        if (pos >= tile.row1 || col >= N) continue;
+        const uint4 v = *reinterpret_cast<const uint4*>(smem + r * ROWO + ((ch ^ (r & (CPR - 1))) * 16));
+        *reinterpret_cast<uint4*>(C + static_cast<int64_t>(pos) * N + col) = v;
     }
 }
 
@@ -551,14 +597,15 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
                                                            int N, int nk, int slots,
                                                            bf16_t* __restrict__ C) {
     __shared__ int s_prefix[MOE_MAX_EXPERTS + 1];
-    build_tile_prefix(offsets, E, kBM, s_prefix);
+    __shared__ int s_off[MOE_MAX_EXPERTS + 1];
+    build_tile_prefix(offsets, E, kBM, s_prefix, s_off);
     const int n_tiles = (N + kDownCols - 1) / kDownCols;
     const SplitPlan sp = split_plan(s_prefix[E] * n_tiles, slots, nk);
     const int t = blockIdx.x >> 4;
     if (t >= sp.total - sp.full) return;
     const int nb = (blockIdx.x >> 2) & 3;
     const int mb = blockIdx.x & 3;
-    const Tile tile = tile_of(sp.full + t, offsets, E, kBM, n_tiles, s_prefix);
+    const Tile tile = tile_of(sp.full + t, s_off, E, kBM, n_tiles, s_prefix);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -600,11 +647,12 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(
     __shared__ float sB0[F_BK][kF32BN + 4];
     __shared__ float sB1[GATEUP ? F_BK : 1][kF32BN + 4];
     __shared__ int s_prefix[MOE_MAX_EXPERTS + 1];
+    __shared__ int s_off[MOE_MAX_EXPERTS + 1];
 
-    build_tile_prefix(offsets, E, kF32BM, s_prefix);
+    build_tile_prefix(offsets, E, kF32BM, s_prefix, s_off);
     const int n_tiles = (N + kF32BN - 1) / kF32BN;
     Tile tile;
-    if (!find_tile(offsets, E, kF32BM, n_tiles, s_prefix, tile)) return;
+    if (!find_tile(s_off, E, kF32BM, n_tiles, s_prefix, tile)) return;
 
     const int tid = threadIdx.x;
     const int tx = tid & 15, ty = tid >> 4;
