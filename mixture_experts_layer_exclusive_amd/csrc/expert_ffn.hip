@@ -23,6 +23,7 @@
 // mostly already in its XCD's L2.
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 #include "device_util.h"
 #include "moe_internal.h"
@@ -444,7 +445,12 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // loads of slice kt + 2 issued before it.
     auto refill = [&](int step, int q, int kt) {  // MFMA q of step 1..3
         const int p = (step - 1) * NM + q;
-        if (p % 3 == 0 && p / 3 < NL) dma(p / 3, kt + 2);
+        if (p % 3 == 0 && p / 3 < NL) {
+            dma(p / 3, kt + 2);
+            // keep each load between its MFMAs (the scheduler would
+            // otherwise gather them into a burst)
+            __builtin_amdgcn_sched_barrier(0);
+        }
     };
     constexpr int BEFORE3 = (2 * NM + 2) / 3 < NL ? (2 * NM + 2) / 3 : NL;  // loads issued in steps 1..2
     // Prologue: the weight rows of slices 0 and 1 go out first (their
@@ -472,10 +478,12 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     for (int i = 0; i < NR; ++i) read_frag(0, i, 0);
     __builtin_amdgcn_sched_barrier(0);
 
-    for (int kt = 0; kt < nk; ++kt) {
+    // One slice; MORE (a compile-time flag, so that the refills need no
+    // branches) says that slice kt + 2 exists: true for all but the last two.
+    auto slice = [&](int kt, auto more_c) {
+        constexpr bool MORE = decltype(more_c)::value;
         const uint32_t so = static_cast<uint32_t>((kt & 1) * STAGE_BYTES);
         const uint32_t nso = static_cast<uint32_t>(((kt + 1) & 1) * STAGE_BYTES);
-        const bool more = kt + 2 < nk;
         // step 0: 24 reads over 16 MFMAs
 #pragma unroll
         for (int kk = 1; kk < KS; ++kk)
@@ -503,13 +511,15 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             for (int q = 0; q < NM; ++q) {
                 if (step == 1) MOE_MFMA(1, q);
                 else MOE_MFMA(2, q);
-                if (more) refill(step, q, kt);
+                if (MORE) refill(step, q, kt);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        if (kt + 1 < nk) {
-            if (more) wait_vmcnt<BEFORE3>();
-            else wait_vmcnt<0>();
+        if (MORE) {
+            wait_vmcnt<BEFORE3>();
+            barrier_lds();
+        } else if (kt + 1 < nk) {
+            wait_vmcnt<0>();
             barrier_lds();
         }
         // step 3 (after the last slice the reads fetch a stale, in-bounds
@@ -517,11 +527,14 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 #pragma unroll
         for (int q = 0; q < NM; ++q) {
             MOE_MFMA(3, q);
-            if (more) refill(3, q, kt);
+            if (MORE) refill(3, q, kt);
             if ((q & 1) && (q >> 1) < NR) read_frag(0, q >> 1, nso);
         }
         __builtin_amdgcn_sched_barrier(0);
-    }
+    };
+    int kt = 0;
+    for (; kt + 2 < nk; ++kt) slice(kt, std::true_type{});
+    for (; kt < nk; ++kt) slice(kt, std::false_type{});
 #undef MOE_MFMA
 
     // A split K range: the fp32 partial sums go to slot work.j, register by
