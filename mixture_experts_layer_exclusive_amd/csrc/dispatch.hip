@@ -3,20 +3,21 @@
 // built during the forward pass, in place of a dense token-by-expert
 // routing matrix).
 //
-// Three passes over the int32 ids:
+// Two passes over the int32 ids:
 //   1. histogram: workgroup b counts the experts of assignments
 //      [b*C, (b+1)*C) with LDS atomics -> block_counts[e][b] (expert-major);
 //      C is a multiple of 256 chosen so that about 256 workgroups run;
-//   2. scan: one workgroup turns block_counts into an exclusive prefix sum in
-//      expert-major order.  Entry [e][b] becomes the first queue position of
-//      expert e owned by block b; entry [e][0] is offsets[e];
-//   3. scatter: each wave of a workgroup owns a contiguous part of the
-//      chunk, counts it, takes its first position per expert from the block
-//      base plus the earlier waves' counts, then walks its part in ascending
-//      a, 64 at a time: lanes holding the same expert are found with log2(E)
-//      ballots (one per id bit) and ranked by the popcount of lower peers.
-//      Ascending a at every level makes the sort stable.
-// Up to 4096 assignments the three passes run in one 1024-thread workgroup.
+//   2. scatter: each workgroup first reduces the expert-major table itself
+//      (no separate scan pass): the first queue position of expert e owned by
+//      block b is the count of all experts below e plus the counts of e in
+//      blocks below b; workgroup 0 also writes counts and offsets.  Then each
+//      wave owns a contiguous part of the chunk, counts it, takes its first
+//      position per expert from the block base plus the earlier waves'
+//      counts, and walks its part in ascending a, 64 at a time: lanes holding
+//      the same expert are found with log2(E) ballots (one per id bit) and
+//      ranked by the popcount of lower peers.  Ascending a at every level
+//      makes the sort stable.
+// Up to 4096 assignments both passes run in one 1024-thread workgroup.
 // The scatter stages its chunk's ids in LDS first (one bulk load).
 // Ids outside [0, E) are skipped (their assign_pos is -1).
 #include "device_util.h"
@@ -26,15 +27,12 @@ namespace moe {
 
 namespace {
 
-constexpr int SCAN_THREADS = 1024;
-
 // Bits needed for an expert id.
 __host__ __device__ __forceinline__ int id_bits(int E) {
     int b = 0;
     while ((1 << b) < E) ++b;
     return b;
 }
-constexpr int SCAN_ITEMS = 8;
 
 // Stable ranks of one 64-lane step of a wave's assignments: lanes holding
 // the same expert are found with one ballot per id bit; the rank of a lane
@@ -72,68 +70,6 @@ __global__ __launch_bounds__(256) void dispatch_hist_kernel(const int32_t* __res
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += 256)
         block_counts[static_cast<int64_t>(e) * nblk + blockIdx.x] = h[e];
-}
-
-// In-place exclusive scan of block_counts[E * nblk] by a single workgroup,
-// then counts[e] and offsets[e] from the scanned table.
-__global__ __launch_bounds__(SCAN_THREADS) void dispatch_scan_kernel(int32_t* __restrict__ bc,
-                                                                    int E, int nblk,
-                                                                    int32_t* __restrict__ counts,
-                                                                    int32_t* __restrict__ offsets) {
-    __shared__ int wave_sums[SCAN_THREADS / 64];
-    __shared__ int carry_s;
-    const int tid = threadIdx.x;
-    const int lane = lane_id();
-    const int wave = tid >> 6;
-    const int64_t total = static_cast<int64_t>(E) * nblk;
-    if (tid == 0) carry_s = 0;
-    __syncthreads();
-
-    for (int64_t base = 0; base < total; base += SCAN_THREADS * SCAN_ITEMS) {
-        const int carry = carry_s;
-        int v[SCAN_ITEMS];
-        int local = 0;
-#pragma unroll
-        for (int i = 0; i < SCAN_ITEMS; ++i) {
-            const int64_t idx = base + static_cast<int64_t>(tid) * SCAN_ITEMS + i;
-            v[i] = idx < total ? bc[idx] : 0;
-            local += v[i];
-        }
-        // inclusive wave scan of the per-thread sums
-        int incl = local;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int o = __shfl_up(incl, off, 64);
-            if (lane >= off) incl += o;
-        }
-        if (lane == 63) wave_sums[wave] = incl;
-        __syncthreads();
-        int wave_prefix = 0;
-        int tile_total = 0;
-        for (int w = 0; w < SCAN_THREADS / 64; ++w) {
-            const int sw = wave_sums[w];
-            if (w < wave) wave_prefix += sw;
-            tile_total += sw;
-        }
-        int run = carry + wave_prefix + incl - local;
-#pragma unroll
-        for (int i = 0; i < SCAN_ITEMS; ++i) {
-            const int64_t idx = base + static_cast<int64_t>(tid) * SCAN_ITEMS + i;
-            if (idx < total) bc[idx] = run;
-            run += v[i];
-        }
-        __syncthreads();
-        if (tid == 0) carry_s = carry + tile_total;
-        __syncthreads();
-    }
-    const int grand = carry_s;
-    for (int e = tid; e < E; e += SCAN_THREADS) {
-        const int lo = bc[static_cast<int64_t>(e) * nblk];
-        const int hi = (e + 1 < E) ? bc[static_cast<int64_t>(e + 1) * nblk] : grand;
-        offsets[e] = lo;
-        counts[e] = hi - lo;
-    }
-    if (tid == 0) offsets[E] = grand;
 }
 
 // Scatters the assignments [a0, a1) whose experts start at block_base[e]
@@ -197,20 +133,84 @@ __device__ __forceinline__ void scatter_chunk(const int* s_ids, int64_t a0, int6
     }
 }
 
+// Block b's first queue position per expert, from the expert-major block
+// counts bc[E][nblk]: base[e] = sum over experts e' < e of their totals plus
+// the counts of e in blocks below b.  One wave per expert row (lanes stride
+// over the blocks), then one wave scans the E totals.  Workgroup 0 also
+// writes counts[E] and offsets[E+1].
+__device__ __forceinline__ void block_bases(const int32_t* __restrict__ bc, int E, int nblk, int b,
+                                            int* s_base, int* s_tot, int32_t* __restrict__ counts,
+                                            int32_t* __restrict__ offsets) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    for (int e = wave; e < E; e += 4) {
+        const int32_t* row = bc + static_cast<int64_t>(e) * nblk;
+        int tot = 0, pre = 0;
+        for (int i = lane; i < nblk; i += 64) {
+            const int v = row[i];
+            tot += v;
+            if (i < b) pre += v;
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            tot += __shfl_xor(tot, off, 64);
+            pre += __shfl_xor(pre, off, 64);
+        }
+        if (lane == 0) {
+            s_tot[e] = tot;
+            s_base[e] = pre;
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) {
+        int c[4], local = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = lane * 4 + i;
+            c[i] = e < E ? s_tot[e] : 0;
+            local += c[i];
+        }
+        int incl = local;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int o = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += o;
+        }
+        int run = incl - local;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = lane * 4 + i;
+            if (e < E) {
+                s_base[e] += run;
+                if (b == 0) {
+                    offsets[e] = run;
+                    counts[e] = c[i];
+                }
+            }
+            run += c[i];
+        }
+        if (b == 0 && lane == 63) offsets[E] = incl;
+    }
+    __syncthreads();
+}
+
 __global__ __launch_bounds__(256) void dispatch_scatter_kernel(const int32_t* __restrict__ ids,
                                                               int64_t n, int64_t chunk, int E, int nbits,
                                                               int nblk,
-                                                              const int32_t* __restrict__ bases,
+                                                              const int32_t* __restrict__ block_counts,
+                                                              int32_t* __restrict__ counts,
+                                                              int32_t* __restrict__ offsets,
                                                               int32_t* __restrict__ sorted_assign,
                                                               int32_t* __restrict__ assign_pos) {
     __shared__ int block_base[MOE_MAX_EXPERTS];
     __shared__ int wcur[4][MOE_MAX_EXPERTS];
     __shared__ int s_ids[kMaxDispatchChunk];
-    for (int e = threadIdx.x; e < E; e += 256)
-        block_base[e] = bases[static_cast<int64_t>(e) * nblk + blockIdx.x];
     const int64_t a0 = static_cast<int64_t>(blockIdx.x) * chunk;
     const int64_t a1 = (a0 + chunk < n) ? a0 + chunk : n;
     for (int64_t a = a0 + threadIdx.x; a < a1; a += 256) s_ids[a - a0] = ids[a];
+    // (wcur[0] doubles as the totals' scratch until the scatter clears it)
+    block_bases(block_counts, E, nblk, static_cast<int>(blockIdx.x), block_base, wcur[0], counts,
+                offsets);
     scatter_chunk<4>(s_ids, a0, a1, E, nbits, block_base, wcur, sorted_assign, assign_pos);
 }
 
@@ -278,8 +278,8 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(const int32_t* __r
 // its k queue rows, x_perm[assign_pos[t*k + j]] = x[t] (assignments with no
 // queue position are skipped).  A workgroup copies TPB whole rows; threads
 // stride over (row, word) pairs, so both the reads and the row writes are
-// contiguous.
-template <typename W>
+// contiguous, and each thread has U loads in flight before its stores.
+template <typename W, int U>
 __global__ __launch_bounds__(256) void gather_rows_kernel(const W* __restrict__ x,
                                                          const int32_t* __restrict__ assign_pos,
                                                          int64_t T, int k, int64_t words_per_row,
@@ -287,13 +287,24 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const W* __restrict__ 
     const int64_t t0 = static_cast<int64_t>(blockIdx.x) * tpb;
     const int64_t nt = (t0 + tpb <= T) ? tpb : T - t0;
     const int64_t total = nt * words_per_row;
-    for (int64_t i = threadIdx.x; i < total; i += 256) {
-        const int64_t t = t0 + i / words_per_row;
-        const int64_t w = i % words_per_row;
-        const W v = load_nt(x + t * words_per_row + w);
-        for (int j = 0; j < k; ++j) {
-            const int pos = assign_pos[t * k + j];
-            if (pos >= 0) x_perm[static_cast<int64_t>(pos) * words_per_row + w] = v;
+    const W* src = x + t0 * words_per_row;
+    for (int64_t i0 = threadIdx.x; i0 < total; i0 += 256 * U) {
+        W v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = i0 + u * 256;
+            if (i < total) v[u] = load_nt(src + i);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = i0 + u * 256;
+            if (i >= total) break;
+            const int64_t t = t0 + i / words_per_row;
+            const int64_t w = i % words_per_row;
+            for (int j = 0; j < k; ++j) {
+                const int pos = assign_pos[t * k + j];
+                if (pos >= 0) x_perm[static_cast<int64_t>(pos) * words_per_row + w] = v[u];
+            }
         }
     }
 }
@@ -312,28 +323,28 @@ hipError_t launch_dispatch_queues(const moe_problem_t& p, const int32_t* ids, in
     const int64_t chunk = dispatch_chunk(n);
     const int nblk = static_cast<int>(dispatch_blocks(n));
     dispatch_hist_kernel<<<nblk, 256, 0, s>>>(ids, n, chunk, p.E, nblk, block_counts);
-    dispatch_scan_kernel<<<1, SCAN_THREADS, 0, s>>>(block_counts, p.E, nblk, counts, offsets);
     dispatch_scatter_kernel<<<nblk, 256, 0, s>>>(ids, n, chunk, p.E, id_bits(p.E), nblk, block_counts,
-                                                 sorted_assign, assign_pos);
+                                                 counts, offsets, sorted_assign, assign_pos);
     return hipGetLastError();
 }
 
 hipError_t launch_gather_rows(const moe_problem_t& p, const void* x, const int32_t* assign_pos,
                               void* x_perm, hipStream_t s) {
     const int64_t row_bytes = static_cast<int64_t>(p.d) * (p.dtype == MOE_DTYPE_F32 ? 4 : 2);
-    // rows per workgroup: about 8 KB of row data per workgroup
-    const int tpb = static_cast<int>(row_bytes >= 8192 ? 1 : 8192 / row_bytes);
+    // rows per workgroup: about 32 KB of row data per workgroup (one pass
+    // of 256 threads x 8 loads of 16 bytes)
+    const int tpb = static_cast<int>(row_bytes >= 32768 ? 1 : 32768 / row_bytes);
     const unsigned grid = static_cast<unsigned>(ceil_div(p.T, tpb));
     if (row_bytes % 16 == 0)
-        gather_rows_kernel<uint4><<<grid, 256, 0, s>>>(static_cast<const uint4*>(x), assign_pos, p.T,
+        gather_rows_kernel<uint4, 8><<<grid, 256, 0, s>>>(static_cast<const uint4*>(x), assign_pos, p.T,
                                                       p.k, row_bytes / 16, tpb,
                                                       static_cast<uint4*>(x_perm));
     else if (row_bytes % 4 == 0)
-        gather_rows_kernel<uint32_t><<<grid, 256, 0, s>>>(static_cast<const uint32_t*>(x), assign_pos,
+        gather_rows_kernel<uint32_t, 8><<<grid, 256, 0, s>>>(static_cast<const uint32_t*>(x), assign_pos,
                                                          p.T, p.k, row_bytes / 4, tpb,
                                                          static_cast<uint32_t*>(x_perm));
     else
-        gather_rows_kernel<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(x), assign_pos,
+        gather_rows_kernel<uint16_t, 8><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(x), assign_pos,
                                                          p.T, p.k, row_bytes / 2, tpb,
                                                          static_cast<uint16_t*>(x_perm));
     return hipGetLastError();
