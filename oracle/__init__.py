@@ -1,4 +1,4 @@
-"""CPU oracle of the MoE-layer forward: TEST INFRASTRUCTURE ONLY.
+"""CPU oracle of the MoE layer (forward and backward): TEST INFRASTRUCTURE ONLY.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  The product path (the HIP library and
@@ -7,11 +7,17 @@ with them.
 
 Parity status: every function in ``moe_oracle`` is pinned by
 ``tests/test_oracle_pins.py`` (brute force on tiny inputs, library routines
-for the special cases, closed forms and invariants).  No function here is
-"parity unpinned".
+for the special cases, closed forms and invariants), and every function in
+``moe_backward`` by ``tests/test_oracle_backward_pins.py`` (finite
+differences, an independent automatic differentiation, linearity).  No
+function here is "parity unpinned".
 """
 from .moe_oracle import (  # noqa: F401
     router_logits, topk_route, expert_histogram, exclusive_scan, stable_scatter,
     dispatch, gather_rows, silu, swiglu_expert, expert_ffn, combine, forward,
     forward_tokens,
+)
+from .moe_backward import (  # noqa: F401
+    sigmoid, silu_grad, gate_grad, dispatch_grad, topk_gates_backward,
+    swiglu_expert_backward, backward,
 )
