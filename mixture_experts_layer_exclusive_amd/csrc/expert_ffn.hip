@@ -186,6 +186,11 @@ __device__ __forceinline__ float silu_mul_fast(float g, float u) {
     return g * u * __builtin_amdgcn_rcpf(1.f + e);
 }
 
+// sigmoid(u) with the same hardware exp2 and reciprocal.
+__device__ __forceinline__ float sigmoid_fast(float u) {
+    return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-u * 1.4426950408889634f));
+}
+
 // ---------------------------------------------------------------------------
 // bf16 grouped GEMM on MFMA (v_mfma_f32_32x32x16_bf16)
 //
@@ -284,12 +289,56 @@ __device__ __forceinline__ const T* uniform_ptr(const T* p) {
     return reinterpret_cast<const T*>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
-template <bool GATEUP, bool GATHER, bool WIDE>
+// What a grouped GEMM launch computes (the pipeline is shared):
+//   kUp    forward GEMM1: gate and up of the queue rows, SwiGLU epilogue -> h
+//   kDown  C = A B^T over the queue rows (forward GEMM2; the backward's dh and dx)
+//   kUpBwd the backward's recompute of gate and up, with an epilogue that
+//          takes dh and writes du, dv (side by side, [rows, 2f]) and h
+//   kWgrad weight gradients: per expert e, C_e[M, N] = A_e B_e^T over the
+//          expert's (padded) queue columns [poff[e], poff[e+1]) of A [M, ldk]
+//          and B [N, ldk] (operands already transposed, padding zero)
+constexpr int kUp = 0, kDown = 1, kUpBwd = 2, kWgrad = 3;
+
+// Work of a weight-gradient workgroup: tile (mt, nt) of expert e, K slices of
+// the expert's padded queue columns.  Same XCD remap and grouping as the
+// forward order.
+__device__ __forceinline__ bool find_wgrad_work(const int32_t* __restrict__ poff, int E, int M, int N,
+                                                Work& w) {
+    const int mtn = (M + kBM - 1) / kBM;
+    const int ntn = (N + kDownCols - 1) / kDownCols;
+    const int per_e = mtn * ntn;
+    const int total = E * per_e;
+    const int hw = blockIdx.x;
+    const int per_xcd = (total + NUM_XCD - 1) / NUM_XCD;
+    if (hw >= per_xcd * NUM_XCD) return false;
+    const int pid = (hw % NUM_XCD) * per_xcd + hw / NUM_XCD;
+    if (pid >= total) return false;
+    const int e = pid / per_e;
+    const int local = pid - e * per_e;
+    const int group = local / (GROUP_M * ntn);
+    const int first_m = group * GROUP_M;
+    const int gsz = min(GROUP_M, mtn - first_m);
+    const int l2 = local - group * GROUP_M * ntn;
+    const int mt = first_m + l2 % gsz;
+    w.t.e = e;
+    w.t.nt = l2 / gsz;
+    w.t.row0 = mt * kBM;
+    w.t.row1 = min(M, w.t.row0 + kBM);
+    const int k0 = poff[e], k1 = poff[e + 1];
+    w.kb = k0 / 64;
+    w.nkl = (k1 - k0) / 64;
+    w.j = -1;
+    return true;
+}
+
+template <int MODE, bool GATHER, bool WIDE>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void grouped_gemm_bf16_kernel(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ sorted_assign, int topk,
     const int32_t* __restrict__ offsets, int E, const bf16_t* __restrict__ B0,
     const bf16_t* __restrict__ B1, bf16_t* __restrict__ C, int N, int K, int slots,
-    float* __restrict__ part) {
+    float* __restrict__ part, const bf16_t* __restrict__ aux, bf16_t* __restrict__ C2, int M) {
+    constexpr bool GATEUP = MODE == kUp || MODE == kUpBwd;
+    constexpr bool WG = MODE == kWgrad;
     constexpr int TM = 256;                  // activation rows per tile
     constexpr int TN = 256;                  // weight rows per tile
     constexpr int BK = 64;                   // K slice width (one 128-byte line per row)
@@ -314,11 +363,16 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     int* const s_prefix = reinterpret_cast<int*>(smem);
     int* const s_off = s_prefix + MOE_MAX_EXPERTS + 1;
 
-    build_tile_prefix(offsets, E, TM, s_prefix, s_off);
-    const int n_tiles = (N + BN_OUT - 1) / BN_OUT;
     Work work;
-    // (GEMM1 never splits: its epilogue is not linear in the partial sums)
-    if (!find_work(s_off, E, TM, n_tiles, s_prefix, K / BK, GATEUP ? 0 : slots, work)) return;
+    if (WG) {
+        // (K is the operands' row stride here; offsets are the padded offsets)
+        if (!find_wgrad_work(offsets, E, M, N, work)) return;
+    } else {
+        build_tile_prefix(offsets, E, TM, s_prefix, s_off);
+        const int n_tiles = (N + BN_OUT - 1) / BN_OUT;
+        // (GEMM1 never splits: its epilogue is not linear in the partial sums)
+        if (!find_work(s_off, E, TM, n_tiles, s_prefix, K / BK, GATEUP ? 0 : slots, work)) return;
+    }
     const Tile tile = work.t;
     __syncthreads();  // every lookup is done before the loads overwrite the table
 
@@ -365,8 +419,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // In GEMM1 the first 128 weight rows are gate rows and the rest up rows,
     // so each wave's rows come from one matrix.
     const int rb0 = wave * (TN / 4);
-    const bf16_t* const b_base =
-        uniform_ptr((GATEUP && rb0 >= TN / 2 ? B1 : B0) + static_cast<int64_t>(tile.e) * N * K + work.kb * BK);
+    const bf16_t* const b_base = uniform_ptr((GATEUP && rb0 >= TN / 2 ? B1 : B0) +
+                                             (WG ? 0 : static_cast<int64_t>(tile.e) * N * K) + work.kb * BK);
     uint32_t b_off[LB];
 #pragma unroll
     for (int j = 0; j < LB; ++j) {
@@ -457,26 +511,30 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // addresses need no lookup), then the activation rows (see above).
     // Issue order B0 B1 A0 A1: slice 0 has landed when at most the LA loads
     // of A1 are pending.
+    // (a weight-gradient tile of an expert with no rows has nk = 0: no loads,
+    // and its zero accumulators are stored)
+    if (nk > 0) {
 #pragma unroll
-    for (int j = 0; j < LB; ++j) dma_b(j, 0);
-    if (nk > 1) {
+        for (int j = 0; j < LB; ++j) dma_b(j, 0);
+        if (nk > 1) {
 #pragma unroll
-        for (int j = 0; j < LB; ++j) dma_b(j, 1);
+            for (int j = 0; j < LB; ++j) dma_b(j, 1);
+        }
+        setup_a();
+#pragma unroll
+        for (int j = 0; j < LA; ++j) dma_a(j, 0);
+        if (nk > 1) {
+#pragma unroll
+            for (int j = 0; j < LA; ++j) dma_a(j, 1);
+            wait_vmcnt_lgkm0<LA>();
+        } else {
+            wait_vmcnt_lgkm0<0>();
+        }
+        barrier_lds();
+#pragma unroll
+        for (int i = 0; i < NR; ++i) read_frag(0, i, 0);
+        __builtin_amdgcn_sched_barrier(0);
     }
-    setup_a();
-#pragma unroll
-    for (int j = 0; j < LA; ++j) dma_a(j, 0);
-    if (nk > 1) {
-#pragma unroll
-        for (int j = 0; j < LA; ++j) dma_a(j, 1);
-        wait_vmcnt_lgkm0<LA>();
-    } else {
-        wait_vmcnt_lgkm0<0>();
-    }
-    barrier_lds();
-#pragma unroll
-    for (int i = 0; i < NR; ++i) read_frag(0, i, 0);
-    __builtin_amdgcn_sched_barrier(0);
 
     // One slice; MORE (a compile-time flag, so that the refills need no
     // branches) says that slice kt + 2 exists: true for all but the last two.
@@ -565,39 +623,105 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     static_assert(TM * ROWO <= 2 * STAGE_BYTES, "the staged tile must fit the ring");
     wait_vmcnt_lgkm0<0>();
     barrier_lds();
+    // stage the tile's output (h = silu(gate) * up for the gate/up modes, the
+    // accumulators otherwise) and store it to out (row stride ldo)
+    auto stage_and_store = [&](bf16_t* __restrict__ out, int64_t ldo) {
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-        const int r = wm * 128 + mb * 32 + l32;
-        char* const srow = smem + r * ROWO + khalf * 8;
-        const int sw = r & (CPR - 1);
+        for (int mb = 0; mb < 4; ++mb) {
+            const int r = wm * 128 + mb * 32 + l32;
+            char* const srow = smem + r * ROWO + khalf * 8;
+            const int sw = r & (CPR - 1);
 #pragma unroll
-        for (int nb = 0; nb < (GATEUP ? 2 : 4); ++nb)
+            for (int nb = 0; nb < (GATEUP ? 2 : 4); ++nb)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                uint2 o;
-                if (GATEUP) {
-                    float v[4];
+                for (int g = 0; g < 4; ++g) {
+                    uint2 o;
+                    if (GATEUP) {
+                        float v[4];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) v[i] = silu_mul_fast(acc[nb][mb][4 * g + i], acc[nb + 2][mb][4 * g + i]);
-                    o = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-                } else {
-                    const f32x16_t& a = acc[nb][mb];
-                    o = make_uint2(pack_bf16x2(a[4 * g], a[4 * g + 1]), pack_bf16x2(a[4 * g + 2], a[4 * g + 3]));
+                        for (int i = 0; i < 4; ++i) v[i] = silu_mul_fast(acc[nb][mb][4 * g + i], acc[nb + 2][mb][4 * g + i]);
+                        o = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                    } else {
+                        const f32x16_t& a = acc[nb][mb];
+                        o = make_uint2(pack_bf16x2(a[4 * g], a[4 * g + 1]), pack_bf16x2(a[4 * g + 2], a[4 * g + 3]));
+                    }
+                    const int ch = (GATEUP ? wn * 8 : wn * 16) + nb * 4 + g;
+                    *reinterpret_cast<uint2*>(srow + ((ch ^ sw) * 16)) = o;
                 }
-                const int ch = (GATEUP ? wn * 8 : wn * 16) + nb * 4 + g;
-                *reinterpret_cast<uint2*>(srow + ((ch ^ sw) * 16)) = o;
-            }
-    }
-    __syncthreads();
+        }
+        __syncthreads();
 #pragma unroll 4
-    for (int idx = tid; idx < TM * CPR; idx += 256) {
-        const int r = idx / CPR;
-        const int ch = idx % CPR;
-        const int pos = tile.row0 + r;
-        const int col = n0 + ch * 8;
-        if (pos >= tile.row1 || col >= N) continue;
-        const uint4 v = *reinterpret_cast<const uint4*>(smem + r * ROWO + ((ch ^ (r & (CPR - 1))) * 16));
-        *reinterpret_cast<uint4*>(C + static_cast<int64_t>(pos) * N + col) = v;
+        for (int idx = tid; idx < TM * CPR; idx += 256) {
+            const int r = idx / CPR;
+            const int ch = idx % CPR;
+            const int pos = tile.row0 + r;
+            const int col = n0 + ch * 8;
+            if (pos >= tile.row1 || col >= N) continue;
+            const uint4 v = *reinterpret_cast<const uint4*>(smem + r * ROWO + ((ch ^ (r & (CPR - 1))) * 16));
+            *reinterpret_cast<uint4*>(out + static_cast<int64_t>(pos) * ldo + col) = v;
+        }
+    };
+
+    if (MODE == kUpBwd) {
+        // The backward of SwiGLU from the recomputed gate u and up v and the
+        // incoming dh (aux, [rows, f]): with sg = sigmoid(u), s = u sg,
+        // du = dh v sg (1 + u (1 - sg)) and dv = dh s.  Pass 1 stages du and
+        // dv side by side (a 256-column row: chunks 0..15 du, 16..31 dv) and
+        // stores them to C = [rows, 2f] (du in columns [0, f), dv in [f, 2f));
+        // pass 2 stores h = s v to C2 (the down projection's weight gradient
+        // reads it).
+        constexpr int CPR2 = 32;
+        constexpr int ROWO2 = CPR2 * 16;
+        static_assert(TM * ROWO2 <= 2 * STAGE_BYTES, "the staged du/dv tile must fit the ring");
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+            const int r = wm * 128 + mb * 32 + l32;
+            const int pos = tile.row0 + r;
+            char* const srow = smem + r * ROWO2 + khalf * 8;
+            const int sw = r & (CPR2 - 1);
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int col = n0 + wn * 64 + nb * 32 + 8 * g + 4 * khalf;
+                    uint2 dhw = make_uint2(0u, 0u);
+                    if (pos < tile.row1 && col < N)
+                        dhw = *reinterpret_cast<const uint2*>(aux + static_cast<int64_t>(pos) * N + col);
+                    const float dh[4] = {lo_bf16(dhw.x), hi_bf16(dhw.x), lo_bf16(dhw.y), hi_bf16(dhw.y)};
+                    float du[4], dv[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float u = acc[nb][mb][4 * g + i];
+                        const float v = acc[nb + 2][mb][4 * g + i];
+                        const float sg = sigmoid_fast(u);
+                        const float su = u * sg;
+                        du[i] = dh[i] * v * sg * (1.f + u * (1.f - sg));
+                        dv[i] = dh[i] * su;
+                    }
+                    const int ch = wn * 8 + nb * 4 + g;
+                    *reinterpret_cast<uint2*>(srow + ((ch ^ sw) * 16)) =
+                        make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
+                    *reinterpret_cast<uint2*>(srow + (((ch + 16) ^ sw) * 16)) =
+                        make_uint2(pack_bf16x2(dv[0], dv[1]), pack_bf16x2(dv[2], dv[3]));
+                }
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int idx = tid; idx < TM * CPR2; idx += 256) {
+            const int r = idx / CPR2;
+            const int ch = idx % CPR2;
+            const int pos = tile.row0 + r;
+            const int col = n0 + (ch & 15) * 8;
+            if (pos >= tile.row1 || col >= N) continue;
+            const uint4 v = *reinterpret_cast<const uint4*>(smem + r * ROWO2 + ((ch ^ (r & (CPR2 - 1))) * 16));
+            *reinterpret_cast<uint4*>(C + static_cast<int64_t>(pos) * (2 * N) + (ch < 16 ? col : N + col)) = v;
+        }
+        __syncthreads();
+        stage_and_store(C2, N);
+    } else if (WG) {
+        stage_and_store(C + static_cast<int64_t>(tile.e) * M * N, N);
+    } else {
+        stage_and_store(C, N);
     }
 }
 
@@ -782,24 +906,24 @@ hipError_t launch_expert_ffn(const moe_problem_t& p, const void* x_perm, const v
         const bf16_t* a = static_cast<const bf16_t*>(gather ? x : x_perm);
         const unsigned g1 = grid_for(n, p.E, kBM, static_cast<int>(ceil_div(p.f, kGateUpCols)));
         if (gather && p.T * p.d >= (int64_t{1} << 31))
-            grouped_gemm_bf16_kernel<true, true, true><<<g1, 256, 0, s>>>(
+            grouped_gemm_bf16_kernel<kUp, true, true><<<g1, 256, 0, s>>>(
                 a, sorted_assign, p.k, offsets, p.E, static_cast<const bf16_t*>(w_gate),
-                static_cast<const bf16_t*>(w_up), static_cast<bf16_t*>(h), p.f, p.d, 0, nullptr);
+                static_cast<const bf16_t*>(w_up), static_cast<bf16_t*>(h), p.f, p.d, 0, nullptr, nullptr, nullptr, 0);
         else if (gather)
-            grouped_gemm_bf16_kernel<true, true, false><<<g1, 256, 0, s>>>(
+            grouped_gemm_bf16_kernel<kUp, true, false><<<g1, 256, 0, s>>>(
                 a, sorted_assign, p.k, offsets, p.E, static_cast<const bf16_t*>(w_gate),
-                static_cast<const bf16_t*>(w_up), static_cast<bf16_t*>(h), p.f, p.d, 0, nullptr);
+                static_cast<const bf16_t*>(w_up), static_cast<bf16_t*>(h), p.f, p.d, 0, nullptr, nullptr, nullptr, 0);
         else
-            grouped_gemm_bf16_kernel<true, false, false><<<g1, 256, 0, s>>>(
+            grouped_gemm_bf16_kernel<kUp, false, false><<<g1, 256, 0, s>>>(
                 a, sorted_assign, p.k, offsets, p.E, static_cast<const bf16_t*>(w_gate),
-                static_cast<const bf16_t*>(w_up), static_cast<bf16_t*>(h), p.f, p.d, 0, nullptr);
+                static_cast<const bf16_t*>(w_up), static_cast<bf16_t*>(h), p.f, p.d, 0, nullptr, nullptr, nullptr, 0);
         const unsigned g2 = grid_for(n, p.E, kBM, static_cast<int>(ceil_div(p.d, kDownCols)));
         const int slots = ffn_can_split(p) ? resident_slots() : 0;
         float* part = slots > 0 ? reinterpret_cast<float*>(static_cast<char*>(ffn_ws) + ffn_h_bytes(p)) : nullptr;
-        grouped_gemm_bf16_kernel<false, false, false><<<g2 + (slots > 0 ? kSplitWGs : 0), 256, 0, s>>>(
+        grouped_gemm_bf16_kernel<kDown, false, false><<<g2 + (slots > 0 ? kSplitWGs : 0), 256, 0, s>>>(
             static_cast<const bf16_t*>(h), sorted_assign, p.k, offsets, p.E,
             static_cast<const bf16_t*>(w_down), nullptr, static_cast<bf16_t*>(y_perm), p.d, p.f, slots,
-            part);
+            part, nullptr, nullptr, 0);
         if (slots > 0)
             split_reduce_kernel<<<kSplitWGs * 16, 256, 0, s>>>(part, offsets, p.E, p.d, p.f / 64, slots,
                                                           static_cast<bf16_t*>(y_perm));
