@@ -23,6 +23,7 @@ MOE_DTYPE_BF16 = 1
 MOE_OP_DISPATCH = 1
 MOE_OP_EXPERT_FFN = 2
 MOE_OP_FORWARD = 3
+MOE_OP_BACKWARD = 4
 
 MOE_MAX_EXPERTS = 256
 MOE_MAX_TOPK = 32
@@ -40,7 +41,17 @@ class MoeProblem(ctypes.Structure):
 
 class MoeForwardOutputs(ctypes.Structure):
     _fields_ = [("logits", _p), ("topk_ids", _p), ("topk_gates", _p), ("counts", _p),
-                ("offsets", _p), ("sorted_assign", _p), ("assign_pos", _p)]
+                ("offsets", _p), ("sorted_assign", _p), ("assign_pos", _p), ("y_perm", _p)]
+
+
+class MoeForwardState(ctypes.Structure):
+    _fields_ = [("topk_ids", _p), ("topk_gates", _p), ("offsets", _p), ("sorted_assign", _p),
+                ("assign_pos", _p), ("y_perm", _p)]
+
+
+class MoeBackwardOutputs(ctypes.Structure):
+    _fields_ = [("dx", _p), ("dw_gate", _p), ("dw_up", _p), ("dw_down", _p), ("dw_router", _p),
+                ("dlogits", _p)]
 
 
 _PP = ctypes.POINTER(MoeProblem)
@@ -55,6 +66,9 @@ SIGNATURES = {
     "moe_combine": (_i32, [_PP, _p, _p, _p, _p, _p]),
     "moe_forward": (_i32, [_PP, _p, _p, _p, _p, _p, _p, _p, ctypes.POINTER(MoeForwardOutputs),
                            _p, _sz, _p]),
+    "moe_backward_weights": (_i32, [_PP, _p, _p, _p, _p, _p, _p]),
+    "moe_backward": (_i32, [_PP, _p, _p, _p, _p, _p, _p, ctypes.POINTER(MoeForwardState), _p,
+                            ctypes.POINTER(MoeBackwardOutputs), _p, _sz, _p]),
 }
 
 _lib = None

@@ -146,7 +146,8 @@ def forward(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor, w_down: t
             intermediates: bool = False, ws: Optional[torch.Tensor] = None,
             y: Optional[torch.Tensor] = None):
     """The whole layer in one call.  Returns y [T, d], or (y, dict of
-    intermediates) with ``intermediates=True``."""
+    intermediates) with ``intermediates=True``; the intermediates include
+    the forward state ``backward`` reads."""
     T, d = x.shape
     E, f, _ = w_gate.shape
     dev = x.device
@@ -163,7 +164,8 @@ def forward(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor, w_down: t
                     counts=torch.empty(E, dtype=torch.int32, device=dev),
                     offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
                     sorted_assign=torch.empty(n, dtype=torch.int32, device=dev),
-                    assign_pos=torch.empty(n, dtype=torch.int32, device=dev))
+                    assign_pos=torch.empty(n, dtype=torch.int32, device=dev),
+                    y_perm=torch.empty(n, d, dtype=x.dtype, device=dev))
         o = L.MoeForwardOutputs(**{key: (None if (key == "logits" and logits is not None) else v.data_ptr())
                                    for key, v in outs.items()})
     ws, nbytes = _workspace(p, L.MOE_OP_FORWARD, dev, ws)
@@ -172,3 +174,63 @@ def forward(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor, w_down: t
                                  ctypes.byref(o) if o is not None else None, _ptr(ws), nbytes,
                                  _stream(dev)), "moe_forward")
     return (y, outs) if intermediates else y
+
+
+def backward_weights(w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor,
+                     w_down_t: Optional[torch.Tensor] = None, w_gu_t: Optional[torch.Tensor] = None):
+    """The weight layouts the backward GEMMs read: (w_down_t [E, f, d],
+    w_gu_t [E, d, 2f]).  Recompute after every change of the weights."""
+    E, f, d = w_gate.shape
+    dev = w_gate.device
+    p = problem(0, d, E, 1, f, w_gate.dtype)
+    if w_down_t is None:
+        w_down_t = torch.empty(E, f, d, dtype=w_gate.dtype, device=dev)
+    if w_gu_t is None:
+        w_gu_t = torch.empty(E, d, 2 * f, dtype=w_gate.dtype, device=dev)
+    L.check(L.load().moe_backward_weights(ctypes.byref(p), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+                                          _ptr(w_down_t), _ptr(w_gu_t), _stream(dev)),
+            "moe_backward_weights")
+    return w_down_t, w_gu_t
+
+
+_STATE_KEYS = ("topk_ids", "topk_gates", "offsets", "sorted_assign", "assign_pos", "y_perm")
+
+
+def backward(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor, k: int, state: dict,
+             dy: torch.Tensor, weights_t, w_router: Optional[torch.Tensor] = None,
+             with_dlogits: bool = False, ws: Optional[torch.Tensor] = None,
+             out: Optional[dict] = None) -> dict:
+    """Gradients of the layer for dy [T, d], given the forward's state (the
+    intermediates of ``forward``) and ``weights_t`` from
+    ``backward_weights``.  Returns dx, dw_gate, dw_up, dw_down, dw_router
+    (None without a router) and dlogits (None unless ``with_dlogits``).
+    ``out`` may supply any of these tensors."""
+    T, d = x.shape
+    E, f, _ = w_gate.shape
+    dev = x.device
+    p = problem(T, d, E, k, f, x.dtype)
+    w_down_t, w_gu_t = weights_t
+    res = dict(out or {})
+    res.setdefault("dx", torch.empty(T, d, dtype=x.dtype, device=dev))
+    res.setdefault("dw_gate", torch.empty(E, f, d, dtype=x.dtype, device=dev))
+    res.setdefault("dw_up", torch.empty(E, f, d, dtype=x.dtype, device=dev))
+    res.setdefault("dw_down", torch.empty(E, d, f, dtype=x.dtype, device=dev))
+    if w_router is not None:
+        res.setdefault("dw_router", torch.empty(E, d, dtype=x.dtype, device=dev))
+    else:
+        res["dw_router"] = None
+    if with_dlogits:
+        res.setdefault("dlogits", torch.empty(T, E, dtype=torch.float32, device=dev))
+    else:
+        res["dlogits"] = None
+    # (with no tokens the forward state is not read)
+    fw = L.MoeForwardState(**{key: (_ptr(state[key]) if T > 0 else None) for key in _STATE_KEYS})
+    o = L.MoeBackwardOutputs(**{key: (_ptr(res[key]) if res[key] is not None and res[key].numel() > 0
+                                      else None)
+                                for key in ("dx", "dw_gate", "dw_up", "dw_down", "dw_router", "dlogits")})
+    ws, nbytes = _workspace(p, L.MOE_OP_BACKWARD, dev, ws)
+    L.check(L.load().moe_backward(ctypes.byref(p), _ptr(x) if T > 0 else None, _ptr(w_router),
+                                  _ptr(w_gate), _ptr(w_up), _ptr(w_down_t), _ptr(w_gu_t),
+                                  ctypes.byref(fw), _ptr(dy) if T > 0 else None, ctypes.byref(o),
+                                  _ptr(ws), nbytes, _stream(dev)), "moe_backward")
+    return res

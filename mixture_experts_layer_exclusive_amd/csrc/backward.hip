@@ -1,0 +1,367 @@
+// Backward of the MoE layer, apart from its grouped GEMMs (expert_ffn.hip).
+//
+// The MoEBlaze summary (euno.news, "MoEBlaze: breaking the memory wall for
+// efficient MoE training on modern GPUs"), Methodology item 2, has the
+// backward run on the forward's compact dispatch queues; item 3 recomputes
+// the SwiGLU intermediates instead of storing them.  Here:
+//   1. per token: slot gradients dg = <dy[t], y_perm[pos]>, the queue rows'
+//      output gradient dy_perm[pos] = g dy[t], and the logit gradient of the
+//      renormalised top-k softmax, dl_j = g_j (dg_j - sum_i g_i dg_i);
+//   2. grouped GEMMs over the queues (dh, the recompute of gate/up with the
+//      SwiGLU backward, dx_perm) and the weight gradients, whose operands are
+//      first transposed here into per-expert column segments padded to a
+//      multiple of 64 with zeros;
+//   3. per token: dx[t] = sum_j dx_perm[pos(t, j)] + sum_j dl_j W_r[id_j];
+//   4. router weight gradient dW_r[e] = sum over expert e's queue of dl x.
+// All reductions run in a fixed order (deterministic); accumulation is fp32,
+// storage bf16.
+#include "device_util.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+// Block-wide sum of 256 threads (fixed order: per wave, then the 4 waves).
+__device__ __forceinline__ float block_sum(float v, float* s_part) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) s_part[threadIdx.x >> 6] = v;
+    __syncthreads();
+    return (s_part[0] + s_part[1]) + (s_part[2] + s_part[3]);
+}
+
+// Step 1, one workgroup per token.
+__global__ __launch_bounds__(256) void bwd_dy_kernel(const uint4* __restrict__ dy,
+                                                    const uint4* __restrict__ y_perm,
+                                                    const int32_t* __restrict__ ids,
+                                                    const float* __restrict__ gates,
+                                                    const int32_t* __restrict__ assign_pos, int k,
+                                                    int E, int chunks, uint4* __restrict__ dy_perm,
+                                                    float* __restrict__ dsel,
+                                                    float* __restrict__ dlogits) {
+    __shared__ float s_part[4];
+    __shared__ float s_dg[MOE_MAX_TOPK];
+    const int64_t t = blockIdx.x;
+    const uint4* dyr = dy + t * chunks;
+    for (int j = 0; j < k; ++j) {
+        const int pos = assign_pos[t * k + j];
+        const float g = gates[t * k + j];
+        float acc = 0.f;
+        for (int c = threadIdx.x; c < chunks; c += 256) {
+            const uint4 a = dyr[c];
+            const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
+            uint32_t o[4] = {0u, 0u, 0u, 0u};
+            if (pos >= 0) {
+                const uint4 b = y_perm[static_cast<int64_t>(pos) * chunks + c];
+                const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    acc = fmaf(lo_bf16(aw[i]), lo_bf16(bw[i]), acc);
+                    acc = fmaf(hi_bf16(aw[i]), hi_bf16(bw[i]), acc);
+                    o[i] = pack_bf16x2(g * lo_bf16(aw[i]), g * hi_bf16(aw[i]));
+                }
+                dy_perm[static_cast<int64_t>(pos) * chunks + c] = make_uint4(o[0], o[1], o[2], o[3]);
+            }
+        }
+        const float dg = block_sum(acc, s_part);
+        if (threadIdx.x == 0) s_dg[j] = pos >= 0 ? dg : 0.f;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float inner = 0.f;
+        for (int j = 0; j < k; ++j) inner = fmaf(gates[t * k + j], s_dg[j], inner);
+        for (int j = 0; j < k; ++j) dsel[t * k + j] = gates[t * k + j] * (s_dg[j] - inner);
+    }
+    if (dlogits != nullptr) {
+        __syncthreads();
+        for (int e = threadIdx.x; e < E; e += 256) dlogits[t * E + e] = 0.f;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            float inner = 0.f;
+            for (int j = 0; j < k; ++j) inner = fmaf(gates[t * k + j], s_dg[j], inner);
+            for (int j = 0; j < k; ++j) {
+                const int e = ids[t * k + j];
+                if (static_cast<unsigned>(e) < static_cast<unsigned>(E))
+                    dlogits[t * E + e] = gates[t * k + j] * (s_dg[j] - inner);
+            }
+        }
+    }
+}
+
+// Padded offsets: expert e's queue columns start at poff[e], each expert's
+// count rounded up to a multiple of 64 (all zero when offsets is null: no
+// tokens).  One wave, E <= 256.
+__global__ __launch_bounds__(64) void bwd_poff_kernel(const int32_t* __restrict__ offsets, int E,
+                                                     int32_t* __restrict__ poff) {
+    const int lane = threadIdx.x;
+    int c[4], local = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = lane * 4 + i;
+        c[i] = (e < E && offsets != nullptr) ? ((offsets[e + 1] - offsets[e] + 63) / 64) * 64 : 0;
+        local += c[i];
+    }
+    int incl = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += o;
+    }
+    int run = incl - local;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = lane * 4 + i;
+        if (e < E) poff[e] = run;
+        run += c[i];
+    }
+    if (lane == 63) poff[E] = incl;
+}
+
+// Transpose of queue rows into padded per-expert column segments:
+//   dst[c, q] = src_row(q)[c] for c < C, q < Kpad,
+// where padded column q of expert e (poff[e] <= q < poff[e+1]) is queue row
+// pos = offsets[e] + q - poff[e] when pos < offsets[e+1], else zero.  The
+// source row is src[pos] (row stride ld_src), or, with GATHER, row
+// sorted_assign[pos] / k of src.  Tiles of 64 columns x 64 rows through LDS.
+template <bool GATHER>
+__global__ __launch_bounds__(256) void bwd_transpose_kernel(const bf16_t* __restrict__ src,
+                                                           int64_t ld_src, int C,
+                                                           const int32_t* __restrict__ offsets,
+                                                           const int32_t* __restrict__ poff, int E,
+                                                           const int32_t* __restrict__ sorted_assign,
+                                                           int k, int64_t kpad,
+                                                           bf16_t* __restrict__ dst) {
+    __shared__ bf16_t tile[64][64 + 2];
+    __shared__ int64_t s_row[64];
+    const int q0 = blockIdx.x * 64;
+    const int c0 = blockIdx.y * 64;
+    if (q0 >= poff[E]) return;
+    if (threadIdx.x < 64) {
+        const int q = q0 + threadIdx.x;
+        int lo = 0, hi = E;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (poff[mid] <= q) lo = mid; else hi = mid;
+        }
+        const int pos = offsets[lo] + (q - poff[lo]);
+        int64_t row = -1;
+        if (q < poff[E] && pos < offsets[lo + 1]) row = GATHER ? sorted_assign[pos] / k : pos;
+        s_row[threadIdx.x] = row;
+    }
+    __syncthreads();
+    // load: thread -> (row i = tid / 4, 16 columns (tid % 4) * 16 ..)
+    {
+        const int i = threadIdx.x >> 2;
+        const int cc = (threadIdx.x & 3) * 16;
+        const int64_t row = s_row[i];
+#pragma unroll
+        for (int u = 0; u < 16; u += 8) {
+            const int c = c0 + cc + u;
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (row >= 0 && c < C) v = *reinterpret_cast<const uint4*>(src + row * ld_src + c);
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                tile[i][cc + u + 2 * h] = static_cast<bf16_t>(w[h] & 0xffffu);
+                tile[i][cc + u + 2 * h + 1] = static_cast<bf16_t>(w[h] >> 16);
+            }
+        }
+    }
+    __syncthreads();
+    // store: thread -> (column c = tid / 4, 16 padded positions (tid % 4) * 16 ..)
+    {
+        const int c = threadIdx.x >> 2;
+        const int qq = (threadIdx.x & 3) * 16;
+        if (c0 + c < C) {
+#pragma unroll
+            for (int u = 0; u < 16; u += 8) {
+                uint32_t w[4];
+#pragma unroll
+                for (int h = 0; h < 4; ++h)
+                    w[h] = static_cast<uint32_t>(tile[qq + u + 2 * h][c]) |
+                           (static_cast<uint32_t>(tile[qq + u + 2 * h + 1][c]) << 16);
+                *reinterpret_cast<uint4*>(dst + static_cast<int64_t>(c0 + c) * kpad + q0 + qq + u) =
+                    make_uint4(w[0], w[1], w[2], w[3]);
+            }
+        }
+    }
+}
+
+// Step 3: dx[t] = sum_j dx_perm[pos(t, j)] (+ sum_j dl_j W_r[id_j]), fp32 in
+// ascending j, one rounding.
+__global__ __launch_bounds__(256) void bwd_dx_kernel(const uint4* __restrict__ dx_perm,
+                                                    const int32_t* __restrict__ assign_pos,
+                                                    const int32_t* __restrict__ ids,
+                                                    const float* __restrict__ dsel,
+                                                    const uint4* __restrict__ w_router, int k, int E,
+                                                    int chunks, uint4* __restrict__ dx) {
+    const int64_t t = blockIdx.x;
+    for (int c = threadIdx.x; c < chunks; c += 256) {
+        float acc[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+        for (int j = 0; j < k; ++j) {
+            const int pos = assign_pos[t * k + j];
+            if (pos < 0) continue;
+            const uint4 v = dx_perm[static_cast<int64_t>(pos) * chunks + c];
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc[2 * i] += lo_bf16(w[i]);
+                acc[2 * i + 1] += hi_bf16(w[i]);
+            }
+        }
+        if (w_router != nullptr) {
+            for (int j = 0; j < k; ++j) {
+                const int e = ids[t * k + j];
+                if (static_cast<unsigned>(e) >= static_cast<unsigned>(E)) continue;
+                const float dl = dsel[t * k + j];
+                const uint4 v = w_router[static_cast<int64_t>(e) * chunks + c];
+                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    acc[2 * i] = fmaf(dl, lo_bf16(w[i]), acc[2 * i]);
+                    acc[2 * i + 1] = fmaf(dl, hi_bf16(w[i]), acc[2 * i + 1]);
+                }
+            }
+        }
+        dx[t * chunks + c] = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                                        pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
+    }
+}
+
+// Step 4: dW_r[e, c] = sum over expert e's queue (ascending) of
+// dl[a] * x[a / k, c]; grid (E, d / 256), one column per thread.
+__global__ __launch_bounds__(256) void bwd_dwr_kernel(const bf16_t* __restrict__ x,
+                                                     const int32_t* __restrict__ offsets,
+                                                     const int32_t* __restrict__ sorted_assign,
+                                                     const float* __restrict__ dsel, int k, int d,
+                                                     bf16_t* __restrict__ dw_router) {
+    const int e = blockIdx.x;
+    const int c = blockIdx.y * 256 + threadIdx.x;
+    if (c >= d) return;
+    float acc = 0.f;
+    const int p1 = offsets[e + 1];
+    for (int pos = offsets[e]; pos < p1; ++pos) {
+        const int a = sorted_assign[pos];
+        acc = fmaf(dsel[a], bf16_to_f32(x[static_cast<int64_t>(a / k) * d + c]), acc);
+    }
+    dw_router[static_cast<int64_t>(e) * d + c] = __builtin_bit_cast(bf16_t, static_cast<__bf16>(acc));
+}
+
+// Weight transpose for the backward GEMMs, per expert (gridDim.z):
+// dst[e][c][col0 + i] = src[e][i][c] for i < R, c < Cc (src rows of Cc,
+// dst rows of ld_dst).  Tiles of 64 x 64 through LDS.
+__global__ __launch_bounds__(256) void weight_transpose_kernel(const bf16_t* __restrict__ src, int R,
+                                                              int Cc, bf16_t* __restrict__ dst,
+                                                              int64_t ld_dst, int col0) {
+    __shared__ bf16_t tile[64][64 + 2];
+    const int64_t e = blockIdx.z;
+    const int i0 = blockIdx.x * 64;
+    const int c0 = blockIdx.y * 64;
+    const bf16_t* s = src + e * R * Cc;
+    bf16_t* dd = dst + e * Cc * ld_dst;
+    {
+        const int i = threadIdx.x >> 2;
+        const int cc = (threadIdx.x & 3) * 16;
+#pragma unroll
+        for (int u = 0; u < 16; u += 8) {
+            const int c = c0 + cc + u;
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (i0 + i < R && c < Cc) v = *reinterpret_cast<const uint4*>(s + static_cast<int64_t>(i0 + i) * Cc + c);
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                tile[i][cc + u + 2 * h] = static_cast<bf16_t>(w[h] & 0xffffu);
+                tile[i][cc + u + 2 * h + 1] = static_cast<bf16_t>(w[h] >> 16);
+            }
+        }
+    }
+    __syncthreads();
+    {
+        const int c = threadIdx.x >> 2;
+        const int ii = (threadIdx.x & 3) * 16;
+        if (c0 + c < Cc) {
+#pragma unroll
+            for (int u = 0; u < 16; u += 8) {
+                if (i0 + ii + u >= R) continue;
+                uint32_t w[4];
+#pragma unroll
+                for (int h = 0; h < 4; ++h)
+                    w[h] = static_cast<uint32_t>(tile[ii + u + 2 * h][c]) |
+                           (static_cast<uint32_t>(tile[ii + u + 2 * h + 1][c]) << 16);
+                *reinterpret_cast<uint4*>(dd + static_cast<int64_t>(c0 + c) * ld_dst + col0 + i0 + ii + u) =
+                    make_uint4(w[0], w[1], w[2], w[3]);
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_backward_weights(const moe_problem_t& p, const void* w_gate, const void* w_up,
+                                   const void* w_down, void* w_down_t, void* w_gu_t, hipStream_t s) {
+    // W_down [E, d, f] -> W_down_t [E, f, d]
+    weight_transpose_kernel<<<dim3(ceil_div(p.d, 64), ceil_div(p.f, 64), p.E), 256, 0, s>>>(
+        static_cast<const bf16_t*>(w_down), p.d, p.f, static_cast<bf16_t*>(w_down_t), p.d, 0);
+    // W_gate, W_up [E, f, d] -> W_gu_t [E, d, 2f] (gate columns, then up columns)
+    const dim3 g(ceil_div(p.f, 64), ceil_div(p.d, 64), p.E);
+    weight_transpose_kernel<<<g, 256, 0, s>>>(static_cast<const bf16_t*>(w_gate), p.f, p.d,
+                                              static_cast<bf16_t*>(w_gu_t), 2 * int64_t{p.f}, 0);
+    weight_transpose_kernel<<<g, 256, 0, s>>>(static_cast<const bf16_t*>(w_up), p.f, p.d,
+                                              static_cast<bf16_t*>(w_gu_t), 2 * int64_t{p.f}, p.f);
+    return hipGetLastError();
+}
+
+hipError_t launch_backward_dy(const moe_problem_t& p, const void* dy, const void* y_perm,
+                              const int32_t* ids, const float* gates, const int32_t* assign_pos,
+                              void* dy_perm, float* dsel, float* dlogits, hipStream_t s) {
+    bwd_dy_kernel<<<static_cast<unsigned>(p.T), 256, 0, s>>>(
+        static_cast<const uint4*>(dy), static_cast<const uint4*>(y_perm), ids, gates, assign_pos, p.k,
+        p.E, p.d / 8, static_cast<uint4*>(dy_perm), dsel, dlogits);
+    return hipGetLastError();
+}
+
+hipError_t launch_backward_poff(const moe_problem_t& p, const int32_t* offsets, int32_t* poff,
+                                hipStream_t s) {
+    bwd_poff_kernel<<<1, 64, 0, s>>>(offsets, p.E, poff);
+    return hipGetLastError();
+}
+
+hipError_t launch_backward_transpose(const moe_problem_t& p, const void* src, int64_t ld_src, int C,
+                                     bool gather, const int32_t* offsets, const int32_t* poff,
+                                     const int32_t* sorted_assign, int64_t kpad, void* dst,
+                                     hipStream_t s) {
+    const dim3 grid(static_cast<unsigned>(kpad / 64), static_cast<unsigned>(ceil_div(C, 64)));
+    if (gather)
+        bwd_transpose_kernel<true><<<grid, 256, 0, s>>>(static_cast<const bf16_t*>(src), ld_src, C, offsets,
+                                                        poff, p.E, sorted_assign, p.k, kpad,
+                                                        static_cast<bf16_t*>(dst));
+    else
+        bwd_transpose_kernel<false><<<grid, 256, 0, s>>>(static_cast<const bf16_t*>(src), ld_src, C, offsets,
+                                                         poff, p.E, sorted_assign, p.k, kpad,
+                                                         static_cast<bf16_t*>(dst));
+    return hipGetLastError();
+}
+
+hipError_t launch_backward_dx(const moe_problem_t& p, const void* dx_perm, const int32_t* assign_pos,
+                              const int32_t* ids, const float* dsel, const void* w_router, void* dx,
+                              hipStream_t s) {
+    bwd_dx_kernel<<<static_cast<unsigned>(p.T), 256, 0, s>>>(
+        static_cast<const uint4*>(dx_perm), assign_pos, ids, dsel, static_cast<const uint4*>(w_router),
+        p.k, p.E, p.d / 8, static_cast<uint4*>(dx));
+    return hipGetLastError();
+}
+
+hipError_t launch_backward_dwr(const moe_problem_t& p, const void* x, const int32_t* offsets,
+                               const int32_t* sorted_assign, const float* dsel, void* dw_router,
+                               hipStream_t s) {
+    bwd_dwr_kernel<<<dim3(p.E, ceil_div(p.d, 256)), 256, 0, s>>>(
+        static_cast<const bf16_t*>(x), offsets, sorted_assign, dsel, p.k, p.d,
+        static_cast<bf16_t*>(dw_router));
+    return hipGetLastError();
+}
+
+}  // namespace moe

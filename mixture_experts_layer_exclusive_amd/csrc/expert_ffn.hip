@@ -946,4 +946,61 @@ hipError_t launch_expert_ffn(const moe_problem_t& p, const void* x_perm, const v
     return hipGetLastError();
 }
 
+// ---- backward GEMMs (bf16) ----------------------------------------------
+
+// dh = dy_perm W_down over the queues (W_down_t = W_down transposed, [E, f, d]).
+hipError_t launch_backward_dh(const moe_problem_t& p, const void* dy_perm, const int32_t* offsets,
+                              const void* w_down_t, void* dh, hipStream_t s) {
+    const int64_t n = p.T * p.k;
+    const unsigned g = grid_for(n, p.E, kBM, static_cast<int>(ceil_div(p.f, kDownCols)));
+    grouped_gemm_bf16_kernel<kDown, false, false><<<g, 256, 0, s>>>(
+        static_cast<const bf16_t*>(dy_perm), nullptr, p.k, offsets, p.E,
+        static_cast<const bf16_t*>(w_down_t), nullptr, static_cast<bf16_t*>(dh), p.f, p.d, 0, nullptr,
+        nullptr, nullptr, 0);
+    return hipGetLastError();
+}
+
+// Recompute of gate and up from x (gathered), with the SwiGLU backward in the
+// epilogue: du, dv -> duv [T*k, 2f], h -> h [T*k, f].
+hipError_t launch_backward_recompute(const moe_problem_t& p, const void* x, const int32_t* sorted_assign,
+                                     const int32_t* offsets, const void* w_gate, const void* w_up,
+                                     const void* dh, void* duv, void* h, hipStream_t s) {
+    const int64_t n = p.T * p.k;
+    const unsigned g = grid_for(n, p.E, kBM, static_cast<int>(ceil_div(p.f, kGateUpCols)));
+    if (p.T * p.d >= (int64_t{1} << 31))
+        grouped_gemm_bf16_kernel<kUpBwd, true, true><<<g, 256, 0, s>>>(
+            static_cast<const bf16_t*>(x), sorted_assign, p.k, offsets, p.E,
+            static_cast<const bf16_t*>(w_gate), static_cast<const bf16_t*>(w_up), static_cast<bf16_t*>(duv),
+            p.f, p.d, 0, nullptr, static_cast<const bf16_t*>(dh), static_cast<bf16_t*>(h), 0);
+    else
+        grouped_gemm_bf16_kernel<kUpBwd, true, false><<<g, 256, 0, s>>>(
+            static_cast<const bf16_t*>(x), sorted_assign, p.k, offsets, p.E,
+            static_cast<const bf16_t*>(w_gate), static_cast<const bf16_t*>(w_up), static_cast<bf16_t*>(duv),
+            p.f, p.d, 0, nullptr, static_cast<const bf16_t*>(dh), static_cast<bf16_t*>(h), 0);
+    return hipGetLastError();
+}
+
+// dx_perm = [du dv] [W_gate; W_up] over the queues (W_gu_t = [E, d, 2f]).
+hipError_t launch_backward_dxperm(const moe_problem_t& p, const void* duv, const int32_t* offsets,
+                                  const void* w_gu_t, void* dx_perm, hipStream_t s) {
+    const int64_t n = p.T * p.k;
+    const unsigned g = grid_for(n, p.E, kBM, static_cast<int>(ceil_div(p.d, kDownCols)));
+    grouped_gemm_bf16_kernel<kDown, false, false><<<g, 256, 0, s>>>(
+        static_cast<const bf16_t*>(duv), nullptr, p.k, offsets, p.E, static_cast<const bf16_t*>(w_gu_t),
+        nullptr, static_cast<bf16_t*>(dx_perm), p.d, 2 * p.f, 0, nullptr, nullptr, nullptr, 0);
+    return hipGetLastError();
+}
+
+// Weight gradient per expert: C[e] [M, N] = A_e B_e^T over the expert's padded
+// queue columns [poff[e], poff[e+1]) of A [M, ldk] and B [N, ldk].
+hipError_t launch_backward_wgrad(const moe_problem_t& p, const void* A, int M, const void* B, int N,
+                                 int64_t ldk, const int32_t* poff, void* C, hipStream_t s) {
+    const int64_t tiles = static_cast<int64_t>(p.E) * ceil_div(M, kBM) * ceil_div(N, kDownCols);
+    const unsigned g = static_cast<unsigned>(align_up(static_cast<size_t>(tiles), NUM_XCD));
+    grouped_gemm_bf16_kernel<kWgrad, false, false><<<g, 256, 0, s>>>(
+        static_cast<const bf16_t*>(A), nullptr, p.k, poff, p.E, static_cast<const bf16_t*>(B), nullptr,
+        static_cast<bf16_t*>(C), N, static_cast<int>(ldk), 0, nullptr, nullptr, nullptr, M);
+    return hipGetLastError();
+}
+
 }  // namespace moe

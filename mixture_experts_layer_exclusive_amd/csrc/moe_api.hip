@@ -11,7 +11,7 @@ using namespace moe;
 
 namespace {
 
-constexpr int32_t kAbiVersion = 1;
+constexpr int32_t kAbiVersion = 2;
 constexpr size_t kAlign = 256;
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
@@ -75,6 +75,36 @@ size_t dispatch_ws(const moe_problem_t& p) {
 
 size_t ffn_ws(const moe_problem_t& p) { return ffn_h_bytes(p) + ffn_split_bytes(p); }
 
+// Backward workspace, in carving order: dsel [T*k] fp32, dy_perm [T*k, d],
+// dh [T*k, f], duv [T*k, 2f], h [T*k, f], dx_perm [T*k, d], poff [E+1],
+// and the transposed operands of the weight gradients dy_perm^T [d, kpad],
+// h^T [f, kpad], duv^T [2f, kpad], x_perm^T [d, kpad].
+size_t backward_ws(const moe_problem_t& p) {
+    const size_t n = static_cast<size_t>(p.T) * p.k;
+    const size_t kp = static_cast<size_t>(backward_kpad(p));
+    size_t b = align_up(n * 4, kAlign);
+    b += align_up(n * p.d * 2, kAlign) * 2;          // dy_perm, dx_perm
+    b += align_up(n * p.f * 2, kAlign) * 2;          // dh, h
+    b += align_up(n * 2 * p.f * 2, kAlign);          // duv
+    b += align_up(static_cast<size_t>(p.E + 1) * 4, kAlign);
+    b += align_up(static_cast<size_t>(p.d) * kp * 2, kAlign) * 2;  // dy^T, x^T
+    b += align_up(static_cast<size_t>(p.f) * kp * 2, kAlign);      // h^T
+    b += align_up(static_cast<size_t>(2 * p.f) * kp * 2, kAlign);  // duv^T
+    return b;
+}
+
+// Limits of the bf16 backward (beyond check_problem): the GEMMs address
+// [E, d, 2f] weight rows and the padded transposed operands with 32-bit
+// byte offsets.
+moe_status_t check_backward(const moe_problem_t* p) {
+    if (p->dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
+    if (static_cast<int64_t>(p->d) * p->f >= (int64_t{1} << 30)) return MOE_ERR_UNSUPPORTED;
+    const int64_t kp = backward_kpad(*p);
+    if (kp > INT32_MAX || static_cast<int64_t>(p->d > p->f ? p->d : p->f) * kp * 2 > UINT32_MAX)
+        return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
 size_t forward_ws(const moe_problem_t& p) {
     const size_t n = static_cast<size_t>(p.T) * p.k;
     size_t b = 0;
@@ -114,6 +144,10 @@ moe_status_t moe_workspace_size(const moe_problem_t* p, int32_t op, size_t* byte
         case MOE_OP_DISPATCH: *bytes = dispatch_ws(*p); break;
         case MOE_OP_EXPERT_FFN: *bytes = ffn_ws(*p); break;
         case MOE_OP_FORWARD: *bytes = forward_ws(*p); break;
+        case MOE_OP_BACKWARD:
+            MOE_TRY(check_backward(p));
+            *bytes = backward_ws(*p);
+            break;
         default: return MOE_ERR_INVALID_ARGUMENT;
     }
     return MOE_OK;
@@ -231,6 +265,7 @@ moe_status_t moe_forward(const moe_problem_t* p, const void* x, const void* w_ro
         MOE_TRY(optional(o.offsets));
         MOE_TRY(optional(o.sorted_assign));
         MOE_TRY(optional(o.assign_pos));
+        MOE_TRY(optional(o.y_perm));
     }
     MOE_TRY(need(ws));
     if (ws_bytes < forward_ws(*p)) return MOE_ERR_WORKSPACE_TOO_SMALL;
@@ -254,6 +289,7 @@ moe_status_t moe_forward(const moe_problem_t* p, const void* x, const void* w_ro
     if (o.assign_pos) ap = o.assign_pos;
     if (o.counts) counts = o.counts;
     if (o.offsets) offsets = o.offsets;
+    if (o.y_perm) y_perm = o.y_perm;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     clear_hip_error();
@@ -266,6 +302,104 @@ moe_status_t moe_forward(const moe_problem_t* p, const void* x, const void* w_ro
     MOE_LAUNCH(launch_dispatch_queues(*p, ids, counts, offsets, sa, ap, bc, s));
     MOE_LAUNCH(launch_expert_ffn(*p, nullptr, x, sa, offsets, w_gate, w_up, w_down, h, y_perm, s));
     MOE_LAUNCH(launch_combine(*p, y_perm, ap, gates, y, s));
+    return MOE_OK;
+}
+
+moe_status_t moe_backward_weights(const moe_problem_t* p, const void* w_gate, const void* w_up,
+                                  const void* w_down, void* w_down_t, void* w_gu_t, void* stream) {
+    MOE_TRY(check_problem(p));
+    MOE_TRY(check_backward(p));
+    MOE_TRY(need(w_gate));
+    MOE_TRY(need(w_up));
+    MOE_TRY(need(w_down));
+    MOE_TRY(need(w_down_t));
+    MOE_TRY(need(w_gu_t));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    clear_hip_error();
+    MOE_LAUNCH(launch_backward_weights(*p, w_gate, w_up, w_down, w_down_t, w_gu_t, s));
+    return MOE_OK;
+}
+
+moe_status_t moe_backward(const moe_problem_t* p, const void* x, const void* w_router,
+                          const void* w_gate, const void* w_up, const void* w_down_t,
+                          const void* w_gu_t, const moe_forward_state_t* fw, const void* dy,
+                          const moe_backward_outputs_t* out, void* ws, size_t ws_bytes,
+                          void* stream) {
+    MOE_TRY(check_problem(p));
+    MOE_TRY(check_backward(p));
+    if (fw == nullptr || out == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+    MOE_TRY(need(w_gate));
+    MOE_TRY(need(w_up));
+    MOE_TRY(need(w_down_t));
+    MOE_TRY(need(w_gu_t));
+    MOE_TRY(need(out->dw_gate));
+    MOE_TRY(need(out->dw_up));
+    MOE_TRY(need(out->dw_down));
+    MOE_TRY(optional(out->dlogits));
+    if (w_router != nullptr) {
+        MOE_TRY(need(w_router));
+        MOE_TRY(need(out->dw_router));
+    } else if (out->dw_router != nullptr) {
+        return MOE_ERR_INVALID_ARGUMENT;
+    }
+    if (p->T > 0) {
+        MOE_TRY(need(x));
+        MOE_TRY(need(dy));
+        MOE_TRY(need(out->dx));
+        MOE_TRY(need(fw->offsets));
+        MOE_TRY(need(fw->topk_ids));
+        MOE_TRY(need(fw->topk_gates));
+        MOE_TRY(need(fw->sorted_assign));
+        MOE_TRY(need(fw->assign_pos));
+        MOE_TRY(need(fw->y_perm));
+    }
+    MOE_TRY(need(ws));
+    if (ws_bytes < backward_ws(*p)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+
+    const size_t n = static_cast<size_t>(p->T) * p->k;
+    const int64_t kp = backward_kpad(*p);
+    Carver c(ws);
+    float* dsel = c.take<float>(n * 4);
+    void* dy_perm = c.take<char>(n * p->d * 2);
+    void* dx_perm = c.take<char>(n * p->d * 2);
+    void* dh = c.take<char>(n * p->f * 2);
+    void* h = c.take<char>(n * p->f * 2);
+    void* duv = c.take<char>(n * 2 * p->f * 2);
+    int32_t* poff = c.take<int32_t>(static_cast<size_t>(p->E + 1) * 4);
+    void* dyT = c.take<char>(static_cast<size_t>(p->d) * kp * 2);
+    void* xT = c.take<char>(static_cast<size_t>(p->d) * kp * 2);
+    void* hT = c.take<char>(static_cast<size_t>(p->f) * kp * 2);
+    void* duvT = c.take<char>(static_cast<size_t>(2 * p->f) * kp * 2);
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    clear_hip_error();
+    // (with no tokens fw is not read: every queue is empty)
+    MOE_LAUNCH(launch_backward_poff(*p, p->T > 0 ? fw->offsets : nullptr, poff, s));
+    if (p->T > 0) {
+        MOE_LAUNCH(launch_backward_dy(*p, dy, fw->y_perm, fw->topk_ids, fw->topk_gates, fw->assign_pos,
+                                      dy_perm, dsel, out->dlogits, s));
+        MOE_LAUNCH(launch_backward_dh(*p, dy_perm, fw->offsets, w_down_t, dh, s));
+        MOE_LAUNCH(launch_backward_recompute(*p, x, fw->sorted_assign, fw->offsets, w_gate, w_up, dh, duv,
+                                             h, s));
+        MOE_LAUNCH(launch_backward_dxperm(*p, duv, fw->offsets, w_gu_t, dx_perm, s));
+        MOE_LAUNCH(launch_backward_dx(*p, dx_perm, fw->assign_pos, fw->topk_ids, dsel, w_router, out->dx,
+                                      s));
+        MOE_LAUNCH(launch_backward_transpose(*p, dy_perm, p->d, p->d, false, fw->offsets, poff, nullptr, kp,
+                                             dyT, s));
+        MOE_LAUNCH(launch_backward_transpose(*p, h, p->f, p->f, false, fw->offsets, poff, nullptr, kp, hT, s));
+        MOE_LAUNCH(launch_backward_transpose(*p, duv, 2 * p->f, 2 * p->f, false, fw->offsets, poff, nullptr,
+                                             kp, duvT, s));
+        MOE_LAUNCH(launch_backward_transpose(*p, x, p->d, p->d, true, fw->offsets, poff, fw->sorted_assign, kp,
+                                             xT, s));
+    }
+    // weight gradients (an expert with no rows gets zeros)
+    MOE_LAUNCH(launch_backward_wgrad(*p, dyT, p->d, hT, p->f, kp, poff, out->dw_down, s));
+    MOE_LAUNCH(launch_backward_wgrad(*p, duvT, p->f, xT, p->d, kp, poff, out->dw_gate, s));
+    MOE_LAUNCH(launch_backward_wgrad(*p, static_cast<char*>(duvT) + static_cast<size_t>(p->f) * kp * 2, p->f,
+                                     xT, p->d, kp, poff, out->dw_up, s));
+    if (w_router != nullptr)
+        MOE_LAUNCH(launch_backward_dwr(*p, x, p->T > 0 ? fw->offsets : poff, fw->sorted_assign, dsel,
+                                       out->dw_router, s));
     return MOE_OK;
 }
 

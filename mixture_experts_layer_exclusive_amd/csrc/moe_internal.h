@@ -84,4 +84,39 @@ hipError_t launch_expert_ffn(const moe_problem_t& p, const void* x_perm, const v
 hipError_t launch_combine(const moe_problem_t& p, const void* y_perm, const int32_t* assign_pos,
                           const float* gates, void* y, hipStream_t s);
 
+// ---- backward (bf16) ------------------------------------------------------
+
+// Padded per-expert column count of the weight-gradient operands: every
+// expert's queue rounded up to 64 columns.
+inline int64_t backward_kpad(const moe_problem_t& p) {
+    return static_cast<int64_t>(align_up(static_cast<size_t>(p.T * p.k + 63 * static_cast<int64_t>(p.E)), 64));
+}
+
+hipError_t launch_backward_weights(const moe_problem_t& p, const void* w_gate, const void* w_up,
+                                   const void* w_down, void* w_down_t, void* w_gu_t, hipStream_t s);
+hipError_t launch_backward_dy(const moe_problem_t& p, const void* dy, const void* y_perm,
+                              const int32_t* ids, const float* gates, const int32_t* assign_pos,
+                              void* dy_perm, float* dsel, float* dlogits, hipStream_t s);
+hipError_t launch_backward_poff(const moe_problem_t& p, const int32_t* offsets, int32_t* poff,
+                                hipStream_t s);
+hipError_t launch_backward_transpose(const moe_problem_t& p, const void* src, int64_t ld_src, int C,
+                                     bool gather, const int32_t* offsets, const int32_t* poff,
+                                     const int32_t* sorted_assign, int64_t kpad, void* dst,
+                                     hipStream_t s);
+hipError_t launch_backward_dx(const moe_problem_t& p, const void* dx_perm, const int32_t* assign_pos,
+                              const int32_t* ids, const float* dsel, const void* w_router, void* dx,
+                              hipStream_t s);
+hipError_t launch_backward_dwr(const moe_problem_t& p, const void* x, const int32_t* offsets,
+                               const int32_t* sorted_assign, const float* dsel, void* dw_router,
+                               hipStream_t s);
+hipError_t launch_backward_dh(const moe_problem_t& p, const void* dy_perm, const int32_t* offsets,
+                              const void* w_down_t, void* dh, hipStream_t s);
+hipError_t launch_backward_recompute(const moe_problem_t& p, const void* x, const int32_t* sorted_assign,
+                                     const int32_t* offsets, const void* w_gate, const void* w_up,
+                                     const void* dh, void* duv, void* h, hipStream_t s);
+hipError_t launch_backward_dxperm(const moe_problem_t& p, const void* duv, const int32_t* offsets,
+                                  const void* w_gu_t, void* dx_perm, hipStream_t s);
+hipError_t launch_backward_wgrad(const moe_problem_t& p, const void* A, int M, const void* B, int N,
+                                 int64_t ldk, const int32_t* poff, void* C, hipStream_t s);
+
 }  // namespace moe

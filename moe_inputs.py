@@ -9,14 +9,14 @@ Recipe (the same for every caller):
 
 * Tensor ``i`` of a problem (0 = x, 1 = router weight, 2 = W_gate,
   3 = W_up, 4 = W_down, 5 = router-logit noise, 6 = tie-heavy logits,
-  7 = token sample) is drawn in row-major order in chunks of ``CHUNK``
+  7 = token sample, 8 = output gradient dy) is drawn in row-major order in chunks of ``CHUNK``
   elements; chunk ``c`` comes from ``numpy.random.default_rng([seed, i, c])``
   as ``standard_normal(dtype=float32)``.  Chunks are independent streams, so
   they are drawn in parallel threads and the result does not depend on the
   thread count.
 * Each draw is multiplied by its standard deviation (computed in fp64 and
   rounded once to fp32): x 1, router weight 0.02, all three expert matrices
-  ``1/sqrt(d)``.  The second parameter of ``N(0, s)`` is read as a standard
+  ``1/sqrt(d)``, output gradient dy 1.  The second parameter of ``N(0, s)`` is read as a standard
   deviation.
 * bf16 problems round the scaled fp32 values to bf16 with round-to-nearest-
   even and store the 16-bit patterns as ``uint16``.
@@ -40,7 +40,7 @@ import numpy as np
 CHUNK = 1 << 22
 
 # stream ids
-S_X, S_WR, S_WG, S_WU, S_WD, S_LOGIT, S_TIES, S_SAMPLE = range(8)
+S_X, S_WR, S_WG, S_WU, S_WD, S_LOGIT, S_TIES, S_SAMPLE, S_DY = range(9)
 
 
 @dataclass(frozen=True)
@@ -149,6 +149,11 @@ def _draw(seed: int, stream: int, shape, sigma: float, dtype: str) -> np.ndarray
 def make_x(p: Problem, seed: int = 0) -> np.ndarray:
     """Activations x[T, d]: N(0, 1)."""
     return _draw(seed, S_X, (p.T, p.d), 1.0, p.dtype)
+
+
+def make_grad_output(p: Problem, seed: int = 0) -> np.ndarray:
+    """Output gradient dy[T, d] for the backward: N(0, 1)."""
+    return _draw(seed, S_DY, (p.T, p.d), 1.0, p.dtype)
 
 
 def make_router_weight(p: Problem, seed: int = 0) -> np.ndarray:

@@ -110,7 +110,10 @@ def backward(x: np.ndarray, k: int, w_gate: np.ndarray, w_up: np.ndarray, w_down
     """Gradients of the whole layer for the output gradient ``dy`` [T, d]:
     dx [T, d], dw_gate, dw_up [E, f, d], dw_down [E, d, f], dlogits [T, E],
     dgates [T, k] and (with a router) dw_router [E, d], all float64.  The
-    routing (ids, gates, queues) is the forward's."""
+    routing (ids, gates, queues) is the forward's.  Given both ``w_router``
+    and ``logits``, the logits stand for the router's output as computed
+    elsewhere (routing and gates read them) and the router gradients still
+    flow through ``w_router``."""
     fw = forward(x, k, w_gate, w_up, w_down, w_router=w_router, logits=logits)
     E = fw["logits"].shape[1]
     T, d = np.asarray(x).shape
@@ -137,7 +140,7 @@ def backward(x: np.ndarray, k: int, w_gate: np.ndarray, w_up: np.ndarray, w_down
         dx += dx_perm[pos[:, j]]
     dlogits = topk_gates_backward(fw["logits"], fw["ids"], fw["gates"], dgates)
     dw_router = None
-    if logits is None:
+    if w_router is not None:
         dw_router = dlogits.T @ _f64(x)
         dx += dlogits @ _f64(w_router)
     return dict(dx=dx, dw_gate=dwg, dw_up=dwu, dw_down=dwd, dlogits=dlogits, dgates=dgates,

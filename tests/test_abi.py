@@ -48,7 +48,7 @@ def test_header_constants_match_binding():
     assert int(re.search(r"#define MOE_MAX_TOPK (\d+)", text).group(1)) == L.MOE_MAX_TOPK
     for name in ("MOE_OK", "MOE_ERR_INVALID_ARGUMENT", "MOE_ERR_UNSUPPORTED",
                  "MOE_ERR_WORKSPACE_TOO_SMALL", "MOE_ERR_HIP", "MOE_DTYPE_F32", "MOE_DTYPE_BF16",
-                 "MOE_OP_DISPATCH", "MOE_OP_EXPERT_FFN", "MOE_OP_FORWARD"):
+                 "MOE_OP_DISPATCH", "MOE_OP_EXPERT_FFN", "MOE_OP_FORWARD", "MOE_OP_BACKWARD"):
         assert int(re.search(name + r"\s*=\s*(\d+)", text).group(1)) == getattr(L, name)
 
 
@@ -168,3 +168,55 @@ def test_workspace_has_no_dense_routing_matrix(lib):
         assert expect <= nw <= expect + 16 * 256
         _, nf = ws_size(lib, p, L.MOE_OP_EXPERT_FFN)
         assert T * k * f * s + split <= nf <= T * k * f * s + split + 256
+
+
+def bwd_args(fw=True, out=True, w_router=A, dw_router=A, ws_bytes=1 << 40, **fields):
+    st = L.MoeForwardState(topk_ids=A, topk_gates=A, offsets=A, sorted_assign=A, assign_pos=A, y_perm=A)
+    o = L.MoeBackwardOutputs(dx=A, dw_gate=A, dw_up=A, dw_down=A, dw_router=dw_router, dlogits=None)
+    for key, v in fields.items():
+        setattr(st if key in dict(L.MoeForwardState._fields_) else o, key, v)
+    return (A, w_router, A, A, A, A, ctypes.byref(st) if fw else None, A,
+            ctypes.byref(o) if out else None, A, ws_bytes, None)
+
+
+def test_backward_validation(lib):
+    U = L.MOE_ERR_UNSUPPORTED
+    E = L.MOE_ERR_INVALID_ARGUMENT
+    good = prob(T=64, d=256, E=8, k=2, f=512)
+    st, need = ws_size(lib, good, L.MOE_OP_BACKWARD)
+    assert st == L.MOE_OK and need > 0
+    for bad, status in [(dict(dtype=L.MOE_DTYPE_F32), U),       # bf16 only
+                        (dict(d=32768, f=32768), U),            # d*f >= 2^30
+                        (dict(k=9), E)]:
+        p = prob(T=64, d=256, E=8, k=2, f=512)
+        for key, v in bad.items():
+            setattr(p, key, v)
+        assert ws_size(lib, p, L.MOE_OP_BACKWARD)[0] == status
+        assert lib.moe_backward_weights(ctypes.byref(p), A, A, A, A, A, None) == status
+        assert lib.moe_backward(ctypes.byref(p), *bwd_args()) == status
+    pp = ctypes.byref(good)
+    assert lib.moe_backward_weights(pp, A, A, None, A, A, None) == E
+    assert lib.moe_backward_weights(pp, A, A, A, MIS, A, None) == U
+    assert lib.moe_backward(pp, *bwd_args(fw=False)) == E
+    assert lib.moe_backward(pp, *bwd_args(out=False)) == E
+    assert lib.moe_backward(pp, *bwd_args(dw_router=None)) == E      # a router needs its gradient
+    assert lib.moe_backward(pp, *bwd_args(w_router=None)) == E       # a gradient needs the router
+    assert lib.moe_backward(pp, *bwd_args(y_perm=None)) == E
+    assert lib.moe_backward(pp, *bwd_args(offsets=MIS)) == U
+    assert lib.moe_backward(pp, *bwd_args(dw_down=None)) == E
+    assert lib.moe_backward(pp, *bwd_args(dlogits=MIS)) == U
+    assert lib.moe_backward(pp, *bwd_args(ws_bytes=need - 1)) == L.MOE_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_backward_workspace_size(lib):
+    # dsel, the queue-order activations and gradients (dy_perm, dx_perm, dh,
+    # h, du|dv) and the transposed operands of the weight gradients, padded to
+    # Kpad = 64-aligned T*k + 63 E columns
+    for T, d, E, k, f in [(8192, 4096, 8, 2, 14336), (16384, 2048, 64, 6, 1408), (64, 256, 8, 2, 512)]:
+        n = T * k
+        kp = -(-(n + 63 * E) // 64) * 64
+        expect = n * 4 + 2 * n * d * 2 + 2 * n * f * 2 + n * 2 * f * 2 + (E + 1) * 4 + \
+            2 * d * kp * 2 + f * kp * 2 + 2 * f * kp * 2
+        st, nb = ws_size(lib, prob(T, d, E, k, f), L.MOE_OP_BACKWARD)
+        assert st == L.MOE_OK
+        assert expect <= nb <= expect + 11 * 256

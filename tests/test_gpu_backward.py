@@ -1,0 +1,163 @@
+"""Parity of the HIP backward against the CPU oracle (``oracle.backward``,
+float64), element by element.
+
+The forward runs on the GPU (its state feeds the backward); the oracle runs
+the whole layer in float64 from the same bf16 inputs.  Routing is held
+identical by supplying logits: either seeded ones, or, with the router on
+the GPU, the GPU's own logits handed to the oracle (the router's gradient
+then still flows through W_r in both).  The HIP path stores every
+intermediate (dy_perm, dh, du|dv, h, dx_perm) in bf16 with fp32
+accumulation, so each gradient must agree with the oracle within
+max|err| / max|ref| <= 1e-2, the bf16 tolerance of the forward tests;
+the weight layouts of the backward are bit-exact transposes.
+Outputs are poisoned before each call so that an unwritten element fails.
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+import oracle as O
+import mixture_experts_layer_exclusive_amd as moe
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TOL = 1e-2
+
+
+def dev(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(DEV)
+    return torch.from_numpy(a).to(DEV)
+
+
+def host(t):
+    if t.dtype == torch.bfloat16:
+        return t.float().cpu().numpy()
+    return t.cpu().numpy()
+
+
+def rel(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape
+    assert np.all(np.isfinite(got)), "non-finite output"
+    return float(np.max(np.abs(got - ref)) / max(np.max(np.abs(ref)), 1e-30))
+
+
+def poisoned_outputs(p, router):
+    nan = float("nan")
+    bf = torch.bfloat16
+    out = dict(dx=torch.full((p.T, p.d), nan, dtype=bf, device=DEV),
+               dw_gate=torch.full((p.E, p.f, p.d), nan, dtype=bf, device=DEV),
+               dw_up=torch.full((p.E, p.f, p.d), nan, dtype=bf, device=DEV),
+               dw_down=torch.full((p.E, p.d, p.f), nan, dtype=bf, device=DEV),
+               dlogits=torch.full((p.T, p.E), nan, dtype=torch.float32, device=DEV))
+    if router:
+        out["dw_router"] = torch.full((p.E, p.d), nan, dtype=bf, device=DEV)
+    return out
+
+
+def run_layer(L, dy, logits=None):
+    """GPU forward (router unless logits are given), then the backward."""
+    p = L["problem"]
+    x = dev(L["x"])
+    wg, wu, wd = dev(L["w_gate"]), dev(L["w_up"]), dev(L["w_down"])
+    wr = dev(L["w_router"]) if logits is None else None
+    _, st = moe.forward(x, wg, wu, wd, p.k, w_router=wr, logits=None if logits is None else dev(logits),
+                        intermediates=True)
+    wt = moe.backward_weights(wg, wu, wd)
+    g = moe.backward(x, wg, wu, p.k, st, dev(dy), wt, w_router=wr, with_dlogits=True,
+                     out=poisoned_outputs(p, wr is not None))
+    torch.cuda.synchronize()
+    return st, g
+
+
+def oracle_grads(L, dy, logits, router):
+    f = lambda n: mi.as_f32(L[n], "bf16")  # noqa: E731
+    return O.backward(f("x"), L["problem"].k, f("w_gate"), f("w_up"), f("w_down"), mi.as_f32(dy, "bf16"),
+                      w_router=f("w_router") if router else None, logits=logits)
+
+
+def check(g, ref, router):
+    for key in ("dx", "dw_gate", "dw_up", "dw_down", "dlogits") + (("dw_router",) if router else ()):
+        r = rel(host(g[key]), ref[key])
+        assert r <= TOL, (key, r)
+
+
+BWD_CASES = [
+    # T, d, E, k, f, logits
+    (600, 256, 8, 2, 512, "gauss"),
+    (1000, 192, 16, 4, 320, "zipf"),     # skewed: empty and tiny experts; column tails
+    (333, 128, 64, 6, 192, "gauss"),     # many experts with a few rows each
+    (64, 128, 128, 8, 64, "gauss"),
+    (1, 64, 8, 2, 64, "gauss"),          # one token
+    (70, 64, 1, 1, 128, "gauss"),        # one expert: the gate is 1, no logit gradient
+    (700, 320, 8, 2, 1088, "gauss"),     # K of the weight GEMMs spans several slices and a padded tail
+]
+
+
+@pytest.mark.parametrize("T,d,E,k,f,kind", BWD_CASES)
+def test_backward_supplied_logits(T, d, E, k, f, kind):
+    print(f"backward logits T={T} d={d} E={E} k={k} f={f} {kind}", flush=True)
+    p = mi.Problem(T, d, E, k, f, "bf16")
+    L = mi.make_layer(p, seed=T + f)
+    l = mi.make_gaussian_logits(p, seed=d) if kind == "gauss" else mi.make_zipf_logits(p, seed=d)
+    dy = mi.make_grad_output(p, seed=T)
+    _, g = run_layer(L, dy, logits=l)
+    ref = oracle_grads(L, dy, l, router=False)
+    check(g, ref, router=False)
+    if E == 1:
+        assert np.all(host(g["dlogits"]) == 0.0)
+
+
+@pytest.mark.parametrize("T,d,E,k,f", [(512, 256, 8, 2, 256), (300, 128, 32, 4, 192)])
+def test_backward_with_router(T, d, E, k, f):
+    print(f"backward router T={T} d={d} E={E} k={k} f={f}", flush=True)
+    p = mi.Problem(T, d, E, k, f, "bf16")
+    L = mi.make_layer(p, seed=E + f)
+    dy = mi.make_grad_output(p, seed=E)
+    st, g = run_layer(L, dy)
+    # the oracle routes on the GPU's logits (routing on equal fp32 logits is
+    # bit-exact), and the router gradient flows through W_r on both sides
+    ref = oracle_grads(L, dy, host(st["logits"]), router=True)
+    assert np.array_equal(host(st["topk_ids"]), ref["forward"]["ids"])
+    check(g, ref, router=True)
+
+
+def test_backward_weight_layouts_are_exact_transposes():
+    p = mi.Problem(1, 192, 3, 1, 320, "bf16")
+    L = mi.make_layer(p, seed=11)
+    wdt, wgut = moe.backward_weights(dev(L["w_gate"]), dev(L["w_up"]), dev(L["w_down"]))
+    torch.cuda.synchronize()
+    wg, wu, wd = (mi.as_f32(L[n], "bf16") for n in ("w_gate", "w_up", "w_down"))
+    assert np.array_equal(host(wdt), np.transpose(wd, (0, 2, 1)))
+    assert np.array_equal(host(wgut), np.concatenate([np.transpose(wg, (0, 2, 1)),
+                                                      np.transpose(wu, (0, 2, 1))], axis=2))
+
+
+def test_backward_twice_is_bitwise_identical():
+    p = mi.Problem(2000, 256, 16, 4, 256, "bf16")
+    L = mi.make_layer(p, seed=3)
+    dy = mi.make_grad_output(p, seed=3)
+    _, g1 = run_layer(L, dy)
+    _, g2 = run_layer(L, dy)
+    for key in g1:
+        assert torch.equal(g1[key], g2[key]), key
+
+
+def test_backward_zero_tokens_gives_zero_weight_gradients():
+    p = mi.Problem(1, 128, 8, 2, 64, "bf16")
+    L = mi.make_layer(p, seed=1)
+    x = dev(L["x"])[:0]
+    wg, wu, wd, wr = (dev(L[n]) for n in ("w_gate", "w_up", "w_down", "w_router"))
+    wt = moe.backward_weights(wg, wu, wd)
+    # no forward state exists for zero tokens: none is read
+    st = {key: None for key in ("topk_ids", "topk_gates", "offsets", "sorted_assign", "assign_pos", "y_perm")}
+    out = poisoned_outputs(mi.Problem(0, 128, 8, 2, 64, "bf16"), True)
+    g = moe.backward(x, wg, wu, 2, st, x, wt, w_router=wr, out=out)
+    torch.cuda.synchronize()
+    for key in ("dw_gate", "dw_up", "dw_down", "dw_router"):
+        assert torch.count_nonzero(g[key]) == 0, key
+    assert g["dx"].shape == (0, 128)
