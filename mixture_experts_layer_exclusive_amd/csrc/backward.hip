@@ -12,7 +12,10 @@
 //      first transposed here into per-expert column segments padded to a
 //      multiple of 64 with zeros;
 //   3. per token: dx[t] = sum_j dx_perm[pos(t, j)] + sum_j dl_j W_r[id_j];
-//   4. router weight gradient dW_r[e] = sum over expert e's queue of dl x.
+//   4. router weight gradient dW_r[e] = sum over expert e's queue of dl x:
+//      partial sums over each 64-column block of the padded queue (one
+//      expert per block) come out of the transpose of x, and a second
+//      kernel adds an expert's blocks in order.
 // All reductions run in a fixed order (deterministic); accumulation is fp32,
 // storage bf16.
 #include "device_util.h"
@@ -125,6 +128,9 @@ __global__ __launch_bounds__(64) void bwd_poff_kernel(const int32_t* __restrict_
 // pos = offsets[e] + q - poff[e] when pos < offsets[e+1], else zero.  The
 // source row is src[pos] (row stride ld_src), or, with GATHER, row
 // sorted_assign[pos] / k of src.  Tiles of 64 columns x 64 rows through LDS.
+// With GATHER and wr_part, block b = q / 64 also yields the router-gradient
+// partial sums wr_part[b, c] = sum over its columns q of dsel[a_q] src[c]
+// (a_q = sorted_assign[pos]; zero for padding), in a fixed order.
 template <bool GATHER>
 __global__ __launch_bounds__(256) void bwd_transpose_kernel(const bf16_t* __restrict__ src,
                                                            int64_t ld_src, int C,
@@ -132,9 +138,12 @@ __global__ __launch_bounds__(256) void bwd_transpose_kernel(const bf16_t* __rest
                                                            const int32_t* __restrict__ poff, int E,
                                                            const int32_t* __restrict__ sorted_assign,
                                                            int k, int64_t kpad,
-                                                           bf16_t* __restrict__ dst) {
+                                                           bf16_t* __restrict__ dst,
+                                                           const float* __restrict__ dsel,
+                                                           float* __restrict__ wr_part) {
     __shared__ bf16_t tile[64][64 + 2];
     __shared__ int64_t s_row[64];
+    __shared__ float s_dsel[64];
     const int q0 = blockIdx.x * 64;
     const int c0 = blockIdx.y * 64;
     if (q0 >= poff[E]) return;
@@ -147,8 +156,14 @@ __global__ __launch_bounds__(256) void bwd_transpose_kernel(const bf16_t* __rest
         }
         const int pos = offsets[lo] + (q - poff[lo]);
         int64_t row = -1;
-        if (q < poff[E] && pos < offsets[lo + 1]) row = GATHER ? sorted_assign[pos] / k : pos;
+        float ds = 0.f;
+        if (q < poff[E] && pos < offsets[lo + 1]) {
+            const int a = GATHER ? sorted_assign[pos] : pos;
+            row = GATHER ? a / k : pos;
+            if (GATHER && wr_part != nullptr) ds = dsel[a];
+        }
         s_row[threadIdx.x] = row;
+        s_dsel[threadIdx.x] = ds;
     }
     __syncthreads();
     // load: thread -> (row i = tid / 4, 16 columns (tid % 4) * 16 ..)
@@ -174,17 +189,30 @@ __global__ __launch_bounds__(256) void bwd_transpose_kernel(const bf16_t* __rest
     {
         const int c = threadIdx.x >> 2;
         const int qq = (threadIdx.x & 3) * 16;
+        float part = 0.f;
         if (c0 + c < C) {
 #pragma unroll
             for (int u = 0; u < 16; u += 8) {
                 uint32_t w[4];
 #pragma unroll
-                for (int h = 0; h < 4; ++h)
-                    w[h] = static_cast<uint32_t>(tile[qq + u + 2 * h][c]) |
-                           (static_cast<uint32_t>(tile[qq + u + 2 * h + 1][c]) << 16);
+                for (int h = 0; h < 4; ++h) {
+                    const uint16_t lo = tile[qq + u + 2 * h][c];
+                    const uint16_t hi = tile[qq + u + 2 * h + 1][c];
+                    w[h] = static_cast<uint32_t>(lo) | (static_cast<uint32_t>(hi) << 16);
+                    if (GATHER) {
+                        part = fmaf(s_dsel[qq + u + 2 * h], bf16_to_f32(lo), part);
+                        part = fmaf(s_dsel[qq + u + 2 * h + 1], bf16_to_f32(hi), part);
+                    }
+                }
                 *reinterpret_cast<uint4*>(dst + static_cast<int64_t>(c0 + c) * kpad + q0 + qq + u) =
                     make_uint4(w[0], w[1], w[2], w[3]);
             }
+        }
+        if (GATHER && wr_part != nullptr) {
+            // the 4 threads of column c are adjacent lanes: (s0 + s1) + (s2 + s3)
+            part += __shfl_xor(part, 1, 64);
+            part += __shfl_xor(part, 2, 64);
+            if ((threadIdx.x & 3) == 0 && c0 + c < C) wr_part[static_cast<int64_t>(q0 / 64) * C + c0 + c] = part;
         }
     }
 }
@@ -232,22 +260,18 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(const uint4* __restrict__ d
     }
 }
 
-// Step 4: dW_r[e, c] = sum over expert e's queue (ascending) of
-// dl[a] * x[a / k, c]; grid (E, d / 256), one column per thread.
-__global__ __launch_bounds__(256) void bwd_dwr_kernel(const bf16_t* __restrict__ x,
-                                                     const int32_t* __restrict__ offsets,
-                                                     const int32_t* __restrict__ sorted_assign,
-                                                     const float* __restrict__ dsel, int k, int d,
+// Step 4: dW_r[e, c] = sum of the partial sums of expert e's 64-column
+// blocks [poff[e] / 64, poff[e+1] / 64), ascending; grid (E, d / 256), one
+// column per thread.
+__global__ __launch_bounds__(256) void bwd_dwr_kernel(const float* __restrict__ wr_part,
+                                                     const int32_t* __restrict__ poff, int d,
                                                      bf16_t* __restrict__ dw_router) {
     const int e = blockIdx.x;
     const int c = blockIdx.y * 256 + threadIdx.x;
     if (c >= d) return;
     float acc = 0.f;
-    const int p1 = offsets[e + 1];
-    for (int pos = offsets[e]; pos < p1; ++pos) {
-        const int a = sorted_assign[pos];
-        acc = fmaf(dsel[a], bf16_to_f32(x[static_cast<int64_t>(a / k) * d + c]), acc);
-    }
+    const int b1 = poff[e + 1] / 64;
+    for (int b = poff[e] / 64; b < b1; ++b) acc += wr_part[static_cast<int64_t>(b) * d + c];
     dw_router[static_cast<int64_t>(e) * d + c] = __builtin_bit_cast(bf16_t, static_cast<__bf16>(acc));
 }
 
@@ -333,16 +357,16 @@ hipError_t launch_backward_poff(const moe_problem_t& p, const int32_t* offsets, 
 hipError_t launch_backward_transpose(const moe_problem_t& p, const void* src, int64_t ld_src, int C,
                                      bool gather, const int32_t* offsets, const int32_t* poff,
                                      const int32_t* sorted_assign, int64_t kpad, void* dst,
-                                     hipStream_t s) {
+                                     const float* dsel, float* wr_part, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(kpad / 64), static_cast<unsigned>(ceil_div(C, 64)));
     if (gather)
         bwd_transpose_kernel<true><<<grid, 256, 0, s>>>(static_cast<const bf16_t*>(src), ld_src, C, offsets,
                                                         poff, p.E, sorted_assign, p.k, kpad,
-                                                        static_cast<bf16_t*>(dst));
+                                                        static_cast<bf16_t*>(dst), dsel, wr_part);
     else
         bwd_transpose_kernel<false><<<grid, 256, 0, s>>>(static_cast<const bf16_t*>(src), ld_src, C, offsets,
                                                          poff, p.E, sorted_assign, p.k, kpad,
-                                                         static_cast<bf16_t*>(dst));
+                                                         static_cast<bf16_t*>(dst), nullptr, nullptr);
     return hipGetLastError();
 }
 
@@ -355,12 +379,10 @@ hipError_t launch_backward_dx(const moe_problem_t& p, const void* dx_perm, const
     return hipGetLastError();
 }
 
-hipError_t launch_backward_dwr(const moe_problem_t& p, const void* x, const int32_t* offsets,
-                               const int32_t* sorted_assign, const float* dsel, void* dw_router,
-                               hipStream_t s) {
-    bwd_dwr_kernel<<<dim3(p.E, ceil_div(p.d, 256)), 256, 0, s>>>(
-        static_cast<const bf16_t*>(x), offsets, sorted_assign, dsel, p.k, p.d,
-        static_cast<bf16_t*>(dw_router));
+hipError_t launch_backward_dwr(const moe_problem_t& p, const float* wr_part, const int32_t* poff,
+                               void* dw_router, hipStream_t s) {
+    bwd_dwr_kernel<<<dim3(p.E, ceil_div(p.d, 256)), 256, 0, s>>>(wr_part, poff, p.d,
+                                                                static_cast<bf16_t*>(dw_router));
     return hipGetLastError();
 }
 

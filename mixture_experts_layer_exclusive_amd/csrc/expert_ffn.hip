@@ -981,13 +981,19 @@ hipError_t launch_backward_recompute(const moe_problem_t& p, const void* x, cons
 }
 
 // dx_perm = [du dv] [W_gate; W_up] over the queues (W_gu_t = [E, d, 2f]).
+// The tail of the tile order splits K as in the forward's down projection
+// (part: kSplitWGs partial tiles, or null when bwd_can_split is false).
 hipError_t launch_backward_dxperm(const moe_problem_t& p, const void* duv, const int32_t* offsets,
-                                  const void* w_gu_t, void* dx_perm, hipStream_t s) {
+                                  const void* w_gu_t, void* dx_perm, float* part, hipStream_t s) {
     const int64_t n = p.T * p.k;
     const unsigned g = grid_for(n, p.E, kBM, static_cast<int>(ceil_div(p.d, kDownCols)));
-    grouped_gemm_bf16_kernel<kDown, false, false><<<g, 256, 0, s>>>(
+    const int slots = (part != nullptr && bwd_can_split(p)) ? resident_slots() : 0;
+    grouped_gemm_bf16_kernel<kDown, false, false><<<g + (slots > 0 ? kSplitWGs : 0), 256, 0, s>>>(
         static_cast<const bf16_t*>(duv), nullptr, p.k, offsets, p.E, static_cast<const bf16_t*>(w_gu_t),
-        nullptr, static_cast<bf16_t*>(dx_perm), p.d, 2 * p.f, 0, nullptr, nullptr, nullptr, 0);
+        nullptr, static_cast<bf16_t*>(dx_perm), p.d, 2 * p.f, slots, part, nullptr, nullptr, 0);
+    if (slots > 0)
+        split_reduce_kernel<<<kSplitWGs * 16, 256, 0, s>>>(part, offsets, p.E, p.d, (2 * p.f) / 64, slots,
+                                                          static_cast<bf16_t*>(dx_perm));
     return hipGetLastError();
 }
 

@@ -75,10 +75,11 @@ size_t dispatch_ws(const moe_problem_t& p) {
 
 size_t ffn_ws(const moe_problem_t& p) { return ffn_h_bytes(p) + ffn_split_bytes(p); }
 
-// Backward workspace, in carving order: dsel [T*k] fp32, dy_perm [T*k, d],
-// dh [T*k, f], duv [T*k, 2f], h [T*k, f], dx_perm [T*k, d], poff [E+1],
-// and the transposed operands of the weight gradients dy_perm^T [d, kpad],
-// h^T [f, kpad], duv^T [2f, kpad], x_perm^T [d, kpad].
+// Backward workspace: dsel [T*k] fp32, dy_perm and dx_perm [T*k, d], dh and
+// h [T*k, f], duv [T*k, 2f], poff [E+1], the transposed operands of the
+// weight gradients dy_perm^T and x_perm^T [d, kpad], h^T [f, kpad],
+// duv^T [2f, kpad], the router-gradient partial sums [kpad / 64, d] fp32
+// and the split-K partial tiles of the dx_perm GEMM.
 size_t backward_ws(const moe_problem_t& p) {
     const size_t n = static_cast<size_t>(p.T) * p.k;
     const size_t kp = static_cast<size_t>(backward_kpad(p));
@@ -90,6 +91,8 @@ size_t backward_ws(const moe_problem_t& p) {
     b += align_up(static_cast<size_t>(p.d) * kp * 2, kAlign) * 2;  // dy^T, x^T
     b += align_up(static_cast<size_t>(p.f) * kp * 2, kAlign);      // h^T
     b += align_up(static_cast<size_t>(2 * p.f) * kp * 2, kAlign);  // duv^T
+    b += align_up(static_cast<size_t>(kp / 64) * p.d * 4, kAlign);
+    b += align_up(bwd_split_bytes(p), kAlign);
     return b;
 }
 
@@ -370,6 +373,8 @@ moe_status_t moe_backward(const moe_problem_t* p, const void* x, const void* w_r
     void* xT = c.take<char>(static_cast<size_t>(p->d) * kp * 2);
     void* hT = c.take<char>(static_cast<size_t>(p->f) * kp * 2);
     void* duvT = c.take<char>(static_cast<size_t>(2 * p->f) * kp * 2);
+    float* wr_part = c.take<float>(static_cast<size_t>(kp / 64) * p->d * 4);
+    float* split = bwd_split_bytes(*p) > 0 ? c.take<float>(bwd_split_bytes(*p)) : nullptr;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     clear_hip_error();
@@ -381,16 +386,18 @@ moe_status_t moe_backward(const moe_problem_t* p, const void* x, const void* w_r
         MOE_LAUNCH(launch_backward_dh(*p, dy_perm, fw->offsets, w_down_t, dh, s));
         MOE_LAUNCH(launch_backward_recompute(*p, x, fw->sorted_assign, fw->offsets, w_gate, w_up, dh, duv,
                                              h, s));
-        MOE_LAUNCH(launch_backward_dxperm(*p, duv, fw->offsets, w_gu_t, dx_perm, s));
+        MOE_LAUNCH(launch_backward_dxperm(*p, duv, fw->offsets, w_gu_t, dx_perm, split, s));
         MOE_LAUNCH(launch_backward_dx(*p, dx_perm, fw->assign_pos, fw->topk_ids, dsel, w_router, out->dx,
                                       s));
         MOE_LAUNCH(launch_backward_transpose(*p, dy_perm, p->d, p->d, false, fw->offsets, poff, nullptr, kp,
-                                             dyT, s));
-        MOE_LAUNCH(launch_backward_transpose(*p, h, p->f, p->f, false, fw->offsets, poff, nullptr, kp, hT, s));
+                                             dyT, nullptr, nullptr, s));
+        MOE_LAUNCH(launch_backward_transpose(*p, h, p->f, p->f, false, fw->offsets, poff, nullptr, kp, hT,
+                                             nullptr, nullptr, s));
         MOE_LAUNCH(launch_backward_transpose(*p, duv, 2 * p->f, 2 * p->f, false, fw->offsets, poff, nullptr,
-                                             kp, duvT, s));
+                                             kp, duvT, nullptr, nullptr, s));
+        // (with a router, the transpose of x also yields the router gradient's partial sums)
         MOE_LAUNCH(launch_backward_transpose(*p, x, p->d, p->d, true, fw->offsets, poff, fw->sorted_assign, kp,
-                                             xT, s));
+                                             xT, dsel, w_router != nullptr ? wr_part : nullptr, s));
     }
     // weight gradients (an expert with no rows gets zeros)
     MOE_LAUNCH(launch_backward_wgrad(*p, dyT, p->d, hT, p->f, kp, poff, out->dw_down, s));
@@ -398,8 +405,7 @@ moe_status_t moe_backward(const moe_problem_t* p, const void* x, const void* w_r
     MOE_LAUNCH(launch_backward_wgrad(*p, static_cast<char*>(duvT) + static_cast<size_t>(p->f) * kp * 2, p->f,
                                      xT, p->d, kp, poff, out->dw_up, s));
     if (w_router != nullptr)
-        MOE_LAUNCH(launch_backward_dwr(*p, x, p->T > 0 ? fw->offsets : poff, fw->sorted_assign, dsel,
-                                       out->dw_router, s));
+        MOE_LAUNCH(launch_backward_dwr(*p, wr_part, poff, out->dw_router, s));
     return MOE_OK;
 }
 

@@ -88,6 +88,11 @@ hipError_t launch_combine(const moe_problem_t& p, const void* y_perm, const int3
 
 // Padded per-expert column count of the weight-gradient operands: every
 // expert's queue rounded up to 64 columns.
+// The backward's dx_perm GEMM (K = 2f) splits its tail like the down projection.
+inline bool bwd_can_split(const moe_problem_t& p) { return (2 * p.f) / 64 >= 2 * kSplitMinSlices; }
+inline size_t bwd_split_bytes(const moe_problem_t& p) {
+    return bwd_can_split(p) ? static_cast<size_t>(kSplitWGs) * kBM * kDownCols * 4 : 0;
+}
 inline int64_t backward_kpad(const moe_problem_t& p) {
     return static_cast<int64_t>(align_up(static_cast<size_t>(p.T * p.k + 63 * static_cast<int64_t>(p.E)), 64));
 }
@@ -102,20 +107,19 @@ hipError_t launch_backward_poff(const moe_problem_t& p, const int32_t* offsets, 
 hipError_t launch_backward_transpose(const moe_problem_t& p, const void* src, int64_t ld_src, int C,
                                      bool gather, const int32_t* offsets, const int32_t* poff,
                                      const int32_t* sorted_assign, int64_t kpad, void* dst,
-                                     hipStream_t s);
+                                     const float* dsel, float* wr_part, hipStream_t s);
 hipError_t launch_backward_dx(const moe_problem_t& p, const void* dx_perm, const int32_t* assign_pos,
                               const int32_t* ids, const float* dsel, const void* w_router, void* dx,
                               hipStream_t s);
-hipError_t launch_backward_dwr(const moe_problem_t& p, const void* x, const int32_t* offsets,
-                               const int32_t* sorted_assign, const float* dsel, void* dw_router,
-                               hipStream_t s);
+hipError_t launch_backward_dwr(const moe_problem_t& p, const float* wr_part, const int32_t* poff,
+                               void* dw_router, hipStream_t s);
 hipError_t launch_backward_dh(const moe_problem_t& p, const void* dy_perm, const int32_t* offsets,
                               const void* w_down_t, void* dh, hipStream_t s);
 hipError_t launch_backward_recompute(const moe_problem_t& p, const void* x, const int32_t* sorted_assign,
                                      const int32_t* offsets, const void* w_gate, const void* w_up,
                                      const void* dh, void* duv, void* h, hipStream_t s);
 hipError_t launch_backward_dxperm(const moe_problem_t& p, const void* duv, const int32_t* offsets,
-                                  const void* w_gu_t, void* dx_perm, hipStream_t s);
+                                  const void* w_gu_t, void* dx_perm, float* part, hipStream_t s);
 hipError_t launch_backward_wgrad(const moe_problem_t& p, const void* A, int M, const void* B, int N,
                                  int64_t ldk, const int32_t* poff, void* C, hipStream_t s);
 
