@@ -10,7 +10,10 @@ and random weights; inputs are resident in HBM before timing starts.
 Besides the step time it measures, with HIP events on the stream the kernels
 run on, the expert-FFN call (the dominant work: 6*k*d*f FLOPs per token),
 the dispatch call with the row gather materialised, and the combine, and it
-times the CPU oracle on a bounded slice of the same workload.
+times the CPU oracle on a bounded slice of the same workload.  For bf16
+workloads it also times the layer's backward (``moe_backward``: 16*k*d*f
+GEMM FLOPs per token) for a seeded output gradient; the transposed weight
+layouts it reads are made once beforehand, as after an optimizer step.
 """
 from __future__ import annotations
 
@@ -42,6 +45,7 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=8192,
                     help="tokens of the workload the CPU oracle runs for the baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter calibration)")
     return ap.parse_args()
@@ -171,6 +175,23 @@ def main():
 
     counts = inter["counts"].cpu().numpy()
 
+    # ---- backward of the layer (bf16 only) ----
+    bwd = None
+    if p.dtype == "bf16" and not args.no_backward:
+        dyg = up(mi.make_grad_output(p, seed=0))
+        wt = moe.backward_weights(wg, wu, wd)
+        bws = torch.empty(moe.workspace_size(prob, 4), dtype=torch.uint8, device=dev)
+        gout = moe.backward(x, wg, wu, p.k, inter, dyg, wt, w_router=wr, ws=bws)
+        gout = {key: v for key, v in gout.items() if v is not None}
+        ms_bwd = timed(lambda: moe.backward(x, wg, wu, p.k, inter, dyg, wt, w_router=wr, ws=bws, out=gout), reps)
+        bwd_flops = 16.0 * p.T * p.k * p.d * p.f
+        bwd = {"ms_per_call": round(ms_bwd, 4), "gemm_flops_per_call": bwd_flops,
+               "gemm_tflops": round(bwd_flops / (ms_bwd * 1e-3) / 1e12, 2),
+               "frac_mfma_peak": round(bwd_flops / (ms_bwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+               "tokens_per_s": round(p.T / (ms_bwd * 1e-3), 1)}
+        print(f"# backward: {ms_bwd:.3f} ms/call", file=sys.stderr, flush=True)
+        del dyg, wt, bws, gout
+
     if args.copy_calibration:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
@@ -232,6 +253,7 @@ def main():
                      "expert_ffn": round(ms_ffn, 4), "combine": round(ms_comb, 4)},
         "expert_counts": {"min": int(counts.min()), "max": int(counts.max()),
                           "empty": int((counts == 0).sum())},
+        "backward": bwd,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -87,10 +87,10 @@ def topk_gates_backward(logits: np.ndarray, ids: np.ndarray, gates: np.ndarray,
 
 
 def swiglu_expert_backward(x_rows: np.ndarray, w_gate_e: np.ndarray, w_up_e: np.ndarray,
-                           w_down_e: np.ndarray, dy_rows: np.ndarray) -> dict:
+                           w_down_e: np.ndarray, dy_rows: np.ndarray, weights: bool = True) -> dict:
     """Backward of one expert ``y = W_down (silu(W_gate x) * (W_up x))`` on
-    rows: returns dx [n, d], dw_gate [f, d], dw_up [f, d], dw_down [d, f],
-    all float64."""
+    rows: returns dx [n, d] and (with ``weights``) dw_gate [f, d], dw_up
+    [f, d], dw_down [d, f], all float64."""
     xr = _f64(x_rows)
     wg, wu, wd = _f64(w_gate_e), _f64(w_up_e), _f64(w_down_e)
     dyr = _f64(dy_rows)
@@ -101,6 +101,8 @@ def swiglu_expert_backward(x_rows: np.ndarray, w_gate_e: np.ndarray, w_up_e: np.
     dh = dyr @ wd
     du = dh * v * silu_grad(u)
     dv = dh * s
+    if not weights:
+        return dict(dx=du @ wg + dv @ wu)
     return dict(dx=du @ wg + dv @ wu, dw_gate=du.T @ xr, dw_up=dv.T @ xr, dw_down=dyr.T @ h)
 
 
@@ -145,3 +147,69 @@ def backward(x: np.ndarray, k: int, w_gate: np.ndarray, w_up: np.ndarray, w_down
         dx += dlogits @ _f64(w_router)
     return dict(dx=dx, dw_gate=dwg, dw_up=dwu, dw_down=dwd, dlogits=dlogits, dgates=dgates,
                 dw_router=dw_router, dy_perm=dy_perm, dx_perm=dx_perm, forward=fw)
+
+
+def backward_tokens(tokens: np.ndarray, x: np.ndarray, logits: np.ndarray, k: int, w_gate, w_up,
+                    w_down, dy: np.ndarray, w_router: np.ndarray | None = None) -> dict:
+    """Per-token definition of the input and logit gradients on a subset of
+    tokens (no queues): for token t with ids e_j and gates g_j from
+    ``topk_route`` on its logits row,
+    ``dg_j = <dy_t, FFN_{e_j}(x_t)>``, ``dl = topk_gates_backward(dg)``,
+    ``dx_t = sum_j J_{e_j}(x_t)^T (g_j dy_t) + sum_j dl_{e_j} W_r[e_j]``
+    (the router term only with ``w_router``), where ``J_e^T`` is the
+    expert's input gradient.  Expert weights may be callables ``w(e)`` as in
+    ``forward_tokens`` (each expert used is widened once).  Returns dx
+    [n, d] and dlogits [n, E], float64."""
+    from .moe_oracle import swiglu_expert, topk_route
+    tokens = np.asarray(tokens, dtype=np.int64)
+    l = np.asarray(logits, dtype=np.float32)[tokens]
+    ids, gates = topk_route(l, k)
+    xs = _f64(np.asarray(x)[tokens])
+    dys = _f64(np.asarray(dy)[tokens])
+
+    def get(w, e):
+        return w(e) if callable(w) else w[e]
+
+    n, d = xs.shape
+    dx = np.zeros((n, d), dtype=np.float64)
+    dg = np.zeros((n, k), dtype=np.float64)
+    for e in np.unique(ids):
+        rows, slots = np.nonzero(ids == e)
+        wg, wu, wd = get(w_gate, e), get(w_up, e), get(w_down, e)
+        dg[rows, slots] = np.sum(dys[rows] * swiglu_expert(xs[rows], wg, wu, wd), axis=1)
+        g = _f64(gates[rows, slots])[:, None]
+        r = swiglu_expert_backward(xs[rows], wg, wu, wd, g * dys[rows], weights=False)
+        np.add.at(dx, rows, r["dx"])
+    dl = topk_gates_backward(l, ids, gates, dg)
+    if w_router is not None:
+        dx += dl @ _f64(w_router)
+    return dict(dx=dx, dlogits=dl, ids=ids, gates=gates)
+
+
+def weight_grad_entries(x: np.ndarray, ids: np.ndarray, gates: np.ndarray, e: int, w_gate_e,
+                        w_up_e, w_down_e, dy: np.ndarray, rows: np.ndarray, cols: np.ndarray) -> dict:
+    """Sampled entries of expert e's weight gradients, each a sum over the
+    (token, slot) pairs routed to e (order irrelevant in float64):
+    ``dW_down[e][rows][:, cols] = sum g dy_t[rows] h(x_t)[cols]``, and the
+    full rows ``dW_gate[e][cols, :] = sum du(x_t)[cols] x_t``,
+    ``dW_up[e][cols, :] = sum dv(x_t)[cols] x_t``, with u, v, h, dh, du, dv
+    of the expert's SwiGLU for the output gradient g dy_t.  Only the
+    requested columns of u, v and dh are formed."""
+    ids = np.asarray(ids)
+    t, j = np.nonzero(ids == e)
+    g = _f64(gates)[t, j]
+    xr = _f64(np.asarray(x)[t])
+    dyr = g[:, None] * _f64(np.asarray(dy)[t])
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.asarray(cols, dtype=np.int64)
+    wg = _f64(np.asarray(w_gate_e)[cols])
+    wu = _f64(np.asarray(w_up_e)[cols])
+    wd = _f64(np.asarray(w_down_e)[:, cols])
+    u = xr @ wg.T
+    v = xr @ wu.T
+    s = silu(u)
+    h = s * v
+    dh = dyr @ wd
+    du = dh * v * silu_grad(u)
+    dv = dh * s
+    return dict(dw_down=dyr[:, rows].T @ h, dw_gate=du.T @ xr, dw_up=dv.T @ xr)

@@ -162,3 +162,25 @@ def test_dispatch_grad_rows():
         for j in range(k):
             pos = q["assign_pos"][t * k + j]
             assert np.array_equal(dyp[pos], np.float64(gates[t, j]) * dy[t])
+
+
+def test_sampled_backward_functions_match_the_whole_backward():
+    # the per-token and per-entry statements agree with the queue-based
+    # backward (itself pinned by autograd and finite differences above)
+    p = mi.Problem(40, 16, 5, 2, 12, "f32")
+    L = mi.make_layer(p, seed=12)
+    dy = np.random.default_rng(13).standard_normal((40, 16))
+    r = B.backward(L["x"], p.k, L["w_gate"], L["w_up"], L["w_down"], dy, w_router=L["w_router"])
+    l = r["forward"]["logits"]
+    tok = np.array([0, 7, 21, 39])
+    s = B.backward_tokens(tok, L["x"], l, p.k, L["w_gate"], L["w_up"], L["w_down"], dy, w_router=L["w_router"])
+    assert rel(s["dx"], r["dx"][tok]) < 1e-12
+    assert rel(s["dlogits"], r["dlogits"][tok]) < 1e-12
+    ids, gates = r["forward"]["ids"], r["forward"]["gates"]
+    rows, cols = np.array([1, 5, 15]), np.array([0, 3, 11])
+    for e in range(p.E):
+        w = B.weight_grad_entries(L["x"], ids, gates, e, L["w_gate"][e], L["w_up"][e], L["w_down"][e], dy,
+                                  rows, cols)
+        assert np.allclose(w["dw_down"], r["dw_down"][e][np.ix_(rows, cols)], rtol=1e-12, atol=1e-14)
+        assert np.allclose(w["dw_gate"], r["dw_gate"][e][cols], rtol=1e-12, atol=1e-14)
+        assert np.allclose(w["dw_up"], r["dw_up"][e][cols], rtol=1e-12, atol=1e-14)
