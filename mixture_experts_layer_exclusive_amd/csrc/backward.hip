@@ -95,9 +95,11 @@ __global__ __launch_bounds__(256) void bwd_dy_kernel(const uint4* __restrict__ d
 
 // Padded offsets: expert e's queue columns start at poff[e], each expert's
 // count rounded up to a multiple of 64 (all zero when offsets is null: no
-// tokens).  One wave, E <= 256.
+// tokens).  Also the experts in descending order of padded count, ties by
+// lower id: order[rank] = e.  One wave, E <= 256.
 __global__ __launch_bounds__(64) void bwd_poff_kernel(const int32_t* __restrict__ offsets, int E,
-                                                     int32_t* __restrict__ poff) {
+                                                     int32_t* __restrict__ poff, int32_t* __restrict__ order) {
+    __shared__ int s_c[MOE_MAX_EXPERTS];
     const int lane = threadIdx.x;
     int c[4], local = 0;
 #pragma unroll
@@ -120,6 +122,17 @@ __global__ __launch_bounds__(64) void bwd_poff_kernel(const int32_t* __restrict_
         run += c[i];
     }
     if (lane == 63) poff[E] = incl;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_c[lane * 4 + i] = c[i];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = lane * 4 + i;
+        if (e >= E) continue;
+        int rank = 0;
+        for (int o = 0; o < E; ++o) rank += (s_c[o] > c[i] || (s_c[o] == c[i] && o < e)) ? 1 : 0;
+        order[rank] = e;
+    }
 }
 
 // Transpose of queue rows into padded per-expert column segments:
@@ -349,8 +362,8 @@ hipError_t launch_backward_dy(const moe_problem_t& p, const void* dy, const void
 }
 
 hipError_t launch_backward_poff(const moe_problem_t& p, const int32_t* offsets, int32_t* poff,
-                                hipStream_t s) {
-    bwd_poff_kernel<<<1, 64, 0, s>>>(offsets, p.E, poff);
+                                int32_t* order, hipStream_t s) {
+    bwd_poff_kernel<<<1, 64, 0, s>>>(offsets, p.E, poff, order);
     return hipGetLastError();
 }
 

@@ -300,21 +300,24 @@ __device__ __forceinline__ const T* uniform_ptr(const T* p) {
 constexpr int kUp = 0, kDown = 1, kUpBwd = 2, kWgrad = 3;
 
 // Work of a weight-gradient workgroup: tile (mt, nt) of expert e, K slices of
-// the expert's padded queue columns.  Same XCD remap and grouping as the
-// forward order.
-__device__ __forceinline__ bool find_wgrad_work(const int32_t* __restrict__ poff, int E, int M, int N,
+// the expert's padded queue columns.  A tile's cost is its expert's row
+// count, so the experts are taken heaviest first (order[], a permutation of
+// the experts by descending count) and the tiles are dealt round-robin to
+// the XCDs: a contiguous range per XCD, as in the forward, would give one
+// XCD all the heavy experts of a skewed routing.  Within an expert, groups
+// of GROUP_M row tiles walk the column tiles, so XCD x keeps row tile
+// x mod GROUP_M of each group (its A rows stay in its L2).
+__device__ __forceinline__ bool find_wgrad_work(const int32_t* __restrict__ poff,
+                                                const int32_t* __restrict__ order, int E, int M, int N,
                                                 Work& w) {
     const int mtn = (M + kBM - 1) / kBM;
     const int ntn = (N + kDownCols - 1) / kDownCols;
     const int per_e = mtn * ntn;
     const int total = E * per_e;
-    const int hw = blockIdx.x;
-    const int per_xcd = (total + NUM_XCD - 1) / NUM_XCD;
-    if (hw >= per_xcd * NUM_XCD) return false;
-    const int pid = (hw % NUM_XCD) * per_xcd + hw / NUM_XCD;
+    const int pid = blockIdx.x;
     if (pid >= total) return false;
-    const int e = pid / per_e;
-    const int local = pid - e * per_e;
+    const int e = order[pid / per_e];
+    const int local = pid % per_e;
     const int group = local / (GROUP_M * ntn);
     const int first_m = group * GROUP_M;
     const int gsz = min(GROUP_M, mtn - first_m);
@@ -365,8 +368,9 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 
     Work work;
     if (WG) {
-        // (K is the operands' row stride here; offsets are the padded offsets)
-        if (!find_wgrad_work(offsets, E, M, N, work)) return;
+        // (K is the operands' row stride here; offsets are the padded
+        // offsets and sorted_assign the expert order, heaviest first)
+        if (!find_wgrad_work(offsets, sorted_assign, E, M, N, work)) return;
     } else {
         build_tile_prefix(offsets, E, TM, s_prefix, s_off);
         const int n_tiles = (N + BN_OUT - 1) / BN_OUT;
@@ -998,13 +1002,15 @@ hipError_t launch_backward_dxperm(const moe_problem_t& p, const void* duv, const
 }
 
 // Weight gradient per expert: C[e] [M, N] = A_e B_e^T over the expert's padded
-// queue columns [poff[e], poff[e+1]) of A [M, ldk] and B [N, ldk].
+// queue columns [poff[e], poff[e+1]) of A [M, ldk] and B [N, ldk]; order: the
+// experts by descending row count.
 hipError_t launch_backward_wgrad(const moe_problem_t& p, const void* A, int M, const void* B, int N,
-                                 int64_t ldk, const int32_t* poff, void* C, hipStream_t s) {
+                                 int64_t ldk, const int32_t* poff, const int32_t* order, void* C,
+                                 hipStream_t s) {
     const int64_t tiles = static_cast<int64_t>(p.E) * ceil_div(M, kBM) * ceil_div(N, kDownCols);
-    const unsigned g = static_cast<unsigned>(align_up(static_cast<size_t>(tiles), NUM_XCD));
+    const unsigned g = static_cast<unsigned>(tiles);
     grouped_gemm_bf16_kernel<kWgrad, false, false><<<g, 256, 0, s>>>(
-        static_cast<const bf16_t*>(A), nullptr, p.k, poff, p.E, static_cast<const bf16_t*>(B), nullptr,
+        static_cast<const bf16_t*>(A), order, p.k, poff, p.E, static_cast<const bf16_t*>(B), nullptr,
         static_cast<bf16_t*>(C), N, static_cast<int>(ldk), 0, nullptr, nullptr, nullptr, M);
     return hipGetLastError();
 }

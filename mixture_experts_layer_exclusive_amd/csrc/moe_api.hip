@@ -76,7 +76,7 @@ size_t dispatch_ws(const moe_problem_t& p) {
 size_t ffn_ws(const moe_problem_t& p) { return ffn_h_bytes(p) + ffn_split_bytes(p); }
 
 // Backward workspace: dsel [T*k] fp32, dy_perm and dx_perm [T*k, d], dh and
-// h [T*k, f], duv [T*k, 2f], poff [E+1], the transposed operands of the
+// h [T*k, f], duv [T*k, 2f], poff [E+1], the expert order [E], the transposed operands of the
 // weight gradients dy_perm^T and x_perm^T [d, kpad], h^T [f, kpad],
 // duv^T [2f, kpad], the router-gradient partial sums [kpad / 64, d] fp32
 // and the split-K partial tiles of the dx_perm GEMM.
@@ -88,6 +88,7 @@ size_t backward_ws(const moe_problem_t& p) {
     b += align_up(n * p.f * 2, kAlign) * 2;          // dh, h
     b += align_up(n * 2 * p.f * 2, kAlign);          // duv
     b += align_up(static_cast<size_t>(p.E + 1) * 4, kAlign);
+    b += align_up(static_cast<size_t>(p.E) * 4, kAlign);           // expert order
     b += align_up(static_cast<size_t>(p.d) * kp * 2, kAlign) * 2;  // dy^T, x^T
     b += align_up(static_cast<size_t>(p.f) * kp * 2, kAlign);      // h^T
     b += align_up(static_cast<size_t>(2 * p.f) * kp * 2, kAlign);  // duv^T
@@ -369,6 +370,7 @@ moe_status_t moe_backward(const moe_problem_t* p, const void* x, const void* w_r
     void* h = c.take<char>(n * p->f * 2);
     void* duv = c.take<char>(n * 2 * p->f * 2);
     int32_t* poff = c.take<int32_t>(static_cast<size_t>(p->E + 1) * 4);
+    int32_t* order = c.take<int32_t>(static_cast<size_t>(p->E) * 4);
     void* dyT = c.take<char>(static_cast<size_t>(p->d) * kp * 2);
     void* xT = c.take<char>(static_cast<size_t>(p->d) * kp * 2);
     void* hT = c.take<char>(static_cast<size_t>(p->f) * kp * 2);
@@ -379,7 +381,7 @@ moe_status_t moe_backward(const moe_problem_t* p, const void* x, const void* w_r
     hipStream_t s = static_cast<hipStream_t>(stream);
     clear_hip_error();
     // (with no tokens fw is not read: every queue is empty)
-    MOE_LAUNCH(launch_backward_poff(*p, p->T > 0 ? fw->offsets : nullptr, poff, s));
+    MOE_LAUNCH(launch_backward_poff(*p, p->T > 0 ? fw->offsets : nullptr, poff, order, s));
     if (p->T > 0) {
         MOE_LAUNCH(launch_backward_dy(*p, dy, fw->y_perm, fw->topk_ids, fw->topk_gates, fw->assign_pos,
                                       dy_perm, dsel, out->dlogits, s));
@@ -400,10 +402,10 @@ moe_status_t moe_backward(const moe_problem_t* p, const void* x, const void* w_r
                                              xT, dsel, w_router != nullptr ? wr_part : nullptr, s));
     }
     // weight gradients (an expert with no rows gets zeros)
-    MOE_LAUNCH(launch_backward_wgrad(*p, dyT, p->d, hT, p->f, kp, poff, out->dw_down, s));
-    MOE_LAUNCH(launch_backward_wgrad(*p, duvT, p->f, xT, p->d, kp, poff, out->dw_gate, s));
+    MOE_LAUNCH(launch_backward_wgrad(*p, dyT, p->d, hT, p->f, kp, poff, order, out->dw_down, s));
+    MOE_LAUNCH(launch_backward_wgrad(*p, duvT, p->f, xT, p->d, kp, poff, order, out->dw_gate, s));
     MOE_LAUNCH(launch_backward_wgrad(*p, static_cast<char*>(duvT) + static_cast<size_t>(p->f) * kp * 2, p->f,
-                                     xT, p->d, kp, poff, out->dw_up, s));
+                                     xT, p->d, kp, poff, order, out->dw_up, s));
     if (w_router != nullptr)
         MOE_LAUNCH(launch_backward_dwr(*p, wr_part, poff, out->dw_router, s));
     return MOE_OK;

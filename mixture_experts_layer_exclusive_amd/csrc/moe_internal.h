@@ -103,7 +103,7 @@ hipError_t launch_backward_dy(const moe_problem_t& p, const void* dy, const void
                               const int32_t* ids, const float* gates, const int32_t* assign_pos,
                               void* dy_perm, float* dsel, float* dlogits, hipStream_t s);
 hipError_t launch_backward_poff(const moe_problem_t& p, const int32_t* offsets, int32_t* poff,
-                                hipStream_t s);
+                                int32_t* order, hipStream_t s);
 hipError_t launch_backward_transpose(const moe_problem_t& p, const void* src, int64_t ld_src, int C,
                                      bool gather, const int32_t* offsets, const int32_t* poff,
                                      const int32_t* sorted_assign, int64_t kpad, void* dst,
@@ -121,6 +121,7 @@ hipError_t launch_backward_recompute(const moe_problem_t& p, const void* x, cons
 hipError_t launch_backward_dxperm(const moe_problem_t& p, const void* duv, const int32_t* offsets,
                                   const void* w_gu_t, void* dx_perm, float* part, hipStream_t s);
 hipError_t launch_backward_wgrad(const moe_problem_t& p, const void* A, int M, const void* B, int N,
-                                 int64_t ldk, const int32_t* poff, void* C, hipStream_t s);
+                                 int64_t ldk, const int32_t* poff, const int32_t* order, void* C,
+                                 hipStream_t s);
 
 }  // namespace moe
