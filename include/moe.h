@@ -81,7 +81,8 @@ typedef enum {
     MOE_OP_DISPATCH = 1,
     MOE_OP_EXPERT_FFN = 2,
     MOE_OP_FORWARD = 3,
-    MOE_OP_BACKWARD = 4
+    MOE_OP_BACKWARD = 4,
+    MOE_OP_EXPERT_FFN_FP8 = 5
 } moe_op_t;
 
 /* The problem statement: T tokens, hidden size d, E experts, top-k, SwiGLU
@@ -129,6 +130,19 @@ typedef struct {
     void* dw_router;   /* [E, d] */
     float* dlogits;    /* [T, E] */
 } moe_backward_outputs_t;
+
+/* Expert weights quantised for moe_expert_ffn_fp8 (moe_quantize_weights_fp8
+ * writes them; caller-owned device buffers): OCP FP8 E4M3 codes, one byte
+ * per element, in the layouts of the bf16 weights, and one power-of-two
+ * scale exponent per weight row (value ~= 2^exp[row] * code value). */
+typedef struct {
+    void* w_gate;          /* [E, f, d] codes */
+    int32_t* w_gate_exp;   /* [E, f] */
+    void* w_up;            /* [E, f, d] codes */
+    int32_t* w_up_exp;     /* [E, f] */
+    void* w_down;          /* [E, d, f] codes */
+    int32_t* w_down_exp;   /* [E, d] */
+} moe_fp8_weights_t;
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* moe_status_string(int32_t status);
@@ -254,6 +268,41 @@ moe_status_t moe_backward(const moe_problem_t* p, const void* x, const void* w_r
                           const void* w_gu_t, const moe_forward_state_t* fw, const void* dy,
                           const moe_backward_outputs_t* out, void* ws, size_t ws_bytes,
                           void* stream);
+
+/*
+ * moe_quantize_rows_fp8 -- per-row FP8 quantisation of a bf16 matrix
+ * src [rows, cols] (quantised experts: MoEBlaze summary, Limitations and
+ * future work; the scheme is this library's reading).  Row r gets the
+ * power-of-two scale 2^exps[r], the smallest with max|row| <= 448 * 2^exps[r]
+ * (0 for an all-zero row), and codes[r, c] = E4M3(src[r, c] / 2^exps[r]),
+ * OCP FP8 E4M3, rounded to nearest even.  cols must be a positive multiple
+ * of 16 (MOE_ERR_UNSUPPORTED otherwise); src, codes and exps 16-byte
+ * aligned.  rows = 0 is a no-op.
+ */
+moe_status_t moe_quantize_rows_fp8(const void* src, int64_t rows, int32_t cols, void* codes, int32_t* exps,
+                                   void* stream);
+
+/*
+ * moe_quantize_weights_fp8 -- moe_quantize_rows_fp8 over every weight row
+ * of W_gate, W_up [E, f, d] and W_down [E, d, f] into `out`.  Once per
+ * weight update.  Needs bf16 with d and f multiples of 128.
+ */
+moe_status_t moe_quantize_weights_fp8(const moe_problem_t* p, const void* w_gate, const void* w_up,
+                                      const void* w_down, const moe_fp8_weights_t* out, void* stream);
+
+/*
+ * moe_expert_ffn_fp8 -- moe_expert_ffn with fp8 GEMMs: x [T, d] bf16 is
+ * quantised per token, GEMM1 multiplies its codes (gathered through
+ * sorted_assign) with the codes of W_gate and W_up on FP8 MFMA with fp32
+ * accumulation, applies both scales exactly and the SwiGLU, and rounds h to
+ * bf16; h is quantised per queue row and GEMM2 does the same with W_down,
+ * writing y_perm [T*k, d] bf16.  Weights from moe_quantize_weights_fp8.
+ * bf16 problems with d and f multiples of 128 and T*d < 2^32 only.
+ * Workspace: moe_workspace_size(p, MOE_OP_EXPERT_FFN_FP8).
+ */
+moe_status_t moe_expert_ffn_fp8(const moe_problem_t* p, const void* x, const int32_t* sorted_assign,
+                                const int32_t* offsets, const moe_fp8_weights_t* w, void* y_perm, void* ws,
+                                size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -24,6 +24,7 @@ MOE_OP_DISPATCH = 1
 MOE_OP_EXPERT_FFN = 2
 MOE_OP_FORWARD = 3
 MOE_OP_BACKWARD = 4
+MOE_OP_EXPERT_FFN_FP8 = 5
 
 MOE_MAX_EXPERTS = 256
 MOE_MAX_TOPK = 32
@@ -49,6 +50,11 @@ class MoeForwardState(ctypes.Structure):
                 ("assign_pos", _p), ("y_perm", _p)]
 
 
+class MoeFp8Weights(ctypes.Structure):
+    _fields_ = [("w_gate", _p), ("w_gate_exp", _p), ("w_up", _p), ("w_up_exp", _p), ("w_down", _p),
+                ("w_down_exp", _p)]
+
+
 class MoeBackwardOutputs(ctypes.Structure):
     _fields_ = [("dx", _p), ("dw_gate", _p), ("dw_up", _p), ("dw_down", _p), ("dw_router", _p),
                 ("dlogits", _p)]
@@ -67,6 +73,9 @@ SIGNATURES = {
     "moe_forward": (_i32, [_PP, _p, _p, _p, _p, _p, _p, _p, ctypes.POINTER(MoeForwardOutputs),
                            _p, _sz, _p]),
     "moe_backward_weights": (_i32, [_PP, _p, _p, _p, _p, _p, _p]),
+    "moe_quantize_rows_fp8": (_i32, [_p, ctypes.c_int64, _i32, _p, _p, _p]),
+    "moe_quantize_weights_fp8": (_i32, [_PP, _p, _p, _p, ctypes.POINTER(MoeFp8Weights), _p]),
+    "moe_expert_ffn_fp8": (_i32, [_PP, _p, _p, _p, ctypes.POINTER(MoeFp8Weights), _p, _p, _sz, _p]),
     "moe_backward": (_i32, [_PP, _p, _p, _p, _p, _p, _p, ctypes.POINTER(MoeForwardState), _p,
                             ctypes.POINTER(MoeBackwardOutputs), _p, _sz, _p]),
 }

@@ -234,3 +234,56 @@ def backward(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor, k: int, 
                                   ctypes.byref(fw), _ptr(dy) if T > 0 else None, ctypes.byref(o),
                                   _ptr(ws), nbytes, _stream(dev)), "moe_backward")
     return res
+
+
+def quantize_rows_fp8(src: torch.Tensor, codes: Optional[torch.Tensor] = None,
+                      exps: Optional[torch.Tensor] = None):
+    """Per-row FP8 E4M3 codes (uint8) and power-of-two scale exponents
+    (int32) of a bf16 matrix [rows, cols]."""
+    rows, cols = src.shape
+    dev = src.device
+    if codes is None:
+        codes = torch.empty(rows, cols, dtype=torch.uint8, device=dev)
+    if exps is None:
+        exps = torch.empty(rows, dtype=torch.int32, device=dev)
+    L.check(L.load().moe_quantize_rows_fp8(_ptr(src) if rows else None, rows, cols,
+                                           _ptr(codes) if rows else None, _ptr(exps) if rows else None,
+                                           _stream(dev)), "moe_quantize_rows_fp8")
+    return codes, exps
+
+
+def quantize_weights_fp8(w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor) -> dict:
+    """The expert weights as FP8 codes with per-row scale exponents (for
+    ``expert_ffn_fp8``)."""
+    E, f, d = w_gate.shape
+    dev = w_gate.device
+    p = problem(1, d, E, 1, f, w_gate.dtype)
+    q = dict(w_gate=torch.empty(E, f, d, dtype=torch.uint8, device=dev),
+             w_gate_exp=torch.empty(E, f, dtype=torch.int32, device=dev),
+             w_up=torch.empty(E, f, d, dtype=torch.uint8, device=dev),
+             w_up_exp=torch.empty(E, f, dtype=torch.int32, device=dev),
+             w_down=torch.empty(E, d, f, dtype=torch.uint8, device=dev),
+             w_down_exp=torch.empty(E, d, dtype=torch.int32, device=dev))
+    st = L.MoeFp8Weights(**{key: _ptr(v) for key, v in q.items()})
+    L.check(L.load().moe_quantize_weights_fp8(ctypes.byref(p), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+                                              ctypes.byref(st), _stream(dev)), "moe_quantize_weights_fp8")
+    return q
+
+
+def expert_ffn_fp8(offsets: torch.Tensor, wq: dict, k: int, x: torch.Tensor, sorted_assign: torch.Tensor,
+                   ws: Optional[torch.Tensor] = None, y_perm: Optional[torch.Tensor] = None):
+    """Grouped SwiGLU FFN on FP8 MFMA (weights from ``quantize_weights_fp8``,
+    x bf16 quantised per token inside); returns y_perm [T*k, d] bf16."""
+    T, d = x.shape
+    E, f, _ = wq["w_gate"].shape
+    dev = x.device
+    p = problem(T, d, E, k, f, x.dtype)
+    if y_perm is None:
+        y_perm = torch.empty(T * k, d, dtype=x.dtype, device=dev)
+    st = L.MoeFp8Weights(**{key: _ptr(v) for key, v in wq.items()})
+    ws, nbytes = _workspace(p, L.MOE_OP_EXPERT_FFN_FP8, dev, ws)
+    L.check(L.load().moe_expert_ffn_fp8(ctypes.byref(p), _ptr(x) if T else None,
+                                        _ptr(sorted_assign) if T else None, _ptr(offsets), ctypes.byref(st),
+                                        _ptr(y_perm) if T else None, _ptr(ws), nbytes, _stream(dev)),
+            "moe_expert_ffn_fp8")
+    return y_perm

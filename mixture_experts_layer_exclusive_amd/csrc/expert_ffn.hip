@@ -34,6 +34,8 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
 #ifndef GEMM_GROUP_M
 #define GEMM_GROUP_M 8
@@ -334,33 +336,43 @@ __device__ __forceinline__ bool find_wgrad_work(const int32_t* __restrict__ poff
     return true;
 }
 
-template <int MODE, bool GATHER, bool WIDE>
+// F8: operands are OCP FP8 E4M3 codes (one byte per element) with per-row
+// power-of-two scale exponents: a_exp per activation row (per token of x with
+// GATHER, else per queue row), b_exp0 / b_exp1 per weight row of B0 / B1
+// (indexed e * N + row).  The MFMA is v_mfma_f32_32x32x64_f8f6f4; the scales
+// are applied exactly (ldexp) to the fp32 sums before the epilogue.
+template <int MODE, bool GATHER, bool WIDE, bool F8 = false>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void grouped_gemm_bf16_kernel(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ sorted_assign, int topk,
     const int32_t* __restrict__ offsets, int E, const bf16_t* __restrict__ B0,
     const bf16_t* __restrict__ B1, bf16_t* __restrict__ C, int N, int K, int slots,
-    float* __restrict__ part, const bf16_t* __restrict__ aux, bf16_t* __restrict__ C2, int M) {
+    float* __restrict__ part, const bf16_t* __restrict__ aux, bf16_t* __restrict__ C2, int M,
+    const int32_t* __restrict__ a_exp = nullptr, const int32_t* __restrict__ b_exp0 = nullptr,
+    const int32_t* __restrict__ b_exp1 = nullptr) {
     constexpr bool GATEUP = MODE == kUp || MODE == kUpBwd;
     constexpr bool WG = MODE == kWgrad;
+    static_assert(!F8 || MODE == kUp || MODE == kDown, "fp8 operands: forward GEMMs only");
+    constexpr int EB = F8 ? 1 : 2;           // bytes per operand element
     constexpr int TM = 256;                  // activation rows per tile
     constexpr int TN = 256;                  // weight rows per tile
-    constexpr int BK = 64;                   // K slice width (one 128-byte line per row)
+    constexpr int BK = 128 / EB;             // K slice width (one 128-byte line per row)
     constexpr int BN_OUT = GATEUP ? TN / 2 : TN;
     constexpr int LA = TM / 32;              // activation loads per wave per slice (8 rows each)
     constexpr int LB = TN / 32;              // weight loads per wave per slice
     constexpr int NL = LA + LB;
-    constexpr int ROWB = BK * 2;             // bytes per row of a slice
+    constexpr int ROWB = 128;                // bytes per row of a slice
     constexpr int SA_BYTES = TM * ROWB;
     constexpr int STAGE_BYTES = (TM + TN) * ROWB;
     constexpr int NR = 8;                    // fragment reads per K step (4 activation, 4 weight)
-    constexpr int NM = 16;                   // MFMAs per K step
-    constexpr int KS = BK / 16;              // K steps per slice
+    constexpr int NM = F8 ? 8 : 16;          // MFMAs per K step (fp8: each twice as long)
+    constexpr int KS = 4;                    // K steps per slice (32 bytes of each row per step)
     // GEMM1 issues its activation loads first, GEMM2 its weight loads first
     // (the order that measured faster for each).
     constexpr bool A_FIRST = GATEUP;
     static_assert(2 * STAGE_BYTES <= 160 * 1024, "two stages must fit the 160 KB of LDS");
-    static_assert(KS == 4 && (KS - 1) * NR == NM + NR, "the step schedule below assumes 4 K steps");
-    static_assert(3 * NL <= (KS - 1) * NM, "the refill spreads one load per 3 MFMAs");
+    static_assert(BK * EB == ROWB, "a slice is one 128-byte line per row");
+    static_assert(F8 ? 3 * NL <= 2 * (KS - 1) * NM : 3 * NL <= (KS - 1) * NM,
+                  "the refill spreads one load per 3 MFMAs (fp8: two per 3)");
     __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE_BYTES];
     // The tile prefix and offsets tables live in stage 0 until the first load.
     int* const s_prefix = reinterpret_cast<int*>(smem);
@@ -376,6 +388,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         const int n_tiles = (N + BN_OUT - 1) / BN_OUT;
         // (GEMM1 never splits: its epilogue is not linear in the partial sums)
         if (!find_work(s_off, E, TM, n_tiles, s_prefix, K / BK, GATEUP ? 0 : slots, work)) return;
+        // (K / BK: K slices of 128 bytes, for both element sizes)
     }
     const Tile tile = work.t;
     __syncthreads();  // every lookup is done before the loads overwrite the table
@@ -397,11 +410,13 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // rows of an x of 2^31 elements or more (WIDE), which take 64-bit
     // addresses.
     static_assert(GATHER || !WIDE, "only gathered rows need 64-bit addresses");
-    const bf16_t* a_src[WIDE ? LA : 1];
+    const char* a_src[WIDE ? LA : 1];
     uint32_t a_off[WIDE ? 1 : LA];
-    // (the K range [work.kb, work.kb + work.nkl) of 64-column slices is folded into the bases)
-    const bf16_t* const a_base =
-        uniform_ptr((GATHER ? A : A + static_cast<int64_t>(tile.row0) * K) + work.kb * BK);
+    const char* const Ab = reinterpret_cast<const char*>(A);
+    const int64_t RB = static_cast<int64_t>(K) * EB;  // bytes per operand row
+    // (the K range [work.kb, work.kb + work.nkl) of 128-byte slices is folded into the bases)
+    const char* const a_base =
+        uniform_ptr((GATHER ? Ab : Ab + static_cast<int64_t>(tile.row0) * RB) + work.kb * 128);
     // (gathered rows need a lookup in sorted_assign: called after the first
     // weight loads are on their way)
     auto setup_a = [&]() {
@@ -413,18 +428,20 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             if (pos >= tile.row1) pos = tile.row1 - 1;
             if (WIDE)
                 a_src[WIDE ? j : 0] =
-                    A + static_cast<int64_t>(sorted_assign[pos] / topk) * K + work.kb * BK + chunk * 8;
+                    Ab + static_cast<int64_t>(sorted_assign[pos] / topk) * RB + work.kb * 128 + chunk * 16;
             else if (GATHER)
-                a_off[WIDE ? 0 : j] = (static_cast<uint32_t>(sorted_assign[pos] / topk) * K + chunk * 8) * 2u;
+                a_off[WIDE ? 0 : j] = static_cast<uint32_t>(sorted_assign[pos] / topk) * static_cast<uint32_t>(RB) +
+                                      chunk * 16u;
             else
-                a_off[WIDE ? 0 : j] = (static_cast<uint32_t>(pos - tile.row0) * K + chunk * 8) * 2u;
+                a_off[WIDE ? 0 : j] = static_cast<uint32_t>(pos - tile.row0) * static_cast<uint32_t>(RB) + chunk * 16u;
         }
     };
     // In GEMM1 the first 128 weight rows are gate rows and the rest up rows,
     // so each wave's rows come from one matrix.
     const int rb0 = wave * (TN / 4);
-    const bf16_t* const b_base = uniform_ptr((GATEUP && rb0 >= TN / 2 ? B1 : B0) +
-                                             (WG ? 0 : static_cast<int64_t>(tile.e) * N * K) + work.kb * BK);
+    const char* const b_base =
+        uniform_ptr(reinterpret_cast<const char*>(GATEUP && rb0 >= TN / 2 ? B1 : B0) +
+                    (WG ? 0 : static_cast<int64_t>(tile.e) * N * RB) + work.kb * 128);
     uint32_t b_off[LB];
 #pragma unroll
     for (int j = 0; j < LB; ++j) {
@@ -432,7 +449,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         const int chunk = lslot ^ slot_swizzle(r);
         int n = n0 + (GATEUP && r >= TN / 2 ? r - TN / 2 : r);
         if (n >= N) n = N - 1;
-        b_off[j] = (static_cast<uint32_t>(n) * K + chunk * 8) * 2u;
+        b_off[j] = static_cast<uint32_t>(n) * static_cast<uint32_t>(RB) + chunk * 16u;
     }
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
     const uint32_t lds_a = lds0 + wave * 64 * ROWB;
@@ -440,12 +457,12 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // activation load j (< LA) and weight load j (< LB) of slice kt
     auto dma_a = [&](int j, int kt) {
         const uint32_t so = static_cast<uint32_t>((kt & 1) * STAGE_BYTES);
-        if (WIDE) lds_dma16(a_src[WIDE ? j : 0] + kt * BK, lds_a + so + j * 8 * ROWB);
-        else lds_dma16_s(a_base + kt * BK, a_off[WIDE ? 0 : j], lds_a + so + j * 8 * ROWB);
+        if (WIDE) lds_dma16(a_src[WIDE ? j : 0] + kt * 128, lds_a + so + j * 8 * ROWB);
+        else lds_dma16_s(a_base + kt * 128, a_off[WIDE ? 0 : j], lds_a + so + j * 8 * ROWB);
     };
     auto dma_b = [&](int j, int kt) {
         const uint32_t so = static_cast<uint32_t>((kt & 1) * STAGE_BYTES);
-        lds_dma16_s(b_base + kt * BK, b_off[j], lds_b + so + j * 8 * ROWB);
+        lds_dma16_s(b_base + kt * 128, b_off[j], lds_b + so + j * 8 * ROWB);
     };
     // load q (< NL) of slice kt, in the GEMM's load order
     auto dma = [&](int q, int kt) {
@@ -480,16 +497,36 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const int nk = work.nkl;
     // All fragments of one slice: step kk's activation blocks f[kk][0..3] and
     // weight blocks f[kk][4..7].
-    bf16x8_t f[KS][NR];
+    bf16x8_t f[F8 ? 1 : KS][NR];
+    // fp8: one MFMA takes 64 K values, 32 bytes of a lane's row: the 16-byte
+    // fragments of steps 2s and 2s + 1 read into one register tuple g[s]
+    // (both operands are laid out alike, so every product pairs the same K
+    // index)
+    i32x8_t g[F8 ? 2 : 1][NR];
     auto read_frag = [&](int kk, int i, uint32_t so) {
-        if (i < 4)
-            f[kk][i] = *reinterpret_cast<const bf16x8_t*>(sa_w + so + i * 32 * ROWB + foff[kk]);
-        else
-            f[kk][i] = *reinterpret_cast<const bf16x8_t*>(sb_w + so + b_row0(i - 4) * ROWB + foff[kk]);
+        const char* base = i < 4 ? sa_w + so + i * 32 * ROWB : sb_w + so + b_row0(i - 4) * ROWB;
+        if constexpr (F8) {
+            const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(base + foff[2 * kk]);
+            const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(base + foff[2 * kk + 1]);
+            g[kk][i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        } else {
+            f[kk][i] = *reinterpret_cast<const bf16x8_t*>(base + foff[kk]);
+        }
     };
-#define MOE_MFMA(KK, Q)                                                                         \
+#define MOE_MFMA_BF16(KK, Q)                                                                    \
     acc[(Q) / 4][(Q) % 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                           \
         f[KK][4 + (Q) / 4], f[KK][(Q) % 4], acc[(Q) / 4][(Q) % 4], 0, 0, 0)
+    // fp8: step S of a slice runs blocks (S & 1) * 8 .. + 8 of fp8 K step S >> 1
+#define MOE_MFMA_F8(S, J)                                                                       \
+    acc[(((S) & 1) * 8 + (J)) / 4][(((S) & 1) * 8 + (J)) % 4] =                                   \
+        __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                                        \
+            g[(S) >> 1][4 + (((S) & 1) * 8 + (J)) / 4], g[(S) >> 1][(((S) & 1) * 8 + (J)) % 4],   \
+            acc[(((S) & 1) * 8 + (J)) / 4][(((S) & 1) * 8 + (J)) % 4], 0, 0, 0, 0, 0, 0)
+#define MOE_MFMA(KK, Q)                                                                         \
+    do {                                                                                        \
+        if constexpr (F8) MOE_MFMA_F8(KK, Q);                                                   \
+        else MOE_MFMA_BF16(KK, Q);                                                              \
+    } while (0)
 
     // Per slice kt (stage kt & 1):
     //   step 0: its MFMAs, with the reads of steps 1..3; then every wave has
@@ -501,16 +538,24 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     //   step 3 also reads slice kt + 1's step-0 fragments.
     // Loads complete in issue order, so each wait leaves pending exactly the
     // loads of slice kt + 2 issued before it.
+    // (fp8: MFMAs twice as long, half as many: two loads per 3 MFMAs)
     auto refill = [&](int step, int q, int kt) {  // MFMA q of step 1..3
         const int p = (step - 1) * NM + q;
-        if (p % 3 == 0 && p / 3 < NL) {
-            dma(p / 3, kt + 2);
+        const bool issue = F8 ? (p % 3 != 2 && p - p / 3 < NL) : (p % 3 == 0 && p / 3 < NL);
+        if (issue) {
+            dma(F8 ? p - p / 3 : p / 3, kt + 2);
             // keep each load between its MFMAs (the scheduler would
             // otherwise gather them into a burst)
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    constexpr int BEFORE3 = (2 * NM + 2) / 3 < NL ? (2 * NM + 2) / 3 : NL;  // loads issued in steps 1..2
+    // loads issued in steps 1..2
+    constexpr int BEFORE3_ = F8 ? 2 * NM - (2 * NM) / 3 : (2 * NM + 2) / 3;
+    constexpr int BEFORE3 = BEFORE3_ < NL ? BEFORE3_ : NL;
+    // fragments read ahead of a slice: bf16 step 0; fp8 step 0 (a register
+    // pair per block, used by the slice's first two quarter steps)
+    constexpr int KPRE = 1;
+    constexpr int KREAD = F8 ? 2 : KS;  // fragment steps per slice
     // Prologue: the weight rows of slices 0 and 1 go out first (their
     // addresses need no lookup), then the activation rows (see above).
     // Issue order B0 B1 A0 A1: slice 0 has landed when at most the LA loads
@@ -546,9 +591,10 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         constexpr bool MORE = decltype(more_c)::value;
         const uint32_t so = static_cast<uint32_t>((kt & 1) * STAGE_BYTES);
         const uint32_t nso = static_cast<uint32_t>(((kt + 1) & 1) * STAGE_BYTES);
-        // step 0: 24 reads over 16 MFMAs
+        // step 0: the reads of the remaining steps (bf16: 24 over 16 MFMAs;
+        // fp8: 16 over 8)
 #pragma unroll
-        for (int kk = 1; kk < KS; ++kk)
+        for (int kk = KPRE; kk < KREAD; ++kk)
 #pragma unroll
             for (int i = 0; i < NR; ++i) read_frag(kk, i, so);
 #pragma unroll
@@ -590,7 +636,11 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         for (int q = 0; q < NM; ++q) {
             MOE_MFMA(3, q);
             if (MORE) refill(3, q, kt);
-            if ((q & 1) && (q >> 1) < NR) read_frag(0, q >> 1, nso);
+            if (F8) {
+                read_frag(0, q, nso);  // two 16-byte reads
+            } else if ((q & 1) && (q >> 1) < NR) {
+                read_frag(0, q >> 1, nso);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -598,6 +648,36 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     for (; kt + 2 < nk; ++kt) slice(kt, std::true_type{});
     for (; kt < nk; ++kt) slice(kt, std::false_type{});
 #undef MOE_MFMA
+#undef MOE_MFMA_F8
+#undef MOE_MFMA_BF16
+
+    // fp8: apply the row and column scales, 2^(a_exp[row] + b_exp[col]),
+    // exactly (before a split partial is stored, which then sums scaled
+    // values: the same result, since the scaling is by a power of two)
+    if constexpr (F8) {
+        int ea[4];
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+            int pos = tile.row0 + wm * 128 + mb * 32 + l32;
+            if (pos >= tile.row1) pos = tile.row1 - 1;
+            ea[mb] = a_exp[GATHER ? sorted_assign[pos] / topk : pos];
+        }
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int col = GATEUP ? n0 + wn * 64 + (nb & 1) * 32 + 8 * g + 4 * khalf
+                                       : n0 + wn * 128 + nb * 32 + 8 * g + 4 * khalf;
+                const int32_t* be = (GATEUP && nb >= 2) ? b_exp1 : b_exp0;
+                i32x4_t eb = {0, 0, 0, 0};
+                if (col < N) eb = *reinterpret_cast<const i32x4_t*>(be + static_cast<int64_t>(tile.e) * N + col);
+#pragma unroll
+                for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        acc[nb][mb][4 * g + i] = __builtin_amdgcn_ldexpf(acc[nb][mb][4 * g + i], ea[mb] + eb[i]);
+            }
+    }
 
     // A split K range: the fp32 partial sums go to slot work.j, register by
     // register (register r of thread t at (j * 256 + r) * 256 + t).
@@ -1012,6 +1092,38 @@ hipError_t launch_backward_wgrad(const moe_problem_t& p, const void* A, int M, c
     grouped_gemm_bf16_kernel<kWgrad, false, false><<<g, 256, 0, s>>>(
         static_cast<const bf16_t*>(A), order, p.k, poff, p.E, static_cast<const bf16_t*>(B), nullptr,
         static_cast<bf16_t*>(C), N, static_cast<int>(ldk), 0, nullptr, nullptr, nullptr, M);
+    return hipGetLastError();
+}
+
+// ---- fp8 expert FFN ------------------------------------------------------
+
+// GEMM1 on fp8 codes of x (gathered per queue row) and of W_gate / W_up, with
+// the SwiGLU epilogue, writes h in bf16; h is quantised per queue row; GEMM2
+// on the codes of h and W_down writes y_perm.  The down projection splits its
+// tail like the bf16 one (part: kSplitWGs partial tiles, or null).
+hipError_t launch_expert_ffn_fp8(const moe_problem_t& p, const void* x_q, const int32_t* x_exp,
+                                 const int32_t* sorted_assign, const int32_t* offsets, const void* wg_q,
+                                 const int32_t* wg_exp, const void* wu_q, const int32_t* wu_exp,
+                                 const void* wd_q, const int32_t* wd_exp, void* h, void* h_q, int32_t* h_exp,
+                                 float* part, void* y_perm, hipStream_t s) {
+    const int64_t n = p.T * p.k;
+    const unsigned g1 = grid_for(n, p.E, kBM, static_cast<int>(ceil_div(p.f, kGateUpCols)));
+    grouped_gemm_bf16_kernel<kUp, true, false, true><<<g1, 256, 0, s>>>(
+        static_cast<const bf16_t*>(x_q), sorted_assign, p.k, offsets, p.E, static_cast<const bf16_t*>(wg_q),
+        static_cast<const bf16_t*>(wu_q), static_cast<bf16_t*>(h), p.f, p.d, 0, nullptr, nullptr, nullptr, 0,
+        x_exp, wg_exp, wu_exp);
+    hipError_t err = launch_quant_rows_fp8(h, n, p.f, h_q, h_exp, s);
+    if (err != hipSuccess) return err;
+    const unsigned g2 = grid_for(n, p.E, kBM, static_cast<int>(ceil_div(p.d, kDownCols)));
+    const int nk2 = p.f / 128;
+    const int slots = (part != nullptr && fp8_can_split(p)) ? resident_slots() : 0;
+    grouped_gemm_bf16_kernel<kDown, false, false, true><<<g2 + (slots > 0 ? kSplitWGs : 0), 256, 0, s>>>(
+        static_cast<const bf16_t*>(h_q), sorted_assign, p.k, offsets, p.E, static_cast<const bf16_t*>(wd_q),
+        nullptr, static_cast<bf16_t*>(y_perm), p.d, p.f, slots, part, nullptr, nullptr, 0, h_exp, wd_exp,
+        nullptr);
+    if (slots > 0)
+        split_reduce_kernel<<<kSplitWGs * 16, 256, 0, s>>>(part, offsets, p.E, p.d, nk2, slots,
+                                                          static_cast<bf16_t*>(y_perm));
     return hipGetLastError();
 }
 

@@ -11,7 +11,7 @@ using namespace moe;
 
 namespace {
 
-constexpr int32_t kAbiVersion = 2;
+constexpr int32_t kAbiVersion = 3;
 constexpr size_t kAlign = 256;
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
@@ -109,6 +109,25 @@ moe_status_t check_backward(const moe_problem_t* p) {
     return MOE_OK;
 }
 
+// fp8 expert FFN workspace: x codes [T, d] and exponents [T], h [T*k, f]
+// bf16, h codes [T*k, f] and exponents [T*k], split-K partial tiles.
+size_t ffn_fp8_ws(const moe_problem_t& p) {
+    const size_t n = static_cast<size_t>(p.T) * p.k;
+    return align_up(static_cast<size_t>(p.T) * p.d, kAlign) + align_up(static_cast<size_t>(p.T) * 4, kAlign) +
+           align_up(n * p.f * 2, kAlign) + align_up(n * p.f, kAlign) + align_up(n * 4, kAlign) +
+           align_up(fp8_split_bytes(p), kAlign);
+}
+
+// Limits of the fp8 path (beyond check_problem): bf16 weights and
+// activations, d and f multiples of 128 (one 128-byte slice of codes), and
+// 32-bit byte offsets into the x codes.
+moe_status_t check_fp8(const moe_problem_t* p) {
+    if (p->dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
+    if (p->d % 128 != 0 || p->f % 128 != 0) return MOE_ERR_UNSUPPORTED;
+    if (p->T * static_cast<int64_t>(p->d) > UINT32_MAX) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
 size_t forward_ws(const moe_problem_t& p) {
     const size_t n = static_cast<size_t>(p.T) * p.k;
     size_t b = 0;
@@ -151,6 +170,10 @@ moe_status_t moe_workspace_size(const moe_problem_t* p, int32_t op, size_t* byte
         case MOE_OP_BACKWARD:
             MOE_TRY(check_backward(p));
             *bytes = backward_ws(*p);
+            break;
+        case MOE_OP_EXPERT_FFN_FP8:
+            MOE_TRY(check_fp8(p));
+            *bytes = ffn_fp8_ws(*p);
             break;
         default: return MOE_ERR_INVALID_ARGUMENT;
     }
@@ -408,6 +431,79 @@ moe_status_t moe_backward(const moe_problem_t* p, const void* x, const void* w_r
                                      xT, p->d, kp, poff, order, out->dw_up, s));
     if (w_router != nullptr)
         MOE_LAUNCH(launch_backward_dwr(*p, wr_part, poff, out->dw_router, s));
+    return MOE_OK;
+}
+
+moe_status_t moe_quantize_rows_fp8(const void* src, int64_t rows, int32_t cols, void* codes, int32_t* exps,
+                                   void* stream) {
+    if (rows < 0 || cols <= 0 || rows > INT32_MAX) return rows < 0 || cols <= 0 ? MOE_ERR_INVALID_ARGUMENT
+                                                                              : MOE_ERR_UNSUPPORTED;
+    if (cols % 16 != 0) return MOE_ERR_UNSUPPORTED;
+    if (rows == 0) return MOE_OK;
+    MOE_TRY(need(src));
+    MOE_TRY(need(codes));
+    MOE_TRY(need(exps));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    clear_hip_error();
+    MOE_LAUNCH(launch_quant_rows_fp8(src, rows, cols, codes, exps, s));
+    return MOE_OK;
+}
+
+moe_status_t moe_quantize_weights_fp8(const moe_problem_t* p, const void* w_gate, const void* w_up,
+                                      const void* w_down, const moe_fp8_weights_t* out, void* stream) {
+    MOE_TRY(check_problem(p));
+    MOE_TRY(check_fp8(p));
+    if (out == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+    MOE_TRY(need(w_gate));
+    MOE_TRY(need(w_up));
+    MOE_TRY(need(w_down));
+    MOE_TRY(need(out->w_gate));
+    MOE_TRY(need(out->w_gate_exp));
+    MOE_TRY(need(out->w_up));
+    MOE_TRY(need(out->w_up_exp));
+    MOE_TRY(need(out->w_down));
+    MOE_TRY(need(out->w_down_exp));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    clear_hip_error();
+    const int64_t ef = static_cast<int64_t>(p->E) * p->f, ed = static_cast<int64_t>(p->E) * p->d;
+    MOE_LAUNCH(launch_quant_rows_fp8(w_gate, ef, p->d, out->w_gate, out->w_gate_exp, s));
+    MOE_LAUNCH(launch_quant_rows_fp8(w_up, ef, p->d, out->w_up, out->w_up_exp, s));
+    MOE_LAUNCH(launch_quant_rows_fp8(w_down, ed, p->f, out->w_down, out->w_down_exp, s));
+    return MOE_OK;
+}
+
+moe_status_t moe_expert_ffn_fp8(const moe_problem_t* p, const void* x, const int32_t* sorted_assign,
+                                const int32_t* offsets, const moe_fp8_weights_t* w, void* y_perm, void* ws,
+                                size_t ws_bytes, void* stream) {
+    MOE_TRY(check_problem(p));
+    MOE_TRY(check_fp8(p));
+    if (w == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+    if (p->T == 0) return MOE_OK;
+    MOE_TRY(need(x));
+    MOE_TRY(need(sorted_assign));
+    MOE_TRY(need(offsets));
+    MOE_TRY(need(w->w_gate));
+    MOE_TRY(need(w->w_gate_exp));
+    MOE_TRY(need(w->w_up));
+    MOE_TRY(need(w->w_up_exp));
+    MOE_TRY(need(w->w_down));
+    MOE_TRY(need(w->w_down_exp));
+    MOE_TRY(need(y_perm));
+    MOE_TRY(need(ws));
+    if (ws_bytes < ffn_fp8_ws(*p)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    const size_t n = static_cast<size_t>(p->T) * p->k;
+    Carver c(ws);
+    void* x_q = c.take<char>(static_cast<size_t>(p->T) * p->d);
+    int32_t* x_exp = c.take<int32_t>(static_cast<size_t>(p->T) * 4);
+    void* h = c.take<char>(n * p->f * 2);
+    void* h_q = c.take<char>(n * p->f);
+    int32_t* h_exp = c.take<int32_t>(n * 4);
+    float* part = fp8_split_bytes(*p) > 0 ? c.take<float>(fp8_split_bytes(*p)) : nullptr;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    clear_hip_error();
+    MOE_LAUNCH(launch_quant_rows_fp8(x, p->T, p->d, x_q, x_exp, s));
+    MOE_LAUNCH(launch_expert_ffn_fp8(*p, x_q, x_exp, sorted_assign, offsets, w->w_gate, w->w_gate_exp, w->w_up,
+                                     w->w_up_exp, w->w_down, w->w_down_exp, h, h_q, h_exp, part, y_perm, s));
     return MOE_OK;
 }
 

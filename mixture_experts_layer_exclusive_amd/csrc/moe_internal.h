@@ -88,6 +88,11 @@ hipError_t launch_combine(const moe_problem_t& p, const void* y_perm, const int3
 
 // Padded per-expert column count of the weight-gradient operands: every
 // expert's queue rounded up to 64 columns.
+// The fp8 down projection (K = f codes, 128 per slice) splits its tail too.
+inline bool fp8_can_split(const moe_problem_t& p) { return p.f / 128 >= 2 * kSplitMinSlices; }
+inline size_t fp8_split_bytes(const moe_problem_t& p) {
+    return fp8_can_split(p) ? static_cast<size_t>(kSplitWGs) * kBM * kDownCols * 4 : 0;
+}
 // The backward's dx_perm GEMM (K = 2f) splits its tail like the down projection.
 inline bool bwd_can_split(const moe_problem_t& p) { return (2 * p.f) / 64 >= 2 * kSplitMinSlices; }
 inline size_t bwd_split_bytes(const moe_problem_t& p) {
@@ -97,6 +102,13 @@ inline int64_t backward_kpad(const moe_problem_t& p) {
     return static_cast<int64_t>(align_up(static_cast<size_t>(p.T * p.k + 63 * static_cast<int64_t>(p.E)), 64));
 }
 
+hipError_t launch_quant_rows_fp8(const void* src, int64_t rows, int cols, void* codes, int32_t* exps,
+                                 hipStream_t s);
+hipError_t launch_expert_ffn_fp8(const moe_problem_t& p, const void* x_q, const int32_t* x_exp,
+                                 const int32_t* sorted_assign, const int32_t* offsets, const void* wg_q,
+                                 const int32_t* wg_exp, const void* wu_q, const int32_t* wu_exp,
+                                 const void* wd_q, const int32_t* wd_exp, void* h, void* h_q, int32_t* h_exp,
+                                 float* part, void* y_perm, hipStream_t s);
 hipError_t launch_backward_weights(const moe_problem_t& p, const void* w_gate, const void* w_up,
                                    const void* w_down, void* w_down_t, void* w_gu_t, hipStream_t s);
 hipError_t launch_backward_dy(const moe_problem_t& p, const void* dy, const void* y_perm,

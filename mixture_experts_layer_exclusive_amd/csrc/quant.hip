@@ -1,0 +1,74 @@
+// Per-row FP8 quantisation for the fp8 expert FFN.
+//
+// Quantised experts are named as future work in the MoEBlaze summary
+// (euno.news, "MoEBlaze: breaking the memory wall for efficient MoE training
+// on modern GPUs"), Limitations and future work; the scheme is this
+// library's reading: each row r of a bf16 matrix gets the power-of-two scale
+// 2^a_r, the smallest with max|row| <= 448 * 2^a_r (a_r = 0 for a zero row),
+// and each element becomes the OCP FP8 E4M3 code of value / 2^a_r, rounded
+// to nearest even by the hardware conversion.  Scaling by a power of two is
+// exact, so the conversion is the only rounding.
+#include "device_util.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+// One workgroup per row: the row's absolute maximum (two passes over the
+// row, the second served by the caches), its scale exponent, and the codes.
+__global__ __launch_bounds__(256) void quant_rows_fp8_kernel(const uint4* __restrict__ src, int chunks,
+                                                            uint2* __restrict__ dst, int32_t* __restrict__ exps) {
+    __shared__ float s_max[4];
+    const int64_t r = blockIdx.x;
+    const uint4* row = src + r * chunks;
+    float m = 0.f;
+    for (int c = threadIdx.x; c < chunks; c += 256) {
+        const uint4 v = row[c];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(lo_bf16(w[i])), fabsf(hi_bf16(w[i]))));
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    if ((threadIdx.x & 63) == 0) s_max[threadIdx.x >> 6] = m;
+    __syncthreads();
+    const float amax = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+    // amax = mm 2^e with mm in [0.5, 1); 448 = 0.875 * 2^9
+    int a = 0;
+    if (amax > 0.f) {
+        int e = 0;
+        const float mm = frexpf(amax, &e);
+        a = mm <= 0.875f ? e - 9 : e - 8;
+    }
+    if (threadIdx.x == 0) exps[r] = a;
+    uint2* out = dst + r * chunks;
+    for (int c = threadIdx.x; c < chunks; c += 256) {
+        const uint4 v = row[c];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        float f[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[2 * i] = __builtin_amdgcn_ldexpf(lo_bf16(w[i]), -a);
+            f[2 * i + 1] = __builtin_amdgcn_ldexpf(hi_bf16(w[i]), -a);
+        }
+        // element 0 in the lowest byte
+        int p0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+        p0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], p0, true);
+        int p1 = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
+        p1 = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], p1, true);
+        out[c] = make_uint2(static_cast<uint32_t>(p0), static_cast<uint32_t>(p1));
+    }
+}
+
+}  // namespace
+
+hipError_t launch_quant_rows_fp8(const void* src, int64_t rows, int cols, void* codes, int32_t* exps,
+                                 hipStream_t s) {
+    if (rows == 0) return hipSuccess;
+    quant_rows_fp8_kernel<<<static_cast<unsigned>(rows), 256, 0, s>>>(static_cast<const uint4*>(src), cols / 8,
+                                                                      static_cast<uint2*>(codes), exps);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -21,7 +21,7 @@ MIS = 0x10004  # not 16-byte aligned
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
 
 
 def prob(T=64, d=128, E=8, k=2, f=256, dtype=L.MOE_DTYPE_BF16):
@@ -48,7 +48,8 @@ def test_header_constants_match_binding():
     assert int(re.search(r"#define MOE_MAX_TOPK (\d+)", text).group(1)) == L.MOE_MAX_TOPK
     for name in ("MOE_OK", "MOE_ERR_INVALID_ARGUMENT", "MOE_ERR_UNSUPPORTED",
                  "MOE_ERR_WORKSPACE_TOO_SMALL", "MOE_ERR_HIP", "MOE_DTYPE_F32", "MOE_DTYPE_BF16",
-                 "MOE_OP_DISPATCH", "MOE_OP_EXPERT_FFN", "MOE_OP_FORWARD", "MOE_OP_BACKWARD"):
+                 "MOE_OP_DISPATCH", "MOE_OP_EXPERT_FFN", "MOE_OP_FORWARD", "MOE_OP_BACKWARD",
+                 "MOE_OP_EXPERT_FFN_FP8"):
         assert int(re.search(name + r"\s*=\s*(\d+)", text).group(1)) == getattr(L, name)
 
 
@@ -222,3 +223,37 @@ def test_backward_workspace_size(lib):
         st, nb = ws_size(lib, prob(T, d, E, k, f), L.MOE_OP_BACKWARD)
         assert st == L.MOE_OK
         assert expect <= nb <= expect + 14 * 256
+
+
+def test_fp8_validation(lib):
+    U = L.MOE_ERR_UNSUPPORTED
+    E = L.MOE_ERR_INVALID_ARGUMENT
+    good = prob(T=64, d=256, E=8, k=2, f=512)
+    st, need = ws_size(lib, good, L.MOE_OP_EXPERT_FFN_FP8)
+    assert st == L.MOE_OK
+    n = 64 * 2
+    assert need >= 64 * 256 + 64 * 4 + n * 512 * 2 + n * 512 + n * 4
+    w = L.MoeFp8Weights(w_gate=A, w_gate_exp=A, w_up=A, w_up_exp=A, w_down=A, w_down_exp=A)
+    for bad in (dict(d=192), dict(f=320), dict(dtype=L.MOE_DTYPE_F32), dict(T=2 ** 22, d=2048)):
+        p = prob(T=64, d=256, E=8, k=2, f=512)
+        for key, v in bad.items():
+            setattr(p, key, v)
+        assert ws_size(lib, p, L.MOE_OP_EXPERT_FFN_FP8)[0] == U, bad
+        assert lib.moe_quantize_weights_fp8(ctypes.byref(p), A, A, A, ctypes.byref(w), None) == U
+        assert lib.moe_expert_ffn_fp8(ctypes.byref(p), A, A, A, ctypes.byref(w), A, A, 1 << 40, None) == U
+    pp = ctypes.byref(good)
+    assert lib.moe_quantize_weights_fp8(pp, A, A, A, None, None) == E
+    assert lib.moe_expert_ffn_fp8(pp, A, A, A, None, A, A, 1 << 40, None) == E
+    w.w_down_exp = None
+    assert lib.moe_expert_ffn_fp8(pp, A, A, A, ctypes.byref(w), A, A, 1 << 40, None) == E
+    w.w_down_exp = MIS
+    assert lib.moe_expert_ffn_fp8(pp, A, A, A, ctypes.byref(w), A, A, 1 << 40, None) == U
+    w.w_down_exp = A
+    assert lib.moe_expert_ffn_fp8(pp, A, A, A, ctypes.byref(w), A, A, need - 1, None) == \
+        L.MOE_ERR_WORKSPACE_TOO_SMALL
+    # quantize rows: cols a positive multiple of 16
+    assert lib.moe_quantize_rows_fp8(A, 4, 24, A, A, None) == U
+    assert lib.moe_quantize_rows_fp8(A, 4, 0, A, A, None) == E
+    assert lib.moe_quantize_rows_fp8(A, -1, 16, A, A, None) == E
+    assert lib.moe_quantize_rows_fp8(None, 0, 16, None, None, None) == L.MOE_OK
+    assert lib.moe_quantize_rows_fp8(A, 4, 16, MIS, A, None) == U

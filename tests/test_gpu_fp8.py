@@ -1,0 +1,132 @@
+"""Parity of the fp8 path against the CPU oracle (``oracle.moe_fp8``).
+
+* Quantisation is byte work decided by floating point: both sides take the
+  same per-row power-of-two scale from the same bf16 values, and the codes
+  must be bit-exact (ties, subnormal codes, zero rows and signed zeros
+  included).
+* The fp8 expert FFN must agree with the oracle's fp8 FFN, which quantises
+  the same bf16 inputs the same way and sums in float64.  The bound follows
+  from where the two may differ.  The GPU sums in fp32 and computes the
+  SwiGLU in fp32 before rounding h to bf16, so about one h element in 2000
+  lands one bf16 unit away from the oracle's.  About one in 16 of those
+  crosses an E4M3 rounding boundary, and its code moves by one step (2^-4
+  relative).  That moves its output row by up to 2^-4 |h_j| |W_down[:, j]|,
+  about 1 % of max|y|.  Hence max|dy| / max|y| <= 3e-2 for such rare flips,
+  and RMS(dy) / RMS(y) <= 3e-3 (the bf16 rounding of y alone is 1.1e-3), so
+  that a systematic error still fails.
+Outputs are poisoned before each call so that an unwritten element fails.
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+import oracle as O
+import mixture_experts_layer_exclusive_amd as moe
+from oracle import moe_fp8 as F
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def dev(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(DEV)
+    return torch.from_numpy(a).to(DEV)
+
+
+def rel(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape
+    assert np.all(np.isfinite(got)), "non-finite output"
+    return float(np.max(np.abs(got - ref)) / max(np.max(np.abs(ref)), 1e-30))
+
+
+def bf16_matrix(rows, cols, seed):
+    """bf16 bit patterns of rows with very different ranges, zero rows,
+    signed zeros and exact ties between neighbouring E4M3 codes."""
+    rng = np.random.default_rng(seed)
+    a = rng.standard_normal((rows, cols)).astype(np.float32)
+    a *= np.float32(2.0) ** rng.integers(-30, 30, (rows, 1)).astype(np.float32)
+    pos = np.sort(F.e4m3_decode(np.arange(0x7F, dtype=np.uint8)))
+    mids = ((pos[:-1] + pos[1:]) / 2).astype(np.float32)          # 5 significant bits: exact in bf16
+    if rows > 3:
+        a[1] = 0.0
+        a[2] = -0.0
+        a[3, :] = rng.choice(np.concatenate([mids, -mids]), cols)
+        a[3, 0] = 448.0                                              # scale 2^0: the ties stay ties
+    if rows > 4:
+        a[4] = rng.choice(pos[:12], cols) * np.float32(2.0 ** -20)   # subnormal codes after scaling
+        a[4, 0] = np.float32(448.0 * 2.0 ** -20)
+    return mi.f32_to_bf16_bits(a)
+
+
+@pytest.mark.parametrize("rows,cols", [(37, 256), (5, 14336), (300, 16), (1, 4096)])
+def test_quantize_rows_bit_exact(rows, cols):
+    a = bf16_matrix(rows, cols, seed=rows)
+    codes, exps = moe.quantize_rows_fp8(dev(a))
+    torch.cuda.synchronize()
+    rc, re_ = F.quantize_rows(mi.bf16_bits_to_f32(a))
+    assert np.array_equal(exps.cpu().numpy(), re_)
+    got = codes.cpu().numpy()
+    bad = np.argwhere(got != rc)
+    assert bad.size == 0, (len(bad), bad[:5], got[tuple(bad[0])] if len(bad) else None)
+
+
+def test_quantize_weights_bit_exact():
+    p = mi.Problem(1, 256, 3, 1, 384, "bf16")
+    W = dict(zip(("w_gate", "w_up", "w_down"), mi.make_expert_weights(p, seed=4)))
+    q = moe.quantize_weights_fp8(dev(W["w_gate"]), dev(W["w_up"]), dev(W["w_down"]))
+    torch.cuda.synchronize()
+    for name in ("w_gate", "w_up", "w_down"):
+        c, e = F.quantize_weights(mi.bf16_bits_to_f32(W[name]))
+        assert np.array_equal(q[name].cpu().numpy(), c), name
+        assert np.array_equal(q[name + "_exp"].cpu().numpy(), e), name
+
+
+FP8_CASES = [
+    # T, d, E, k, f, logits
+    (600, 256, 8, 2, 512, "gauss"),
+    (1000, 384, 16, 4, 640, "zipf"),      # skewed: empty and tiny experts, column tail in GEMM2
+    (333, 128, 64, 6, 256, "gauss"),      # many experts, few rows each
+    (1, 128, 8, 2, 128, "gauss"),
+    (70, 128, 1, 1, 384, "gauss"),
+    (1024, 512, 2, 2, 2048, "gauss"),     # the down projection splits its K tail
+]
+
+
+@pytest.mark.parametrize("T,d,E,k,f,kind", FP8_CASES)
+def test_fp8_expert_ffn(T, d, E, k, f, kind):
+    print(f"fp8 ffn T={T} d={d} E={E} k={k} f={f} {kind}", flush=True)
+    p = mi.Problem(T, d, E, k, f, "bf16")
+    L = mi.make_layer(p, seed=T + f)
+    logits = mi.make_gaussian_logits(p, d) if kind == "gauss" else mi.make_zipf_logits(p, d)
+    ids, _ = O.topk_route(logits, k)
+    q = O.dispatch(ids, E)
+    f32 = lambda n: mi.bf16_bits_to_f32(L[n])  # noqa: E731
+    ref = F.fp8_expert_ffn(f32("x"), q["sorted_assign"], q["offsets"], k, f32("w_gate"), f32("w_up"),
+                           f32("w_down"))
+    wq = moe.quantize_weights_fp8(dev(L["w_gate"]), dev(L["w_up"]), dev(L["w_down"]))
+    y_perm = torch.full((T * k, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+    moe.expert_ffn_fp8(dev(q["offsets"]), wq, k, dev(L["x"]), dev(q["sorted_assign"]), y_perm=y_perm)
+    torch.cuda.synchronize()
+    got = y_perm.float().cpu().numpy()
+    err = rel(got, ref["y_perm"])
+    rms = float(np.sqrt(np.mean((got - ref["y_perm"]) ** 2) / np.mean(ref["y_perm"] ** 2)))
+    print(f"fp8 ffn: max|dy|/max|y| = {err:.2e}, rms {rms:.2e}", flush=True)
+    assert err <= 3e-2 and rms <= 3e-3
+
+
+def test_fp8_expert_ffn_twice_is_bitwise_identical():
+    p = mi.Problem(2000, 256, 8, 2, 2048, "bf16")
+    L = mi.make_layer(p, seed=9)
+    ids, _ = O.topk_route(mi.make_gaussian_logits(p, 9), 2)
+    q = O.dispatch(ids, 8)
+    wq = moe.quantize_weights_fp8(dev(L["w_gate"]), dev(L["w_up"]), dev(L["w_down"]))
+    args = (dev(q["offsets"]), wq, 2, dev(L["x"]), dev(q["sorted_assign"]))
+    y1 = moe.expert_ffn_fp8(*args)
+    y2 = moe.expert_ffn_fp8(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
