@@ -13,7 +13,10 @@ the dispatch call with the row gather materialised, and the combine, and it
 times the CPU oracle on a bounded slice of the same workload.  For bf16
 workloads it also times the layer's backward (``moe_backward``: 16*k*d*f
 GEMM FLOPs per token) for a seeded output gradient; the transposed weight
-layouts it reads are made once beforehand, as after an optimizer step.
+layouts it reads are made once beforehand, as after an optimizer step.  With
+d and f multiples of 128 it also times the fp8 expert FFN
+(``moe_expert_ffn_fp8``: E4M3 codes with per-row power-of-two scales, FP8
+MFMA, the quantisation of x and h included) against the dense fp8 peak.
 """
 from __future__ import annotations
 
@@ -30,6 +33,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "MoE layer fwd tokens/s; expert-GEMM TFLOP/s (% MFMA peak); dispatch GB/s"
 FFN_SRC = os.path.join(ROOT, "mixture_experts_layer_exclusive_amd", "csrc", "expert_ffn.hip")
@@ -46,6 +50,7 @@ def parse():
                     help="tokens of the workload the CPU oracle runs for the baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 expert-FFN timing")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter calibration)")
     return ap.parse_args()
@@ -200,6 +205,21 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
+    # ---- fp8 expert FFN (bf16 workloads with d, f multiples of 128) ----
+    fp8 = None
+    if p.dtype == "bf16" and p.d % 128 == 0 and p.f % 128 == 0 and not args.no_fp8:
+        wq = moe.quantize_weights_fp8(wg, wu, wd)
+        ws8 = torch.empty(moe.workspace_size(prob, 5), dtype=torch.uint8, device=dev)
+        ms_fp8 = timed(lambda: moe.expert_ffn_fp8(offsets, wq, p.k, x, sa, ws=ws8, y_perm=y_perm), reps)
+        fp8_tflops = ffn_flops / (ms_fp8 * 1e-3) / 1e12
+        fp8 = {"ms_per_call": round(ms_fp8, 4), "flops_per_call": ffn_flops, "tflops": round(fp8_tflops, 2),
+               "peak": PEAK_FP8_TFLOPS, "frac_mfma_peak": round(fp8_tflops / PEAK_FP8_TFLOPS, 4),
+               "speedup_vs_bf16": round(ms_ffn / ms_fp8, 3),
+               "scheme": "OCP E4M3 codes, power-of-two scale per token (x), per queue row (h) and per "
+                         "weight row; fp32 accumulation; quantisation of x and h included"}
+        print(f"# fp8 expert FFN: {ms_fp8:.3f} ms/call", file=sys.stderr, flush=True)
+        del wq, ws8
+
     # ---- the analytic resource model's prediction for this workload ----
     from mixture_experts_layer_exclusive_amd import resource_model as RM
     lay = RM.Layer(p.T, p.d, p.E, p.k, p.f, 2 if p.dtype == "bf16" else 4)
@@ -267,6 +287,7 @@ def main():
         "expert_counts": {"min": int(counts.min()), "max": int(counts.max()),
                           "empty": int((counts == 0).sum())},
         "backward": bwd,
+        "fp8_expert_ffn": fp8,
         "resource_model": model,
         "cpu_baseline": cpu,
     }

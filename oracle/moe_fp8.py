@@ -87,15 +87,26 @@ def quantize_rows(a: np.ndarray):
     """Per-row power-of-two scaled E4M3 codes of a 2-D array.  Returns
     (codes uint8 [R, C], exponents int32 [R]) with
     a[r] ~= 2^exp[r] * decode(codes[r])."""
-    a = np.asarray(a, dtype=np.float64)
-    exps = np.array([pow2_scale_exponent(m) for m in np.max(np.abs(a), axis=1)], dtype=np.int32) \
-        if a.shape[0] else np.zeros(0, np.int32)
-    codes = e4m3_encode(np.ldexp(a, -exps[:, None]))
+    a = np.asarray(a)
+    R, C = a.shape
+    codes = np.zeros((R, C), dtype=np.uint8)
+    exps = np.zeros(R, dtype=np.int32)
+    for r0 in range(0, R, 256):  # blocks of rows (the rows are independent)
+        blk = np.asarray(a[r0:r0 + 256], dtype=np.float64)
+        ex = np.array([pow2_scale_exponent(m) for m in np.max(np.abs(blk), axis=1)], dtype=np.int32)
+        codes[r0:r0 + 256] = e4m3_encode(np.ldexp(blk, -ex[:, None]))
+        exps[r0:r0 + 256] = ex
     return codes, exps
 
 
 def dequantize_rows(codes: np.ndarray, exps: np.ndarray) -> np.ndarray:
-    return np.ldexp(e4m3_decode(codes), np.asarray(exps, dtype=np.int64)[:, None])
+    """2^exps[r] * value(codes[r, c]), float64 (in blocks of rows)."""
+    codes = np.asarray(codes)
+    exps = np.asarray(exps, dtype=np.int64)
+    out = np.empty(codes.shape, dtype=np.float64)
+    for r0 in range(0, codes.shape[0], 256):
+        out[r0:r0 + 256] = np.ldexp(e4m3_decode(codes[r0:r0 + 256]), exps[r0:r0 + 256, None])
+    return out
 
 
 def round_bf16(v: np.ndarray) -> np.ndarray:
@@ -147,3 +158,30 @@ def fp8_expert_ffn(x: np.ndarray, sorted_assign: np.ndarray, offsets: np.ndarray
             y[lo:hi] = hdq[lo:hi] @ dequantize_rows(wd[e], de[e]).T
     return dict(y_perm=y, h=h, x_codes=xq, x_exp=xe, h_codes=hq, h_exp=he,
                 w_gate=(wg, ge), w_up=(wu, ue), w_down=(wd, de))
+
+
+def fp8_ffn_rows(x_rows: np.ndarray, experts: np.ndarray, w_gate, w_up, w_down) -> np.ndarray:
+    """The fp8 FFN of single queue rows (every quantisation above is per
+    row, so a row's output depends only on its token and expert): row i is
+    token row x_rows[i] through expert experts[i].  Weights may be callables
+    ``w(e)`` returning one expert's matrix; each expert used is quantised
+    once.  Returns float64 [n, d]."""
+    def get(w, e):
+        return w(e) if callable(w) else w[e]
+
+    xq, xe = quantize_rows(x_rows)
+    xdq = dequantize_rows(xq, xe)
+    experts = np.asarray(experts, dtype=np.int64)
+    out = None
+    for e in np.unique(experts):
+        rows = np.nonzero(experts == e)[0]
+        wg = dequantize_rows(*quantize_rows(get(w_gate, e)))
+        wu = dequantize_rows(*quantize_rows(get(w_up, e)))
+        wd = dequantize_rows(*quantize_rows(get(w_down, e)))
+        xr = xdq[rows]
+        h = round_bf16(silu(xr @ wg.T) * (xr @ wu.T))
+        y = dequantize_rows(*quantize_rows(h)) @ wd.T
+        if out is None:
+            out = np.zeros((len(experts), y.shape[1]), dtype=np.float64)
+        out[rows] = y
+    return out

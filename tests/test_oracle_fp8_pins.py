@@ -158,3 +158,16 @@ def test_fp8_ffn_token_independence_and_wdown_scaling():
     # and close to the exact layer (E4M3 keeps 4 significant bits)
     exact = O.expert_ffn(L["x"], q["sorted_assign"], q["offsets"], 2, L["w_gate"], L["w_up"], L["w_down"])
     assert np.max(np.abs(r["y_perm"] - exact)) / np.max(np.abs(exact)) < 0.1
+
+
+def test_fp8_rows_match_the_queue_ffn():
+    p = mi.Problem(30, 64, 5, 2, 48, "f32")
+    L = mi.make_layer(p, seed=10)
+    ids, _ = O.topk_route(mi.make_gaussian_logits(p, 10), 2)
+    q = O.dispatch(ids, 5)
+    r = F.fp8_expert_ffn(L["x"], q["sorted_assign"], q["offsets"], 2, L["w_gate"], L["w_up"], L["w_down"])
+    tok = np.array([0, 3, 17, 29])
+    rows = F.fp8_ffn_rows(np.repeat(L["x"][tok], 2, axis=0), ids[tok].reshape(-1), L["w_gate"], L["w_up"],
+                          L["w_down"])
+    pos = q["assign_pos"][(tok[:, None] * 2 + np.arange(2)).reshape(-1)]
+    assert np.array_equal(rows, r["y_perm"][pos])
