@@ -75,7 +75,7 @@ def measured_traffic():
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: this library has no multi-GPU path "
               "(each GPU would run this same layer on its own token shard); use --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
