@@ -15,19 +15,37 @@ namespace moe {
 
 namespace {
 
-// One workgroup per row: the row's absolute maximum (two passes over the
-// row, the second served by the caches), its scale exponent, and the codes.
+// One workgroup per row: the row's absolute maximum, its scale exponent,
+// and the codes.  Rows of at most 256 * RC 16-byte chunks stay in registers
+// between the two steps (one read of the row); longer rows (RC = 0) are read
+// twice, the second time from the caches.
+template <int RC>
 __global__ __launch_bounds__(256) void quant_rows_fp8_kernel(const uint4* __restrict__ src, int chunks,
                                                             uint2* __restrict__ dst, int32_t* __restrict__ exps) {
     __shared__ float s_max[4];
     const int64_t r = blockIdx.x;
     const uint4* row = src + r * chunks;
+    uint4 keep[RC > 0 ? RC : 1];
     float m = 0.f;
-    for (int c = threadIdx.x; c < chunks; c += 256) {
-        const uint4 v = row[c];
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    if (RC > 0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(lo_bf16(w[i])), fabsf(hi_bf16(w[i]))));
+        for (int i = 0; i < RC; ++i) {
+            const int c = threadIdx.x + 256 * i;
+            keep[RC > 0 ? i : 0] = c < chunks ? row[c] : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int i = 0; i < RC; ++i) {
+            const uint32_t w[4] = {keep[i].x, keep[i].y, keep[i].z, keep[i].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) m = fmaxf(m, fmaxf(fabsf(lo_bf16(w[j])), fabsf(hi_bf16(w[j]))));
+        }
+    } else {
+        for (int c = threadIdx.x; c < chunks; c += 256) {
+            const uint4 v = row[c];
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) m = fmaxf(m, fmaxf(fabsf(lo_bf16(w[j])), fabsf(hi_bf16(w[j]))));
+        }
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
@@ -43,8 +61,7 @@ __global__ __launch_bounds__(256) void quant_rows_fp8_kernel(const uint4* __rest
     }
     if (threadIdx.x == 0) exps[r] = a;
     uint2* out = dst + r * chunks;
-    for (int c = threadIdx.x; c < chunks; c += 256) {
-        const uint4 v = row[c];
+    auto convert = [&](const uint4 v) {
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
         float f[8];
 #pragma unroll
@@ -57,7 +74,16 @@ __global__ __launch_bounds__(256) void quant_rows_fp8_kernel(const uint4* __rest
         p0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], p0, true);
         int p1 = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
         p1 = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], p1, true);
-        out[c] = make_uint2(static_cast<uint32_t>(p0), static_cast<uint32_t>(p1));
+        return make_uint2(static_cast<uint32_t>(p0), static_cast<uint32_t>(p1));
+    };
+    if (RC > 0) {
+#pragma unroll
+        for (int i = 0; i < RC; ++i) {
+            const int c = threadIdx.x + 256 * i;
+            if (c < chunks) out[c] = convert(keep[RC > 0 ? i : 0]);
+        }
+    } else {
+        for (int c = threadIdx.x; c < chunks; c += 256) out[c] = convert(row[c]);
     }
 }
 
@@ -66,8 +92,17 @@ __global__ __launch_bounds__(256) void quant_rows_fp8_kernel(const uint4* __rest
 hipError_t launch_quant_rows_fp8(const void* src, int64_t rows, int cols, void* codes, int32_t* exps,
                                  hipStream_t s) {
     if (rows == 0) return hipSuccess;
-    quant_rows_fp8_kernel<<<static_cast<unsigned>(rows), 256, 0, s>>>(static_cast<const uint4*>(src), cols / 8,
-                                                                      static_cast<uint2*>(codes), exps);
+    const int chunks = cols / 8;
+    const unsigned g = static_cast<unsigned>(rows);
+    if (chunks <= 256 * 2)
+        quant_rows_fp8_kernel<2><<<g, 256, 0, s>>>(static_cast<const uint4*>(src), chunks, static_cast<uint2*>(codes),
+                                                   exps);
+    else if (chunks <= 256 * 8)
+        quant_rows_fp8_kernel<8><<<g, 256, 0, s>>>(static_cast<const uint4*>(src), chunks, static_cast<uint2*>(codes),
+                                                   exps);
+    else
+        quant_rows_fp8_kernel<0><<<g, 256, 0, s>>>(static_cast<const uint4*>(src), chunks, static_cast<uint2*>(codes),
+                                                   exps);
     return hipGetLastError();
 }
 

@@ -63,7 +63,7 @@ def bf16_matrix(rows, cols, seed):
     return mi.f32_to_bf16_bits(a)
 
 
-@pytest.mark.parametrize("rows,cols", [(37, 256), (5, 14336), (300, 16), (1, 4096)])
+@pytest.mark.parametrize("rows,cols", [(37, 256), (5, 14336), (300, 16), (1, 4096), (3, 20480)])
 def test_quantize_rows_bit_exact(rows, cols):
     a = bf16_matrix(rows, cols, seed=rows)
     codes, exps = moe.quantize_rows_fp8(dev(a))
