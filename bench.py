@@ -158,11 +158,30 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(b) / reps  # ms
 
+    def timed_cold(fn, reps):
+        """Median of single calls, each after writing a 1 GiB buffer (more than
+        the 256 MB Infinity Cache), so that the call's inputs come from HBM."""
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        out = []
+        for _ in range(reps + 1):
+            flush.fill_(1)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            out.append(a.elapsed_time(b))
+        del flush
+        return float(sorted(out[1:])[len(out[1:]) // 2])
+
     reps = max(5, args.steps)
     ms_ffn = timed(lambda: moe.expert_ffn(offsets, wg, wu, wd, p.k, p.T, x=x, sorted_assign=sa,
                                           ws=ffn_ws, y_perm=y_perm), reps)
     ms_disp = timed(lambda: moe.dispatch(ids, p.E, x=x, with_x_perm=True, ws=disp_ws, out=disp_out), reps)
     ms_comb = timed(lambda: moe.combine(y_perm, apos, gates, y=y2), reps)
+    ms_disp_cold = timed_cold(lambda: moe.dispatch(ids, p.E, x=x, with_x_perm=True, ws=disp_ws, out=disp_out),
+                              min(reps, 10))
+    ms_comb_cold = timed_cold(lambda: moe.combine(y_perm, apos, gates, y=y2), min(reps, 10))
     if lg is None:
         lo = torch.empty(p.T, p.E, dtype=torch.float32, device=dev)
         ms_route = timed(lambda: moe.route(p.k, x=x, w_router=wr, ids=ids, gates=gates, logits_out=lo), reps)
@@ -284,6 +303,11 @@ def main():
         "combine_frac_hbm_peak": round(comb_gbs / PEAK_HBM_GBS, 4),
         "stage_ms": {"route": round(ms_route, 4), "dispatch_with_x_perm": round(ms_disp, 4),
                      "expert_ffn": round(ms_ffn, 4), "combine": round(ms_comb, 4)},
+        "cold_cache": {"note": "median single call after a 1 GiB write (inputs from HBM, not the Infinity Cache)",
+                       "dispatch_with_x_perm_ms": round(ms_disp_cold, 4),
+                       "dispatch_gbs": round(disp_bytes / (ms_disp_cold * 1e-3) / 1e9, 1),
+                       "combine_ms": round(ms_comb_cold, 4),
+                       "combine_gbs": round(comb_bytes / (ms_comb_cold * 1e-3) / 1e9, 1)},
         "expert_counts": {"min": int(counts.min()), "max": int(counts.max()),
                           "empty": int((counts == 0).sum())},
         "backward": bwd,
