@@ -224,6 +224,14 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
+    # ---- measured ceilings: MFMA-only kernel, device copy ----
+    mfma_meas = moe.mfma_peak_tflops(dev)
+    ca = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cb = torch.empty_like(ca)
+    ms_copy = timed(lambda: cb.copy_(ca), 5)
+    copy_gbs = 2.0 * ca.numel() / (ms_copy * 1e-3) / 1e9
+    del ca, cb
+
     # ---- fp8 expert FFN (bf16 workloads with d, f multiples of 128) ----
     fp8 = None
     if p.dtype == "bf16" and p.d % 128 == 0 and p.f % 128 == 0 and not args.no_fp8:
@@ -295,6 +303,14 @@ def main():
                      "unit": "TFLOP/s", "frac": round(ffn_tflops / peak, 4),
                      "traffic": traffic, "ms_per_launch": round(ms_ffn, 4),
                      "flops_per_launch": ffn_flops},
+        "measured_peaks": {
+            "mfma_bf16_tflops": round(mfma_meas, 1),
+            "note": "moe_mfma_peak: register-operand MFMAs only, at the clock this GPU holds under full matrix "
+                    "load; copy: 1 GiB device copy, read + write bytes",
+            "copy_gbs": round(copy_gbs, 1),
+            "expert_gemm_frac_of_measured_mfma": round(ffn_tflops / mfma_meas, 4) if p.dtype == "bf16" else None,
+            "dispatch_frac_of_copy": round(disp_gbs / copy_gbs, 4),
+            "combine_frac_of_copy": round(comb_gbs / copy_gbs, 4)},
         "expert_gemm_tflops": round(ffn_tflops, 2),
         "expert_gemm_frac_mfma_peak": round(ffn_tflops / peak, 4),
         "dispatch_gbs": round(disp_gbs, 1),

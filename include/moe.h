@@ -304,6 +304,18 @@ moe_status_t moe_expert_ffn_fp8(const moe_problem_t* p, const void* x, const int
                                 const int32_t* offsets, const moe_fp8_weights_t* w, void* y_perm, void* ws,
                                 size_t ws_bytes, void* stream);
 
+/*
+ * moe_mfma_peak -- measurement kernel, not part of the layer: `workgroups`
+ * workgroups of 4 waves each run `iters` rounds of 8 independent bf16
+ * 32x32x16 MFMAs on register operands (no memory traffic), i.e.
+ * workgroups * 4 * iters * 8 * 32768 FLOP, and write one float per
+ * workgroup to sink [workgroups].  Timed by the caller, it gives the MFMA
+ * rate this GPU sustains (its clock under full matrix load), the ceiling
+ * the expert GEMMs are also reported against.  workgroups and iters must be
+ * positive.
+ */
+moe_status_t moe_mfma_peak(int32_t workgroups, int32_t iters, float* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

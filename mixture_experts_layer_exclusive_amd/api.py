@@ -287,3 +287,21 @@ def expert_ffn_fp8(offsets: torch.Tensor, wq: dict, k: int, x: torch.Tensor, sor
                                         _ptr(y_perm) if T else None, _ptr(ws), nbytes, _stream(dev)),
             "moe_expert_ffn_fp8")
     return y_perm
+
+
+def mfma_peak_tflops(device=None, workgroups: int = 1024, iters: int = 4000, reps: int = 3) -> float:
+    """The bf16 MFMA rate this GPU sustains with register operands only
+    (``moe_mfma_peak``), in TFLOP/s: the best of ``reps`` timed launches."""
+    dev = torch.device(device or "cuda:0")
+    sink = torch.empty(workgroups, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    best = 0.0
+    for r in range(reps + 1):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        L.check(L.load().moe_mfma_peak(workgroups, iters, _ptr(sink), _stream(dev)), "moe_mfma_peak")
+        b.record(stream)
+        torch.cuda.synchronize(dev)
+        if r > 0:
+            best = max(best, workgroups * 4 * iters * 8 * 32768.0 / (a.elapsed_time(b) * 1e-3) / 1e12)
+    return best

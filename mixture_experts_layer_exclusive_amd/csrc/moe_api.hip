@@ -507,4 +507,12 @@ moe_status_t moe_expert_ffn_fp8(const moe_problem_t* p, const void* x, const int
     return MOE_OK;
 }
 
+moe_status_t moe_mfma_peak(int32_t workgroups, int32_t iters, float* sink, void* stream) {
+    if (workgroups <= 0 || iters <= 0) return MOE_ERR_INVALID_ARGUMENT;
+    MOE_TRY(need(sink));
+    clear_hip_error();
+    MOE_LAUNCH(launch_mfma_peak(workgroups, iters, sink, static_cast<hipStream_t>(stream)));
+    return MOE_OK;
+}
+
 }  // extern "C"

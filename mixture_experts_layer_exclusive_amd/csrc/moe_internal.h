@@ -102,6 +102,7 @@ inline int64_t backward_kpad(const moe_problem_t& p) {
     return static_cast<int64_t>(align_up(static_cast<size_t>(p.T * p.k + 63 * static_cast<int64_t>(p.E)), 64));
 }
 
+hipError_t launch_mfma_peak(int workgroups, int iters, float* sink, hipStream_t s);
 hipError_t launch_quant_rows_fp8(const void* src, int64_t rows, int cols, void* codes, int32_t* exps,
                                  hipStream_t s);
 hipError_t launch_expert_ffn_fp8(const moe_problem_t& p, const void* x_q, const int32_t* x_exp,

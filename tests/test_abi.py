@@ -257,3 +257,10 @@ def test_fp8_validation(lib):
     assert lib.moe_quantize_rows_fp8(A, -1, 16, A, A, None) == E
     assert lib.moe_quantize_rows_fp8(None, 0, 16, None, None, None) == L.MOE_OK
     assert lib.moe_quantize_rows_fp8(A, 4, 16, MIS, A, None) == U
+
+
+def test_mfma_peak_validation(lib):
+    assert lib.moe_mfma_peak(0, 10, A, None) == L.MOE_ERR_INVALID_ARGUMENT
+    assert lib.moe_mfma_peak(4, 0, A, None) == L.MOE_ERR_INVALID_ARGUMENT
+    assert lib.moe_mfma_peak(4, 10, None, None) == L.MOE_ERR_INVALID_ARGUMENT
+    assert lib.moe_mfma_peak(4, 10, MIS, None) == L.MOE_ERR_UNSUPPORTED
