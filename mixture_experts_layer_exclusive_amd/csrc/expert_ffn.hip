@@ -1051,16 +1051,11 @@ hipError_t launch_backward_recompute(const moe_problem_t& p, const void* x, cons
                                      const void* dh, void* duv, void* h, hipStream_t s) {
     const int64_t n = p.T * p.k;
     const unsigned g = grid_for(n, p.E, kBM, static_cast<int>(ceil_div(p.f, kGateUpCols)));
-    if (p.T * p.d >= (int64_t{1} << 31))
-        grouped_gemm_bf16_kernel<kUpBwd, true, true><<<g, 256, 0, s>>>(
-            static_cast<const bf16_t*>(x), sorted_assign, p.k, offsets, p.E,
-            static_cast<const bf16_t*>(w_gate), static_cast<const bf16_t*>(w_up), static_cast<bf16_t*>(duv),
-            p.f, p.d, 0, nullptr, static_cast<const bf16_t*>(dh), static_cast<bf16_t*>(h), 0);
-    else
-        grouped_gemm_bf16_kernel<kUpBwd, true, false><<<g, 256, 0, s>>>(
-            static_cast<const bf16_t*>(x), sorted_assign, p.k, offsets, p.E,
-            static_cast<const bf16_t*>(w_gate), static_cast<const bf16_t*>(w_up), static_cast<bf16_t*>(duv),
-            p.f, p.d, 0, nullptr, static_cast<const bf16_t*>(dh), static_cast<bf16_t*>(h), 0);
+    // (the backward's limits keep T * d below 2^31: 32-bit gather offsets)
+    grouped_gemm_bf16_kernel<kUpBwd, true, false><<<g, 256, 0, s>>>(
+        static_cast<const bf16_t*>(x), sorted_assign, p.k, offsets, p.E, static_cast<const bf16_t*>(w_gate),
+        static_cast<const bf16_t*>(w_up), static_cast<bf16_t*>(duv), p.f, p.d, 0, nullptr,
+        static_cast<const bf16_t*>(dh), static_cast<bf16_t*>(h), 0);
     return hipGetLastError();
 }
 

@@ -99,7 +99,8 @@ size_t backward_ws(const moe_problem_t& p) {
 
 // Limits of the bf16 backward (beyond check_problem): the GEMMs address
 // [E, d, 2f] weight rows and the padded transposed operands with 32-bit
-// byte offsets.
+// byte offsets (which also keeps T * d below 2^31, so the recompute's
+// gather of x needs no 64-bit addresses).
 moe_status_t check_backward(const moe_problem_t* p) {
     if (p->dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
     if (static_cast<int64_t>(p->d) * p->f >= (int64_t{1} << 30)) return MOE_ERR_UNSUPPORTED;

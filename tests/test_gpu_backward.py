@@ -96,6 +96,7 @@ BWD_CASES = [
     (1, 64, 8, 2, 64, "gauss"),          # one token
     (70, 64, 1, 1, 128, "gauss"),        # one expert: the gate is 1, no logit gradient
     (700, 320, 8, 2, 1088, "gauss"),     # K of the weight GEMMs spans several slices and a padded tail
+    (160, 64, 256, 32, 128, "gauss"),    # the largest E and k: 256 experts, padded queues of 64
 ]
 
 

@@ -156,6 +156,7 @@ FFN_CASES = [
     (1, 64, 8, 2, 64, "bf16", "gauss"),
     (1024, 256, 4, 2, 2048, "bf16", "gauss"),  # few tiles: the down projection splits K (S = 4)
     (700, 320, 8, 2, 1088, "bf16", "gauss"),   # uneven split ranges (17 slices), column tail
+    (160, 64, 256, 32, 128, "bf16", "gauss"),  # the largest E and k: 256 experts of about 20 rows
 ]
 
 
