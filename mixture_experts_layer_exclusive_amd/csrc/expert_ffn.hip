@@ -26,6 +26,7 @@
 #include <type_traits>
 
 #include "device_util.h"
+#include "lds_dma.h"
 #include "moe_internal.h"
 
 namespace moe {
@@ -226,60 +227,6 @@ __device__ __forceinline__ float sigmoid_fast(float u) {
 
 // LDS slot of chunk c of tile row r: c ^ slot_swizzle(r).
 __device__ __forceinline__ int slot_swizzle(int r) { return (r >> 1) & 7; }
-
-// s_waitcnt with only the vector-memory counter limited (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// s_waitcnt: vector-memory counter <= N and all LDS reads returned
-// (N = 63: LDS reads only).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt_lgkm0() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
-}
-
-// 16 bytes per lane from global memory straight into LDS: lane i's bytes land
-// at LDS address lds_base + 16 * i.  Issued as inline assembly so that the
-// compiler does not treat every later LDS read as dependent on it; the caller
-// orders it with wait_vmcnt and the workgroup barrier.
-__device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_base) {
-    asm volatile(
-        "s_mov_b32 m0, %1\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %0, off"
-        :
-        : "v"(gptr), "s"(lds_base)
-        : "memory");
-}
-
-// The same from a wave-uniform base address plus a 32-bit per-lane byte
-// offset (the scalar-base form of the load).
-__device__ __forceinline__ void lds_dma16_s(const void* sbase, uint32_t voff, uint32_t lds_base) {
-    asm volatile(
-        "s_mov_b32 m0, %2\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %0, %1"
-        :
-        : "v"(voff), "s"(sbase), "s"(lds_base)
-        : "memory");
-}
-
-// Workgroup barrier without a memory fence (the LDS traffic it orders is
-// waited for explicitly); the empty asm statements keep the compiler from
-// moving memory accesses across it.
-__device__ __forceinline__ void barrier_lds() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
-}
 
 // A pointer that is wave-uniform but not provably so to the compiler, moved
 // to scalar registers.

@@ -84,6 +84,10 @@ ROUTE_CASES = [
     (32768, 128, 8, "gauss"), (65536, 128, 8, "zipf"), (4099, 128, 8, "ties"),
     (1000, 256, 32, "gauss"), (333, 3, 3, "ties"), (17, 1, 1, "gauss"), (1, 64, 5, "gauss"),
     (777, 65, 7, "ties"), (2049, 200, 4, "zipf"),
+    # k <= 8 runs the lane-group top-k: k = E, E not a multiple of 4 (scalar
+    # loads), the largest E, and k = 1
+    (4096, 8, 8, "ties"), (999, 16, 3, "ties"), (513, 255, 8, "ties"), (300, 256, 8, "zipf"),
+    (100, 7, 1, "ties"), (64, 9, 9, "gauss"),
 ]
 
 
@@ -130,7 +134,12 @@ def test_dispatch_f32_rows_and_odd_width():
 
 @pytest.mark.parametrize("T,d,E,dtype", [(256, 128, 8, "f32"), (1000, 4096, 8, "bf16"),
                                          (777, 2048, 128, "bf16"), (300, 2048, 64, "bf16"),
-                                         (65, 100, 7, "f32"), (129, 192, 256, "bf16")])
+                                         (65, 100, 7, "f32"), (129, 192, 256, "bf16"),
+                                         # one and two K chunks, E past the last full block,
+                                         # 5 and 7 expert blocks (K steps split over the waves)
+                                         (100, 64, 3, "bf16"), (513, 128, 40, "bf16"),
+                                         (260, 320, 100, "bf16"), (97, 256, 200, "bf16"),
+                                         (33, 1024, 160, "bf16")])
 def test_router_logits(T, d, E, dtype):
     p = mi.Problem(T, d, E, min(2, E), 64, dtype)
     x = mi.make_x(p, 5)
