@@ -349,11 +349,12 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // the slice lands in stage 0), and the next tile's activation row
     // lookups with it: pf says that the current tile's slice 0 was issued
     // that way, a_off_pf holds its activation offsets.  (Measured on the
-    // 8192-token, 8-expert layer: fp8 FFN 2.98 -> 2.70 ms; the same in bf16
-    // made the FFN 5 % slower, 4.77 -> 5.03 ms, so bf16 does not prefetch.)
+    // 8192-token, 8-expert layer: fp8 FFN 2.95-3.02 -> 2.58 ms; the same in
+    // bf16 made the FFN 1.5 % slower, 4.78 -> 4.85 ms, so bf16 does not
+    // prefetch.)
     constexpr bool PF = MODE == kUp && !WIDE && F8;
     bool pf = false;
-    uint32_t a_off_pf[PF ? LA : 1];
+    uint32_t a_off_pf[PF ? LA : 1] = {};
     for (int wid = blockIdx.x; wid < n_ids; wid += gridDim.x) {
         Work work;
         if (WG) {
@@ -712,36 +713,54 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                 pf = nid < n_ids && find_work(s_off, E, TM, n_tiles, s_prefix, K / BK, split_slots, nid, nw);
                 if (pf) {
                     nt_pf = nw.t;
-                    const char* const nb_base = uniform_ptr(reinterpret_cast<const char*>(rb0 >= TN / 2 ? B1 : B0) +
+                    // the lane's load coordinates, recomputed from a fresh
+                    // opaque zero so that none of them stays live across the
+                    // K loop above
+                    int z;
+                    asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+                    const int ptid = static_cast<int>(threadIdx.x) + z;
+                    const int pwave = __builtin_amdgcn_readfirstlane(ptid >> 6);
+                    const int prow = (ptid & 63) >> 3;
+                    const int pslot = ptid & 7;
+                    const int prb0 = pwave * (TN / 4);
+                    const uint32_t plds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+                    const char* const nb_base = uniform_ptr(reinterpret_cast<const char*>(prb0 >= TN / 2 ? B1 : B0) +
                                                             static_cast<int64_t>(nt_pf.e) * N * RB);
                     const int nn0 = nt_pf.nt * BN_OUT;
 #pragma unroll
                     for (int j = 0; j < LB; ++j) {
-                        const int r = rb0 + j * 8 + lrow;
-                        const int chunk = lslot ^ slot_swizzle(r);
+                        const int r = prb0 + j * 8 + prow;
+                        const int chunk = pslot ^ slot_swizzle(r);
                         int n = nn0 + (r >= TN / 2 ? r - TN / 2 : r);
                         if (n >= N) n = N - 1;
                         lds_dma16_s(nb_base, static_cast<uint32_t>(n) * static_cast<uint32_t>(RB) + chunk * 16u,
-                                    lds_b + j * 8 * ROWB);
+                                    plds0 + SA_BYTES + prb0 * ROWB + j * 8 * ROWB);
                     }
                     na_base = uniform_ptr(GATHER ? Ab : Ab + static_cast<int64_t>(nt_pf.row0) * RB);
 #pragma unroll
                     for (int j = 0; j < LA; ++j) {
-                        const int r = wave * 64 + j * 8 + lrow;
-                        const int chunk = lslot ^ slot_swizzle(r);
+                        const int r = pwave * 64 + j * 8 + prow;
+                        const int chunk = pslot ^ slot_swizzle(r);
                         int pos = nt_pf.row0 + r;
                         if (pos >= nt_pf.row1) pos = nt_pf.row1 - 1;
                         const uint32_t row = GATHER ? static_cast<uint32_t>(sorted_assign[pos] / topk)
                                                     : static_cast<uint32_t>(pos - nt_pf.row0);
                         a_off_pf[PF ? j : 0] = row * static_cast<uint32_t>(RB) + chunk * 16u;
                     }
+                } else {
+                    // (assigned on every path, so that the previous values
+                    // are dead after the prologue that reads them)
+#pragma unroll
+                    for (int j = 0; j < LA; ++j) a_off_pf[PF ? j : 0] = 0;
                 }
             }
             auto prefetch_a = [&]() {
                 if constexpr (PF) {
                     if (pf) {
 #pragma unroll
-                        for (int j = 0; j < LA; ++j) lds_dma16_s(na_base, a_off_pf[PF ? j : 0], lds_a + j * 8 * ROWB);
+                        for (int j = 0; j < LA; ++j)
+                            lds_dma16_s(na_base, a_off_pf[PF ? j : 0],
+                                        __builtin_amdgcn_readfirstlane(lds_addr(smem)) + wave * 64 * ROWB + j * 8 * ROWB);
                     }
                 }
             };
