@@ -135,30 +135,47 @@ __device__ __forceinline__ void scatter_chunk(const int* s_ids, int64_t a0, int6
 
 // Block b's first queue position per expert, from the expert-major block
 // counts bc[E][nblk]: base[e] = sum over experts e' < e of their totals plus
-// the counts of e in blocks below b.  One wave per expert row (lanes stride
-// over the blocks), then one wave scans the E totals.  Workgroup 0 also
-// writes counts[E] and offsets[E+1].
+// the counts of e in blocks below b.  Each wave reduces BR expert rows at a
+// time (lanes stride over the blocks, so every load is coalesced), with the
+// loads of all BR rows in flight together: one row at a time made this a
+// chain of E / 4 round trips, the larger part of the scatter at 128 experts.
+// Then one wave scans the E totals.  Workgroup 0 also writes counts[E] and
+// offsets[E+1].
 __device__ __forceinline__ void block_bases(const int32_t* __restrict__ bc, int E, int nblk, int b,
                                             int* s_base, int* s_tot, int32_t* __restrict__ counts,
                                             int32_t* __restrict__ offsets) {
+    constexpr int BR = 8;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    for (int e = wave; e < E; e += 4) {
-        const int32_t* row = bc + static_cast<int64_t>(e) * nblk;
-        int tot = 0, pre = 0;
+    for (int e0 = wave * BR; e0 < E; e0 += 4 * BR) {
+        int tot[BR], pre[BR];
+#pragma unroll
+        for (int r = 0; r < BR; ++r) tot[r] = pre[r] = 0;
+#pragma unroll 4
         for (int i = lane; i < nblk; i += 64) {
-            const int v = row[i];
-            tot += v;
-            if (i < b) pre += v;
+            int v[BR];
+#pragma unroll
+            for (int r = 0; r < BR; ++r) v[r] = e0 + r < E ? bc[static_cast<int64_t>(e0 + r) * nblk + i] : 0;
+#pragma unroll
+            for (int r = 0; r < BR; ++r) {
+                tot[r] += v[r];
+                pre[r] += i < b ? v[r] : 0;
+            }
         }
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            tot += __shfl_xor(tot, off, 64);
-            pre += __shfl_xor(pre, off, 64);
-        }
+        for (int off = 32; off > 0; off >>= 1)
+#pragma unroll
+            for (int r = 0; r < BR; ++r) {
+                tot[r] += __shfl_xor(tot[r], off, 64);
+                pre[r] += __shfl_xor(pre[r], off, 64);
+            }
         if (lane == 0) {
-            s_tot[e] = tot;
-            s_base[e] = pre;
+#pragma unroll
+            for (int r = 0; r < BR; ++r)
+                if (e0 + r < E) {
+                    s_tot[e0 + r] = tot[r];
+                    s_base[e0 + r] = pre[r];
+                }
         }
     }
     __syncthreads();
