@@ -146,8 +146,9 @@ struct Work {
     int kb, nkl, j;
 };
 __device__ __forceinline__ bool find_work(const int* s_off, int E, int bm, int n_tiles,
-                                          const int* s_prefix, int nk, int slots, int hw, Work& w) {
+                                          const int* s_prefix, int nk, int slots, Work& w) {
     const SplitPlan sp = split_plan(s_prefix[E] * n_tiles, slots, nk);
+    const int hw = blockIdx.x;
     const int per_xcd = (sp.full + NUM_XCD - 1) / NUM_XCD;
     int pid;
     if (hw < per_xcd * NUM_XCD) {
@@ -169,18 +170,11 @@ __device__ __forceinline__ bool find_work(const int* s_off, int E, int bm, int n
     return true;
 }
 
-// Number of workgroup ids that find_work maps: the XCD-interleaved whole
-// tiles (rounded up to whole XCD ranges) and the split parts of the tail.
-__device__ __forceinline__ int work_ids(const int* s_prefix, int E, int n_tiles, int nk, int slots) {
-    const SplitPlan sp = split_plan(s_prefix[E] * n_tiles, slots, nk);
-    return (sp.full + NUM_XCD - 1) / NUM_XCD * NUM_XCD + (sp.total - sp.full) * sp.S;
-}
-
 // This workgroup's whole tile (no split); false when it has no work.
 __device__ __forceinline__ bool find_tile(const int* s_off, int E, int bm, int n_tiles,
                                           const int* s_prefix, Tile& t) {
     Work w;
-    if (!find_work(s_off, E, bm, n_tiles, s_prefix, 1, 0, blockIdx.x, w)) return false;
+    if (!find_work(s_off, E, bm, n_tiles, s_prefix, 1, 0, w)) return false;
     t = w.t;
     return true;
 }
@@ -264,11 +258,12 @@ constexpr int kUp = 0, kDown = 1, kUpBwd = 2, kWgrad = 3;
 // x mod GROUP_M of each group (its A rows stay in its L2).
 __device__ __forceinline__ bool find_wgrad_work(const int32_t* __restrict__ poff,
                                                 const int32_t* __restrict__ order, int E, int M, int N,
-                                                int pid, Work& w) {
+                                                Work& w) {
     const int mtn = (M + kBM - 1) / kBM;
     const int ntn = (N + kDownCols - 1) / kDownCols;
     const int per_e = mtn * ntn;
     const int total = E * per_e;
+    const int pid = blockIdx.x;
     if (pid >= total) return false;
     const int e = order[pid / per_e];
     const int local = pid % per_e;
@@ -326,552 +321,438 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     static_assert(F8 ? 3 * NL <= 2 * (KS - 1) * NM : 3 * NL <= (KS - 1) * NM,
                   "the refill spreads one load per 3 MFMAs (fp8: two per 3)");
     __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE_BYTES];
-    // The tile prefix and offsets tables, built once per workgroup.
-    __shared__ int s_tab[2 * (MOE_MAX_EXPERTS + 1)];
-    int* const s_prefix = s_tab;
-    int* const s_off = s_tab + MOE_MAX_EXPERTS + 1;
+    // The tile prefix and offsets tables live in stage 0 until the first load.
+    int* const s_prefix = reinterpret_cast<int*>(smem);
+    int* const s_off = s_prefix + MOE_MAX_EXPERTS + 1;
 
-    // Persistent: workgroup b runs work ids b, b + gridDim.x, ... (a
-    // launch of one workgroup per id runs one each).  gridDim.x is a
-    // multiple of the XCD count, so every id runs on the XCD it would have
-    // been dealt to, and each XCD still walks one contiguous range of tiles.
-    const int n_tiles = (N + BN_OUT - 1) / BN_OUT;
-    // (K / BK: K slices of 128 bytes, for both element sizes; GEMM1 never
-    // splits: its epilogue is not linear in the partial sums)
-    const int split_slots = GATEUP ? 0 : slots;
-    int n_ids = static_cast<int>(gridDim.x);
-    if (!WG) {
+    Work work;
+    if (WG) {
+        // (K is the operands' row stride here; offsets are the padded
+        // offsets and sorted_assign the expert order, heaviest first)
+        if (!find_wgrad_work(offsets, sorted_assign, E, M, N, work)) return;
+    } else {
         build_tile_prefix(offsets, E, TM, s_prefix, s_off);
-        n_ids = work_ids(s_prefix, E, n_tiles, K / BK, split_slots);
+        const int n_tiles = (N + BN_OUT - 1) / BN_OUT;
+        // (GEMM1 never splits: its epilogue is not linear in the partial sums)
+        if (!find_work(s_off, E, TM, n_tiles, s_prefix, K / BK, GATEUP ? 0 : slots, work)) return;
+        // (K / BK: K slices of 128 bytes, for both element sizes)
     }
-    // The fp8 forward GEMM1 prefetches the next tile's first K slice during
-    // this tile's epilogue (its 256 x 128 output is staged in ring stage 1,
-    // the slice lands in stage 0), and the next tile's activation row
-    // lookups with it: pf says that the current tile's slice 0 was issued
-    // that way, a_off_pf holds its activation offsets.  (Measured on the
-    // 8192-token, 8-expert layer: fp8 FFN 2.95-3.02 -> 2.58 ms; the same in
-    // bf16 made the FFN 1.5 % slower, 4.78 -> 4.85 ms, so bf16 does not
-    // prefetch.)
-    constexpr bool PF = MODE == kUp && !WIDE && F8;
-    bool pf = false;
-    uint32_t a_off_pf[PF ? LA : 1] = {};
-    for (int wid = blockIdx.x; wid < n_ids; wid += gridDim.x) {
-        Work work;
-        if (WG) {
-            // (K is the operands' row stride here; offsets are the padded
-            // offsets and sorted_assign the expert order, heaviest first)
-            if (!find_wgrad_work(offsets, sorted_assign, E, M, N, wid, work)) continue;
-        } else {
-            if (!find_work(s_off, E, TM, n_tiles, s_prefix, K / BK, split_slots, wid, work)) continue;
+    const Tile tile = work.t;
+    __syncthreads();  // every lookup is done before the loads overwrite the table
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1;
+    const int wn = wave & 1;
+    const int n0 = tile.nt * BN_OUT;
+    const int lrow = lane >> 3;
+    const int lslot = lane & 7;
+
+    // Loads: wave w fills activation rows w*64 .. +64 and weight rows
+    // w*64 .. +64 of a stage; load j covers 8 rows, lane -> (row lrow, LDS
+    // slot lslot), and the slot receives global chunk lslot ^ swizzle(row).
+    // Operand rows are addressed as a uniform base plus 32-bit byte offsets
+    // (one expert's weights stay below 4 GiB), except gathered activation
+    // rows of an x of 2^31 elements or more (WIDE), which take 64-bit
+    // addresses.
+    static_assert(GATHER || !WIDE, "only gathered rows need 64-bit addresses");
+    const char* a_src[WIDE ? LA : 1];
+    uint32_t a_off[WIDE ? 1 : LA];
+    const char* const Ab = reinterpret_cast<const char*>(A);
+    const int64_t RB = static_cast<int64_t>(K) * EB;  // bytes per operand row
+    // (the K range [work.kb, work.kb + work.nkl) of 128-byte slices is folded into the bases)
+    const char* const a_base =
+        uniform_ptr((GATHER ? Ab : Ab + static_cast<int64_t>(tile.row0) * RB) + work.kb * 128);
+    // (gathered rows need a lookup in sorted_assign: called after the first
+    // weight loads are on their way)
+    auto setup_a = [&]() {
+#pragma unroll
+        for (int j = 0; j < LA; ++j) {
+            const int r = wave * 64 + j * 8 + lrow;
+            const int chunk = lslot ^ slot_swizzle(r);
+            int pos = tile.row0 + r;
+            if (pos >= tile.row1) pos = tile.row1 - 1;
+            if (WIDE)
+                a_src[WIDE ? j : 0] =
+                    Ab + static_cast<int64_t>(sorted_assign[pos] / topk) * RB + work.kb * 128 + chunk * 16;
+            else if (GATHER)
+                a_off[WIDE ? 0 : j] = static_cast<uint32_t>(sorted_assign[pos] / topk) * static_cast<uint32_t>(RB) +
+                                      chunk * 16u;
+            else
+                a_off[WIDE ? 0 : j] = static_cast<uint32_t>(pos - tile.row0) * static_cast<uint32_t>(RB) + chunk * 16u;
         }
-        const Tile tile = work.t;
-        do {  // one tile; "break" ends it
+    };
+    // In GEMM1 the first 128 weight rows are gate rows and the rest up rows,
+    // so each wave's rows come from one matrix.
+    const int rb0 = wave * (TN / 4);
+    const char* const b_base =
+        uniform_ptr(reinterpret_cast<const char*>(GATEUP && rb0 >= TN / 2 ? B1 : B0) +
+                    (WG ? 0 : static_cast<int64_t>(tile.e) * N * RB) + work.kb * 128);
+    uint32_t b_off[LB];
+#pragma unroll
+    for (int j = 0; j < LB; ++j) {
+        const int r = rb0 + j * 8 + lrow;
+        const int chunk = lslot ^ slot_swizzle(r);
+        int n = n0 + (GATEUP && r >= TN / 2 ? r - TN / 2 : r);
+        if (n >= N) n = N - 1;
+        b_off[j] = static_cast<uint32_t>(n) * static_cast<uint32_t>(RB) + chunk * 16u;
+    }
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+    const uint32_t lds_a = lds0 + wave * 64 * ROWB;
+    const uint32_t lds_b = lds0 + SA_BYTES + rb0 * ROWB;
+    // activation load j (< LA) and weight load j (< LB) of slice kt
+    auto dma_a = [&](int j, int kt) {
+        const uint32_t so = static_cast<uint32_t>((kt & 1) * STAGE_BYTES);
+        if (WIDE) lds_dma16(a_src[WIDE ? j : 0] + kt * 128, lds_a + so + j * 8 * ROWB);
+        else lds_dma16_s(a_base + kt * 128, a_off[WIDE ? 0 : j], lds_a + so + j * 8 * ROWB);
+    };
+    auto dma_b = [&](int j, int kt) {
+        const uint32_t so = static_cast<uint32_t>((kt & 1) * STAGE_BYTES);
+        lds_dma16_s(b_base + kt * 128, b_off[j], lds_b + so + j * 8 * ROWB);
+    };
+    // load q (< NL) of slice kt, in the GEMM's load order
+    auto dma = [&](int q, int kt) {
+        const bool a_op = A_FIRST ? q < LA : q >= LB;
+        if (a_op) dma_a(A_FIRST ? q : q - LB, kt);
+        else dma_b(A_FIRST ? q - LA : q, kt);
+    };
 
-            // An opaque zero, produced anew in every tile: the per-lane values below
-            // derive from it, so the compiler recomputes them per tile instead of
-            // keeping them live (in registers the K loop needs) across the tile loop.
-            int zero;
-            asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
-            const int tid = static_cast<int>(threadIdx.x) + zero;
-            const int lane = tid & 63;
-            const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-            const int wm = wave >> 1;
-            const int wn = wave & 1;
-            const int n0 = tile.nt * BN_OUT;
-            const int lrow = lane >> 3;
-            const int lslot = lane & 7;
+    f32x16_t acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-            // Loads: wave w fills activation rows w*64 .. +64 and weight rows
-            // w*64 .. +64 of a stage; load j covers 8 rows, lane -> (row lrow, LDS
-            // slot lslot), and the slot receives global chunk lslot ^ swizzle(row).
-            // Operand rows are addressed as a uniform base plus 32-bit byte offsets
-            // (one expert's weights stay below 4 GiB), except gathered activation
-            // rows of an x of 2^31 elements or more (WIDE), which take 64-bit
-            // addresses.
-            static_assert(GATHER || !WIDE, "only gathered rows need 64-bit addresses");
-            const char* a_src[WIDE ? LA : 1];
-            uint32_t a_off[WIDE ? 1 : LA];
-            const char* const Ab = reinterpret_cast<const char*>(A);
-            const int64_t RB = static_cast<int64_t>(K) * EB;  // bytes per operand row
-            // (the K range [work.kb, work.kb + work.nkl) of 128-byte slices is folded into the bases)
-            const char* const a_base =
-                uniform_ptr((GATHER ? Ab : Ab + static_cast<int64_t>(tile.row0) * RB) + work.kb * 128);
-            // (gathered rows need a lookup in sorted_assign: called after the first
-            // weight loads are on their way)
-            auto setup_a = [&]() {
+    // Fragment reads.  A 32-row block starts at a multiple of 32 rows, so the
+    // slot swizzle of the lane's row (lane & 31 within the block) is the same
+    // in every block: one byte offset per K step serves all blocks.
+    const int khalf = lane >> 5;
+    const int l32 = lane & 31;
+    uint32_t foff[KS];
 #pragma unroll
-                for (int j = 0; j < LA; ++j) {
-                    const int r = wave * 64 + j * 8 + lrow;
-                    const int chunk = lslot ^ slot_swizzle(r);
-                    int pos = tile.row0 + r;
-                    if (pos >= tile.row1) pos = tile.row1 - 1;
-                    if (WIDE)
-                        a_src[WIDE ? j : 0] =
-                            Ab + static_cast<int64_t>(sorted_assign[pos] / topk) * RB + work.kb * 128 + chunk * 16;
-                    else if (GATHER)
-                        a_off[WIDE ? 0 : j] = static_cast<uint32_t>(sorted_assign[pos] / topk) * static_cast<uint32_t>(RB) +
-                                              chunk * 16u;
-                    else
-                        a_off[WIDE ? 0 : j] = static_cast<uint32_t>(pos - tile.row0) * static_cast<uint32_t>(RB) + chunk * 16u;
-                }
-            };
-            // In GEMM1 the first 128 weight rows are gate rows and the rest up rows,
-            // so each wave's rows come from one matrix.
-            const int rb0 = wave * (TN / 4);
-            const char* const b_base =
-                uniform_ptr(reinterpret_cast<const char*>(GATEUP && rb0 >= TN / 2 ? B1 : B0) +
-                            (WG ? 0 : static_cast<int64_t>(tile.e) * N * RB) + work.kb * 128);
-            uint32_t b_off[LB];
-#pragma unroll
-            for (int j = 0; j < LB; ++j) {
-                const int r = rb0 + j * 8 + lrow;
-                const int chunk = lslot ^ slot_swizzle(r);
-                int n = n0 + (GATEUP && r >= TN / 2 ? r - TN / 2 : r);
-                if (n >= N) n = N - 1;
-                b_off[j] = static_cast<uint32_t>(n) * static_cast<uint32_t>(RB) + chunk * 16u;
-            }
-            const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
-            const uint32_t lds_a = lds0 + wave * 64 * ROWB;
-            const uint32_t lds_b = lds0 + SA_BYTES + rb0 * ROWB;
-            // activation load j (< LA) and weight load j (< LB) of slice kt
-            auto dma_a = [&](int j, int kt) {
-                const uint32_t so = static_cast<uint32_t>((kt & 1) * STAGE_BYTES);
-                if (WIDE) lds_dma16(a_src[WIDE ? j : 0] + kt * 128, lds_a + so + j * 8 * ROWB);
-                else lds_dma16_s(a_base + kt * 128, a_off[WIDE ? 0 : j], lds_a + so + j * 8 * ROWB);
-            };
-            auto dma_b = [&](int j, int kt) {
-                const uint32_t so = static_cast<uint32_t>((kt & 1) * STAGE_BYTES);
-                lds_dma16_s(b_base + kt * 128, b_off[j], lds_b + so + j * 8 * ROWB);
-            };
-            // load q (< NL) of slice kt, in the GEMM's load order
-            auto dma = [&](int q, int kt) {
-                const bool a_op = A_FIRST ? q < LA : q >= LB;
-                if (a_op) dma_a(A_FIRST ? q : q - LB, kt);
-                else dma_b(A_FIRST ? q - LA : q, kt);
-            };
+    for (int kk = 0; kk < KS; ++kk) foff[kk] = l32 * ROWB + (((2 * kk + khalf) ^ slot_swizzle(l32)) * 16);
+    const char* const sa_w = smem + wm * 128 * ROWB;
+    const char* const sb_w = smem + SA_BYTES;
+    auto b_row0 = [&](int nb) {
+        if (GATEUP) return (nb >> 1) * (TN / 2) + wn * (TN / 4) + (nb & 1) * 32;
+        return wn * (TN / 2) + nb * 32;
+    };
 
-            f32x16_t acc[4][4];
-#pragma unroll
-            for (int a = 0; a < 4; ++a)
-#pragma unroll
-                for (int b = 0; b < 4; ++b)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
-
-            // Fragment reads.  A 32-row block starts at a multiple of 32 rows, so the
-            // slot swizzle of the lane's row (lane & 31 within the block) is the same
-            // in every block: one byte offset per K step serves all blocks.
-            const int khalf = lane >> 5;
-            const int l32 = lane & 31;
-            uint32_t foff[KS];
-#pragma unroll
-            for (int kk = 0; kk < KS; ++kk) foff[kk] = l32 * ROWB + (((2 * kk + khalf) ^ slot_swizzle(l32)) * 16);
-            const char* const sa_w = smem + wm * 128 * ROWB;
-            const char* const sb_w = smem + SA_BYTES;
-            auto b_row0 = [&](int nb) {
-                if (GATEUP) return (nb >> 1) * (TN / 2) + wn * (TN / 4) + (nb & 1) * 32;
-                return wn * (TN / 2) + nb * 32;
-            };
-
-            const int nk = work.nkl;
-            // All fragments of one slice: step kk's activation blocks f[kk][0..3] and
-            // weight blocks f[kk][4..7].
-            bf16x8_t f[F8 ? 1 : KS][NR];
-            // fp8: one MFMA takes 64 K values, 32 bytes of a lane's row: the 16-byte
-            // fragments of steps 2s and 2s + 1 read into one register tuple g[s]
-            // (both operands are laid out alike, so every product pairs the same K
-            // index)
-            i32x8_t g[F8 ? 2 : 1][NR];
-            auto read_frag = [&](int kk, int i, uint32_t so) {
-                const char* base = i < 4 ? sa_w + so + i * 32 * ROWB : sb_w + so + b_row0(i - 4) * ROWB;
-                if constexpr (F8) {
-                    const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(base + foff[2 * kk]);
-                    const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(base + foff[2 * kk + 1]);
-                    g[kk][i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                } else {
-                    f[kk][i] = *reinterpret_cast<const bf16x8_t*>(base + foff[kk]);
-                }
-            };
+    const int nk = work.nkl;
+    // All fragments of one slice: step kk's activation blocks f[kk][0..3] and
+    // weight blocks f[kk][4..7].
+    bf16x8_t f[F8 ? 1 : KS][NR];
+    // fp8: one MFMA takes 64 K values, 32 bytes of a lane's row: the 16-byte
+    // fragments of steps 2s and 2s + 1 read into one register tuple g[s]
+    // (both operands are laid out alike, so every product pairs the same K
+    // index)
+    i32x8_t g[F8 ? 2 : 1][NR];
+    auto read_frag = [&](int kk, int i, uint32_t so) {
+        const char* base = i < 4 ? sa_w + so + i * 32 * ROWB : sb_w + so + b_row0(i - 4) * ROWB;
+        if constexpr (F8) {
+            const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(base + foff[2 * kk]);
+            const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(base + foff[2 * kk + 1]);
+            g[kk][i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        } else {
+            f[kk][i] = *reinterpret_cast<const bf16x8_t*>(base + foff[kk]);
+        }
+    };
 #define MOE_MFMA_BF16(KK, Q)                                                                    \
-            acc[(Q) / 4][(Q) % 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                           \
-                f[KK][4 + (Q) / 4], f[KK][(Q) % 4], acc[(Q) / 4][(Q) % 4], 0, 0, 0)
-            // fp8: step S of a slice runs blocks (S & 1) * 8 .. + 8 of fp8 K step S >> 1
+    acc[(Q) / 4][(Q) % 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                           \
+        f[KK][4 + (Q) / 4], f[KK][(Q) % 4], acc[(Q) / 4][(Q) % 4], 0, 0, 0)
+    // fp8: step S of a slice runs blocks (S & 1) * 8 .. + 8 of fp8 K step S >> 1
 #define MOE_MFMA_F8(S, J)                                                                       \
-            acc[(((S) & 1) * 8 + (J)) / 4][(((S) & 1) * 8 + (J)) % 4] =                                   \
-                __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                                        \
-                    g[(S) >> 1][4 + (((S) & 1) * 8 + (J)) / 4], g[(S) >> 1][(((S) & 1) * 8 + (J)) % 4],   \
-                    acc[(((S) & 1) * 8 + (J)) / 4][(((S) & 1) * 8 + (J)) % 4], 0, 0, 0, 0, 0, 0)
+    acc[(((S) & 1) * 8 + (J)) / 4][(((S) & 1) * 8 + (J)) % 4] =                                   \
+        __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                                        \
+            g[(S) >> 1][4 + (((S) & 1) * 8 + (J)) / 4], g[(S) >> 1][(((S) & 1) * 8 + (J)) % 4],   \
+            acc[(((S) & 1) * 8 + (J)) / 4][(((S) & 1) * 8 + (J)) % 4], 0, 0, 0, 0, 0, 0)
 #define MOE_MFMA(KK, Q)                                                                         \
-            do {                                                                                        \
-                if constexpr (F8) MOE_MFMA_F8(KK, Q);                                                   \
-                else MOE_MFMA_BF16(KK, Q);                                                              \
-            } while (0)
+    do {                                                                                        \
+        if constexpr (F8) MOE_MFMA_F8(KK, Q);                                                   \
+        else MOE_MFMA_BF16(KK, Q);                                                              \
+    } while (0)
 
-            // Per slice kt (stage kt & 1):
-            //   step 0: its MFMAs, with the reads of steps 1..3; then every wave has
-            //           read the stage, and a barrier frees it;
-            //   steps 1..3: MFMAs, with the loads of slice kt + 2 into the freed
-            //           stage spread one per 3 MFMAs (almost two slices to land);
-            //           before step 3, the wait for slice kt + 1 and the barrier that
-            //           publishes it;
-            //   step 3 also reads slice kt + 1's step-0 fragments.
-            // Loads complete in issue order, so each wait leaves pending exactly the
-            // loads of slice kt + 2 issued before it.
-            // (fp8: MFMAs twice as long, half as many: two loads per 3 MFMAs)
-            auto refill = [&](int step, int q, int kt) {  // MFMA q of step 1..3
-                const int p = (step - 1) * NM + q;
-                const bool issue = F8 ? (p % 3 != 2 && p - p / 3 < NL) : (p % 3 == 0 && p / 3 < NL);
-                if (issue) {
-                    dma(F8 ? p - p / 3 : p / 3, kt + 2);
-                    // keep each load between its MFMAs (the scheduler would
-                    // otherwise gather them into a burst)
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            };
-            // loads issued in steps 1..2
-            constexpr int BEFORE3_ = F8 ? 2 * NM - (2 * NM) / 3 : (2 * NM + 2) / 3;
-            constexpr int BEFORE3 = BEFORE3_ < NL ? BEFORE3_ : NL;
-            // fragments read ahead of a slice: bf16 step 0; fp8 step 0 (a register
-            // pair per block, used by the slice's first two quarter steps)
-            constexpr int KPRE = 1;
-            constexpr int KREAD = F8 ? 2 : KS;  // fragment steps per slice
-            // Prologue: the weight rows of slices 0 and 1 go out first (their
-            // addresses need no lookup), then the activation rows (see above).
-            // Issue order B0 B1 A0 A1: slice 0 has landed when at most the LA loads
-            // of A1 are pending.
-            // (a weight-gradient tile of an expert with no rows has nk = 0: no loads,
-            // and its zero accumulators are stored)
-            if (PF && pf && nk > 0) {
-                // slice 0 landed during the previous tile's epilogue, whose
-                // end waited for every load and synchronised the workgroup
+    // Per slice kt (stage kt & 1):
+    //   step 0: its MFMAs, with the reads of steps 1..3; then every wave has
+    //           read the stage, and a barrier frees it;
+    //   steps 1..3: MFMAs, with the loads of slice kt + 2 into the freed
+    //           stage spread one per 3 MFMAs (almost two slices to land);
+    //           before step 3, the wait for slice kt + 1 and the barrier that
+    //           publishes it;
+    //   step 3 also reads slice kt + 1's step-0 fragments.
+    // Loads complete in issue order, so each wait leaves pending exactly the
+    // loads of slice kt + 2 issued before it.
+    // (fp8: MFMAs twice as long, half as many: two loads per 3 MFMAs)
+    auto refill = [&](int step, int q, int kt) {  // MFMA q of step 1..3
+        const int p = (step - 1) * NM + q;
+        const bool issue = F8 ? (p % 3 != 2 && p - p / 3 < NL) : (p % 3 == 0 && p / 3 < NL);
+        if (issue) {
+            dma(F8 ? p - p / 3 : p / 3, kt + 2);
+            // keep each load between its MFMAs (the scheduler would
+            // otherwise gather them into a burst)
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    // loads issued in steps 1..2
+    constexpr int BEFORE3_ = F8 ? 2 * NM - (2 * NM) / 3 : (2 * NM + 2) / 3;
+    constexpr int BEFORE3 = BEFORE3_ < NL ? BEFORE3_ : NL;
+    // fragments read ahead of a slice: bf16 step 0; fp8 step 0 (a register
+    // pair per block, used by the slice's first two quarter steps)
+    constexpr int KPRE = 1;
+    constexpr int KREAD = F8 ? 2 : KS;  // fragment steps per slice
+    // Prologue: the weight rows of slices 0 and 1 go out first (their
+    // addresses need no lookup), then the activation rows (see above).
+    // Issue order B0 B1 A0 A1: slice 0 has landed when at most the LA loads
+    // of A1 are pending.
+    // (a weight-gradient tile of an expert with no rows has nk = 0: no loads,
+    // and its zero accumulators are stored)
+    if (nk > 0) {
 #pragma unroll
-                for (int j = 0; j < LA; ++j) a_off[WIDE ? 0 : j] = a_off_pf[PF ? j : 0];
-                if (nk > 1) {
+        for (int j = 0; j < LB; ++j) dma_b(j, 0);
+        if (nk > 1) {
 #pragma unroll
-                    for (int j = 0; j < LB; ++j) dma_b(j, 1);
+            for (int j = 0; j < LB; ++j) dma_b(j, 1);
+        }
+        setup_a();
 #pragma unroll
-                    for (int j = 0; j < LA; ++j) dma_a(j, 1);
-                }
+        for (int j = 0; j < LA; ++j) dma_a(j, 0);
+        if (nk > 1) {
 #pragma unroll
-                for (int i = 0; i < NR; ++i) read_frag(0, i, 0);
-                __builtin_amdgcn_sched_barrier(0);
-            } else if (nk > 0) {
+            for (int j = 0; j < LA; ++j) dma_a(j, 1);
+            wait_vmcnt_lgkm0<LA>();
+        } else {
+            wait_vmcnt_lgkm0<0>();
+        }
+        barrier_lds();
 #pragma unroll
-                for (int j = 0; j < LB; ++j) dma_b(j, 0);
-                if (nk > 1) {
+        for (int i = 0; i < NR; ++i) read_frag(0, i, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // One slice; MORE (a compile-time flag, so that the refills need no
+    // branches) says that slice kt + 2 exists: true for all but the last two.
+    auto slice = [&](int kt, auto more_c) {
+        constexpr bool MORE = decltype(more_c)::value;
+        const uint32_t so = static_cast<uint32_t>((kt & 1) * STAGE_BYTES);
+        const uint32_t nso = static_cast<uint32_t>(((kt + 1) & 1) * STAGE_BYTES);
+        // step 0: the reads of the remaining steps (bf16: 24 over 16 MFMAs;
+        // fp8: 16 over 8)
 #pragma unroll
-                    for (int j = 0; j < LB; ++j) dma_b(j, 1);
-                }
-                setup_a();
+        for (int kk = KPRE; kk < KREAD; ++kk)
 #pragma unroll
-                for (int j = 0; j < LA; ++j) dma_a(j, 0);
-                if (nk > 1) {
+            for (int i = 0; i < NR; ++i) read_frag(kk, i, so);
 #pragma unroll
-                    for (int j = 0; j < LA; ++j) dma_a(j, 1);
-                    wait_vmcnt_lgkm0<LA>();
-                } else {
-                    wait_vmcnt_lgkm0<0>();
-                }
-                barrier_lds();
+        for (int q = 0; q < NM; ++q) MOE_MFMA(0, q);
 #pragma unroll
-                for (int i = 0; i < NR; ++i) read_frag(0, i, 0);
-                __builtin_amdgcn_sched_barrier(0);
+        for (int i = 0; i < NR; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+#pragma unroll
+        for (int i = NR; i < NM; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt_lgkm0<63>();
+        barrier_lds();
+        // steps 1 and 2
+#pragma unroll
+        for (int step = 1; step <= 2; ++step) {
+#pragma unroll
+            for (int q = 0; q < NM; ++q) {
+                if (step == 1) MOE_MFMA(1, q);
+                else MOE_MFMA(2, q);
+                if (MORE) refill(step, q, kt);
             }
-
-            // One slice; MORE (a compile-time flag, so that the refills need no
-            // branches) says that slice kt + 2 exists: true for all but the last two.
-            auto slice = [&](int kt, auto more_c) {
-                constexpr bool MORE = decltype(more_c)::value;
-                const uint32_t so = static_cast<uint32_t>((kt & 1) * STAGE_BYTES);
-                const uint32_t nso = static_cast<uint32_t>(((kt + 1) & 1) * STAGE_BYTES);
-                // step 0: the reads of the remaining steps (bf16: 24 over 16 MFMAs;
-                // fp8: 16 over 8)
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (MORE) {
+            wait_vmcnt<BEFORE3>();
+            barrier_lds();
+        } else if (kt + 1 < nk) {
+            wait_vmcnt<0>();
+            barrier_lds();
+        }
+        // step 3 (after the last slice the reads fetch a stale, in-bounds
+        // stage whose values are never used)
 #pragma unroll
-                for (int kk = KPRE; kk < KREAD; ++kk)
-#pragma unroll
-                    for (int i = 0; i < NR; ++i) read_frag(kk, i, so);
-#pragma unroll
-                for (int q = 0; q < NM; ++q) MOE_MFMA(0, q);
-#pragma unroll
-                for (int i = 0; i < NR; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-                }
-#pragma unroll
-                for (int i = NR; i < NM; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-                wait_vmcnt_lgkm0<63>();
-                barrier_lds();
-                // steps 1 and 2
-#pragma unroll
-                for (int step = 1; step <= 2; ++step) {
-#pragma unroll
-                    for (int q = 0; q < NM; ++q) {
-                        if (step == 1) MOE_MFMA(1, q);
-                        else MOE_MFMA(2, q);
-                        if (MORE) refill(step, q, kt);
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-                if (MORE) {
-                    wait_vmcnt<BEFORE3>();
-                    barrier_lds();
-                } else if (kt + 1 < nk) {
-                    wait_vmcnt<0>();
-                    barrier_lds();
-                }
-                // step 3 (after the last slice the reads fetch a stale, in-bounds
-                // stage whose values are never used)
-#pragma unroll
-                for (int q = 0; q < NM; ++q) {
-                    MOE_MFMA(3, q);
-                    if (MORE) refill(3, q, kt);
-                    if (F8) {
-                        read_frag(0, q, nso);  // two 16-byte reads
-                    } else if ((q & 1) && (q >> 1) < NR) {
-                        read_frag(0, q >> 1, nso);
-                    }
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            };
-            int kt = 0;
-            for (; kt + 2 < nk; ++kt) slice(kt, std::true_type{});
-            for (; kt < nk; ++kt) slice(kt, std::false_type{});
+        for (int q = 0; q < NM; ++q) {
+            MOE_MFMA(3, q);
+            if (MORE) refill(3, q, kt);
+            if (F8) {
+                read_frag(0, q, nso);  // two 16-byte reads
+            } else if ((q & 1) && (q >> 1) < NR) {
+                read_frag(0, q >> 1, nso);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    int kt = 0;
+    for (; kt + 2 < nk; ++kt) slice(kt, std::true_type{});
+    for (; kt < nk; ++kt) slice(kt, std::false_type{});
 #undef MOE_MFMA
 #undef MOE_MFMA_F8
 #undef MOE_MFMA_BF16
 
-            // fp8: apply the row and column scales, 2^(a_exp[row] + b_exp[col]),
-            // exactly (before a split partial is stored, which then sums scaled
-            // values: the same result, since the scaling is by a power of two)
-            if constexpr (F8) {
-                int ea[4];
+    // fp8: apply the row and column scales, 2^(a_exp[row] + b_exp[col]),
+    // exactly (before a split partial is stored, which then sums scaled
+    // values: the same result, since the scaling is by a power of two)
+    if constexpr (F8) {
+        int ea[4];
 #pragma unroll
-                for (int mb = 0; mb < 4; ++mb) {
-                    int pos = tile.row0 + wm * 128 + mb * 32 + l32;
-                    if (pos >= tile.row1) pos = tile.row1 - 1;
-                    ea[mb] = a_exp[GATHER ? sorted_assign[pos] / topk : pos];
-                }
+        for (int mb = 0; mb < 4; ++mb) {
+            int pos = tile.row0 + wm * 128 + mb * 32 + l32;
+            if (pos >= tile.row1) pos = tile.row1 - 1;
+            ea[mb] = a_exp[GATHER ? sorted_assign[pos] / topk : pos];
+        }
 #pragma unroll
-                for (int nb = 0; nb < 4; ++nb)
+        for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const int col = GATEUP ? n0 + wn * 64 + (nb & 1) * 32 + 8 * g + 4 * khalf
-                                               : n0 + wn * 128 + nb * 32 + 8 * g + 4 * khalf;
-                        const int32_t* be = (GATEUP && nb >= 2) ? b_exp1 : b_exp0;
-                        i32x4_t eb = {0, 0, 0, 0};
-                        if (col < N) eb = *reinterpret_cast<const i32x4_t*>(be + static_cast<int64_t>(tile.e) * N + col);
-#pragma unroll
-                        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-                            for (int i = 0; i < 4; ++i)
-                                acc[nb][mb][4 * g + i] = __builtin_amdgcn_ldexpf(acc[nb][mb][4 * g + i], ea[mb] + eb[i]);
-                    }
-            }
-
-            // A split K range: the fp32 partial sums go to slot work.j, register by
-            // register (register r of thread t at (j * 256 + r) * 256 + t).
-            if (!GATEUP && work.j >= 0) {
-                float* const dst = const_cast<float*>(uniform_ptr(part + static_cast<int64_t>(work.j) * 256 * 256));
+            for (int g = 0; g < 4; ++g) {
+                const int col = GATEUP ? n0 + wn * 64 + (nb & 1) * 32 + 8 * g + 4 * khalf
+                                       : n0 + wn * 128 + nb * 32 + 8 * g + 4 * khalf;
+                const int32_t* be = (GATEUP && nb >= 2) ? b_exp1 : b_exp0;
+                i32x4_t eb = {0, 0, 0, 0};
+                if (col < N) eb = *reinterpret_cast<const i32x4_t*>(be + static_cast<int64_t>(tile.e) * N + col);
 #pragma unroll
                 for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-                    for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) dst[((nb * 4 + mb) * 16 + i) * 256 + tid] = acc[nb][mb][i];
-                break;
+                    for (int i = 0; i < 4; ++i)
+                        acc[nb][mb][4 * g + i] = __builtin_amdgcn_ldexpf(acc[nb][mb][4 * g + i], ea[mb] + eb[i]);
             }
+    }
 
-            // Epilogue through LDS.  Block (nb, mb): lane owns tile row wm*128 +
-            // mb*32 + (lane & 31) and, for g = 0..3, the 4 output columns 8g +
-            // 4*(lane >> 5) + 0..3 of the block (registers 4g .. 4g+3).  The ring is
-            // free once every wave has left the loop: the output tile is staged there
-            // row-major, 16-byte chunk ch of row r at chunk ch ^ (r mod CPR), which
-            // spreads the 8-byte writes of 32 rows over the banks, and then written
-            // out in whole 16-byte chunks, consecutive lanes on consecutive chunks of
-            // a row, so that every store instruction covers whole 128-byte lines
-            // (8-byte stores into 32 rows each took 5-12 us per tile, measured).
-            constexpr int OUTC = GATEUP ? TN / 2 : TN;  // output columns of a tile
-            constexpr int CPR = OUTC / 8;               // 16-byte chunks per row
-            constexpr int ROWO = OUTC * 2;              // bytes per staged row
-            static_assert(TM * ROWO <= 2 * STAGE_BYTES, "the staged tile must fit the ring");
-            static_assert(!PF || TM * ROWO <= STAGE_BYTES, "with the prefetch, the staged tile takes stage 1 only");
-            char* const sout = smem + (PF ? STAGE_BYTES : 0);
-            wait_vmcnt_lgkm0<0>();
-            barrier_lds();
-            // The prefetch: the next tile's weight rows of slice 0 and its
-            // activation row lookups go out now; the activation loads, which
-            // need the lookups, go out after the staging below.
-            Tile nt_pf{};
-            const char* na_base = nullptr;
-            if constexpr (PF) {
-                Work nw;
-                const int nid = wid + static_cast<int>(gridDim.x);
-                pf = nid < n_ids && find_work(s_off, E, TM, n_tiles, s_prefix, K / BK, split_slots, nid, nw);
-                if (pf) {
-                    nt_pf = nw.t;
-                    // the lane's load coordinates, recomputed from a fresh
-                    // opaque zero so that none of them stays live across the
-                    // K loop above
-                    int z;
-                    asm volatile("v_mov_b32 %0, 0" : "=v"(z));
-                    const int ptid = static_cast<int>(threadIdx.x) + z;
-                    const int pwave = __builtin_amdgcn_readfirstlane(ptid >> 6);
-                    const int prow = (ptid & 63) >> 3;
-                    const int pslot = ptid & 7;
-                    const int prb0 = pwave * (TN / 4);
-                    const uint32_t plds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
-                    const char* const nb_base = uniform_ptr(reinterpret_cast<const char*>(prb0 >= TN / 2 ? B1 : B0) +
-                                                            static_cast<int64_t>(nt_pf.e) * N * RB);
-                    const int nn0 = nt_pf.nt * BN_OUT;
+    // A split K range: the fp32 partial sums go to slot work.j, register by
+    // register (register r of thread t at (j * 256 + r) * 256 + t).
+    if (!GATEUP && work.j >= 0) {
+        float* const dst = const_cast<float*>(uniform_ptr(part + static_cast<int64_t>(work.j) * 256 * 256));
 #pragma unroll
-                    for (int j = 0; j < LB; ++j) {
-                        const int r = prb0 + j * 8 + prow;
-                        const int chunk = pslot ^ slot_swizzle(r);
-                        int n = nn0 + (r >= TN / 2 ? r - TN / 2 : r);
-                        if (n >= N) n = N - 1;
-                        lds_dma16_s(nb_base, static_cast<uint32_t>(n) * static_cast<uint32_t>(RB) + chunk * 16u,
-                                    plds0 + SA_BYTES + prb0 * ROWB + j * 8 * ROWB);
-                    }
-                    na_base = uniform_ptr(GATHER ? Ab : Ab + static_cast<int64_t>(nt_pf.row0) * RB);
+        for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-                    for (int j = 0; j < LA; ++j) {
-                        const int r = pwave * 64 + j * 8 + prow;
-                        const int chunk = pslot ^ slot_swizzle(r);
-                        int pos = nt_pf.row0 + r;
-                        if (pos >= nt_pf.row1) pos = nt_pf.row1 - 1;
-                        const uint32_t row = GATHER ? static_cast<uint32_t>(sorted_assign[pos] / topk)
-                                                    : static_cast<uint32_t>(pos - nt_pf.row0);
-                        a_off_pf[PF ? j : 0] = row * static_cast<uint32_t>(RB) + chunk * 16u;
-                    }
-                } else {
-                    // (assigned on every path, so that the previous values
-                    // are dead after the prologue that reads them)
+            for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-                    for (int j = 0; j < LA; ++j) a_off_pf[PF ? j : 0] = 0;
-                }
-            }
-            auto prefetch_a = [&]() {
-                if constexpr (PF) {
-                    if (pf) {
-#pragma unroll
-                        for (int j = 0; j < LA; ++j)
-                            lds_dma16_s(na_base, a_off_pf[PF ? j : 0],
-                                        __builtin_amdgcn_readfirstlane(lds_addr(smem)) + wave * 64 * ROWB + j * 8 * ROWB);
-                    }
-                }
-            };
-            // stage the tile's output (h = silu(gate) * up for the gate/up modes, the
-            // accumulators otherwise) and store it to out (row stride ldo)
-            auto stage_and_store = [&](bf16_t* __restrict__ out, int64_t ldo) {
-#pragma unroll
-                for (int mb = 0; mb < 4; ++mb) {
-                    const int r = wm * 128 + mb * 32 + l32;
-                    char* const srow = sout + r * ROWO + khalf * 8;
-                    const int sw = r & (CPR - 1);
-#pragma unroll
-                    for (int nb = 0; nb < (GATEUP ? 2 : 4); ++nb)
-#pragma unroll
-                        for (int g = 0; g < 4; ++g) {
-                            uint2 o;
-                            if (GATEUP) {
-                                float v[4];
-#pragma unroll
-                                for (int i = 0; i < 4; ++i) v[i] = silu_mul_fast(acc[nb][mb][4 * g + i], acc[nb + 2][mb][4 * g + i]);
-                                o = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-                            } else {
-                                const f32x16_t& a = acc[nb][mb];
-                                o = make_uint2(pack_bf16x2(a[4 * g], a[4 * g + 1]), pack_bf16x2(a[4 * g + 2], a[4 * g + 3]));
-                            }
-                            const int ch = (GATEUP ? wn * 8 : wn * 16) + nb * 4 + g;
-                            *reinterpret_cast<uint2*>(srow + ((ch ^ sw) * 16)) = o;
-                        }
-                }
-                prefetch_a();
-                __syncthreads();
-#pragma unroll 4
-                for (int idx = tid; idx < TM * CPR; idx += 256) {
-                    const int r = idx / CPR;
-                    const int ch = idx % CPR;
-                    const int pos = tile.row0 + r;
-                    const int col = n0 + ch * 8;
-                    if (pos >= tile.row1 || col >= N) continue;
-                    const uint4 v = *reinterpret_cast<const uint4*>(sout + r * ROWO + ((ch ^ (r & (CPR - 1))) * 16));
-                    *reinterpret_cast<uint4*>(out + static_cast<int64_t>(pos) * ldo + col) = v;
-                }
-            };
+                for (int i = 0; i < 16; ++i) dst[((nb * 4 + mb) * 16 + i) * 256 + tid] = acc[nb][mb][i];
+        return;
+    }
 
-            if (MODE == kUpBwd) {
-                // The backward of SwiGLU from the recomputed gate u and up v and the
-                // incoming dh (aux, [rows, f]): with sg = sigmoid(u), s = u sg,
-                // du = dh v sg (1 + u (1 - sg)) and dv = dh s.  Pass 1 stages du and
-                // dv side by side (a 256-column row: chunks 0..15 du, 16..31 dv) and
-                // stores them to C = [rows, 2f] (du in columns [0, f), dv in [f, 2f));
-                // pass 2 stores h = s v to C2 (the down projection's weight gradient
-                // reads it).
-                constexpr int CPR2 = 32;
-                constexpr int ROWO2 = CPR2 * 16;
-                static_assert(TM * ROWO2 <= 2 * STAGE_BYTES, "the staged du/dv tile must fit the ring");
+    // Epilogue through LDS.  Block (nb, mb): lane owns tile row wm*128 +
+    // mb*32 + (lane & 31) and, for g = 0..3, the 4 output columns 8g +
+    // 4*(lane >> 5) + 0..3 of the block (registers 4g .. 4g+3).  The ring is
+    // free once every wave has left the loop: the output tile is staged there
+    // row-major, 16-byte chunk ch of row r at chunk ch ^ (r mod CPR), which
+    // spreads the 8-byte writes of 32 rows over the banks, and then written
+    // out in whole 16-byte chunks, consecutive lanes on consecutive chunks of
+    // a row, so that every store instruction covers whole 128-byte lines
+    // (8-byte stores into 32 rows each took 5-12 us per tile, measured).
+    constexpr int OUTC = GATEUP ? TN / 2 : TN;  // output columns of a tile
+    constexpr int CPR = OUTC / 8;               // 16-byte chunks per row
+    constexpr int ROWO = OUTC * 2;              // bytes per staged row
+    static_assert(TM * ROWO <= 2 * STAGE_BYTES, "the staged tile must fit the ring");
+    wait_vmcnt_lgkm0<0>();
+    barrier_lds();
+    // stage the tile's output (h = silu(gate) * up for the gate/up modes, the
+    // accumulators otherwise) and store it to out (row stride ldo)
+    auto stage_and_store = [&](bf16_t* __restrict__ out, int64_t ldo) {
 #pragma unroll
-                for (int mb = 0; mb < 4; ++mb) {
-                    const int r = wm * 128 + mb * 32 + l32;
-                    const int pos = tile.row0 + r;
-                    char* const srow = smem + r * ROWO2 + khalf * 8;
-                    const int sw = r & (CPR2 - 1);
+        for (int mb = 0; mb < 4; ++mb) {
+            const int r = wm * 128 + mb * 32 + l32;
+            char* const srow = smem + r * ROWO + khalf * 8;
+            const int sw = r & (CPR - 1);
 #pragma unroll
-                    for (int nb = 0; nb < 2; ++nb)
+            for (int nb = 0; nb < (GATEUP ? 2 : 4); ++nb)
 #pragma unroll
-                        for (int g = 0; g < 4; ++g) {
-                            const int col = n0 + wn * 64 + nb * 32 + 8 * g + 4 * khalf;
-                            uint2 dhw = make_uint2(0u, 0u);
-                            if (pos < tile.row1 && col < N)
-                                dhw = *reinterpret_cast<const uint2*>(aux + static_cast<int64_t>(pos) * N + col);
-                            const float dh[4] = {lo_bf16(dhw.x), hi_bf16(dhw.x), lo_bf16(dhw.y), hi_bf16(dhw.y)};
-                            float du[4], dv[4];
+                for (int g = 0; g < 4; ++g) {
+                    uint2 o;
+                    if (GATEUP) {
+                        float v[4];
 #pragma unroll
-                            for (int i = 0; i < 4; ++i) {
-                                const float u = acc[nb][mb][4 * g + i];
-                                const float v = acc[nb + 2][mb][4 * g + i];
-                                const float sg = sigmoid_fast(u);
-                                const float su = u * sg;
-                                du[i] = dh[i] * v * sg * (1.f + u * (1.f - sg));
-                                dv[i] = dh[i] * su;
-                            }
-                            const int ch = wn * 8 + nb * 4 + g;
-                            *reinterpret_cast<uint2*>(srow + ((ch ^ sw) * 16)) =
-                                make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
-                            *reinterpret_cast<uint2*>(srow + (((ch + 16) ^ sw) * 16)) =
-                                make_uint2(pack_bf16x2(dv[0], dv[1]), pack_bf16x2(dv[2], dv[3]));
-                        }
+                        for (int i = 0; i < 4; ++i) v[i] = silu_mul_fast(acc[nb][mb][4 * g + i], acc[nb + 2][mb][4 * g + i]);
+                        o = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                    } else {
+                        const f32x16_t& a = acc[nb][mb];
+                        o = make_uint2(pack_bf16x2(a[4 * g], a[4 * g + 1]), pack_bf16x2(a[4 * g + 2], a[4 * g + 3]));
+                    }
+                    const int ch = (GATEUP ? wn * 8 : wn * 16) + nb * 4 + g;
+                    *reinterpret_cast<uint2*>(srow + ((ch ^ sw) * 16)) = o;
                 }
-                __syncthreads();
-#pragma unroll 4
-                for (int idx = tid; idx < TM * CPR2; idx += 256) {
-                    const int r = idx / CPR2;
-                    const int ch = idx % CPR2;
-                    const int pos = tile.row0 + r;
-                    const int col = n0 + (ch & 15) * 8;
-                    if (pos >= tile.row1 || col >= N) continue;
-                    const uint4 v = *reinterpret_cast<const uint4*>(smem + r * ROWO2 + ((ch ^ (r & (CPR2 - 1))) * 16));
-                    *reinterpret_cast<uint4*>(C + static_cast<int64_t>(pos) * (2 * N) + (ch < 16 ? col : N + col)) = v;
-                }
-                __syncthreads();
-                stage_and_store(C2, N);
-            } else if (WG) {
-                stage_and_store(C + static_cast<int64_t>(tile.e) * M * N, N);
-            } else {
-                stage_and_store(C, N);
-            }
-        } while (false);
-        // Before the next tile's loads refill the ring: every wave has read its
-        // staged output, and this wave's stores have completed (loads and
-        // stores share one counter, so the next tile's counted waits must not
-        // find stores in flight).
-        wait_vmcnt_lgkm0<0>();
+        }
         __syncthreads();
+#pragma unroll 4
+        for (int idx = tid; idx < TM * CPR; idx += 256) {
+            const int r = idx / CPR;
+            const int ch = idx % CPR;
+            const int pos = tile.row0 + r;
+            const int col = n0 + ch * 8;
+            if (pos >= tile.row1 || col >= N) continue;
+            const uint4 v = *reinterpret_cast<const uint4*>(smem + r * ROWO + ((ch ^ (r & (CPR - 1))) * 16));
+            *reinterpret_cast<uint4*>(out + static_cast<int64_t>(pos) * ldo + col) = v;
+        }
+    };
+
+    if (MODE == kUpBwd) {
+        // The backward of SwiGLU from the recomputed gate u and up v and the
+        // incoming dh (aux, [rows, f]): with sg = sigmoid(u), s = u sg,
+        // du = dh v sg (1 + u (1 - sg)) and dv = dh s.  Pass 1 stages du and
+        // dv side by side (a 256-column row: chunks 0..15 du, 16..31 dv) and
+        // stores them to C = [rows, 2f] (du in columns [0, f), dv in [f, 2f));
+        // pass 2 stores h = s v to C2 (the down projection's weight gradient
+        // reads it).
+        constexpr int CPR2 = 32;
+        constexpr int ROWO2 = CPR2 * 16;
+        static_assert(TM * ROWO2 <= 2 * STAGE_BYTES, "the staged du/dv tile must fit the ring");
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+            const int r = wm * 128 + mb * 32 + l32;
+            const int pos = tile.row0 + r;
+            char* const srow = smem + r * ROWO2 + khalf * 8;
+            const int sw = r & (CPR2 - 1);
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int col = n0 + wn * 64 + nb * 32 + 8 * g + 4 * khalf;
+                    uint2 dhw = make_uint2(0u, 0u);
+                    if (pos < tile.row1 && col < N)
+                        dhw = *reinterpret_cast<const uint2*>(aux + static_cast<int64_t>(pos) * N + col);
+                    const float dh[4] = {lo_bf16(dhw.x), hi_bf16(dhw.x), lo_bf16(dhw.y), hi_bf16(dhw.y)};
+                    float du[4], dv[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float u = acc[nb][mb][4 * g + i];
+                        const float v = acc[nb + 2][mb][4 * g + i];
+                        const float sg = sigmoid_fast(u);
+                        const float su = u * sg;
+                        du[i] = dh[i] * v * sg * (1.f + u * (1.f - sg));
+                        dv[i] = dh[i] * su;
+                    }
+                    const int ch = wn * 8 + nb * 4 + g;
+                    *reinterpret_cast<uint2*>(srow + ((ch ^ sw) * 16)) =
+                        make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
+                    *reinterpret_cast<uint2*>(srow + (((ch + 16) ^ sw) * 16)) =
+                        make_uint2(pack_bf16x2(dv[0], dv[1]), pack_bf16x2(dv[2], dv[3]));
+                }
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int idx = tid; idx < TM * CPR2; idx += 256) {
+            const int r = idx / CPR2;
+            const int ch = idx % CPR2;
+            const int pos = tile.row0 + r;
+            const int col = n0 + (ch & 15) * 8;
+            if (pos >= tile.row1 || col >= N) continue;
+            const uint4 v = *reinterpret_cast<const uint4*>(smem + r * ROWO2 + ((ch ^ (r & (CPR2 - 1))) * 16));
+            *reinterpret_cast<uint4*>(C + static_cast<int64_t>(pos) * (2 * N) + (ch < 16 ? col : N + col)) = v;
+        }
+        __syncthreads();
+        stage_and_store(C2, N);
+    } else if (WG) {
+        stage_and_store(C + static_cast<int64_t>(tile.e) * M * N, N);
+    } else {
+        stage_and_store(C, N);
     }
 }
 
@@ -1045,15 +926,6 @@ int resident_slots() {
     return v;
 }
 
-// Grid of a queue-row GEMM launch that covers `ids` work ids: one
-// persistent workgroup per CU (the kernel's LDS allows one), a multiple of
-// the XCD count, or one workgroup per id when there are fewer ids.
-unsigned gemm_grid(unsigned ids) {
-    const int slots = resident_slots();
-    if (slots < NUM_XCD) return ids;
-    return std::min(ids, static_cast<unsigned>(slots / NUM_XCD * NUM_XCD));
-}
-
 hipError_t launch_expert_ffn(const moe_problem_t& p, const void* x_perm, const void* x,
                              const int32_t* sorted_assign, const int32_t* offsets,
                              const void* w_gate, const void* w_up, const void* w_down,
@@ -1065,21 +937,21 @@ hipError_t launch_expert_ffn(const moe_problem_t& p, const void* x_perm, const v
         const bf16_t* a = static_cast<const bf16_t*>(gather ? x : x_perm);
         const unsigned g1 = grid_for(n, p.E, kBM, static_cast<int>(ceil_div(p.f, kGateUpCols)));
         if (gather && p.T * p.d >= (int64_t{1} << 31))
-            grouped_gemm_bf16_kernel<kUp, true, true><<<gemm_grid(g1), 256, 0, s>>>(
+            grouped_gemm_bf16_kernel<kUp, true, true><<<g1, 256, 0, s>>>(
                 a, sorted_assign, p.k, offsets, p.E, static_cast<const bf16_t*>(w_gate),
                 static_cast<const bf16_t*>(w_up), static_cast<bf16_t*>(h), p.f, p.d, 0, nullptr, nullptr, nullptr, 0);
         else if (gather)
-            grouped_gemm_bf16_kernel<kUp, true, false><<<gemm_grid(g1), 256, 0, s>>>(
+            grouped_gemm_bf16_kernel<kUp, true, false><<<g1, 256, 0, s>>>(
                 a, sorted_assign, p.k, offsets, p.E, static_cast<const bf16_t*>(w_gate),
                 static_cast<const bf16_t*>(w_up), static_cast<bf16_t*>(h), p.f, p.d, 0, nullptr, nullptr, nullptr, 0);
         else
-            grouped_gemm_bf16_kernel<kUp, false, false><<<gemm_grid(g1), 256, 0, s>>>(
+            grouped_gemm_bf16_kernel<kUp, false, false><<<g1, 256, 0, s>>>(
                 a, sorted_assign, p.k, offsets, p.E, static_cast<const bf16_t*>(w_gate),
                 static_cast<const bf16_t*>(w_up), static_cast<bf16_t*>(h), p.f, p.d, 0, nullptr, nullptr, nullptr, 0);
         const unsigned g2 = grid_for(n, p.E, kBM, static_cast<int>(ceil_div(p.d, kDownCols)));
         const int slots = ffn_can_split(p) ? resident_slots() : 0;
         float* part = slots > 0 ? reinterpret_cast<float*>(static_cast<char*>(ffn_ws) + ffn_h_bytes(p)) : nullptr;
-        grouped_gemm_bf16_kernel<kDown, false, false><<<gemm_grid(g2 + (slots > 0 ? kSplitWGs : 0)), 256, 0, s>>>(
+        grouped_gemm_bf16_kernel<kDown, false, false><<<g2 + (slots > 0 ? kSplitWGs : 0), 256, 0, s>>>(
             static_cast<const bf16_t*>(h), sorted_assign, p.k, offsets, p.E,
             static_cast<const bf16_t*>(w_down), nullptr, static_cast<bf16_t*>(y_perm), p.d, p.f, slots,
             part, nullptr, nullptr, 0);
@@ -1112,7 +984,7 @@ hipError_t launch_backward_dh(const moe_problem_t& p, const void* dy_perm, const
                               const void* w_down_t, void* dh, hipStream_t s) {
     const int64_t n = p.T * p.k;
     const unsigned g = grid_for(n, p.E, kBM, static_cast<int>(ceil_div(p.f, kDownCols)));
-    grouped_gemm_bf16_kernel<kDown, false, false><<<gemm_grid(g), 256, 0, s>>>(
+    grouped_gemm_bf16_kernel<kDown, false, false><<<g, 256, 0, s>>>(
         static_cast<const bf16_t*>(dy_perm), nullptr, p.k, offsets, p.E,
         static_cast<const bf16_t*>(w_down_t), nullptr, static_cast<bf16_t*>(dh), p.f, p.d, 0, nullptr,
         nullptr, nullptr, 0);
@@ -1127,7 +999,7 @@ hipError_t launch_backward_recompute(const moe_problem_t& p, const void* x, cons
     const int64_t n = p.T * p.k;
     const unsigned g = grid_for(n, p.E, kBM, static_cast<int>(ceil_div(p.f, kGateUpCols)));
     // (the backward's limits keep T * d below 2^31: 32-bit gather offsets)
-    grouped_gemm_bf16_kernel<kUpBwd, true, false><<<gemm_grid(g), 256, 0, s>>>(
+    grouped_gemm_bf16_kernel<kUpBwd, true, false><<<g, 256, 0, s>>>(
         static_cast<const bf16_t*>(x), sorted_assign, p.k, offsets, p.E, static_cast<const bf16_t*>(w_gate),
         static_cast<const bf16_t*>(w_up), static_cast<bf16_t*>(duv), p.f, p.d, 0, nullptr,
         static_cast<const bf16_t*>(dh), static_cast<bf16_t*>(h), 0);
@@ -1142,7 +1014,7 @@ hipError_t launch_backward_dxperm(const moe_problem_t& p, const void* duv, const
     const int64_t n = p.T * p.k;
     const unsigned g = grid_for(n, p.E, kBM, static_cast<int>(ceil_div(p.d, kDownCols)));
     const int slots = (part != nullptr && bwd_can_split(p)) ? resident_slots() : 0;
-    grouped_gemm_bf16_kernel<kDown, false, false><<<gemm_grid(g + (slots > 0 ? kSplitWGs : 0)), 256, 0, s>>>(
+    grouped_gemm_bf16_kernel<kDown, false, false><<<g + (slots > 0 ? kSplitWGs : 0), 256, 0, s>>>(
         static_cast<const bf16_t*>(duv), nullptr, p.k, offsets, p.E, static_cast<const bf16_t*>(w_gu_t),
         nullptr, static_cast<bf16_t*>(dx_perm), p.d, 2 * p.f, slots, part, nullptr, nullptr, 0);
     if (slots > 0)
@@ -1178,7 +1050,7 @@ hipError_t launch_expert_ffn_fp8(const moe_problem_t& p, const void* x_q, const 
                                  float* part, void* y_perm, hipStream_t s) {
     const int64_t n = p.T * p.k;
     const unsigned g1 = grid_for(n, p.E, kBM, static_cast<int>(ceil_div(p.f, kGateUpCols)));
-    grouped_gemm_bf16_kernel<kUp, true, false, true><<<gemm_grid(g1), 256, 0, s>>>(
+    grouped_gemm_bf16_kernel<kUp, true, false, true><<<g1, 256, 0, s>>>(
         static_cast<const bf16_t*>(x_q), sorted_assign, p.k, offsets, p.E, static_cast<const bf16_t*>(wg_q),
         static_cast<const bf16_t*>(wu_q), static_cast<bf16_t*>(h), p.f, p.d, 0, nullptr, nullptr, nullptr, 0,
         x_exp, wg_exp, wu_exp);
@@ -1187,7 +1059,7 @@ hipError_t launch_expert_ffn_fp8(const moe_problem_t& p, const void* x_q, const 
     const unsigned g2 = grid_for(n, p.E, kBM, static_cast<int>(ceil_div(p.d, kDownCols)));
     const int nk2 = p.f / 128;
     const int slots = (part != nullptr && fp8_can_split(p)) ? resident_slots() : 0;
-    grouped_gemm_bf16_kernel<kDown, false, false, true><<<gemm_grid(g2 + (slots > 0 ? kSplitWGs : 0)), 256, 0, s>>>(
+    grouped_gemm_bf16_kernel<kDown, false, false, true><<<g2 + (slots > 0 ? kSplitWGs : 0), 256, 0, s>>>(
         static_cast<const bf16_t*>(h_q), sorted_assign, p.k, offsets, p.E, static_cast<const bf16_t*>(wd_q),
         nullptr, static_cast<bf16_t*>(y_perm), p.d, p.f, slots, part, nullptr, nullptr, 0, h_exp, wd_exp,
         nullptr);
