@@ -87,7 +87,7 @@ ROUTE_CASES = [
     # k <= 8 runs the lane-group top-k: k = E, E not a multiple of 4 (scalar
     # loads), the largest E, and k = 1
     (4096, 8, 8, "ties"), (999, 16, 3, "ties"), (513, 255, 8, "ties"), (300, 256, 8, "zipf"),
-    (100, 7, 1, "ties"), (64, 9, 9, "gauss"),
+    (100, 7, 1, "ties"), (64, 9, 9, "gauss"), (123, 5, 5, "ties"), (5000, 32, 4, "gauss"),
 ]
 
 
@@ -139,7 +139,8 @@ def test_dispatch_f32_rows_and_odd_width():
                                          # 5 and 7 expert blocks (K steps split over the waves)
                                          (100, 64, 3, "bf16"), (513, 128, 40, "bf16"),
                                          (260, 320, 100, "bf16"), (97, 256, 200, "bf16"),
-                                         (33, 1024, 160, "bf16")])
+                                         (33, 1024, 160, "bf16"), (211, 384, 96, "bf16"),
+                                         (77, 192, 190, "bf16")])
 def test_router_logits(T, d, E, dtype):
     p = mi.Problem(T, d, E, min(2, E), 64, dtype)
     x = mi.make_x(p, 5)
