@@ -188,16 +188,20 @@ __global__ __launch_bounds__(256) void router_logits_mfma_kernel(const bf16_t* _
 // the logits do not depend on scheduling.  Row r's 16-byte chunk c sits at
 // slot c ^ ((r >> 1) & 7) of its 128-byte line, which puts the fragment
 // reads of consecutive rows on distinct LDS banks.
-template <int EB>
+//
+// TB token blocks of 32 per workgroup (TB = 2 only when the waves split the
+// expert blocks): the router rows of a chunk then serve 64 tokens, halving
+// their L2 and LDS traffic per token.
+template <int EB, int TB = 1, int NS = 4>
 __global__ __launch_bounds__(256) void router_logits_lds_kernel(const bf16_t* __restrict__ x,
                                                                const bf16_t* __restrict__ w,
                                                                float* __restrict__ logits, int64_t T,
                                                                int d, int E) {
     constexpr bool SPLIT_E = EB % 4 == 0;
+    static_assert(TB == 1 || SPLIT_E, "two token blocks only when the waves split the expert blocks");
     constexpr int NB = SPLIT_E ? EB / 4 : EB;  // expert blocks per wave
-    constexpr int ROWS = EB * 32 + 32;         // router rows, then the token rows
+    constexpr int ROWS = EB * 32 + 32 * TB;    // router rows, then the token rows
     constexpr int LPW = ROWS / 32;             // load instructions per wave and chunk (8 rows each)
-    constexpr int NS = 4;                      // ring stages
     constexpr int STAGE = ROWS * 128;
     static_assert(NS * STAGE <= 160 * 1024, "the ring must fit the LDS");
     static_assert(SPLIT_E || 3 * EB * 16 * 64 * 4 <= NS * STAGE, "the partial sums reuse the ring");
@@ -205,7 +209,7 @@ __global__ __launch_bounds__(256) void router_logits_lds_kernel(const bf16_t* __
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * 32;
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * (32 * TB);
 
     // load j of wave w covers rows (w LPW + j) * 8 .. + 8; lane l fills slot
     // l & 7 of row (l >> 3) with the row's global chunk (l & 7) ^ swizzle
@@ -235,11 +239,13 @@ __global__ __launch_bounds__(256) void router_logits_lds_kernel(const bf16_t* __
     for (int c = 0; c < NS - 1; ++c)
         if (c < nchunk) issue(c);
 
-    f32x16_t acc[NB];
+    f32x16_t acc[NB][TB];
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[b][r] = 0.f;
+        for (int u = 0; u < TB; ++u)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[b][u][r] = 0.f;
     // fragment of K step s of a 32-row block starting at row rb: lane l
     // reads row rb + (l & 31), 8 columns from 16 s + 8 (l >> 5)
     const int l32 = lane & 31;
@@ -253,8 +259,9 @@ __global__ __launch_bounds__(256) void router_logits_lds_kernel(const bf16_t* __
         // kc + 2 are pending; the barrier then publishes it, and every wave
         // is done with chunk kc - 1, whose stage chunk kc + 3 refills
         const int ahead = nchunk - 1 - kc;
-        if (ahead >= 2) wait_vmcnt_lgkm0<2 * LPW>();
-        else if (ahead == 1) wait_vmcnt_lgkm0<LPW>();
+        static_assert(NS == 3 || NS == 4, "ring of 3 or 4 stages");
+        if (NS == 4 && ahead >= 2) wait_vmcnt_lgkm0<(NS - 2) * LPW>();
+        else if (ahead >= 1) wait_vmcnt_lgkm0<LPW>();
         else wait_vmcnt_lgkm0<0>();
         barrier_lds();
         if (kc + NS - 1 < nchunk) issue(kc + NS - 1);
@@ -262,33 +269,43 @@ __global__ __launch_bounds__(256) void router_logits_lds_kernel(const bf16_t* __
         if (SPLIT_E) {
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const bf16x8_t xf = frag(st, EB * 32, s);
+                bf16x8_t xf[TB];
 #pragma unroll
-                for (int b = 0; b < NB; ++b)
-                    acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag(st, (wave + 4 * b) * 32, s), xf, acc[b], 0, 0, 0);
+                for (int u = 0; u < TB; ++u) xf[u] = frag(st, EB * 32 + 32 * u, s);
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    const bf16x8_t wf = frag(st, (wave + 4 * b) * 32, s);
+#pragma unroll
+                    for (int u = 0; u < TB; ++u)
+                        acc[b][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, xf[u], acc[b][u], 0, 0, 0);
+                }
             }
         } else {
             const bf16x8_t xf = frag(st, EB * 32, wave);
 #pragma unroll
             for (int b = 0; b < NB; ++b)
-                acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag(st, b * 32, wave), xf, acc[b], 0, 0, 0);
+                acc[b][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag(st, b * 32, wave), xf, acc[b][0], 0, 0, 0);
         }
     }
 
     // lane holds token (lane & 31); register r of block b holds expert
     // 32 b + 8 (r / 4) + 4 (lane / 32) + r % 4
-    const int64_t t = t0 + l32;
     if (SPLIT_E) {
-        if (t >= T) return;
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
+        for (int u = 0; u < TB; ++u) {
+            const int64_t tu = t0 + 32 * u + l32;
+            if (tu >= T) continue;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int e = (wave + 4 * b) * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                if (e < E) logits[t * E + e] = acc[b][r];
-            }
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int e = (wave + 4 * b) * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                    if (e < E) logits[tu * E + e] = acc[b][u][r];
+                }
+        }
         return;
     }
+    const int64_t t = t0 + l32;
     // partial sums of waves 1..3 in the (now idle) ring: [3][EB][16][64]
     float* const part = reinterpret_cast<float*>(ring);
     __syncthreads();
@@ -296,7 +313,7 @@ __global__ __launch_bounds__(256) void router_logits_lds_kernel(const bf16_t* __
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) part[(((wave - 1) * EB + b) * 16 + r) * 64 + lane] = acc[b][r];
+            for (int r = 0; r < 16; ++r) part[(((wave - 1) * EB + b) * 16 + r) * 64 + lane] = acc[b][0][r];
     }
     __syncthreads();
     if (wave != 0 || t >= T) return;
@@ -305,7 +322,7 @@ __global__ __launch_bounds__(256) void router_logits_lds_kernel(const bf16_t* __
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             // fixed order: K step 0 + step 1 + step 2 + step 3
-            const float v = ((acc[b][r] + part[((0 * EB + b) * 16 + r) * 64 + lane]) +
+            const float v = ((acc[b][0][r] + part[((0 * EB + b) * 16 + r) * 64 + lane]) +
                              part[((1 * EB + b) * 16 + r) * 64 + lane]) +
                             part[((2 * EB + b) * 16 + r) * 64 + lane];
             const int e = b * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
@@ -505,17 +522,18 @@ hipError_t launch_router_logits(const moe_problem_t& p, const void* x, const voi
     // blocks re-read the router rows per token block, and the LDS ring wins
     // (58 against 115 us with top-k, 32768 x 2048 tokens, 128 experts).
     const bool use_lds_router = p.E > 32;
+    const unsigned grid2 = static_cast<unsigned>(ceil_div(p.T, 64));  // two token blocks per workgroup
     const bf16_t* xb = static_cast<const bf16_t*>(x);
     const bf16_t* wb = static_cast<const bf16_t*>(w_router);
     if (use_lds_router) {
         switch (ceil_div(p.E, 32)) {
             case 2: router_logits_lds_kernel<2><<<grid, 256, 0, s>>>(xb, wb, logits, p.T, p.d, p.E); break;  // (E > 32: two blocks or more)
             case 3: router_logits_lds_kernel<3><<<grid, 256, 0, s>>>(xb, wb, logits, p.T, p.d, p.E); break;
-            case 4: router_logits_lds_kernel<4><<<grid, 256, 0, s>>>(xb, wb, logits, p.T, p.d, p.E); break;
+            case 4: router_logits_lds_kernel<4, 2, 3><<<grid2, 256, 0, s>>>(xb, wb, logits, p.T, p.d, p.E); break;
             case 5: router_logits_lds_kernel<5><<<grid, 256, 0, s>>>(xb, wb, logits, p.T, p.d, p.E); break;
             case 6: router_logits_lds_kernel<6><<<grid, 256, 0, s>>>(xb, wb, logits, p.T, p.d, p.E); break;
             case 7: router_logits_lds_kernel<7><<<grid, 256, 0, s>>>(xb, wb, logits, p.T, p.d, p.E); break;
-            default: router_logits_lds_kernel<8><<<grid, 256, 0, s>>>(xb, wb, logits, p.T, p.d, p.E); break;
+            default: router_logits_lds_kernel<8, 2, 3><<<grid2, 256, 0, s>>>(xb, wb, logits, p.T, p.d, p.E); break;
         }
         return hipGetLastError();
     }
