@@ -140,7 +140,11 @@ def test_dispatch_f32_rows_and_odd_width():
                                          (100, 64, 3, "bf16"), (513, 128, 40, "bf16"),
                                          (260, 320, 100, "bf16"), (97, 256, 200, "bf16"),
                                          (33, 1024, 160, "bf16"), (211, 384, 96, "bf16"),
-                                         (77, 192, 190, "bf16")])
+                                         (77, 192, 190, "bf16"),
+                                         # 64 tokens per workgroup (128 and 256 experts): one
+                                         # token, one and two K chunks on the 3-stage ring
+                                         (1, 128, 128, "bf16"), (65, 64, 256, "bf16"),
+                                         (190, 128, 128, "bf16")])
 def test_router_logits(T, d, E, dtype):
     p = mi.Problem(T, d, E, min(2, E), 64, dtype)
     x = mi.make_x(p, 5)
