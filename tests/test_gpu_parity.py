@@ -277,6 +277,31 @@ def test_forward_supplied_logits(T, d, E, k, f, dtype, kind):
     assert rel(host(y), ref["y"]) <= TOL[dtype]
 
 
+def fuzz_cases(n=40, seed=2024):
+    """Seeded random shapes: T in [1, 300], E in {1, 2, 3, 8, 64, 128},
+    k in [1, min(E, 8)]; bf16 with d, f multiples of 64, fp32 with any d, f;
+    Gaussian or tie-heavy supplied logits."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        E = int(rng.choice([1, 2, 3, 8, 64, 128]))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        T = int(rng.integers(1, 301))
+        dtype = "f32" if i % 4 == 0 else "bf16"
+        if dtype == "bf16":
+            d, f = int(rng.choice([64, 128, 192])), int(rng.choice([64, 128, 320]))
+        else:
+            d, f = int(rng.integers(1, 100)), int(rng.integers(1, 100))
+        kind = "ties" if rng.random() < 0.5 else "gauss"
+        cases.append((T, d, E, k, f, dtype, kind))
+    return cases
+
+
+@pytest.mark.parametrize("T,d,E,k,f,dtype,kind", fuzz_cases())
+def test_fuzz_forward_supplied_logits(T, d, E, k, f, dtype, kind):
+    test_forward_supplied_logits(T, d, E, k, f, dtype, kind)
+
+
 def margins(l, k):
     """Gap between the k-th and (k+1)-th largest logit per token (inf if k == E)."""
     s = -np.sort(-l.astype(np.float64), axis=1)
