@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 expert-FFN timing")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter calibration)")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="also time the vendor library's dense bf16 GEMM (torch.mm, hipBLASLt) on the "
+                         "shapes of the two expert GEMMs with all T*k rows as one matrix (a measured ceiling)")
     return ap.parse_args()
 
 
@@ -232,6 +235,22 @@ def main():
     copy_gbs = 2.0 * ca.numel() / (ms_copy * 1e-3) / 1e9
     del ca, cb
 
+    # ---- the vendor library's dense GEMM on the expert GEMMs' shapes (bf16 only) ----
+    lib_gemm = None
+    if args.library_gemm and p.dtype == "bf16":
+        lib_gemm = {"note": "torch.mm (hipBLASLt), bf16, one dense GEMM with all T*k rows: "
+                            "GEMM1 [T*k, d] x [2f, d]^T, GEMM2 [T*k, f] x [d, f]^T; no gather, routing or SwiGLU"}
+        for name, (m_, n_, k_) in (("gemm1", (n, 2 * p.f, p.d)), ("gemm2", (n, p.d, p.f))):
+            ga = torch.randn(m_, k_, device=dev, dtype=torch.bfloat16)
+            gb = torch.randn(n_, k_, device=dev, dtype=torch.bfloat16)
+            gc = torch.empty(m_, n_, device=dev, dtype=torch.bfloat16)
+            ms_g = timed(lambda: torch.mm(ga, gb.t(), out=gc), reps)
+            lib_gemm[name] = {"m_n_k": [m_, n_, k_], "ms": round(ms_g, 4),
+                              "tflops": round(2.0 * m_ * n_ * k_ / (ms_g * 1e-3) / 1e12, 1)}
+            del ga, gb, gc
+        print(f"# library GEMM: {lib_gemm['gemm1']['tflops']} / {lib_gemm['gemm2']['tflops']} TFLOP/s",
+              file=sys.stderr, flush=True)
+
     # ---- fp8 expert FFN (bf16 workloads with d, f multiples of 128) ----
     fp8 = None
     if p.dtype == "bf16" and p.d % 128 == 0 and p.f % 128 == 0 and not args.no_fp8:
@@ -310,7 +329,8 @@ def main():
             "copy_gbs": round(copy_gbs, 1),
             "expert_gemm_frac_of_measured_mfma": round(ffn_tflops / mfma_meas, 4) if p.dtype == "bf16" else None,
             "dispatch_frac_of_copy": round(disp_gbs / copy_gbs, 4),
-            "combine_frac_of_copy": round(comb_gbs / copy_gbs, 4)},
+            "combine_frac_of_copy": round(comb_gbs / copy_gbs, 4),
+            "library_gemm": lib_gemm},
         "expert_gemm_tflops": round(ffn_tflops, 2),
         "expert_gemm_frac_mfma_peak": round(ffn_tflops / peak, 4),
         "dispatch_gbs": round(disp_gbs, 1),
