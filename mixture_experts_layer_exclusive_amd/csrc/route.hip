@@ -176,11 +176,11 @@ __global__ __launch_bounds__(256) void router_logits_mfma_kernel(const bf16_t* _
 
 // ---- bf16 router GEMM with the operands staged in LDS -----------------------
 //
-// A workgroup takes 32 tokens and all E experts (EB blocks of 32).  Per K
-// chunk of 64 columns, the chunk of every router row and of the 32 token
+// A workgroup takes 32 TB tokens and all E experts (EB blocks of 32).  Per K
+// chunk of 64 columns, the chunk of every router row and of the token
 // rows is copied global -> LDS in whole 128-byte lines (global_load_lds,
-// 16 bytes per lane, 8 rows per instruction) into a ring of 4 stages, so
-// the loads of the next three chunks are in flight while the MFMAs run on
+// 16 bytes per lane, 8 rows per instruction) into a ring of NS stages, so
+// the loads of the next NS - 1 chunks are in flight while the MFMAs run on
 // the current one.  When EB is a multiple of 4 the waves split the expert
 // blocks (wave w: blocks w, w + 4, ...) and each sums over the whole hidden
 // dimension; otherwise wave w runs K step w of every chunk and the four
@@ -191,7 +191,8 @@ __global__ __launch_bounds__(256) void router_logits_mfma_kernel(const bf16_t* _
 //
 // TB token blocks of 32 per workgroup (TB = 2 only when the waves split the
 // expert blocks): the router rows of a chunk then serve 64 tokens, halving
-// their L2 and LDS traffic per token.
+// their L2 and LDS traffic per token; with 3 stages two such workgroups fit
+// a CU's LDS.
 template <int EB, int TB = 1, int NS = 4>
 __global__ __launch_bounds__(256) void router_logits_lds_kernel(const bf16_t* __restrict__ x,
                                                                const bf16_t* __restrict__ w,
@@ -520,7 +521,7 @@ hipError_t launch_router_logits(const moe_problem_t& p, const void* x, const voi
     // One expert block (E <= 32): fragments straight from global memory are
     // faster (18.5 against 22 us on 8192 x 4096 tokens, 8 experts); more
     // blocks re-read the router rows per token block, and the LDS ring wins
-    // (58 against 115 us with top-k, 32768 x 2048 tokens, 128 experts).
+    // (50 against 115 us with top-k, 32768 x 2048 tokens, 128 experts).
     const bool use_lds_router = p.E > 32;
     const unsigned grid2 = static_cast<unsigned>(ceil_div(p.T, 64));  // two token blocks per workgroup
     const bf16_t* xb = static_cast<const bf16_t*>(x);
@@ -537,16 +538,7 @@ hipError_t launch_router_logits(const moe_problem_t& p, const void* x, const voi
         }
         return hipGetLastError();
     }
-    switch (ceil_div(p.E, 32)) {
-        case 1: router_logits_mfma_kernel<1><<<grid, 256, 0, s>>>(xb, wb, logits, p.T, p.d, p.E); break;
-        case 2: router_logits_mfma_kernel<2><<<grid, 256, 0, s>>>(xb, wb, logits, p.T, p.d, p.E); break;
-        case 3: router_logits_mfma_kernel<3><<<grid, 256, 0, s>>>(xb, wb, logits, p.T, p.d, p.E); break;
-        case 4: router_logits_mfma_kernel<4><<<grid, 256, 0, s>>>(xb, wb, logits, p.T, p.d, p.E); break;
-        case 5: router_logits_mfma_kernel<5><<<grid, 256, 0, s>>>(xb, wb, logits, p.T, p.d, p.E); break;
-        case 6: router_logits_mfma_kernel<6><<<grid, 256, 0, s>>>(xb, wb, logits, p.T, p.d, p.E); break;
-        case 7: router_logits_mfma_kernel<7><<<grid, 256, 0, s>>>(xb, wb, logits, p.T, p.d, p.E); break;
-        default: router_logits_mfma_kernel<8><<<grid, 256, 0, s>>>(xb, wb, logits, p.T, p.d, p.E); break;
-    }
+    router_logits_mfma_kernel<1><<<grid, 256, 0, s>>>(xb, wb, logits, p.T, p.d, p.E);
     return hipGetLastError();
 }
 
