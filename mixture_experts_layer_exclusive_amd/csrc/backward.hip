@@ -57,7 +57,7 @@ __global__ __launch_bounds__(256) void bwd_dy_kernel(const uint4* __restrict__ d
             const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
             uint32_t o[4] = {0u, 0u, 0u, 0u};
             if (pos >= 0) {
-                const uint4 b = y_perm[static_cast<int64_t>(pos) * chunks + c];
+                const uint4 b = load_nt(y_perm + static_cast<int64_t>(pos) * chunks + c);
                 const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -246,7 +246,7 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(const uint4* __restrict__ d
         for (int j = 0; j < k; ++j) {
             const int pos = assign_pos[t * k + j];
             if (pos < 0) continue;
-            const uint4 v = dx_perm[static_cast<int64_t>(pos) * chunks + c];
+            const uint4 v = load_nt(dx_perm + static_cast<int64_t>(pos) * chunks + c);
             const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
