@@ -63,7 +63,9 @@ def bf16_matrix(rows, cols, seed):
     return mi.f32_to_bf16_bits(a)
 
 
-@pytest.mark.parametrize("rows,cols", [(37, 256), (5, 14336), (300, 16), (1, 4096), (3, 20480)])
+@pytest.mark.parametrize("rows,cols", [(37, 256), (5, 14336), (300, 16), (1, 4096), (3, 20480),
+                                       # a wave per row: 1, 2 and 4 chunks per lane, ragged lanes
+                                       (9, 768), (6, 2048), (130, 1408), (5, 528), (7, 512)])
 def test_quantize_rows_bit_exact(rows, cols):
     a = bf16_matrix(rows, cols, seed=rows)
     codes, exps = moe.quantize_rows_fp8(dev(a))
