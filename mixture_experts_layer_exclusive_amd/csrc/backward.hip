@@ -135,10 +135,12 @@ __global__ __launch_bounds__(64) void bwd_poff_kernel(const int32_t* __restrict_
     }
 }
 
-// Transpose of queue rows into padded per-expert column segments:
-//   dst[c, q] = src_row(q)[c] for c < C, q < Kpad,
-// where padded column q of expert e (poff[e] <= q < poff[e+1]) is queue row
-// pos = offsets[e] + q - poff[e] when pos < offsets[e+1], else zero.  The
+// Transpose of queue rows into padded per-expert blocks: expert e's block
+// [C, K_e] (K_e = poff[e+1] - poff[e]) starts at element poff[e] * C and
+//   block_e[c, q - poff[e]] = src_row(q)[c] for c < C, poff[e] <= q < poff[e+1],
+// where padded column q is queue row pos = offsets[e] + q - poff[e] when
+// pos < offsets[e+1], else zero.  Compact blocks keep the rows a weight-
+// gradient tile reads K_e (not all Kpad) columns apart.  The
 // source row is src[pos] (row stride ld_src), or, with GATHER, row
 // sorted_assign[pos] / k of src.  Tiles of 64 columns x 64 rows through LDS.
 // With GATHER and wr_part, block b = q / 64 also yields the router-gradient
@@ -150,13 +152,13 @@ __global__ __launch_bounds__(256) void bwd_transpose_kernel(const bf16_t* __rest
                                                            const int32_t* __restrict__ offsets,
                                                            const int32_t* __restrict__ poff, int E,
                                                            const int32_t* __restrict__ sorted_assign,
-                                                           int k, int64_t kpad,
-                                                           bf16_t* __restrict__ dst,
+                                                           int k, bf16_t* __restrict__ dst,
                                                            const float* __restrict__ dsel,
                                                            float* __restrict__ wr_part) {
     __shared__ bf16_t tile[64][64 + 2];
     __shared__ int64_t s_row[64];
     __shared__ float s_dsel[64];
+    __shared__ int s_e;
     const int q0 = blockIdx.x * 64;
     const int c0 = blockIdx.y * 64;
     if (q0 >= poff[E]) return;
@@ -177,8 +179,13 @@ __global__ __launch_bounds__(256) void bwd_transpose_kernel(const bf16_t* __rest
         }
         s_row[threadIdx.x] = row;
         s_dsel[threadIdx.x] = ds;
+        // (poff is a multiple of 64: the block's 64 columns share one expert)
+        if (threadIdx.x == 0) s_e = lo;
     }
     __syncthreads();
+    const int eb = s_e;
+    const int64_t ke = poff[eb + 1] - poff[eb];
+    bf16_t* const dst_e = dst + static_cast<int64_t>(poff[eb]) * C + (q0 - poff[eb]);
     // load: thread -> (row i = tid / 4, 16 columns (tid % 4) * 16 ..)
     {
         const int i = threadIdx.x >> 2;
@@ -217,7 +224,7 @@ __global__ __launch_bounds__(256) void bwd_transpose_kernel(const bf16_t* __rest
                         part = fmaf(s_dsel[qq + u + 2 * h + 1], bf16_to_f32(hi), part);
                     }
                 }
-                *reinterpret_cast<uint4*>(dst + static_cast<int64_t>(c0 + c) * kpad + q0 + qq + u) =
+                *reinterpret_cast<uint4*>(dst_e + static_cast<int64_t>(c0 + c) * ke + qq + u) =
                     make_uint4(w[0], w[1], w[2], w[3]);
             }
         }
@@ -374,11 +381,11 @@ hipError_t launch_backward_transpose(const moe_problem_t& p, const void* src, in
     const dim3 grid(static_cast<unsigned>(kpad / 64), static_cast<unsigned>(ceil_div(C, 64)));
     if (gather)
         bwd_transpose_kernel<true><<<grid, 256, 0, s>>>(static_cast<const bf16_t*>(src), ld_src, C, offsets,
-                                                        poff, p.E, sorted_assign, p.k, kpad,
+                                                        poff, p.E, sorted_assign, p.k,
                                                         static_cast<bf16_t*>(dst), dsel, wr_part);
     else
         bwd_transpose_kernel<false><<<grid, 256, 0, s>>>(static_cast<const bf16_t*>(src), ld_src, C, offsets,
-                                                         poff, p.E, sorted_assign, p.k, kpad,
+                                                         poff, p.E, sorted_assign, p.k,
                                                          static_cast<bf16_t*>(dst), nullptr, nullptr);
     return hipGetLastError();
 }

@@ -244,8 +244,11 @@ __device__ __forceinline__ const T* uniform_ptr(const T* p) {
 //   kUpBwd the backward's recompute of gate and up, with an epilogue that
 //          takes dh and writes du, dv (side by side, [rows, 2f]) and h
 //   kWgrad weight gradients: per expert e, C_e[M, N] = A_e B_e^T over the
-//          expert's (padded) queue columns [poff[e], poff[e+1]) of A [M, ldk]
-//          and B [N, ldk] (operands already transposed, padding zero)
+//          expert's K_e = poff[e+1] - poff[e] padded queue columns.  The
+//          operands are transposed, padding zero, and stored per expert:
+//          expert e's block of A (K rows, of which rows a_row_off ..
+//          a_row_off + M are used) starts at element poff[e] * K, that of B
+//          (N rows) at poff[e] * N, each row K_e elements long
 constexpr int kUp = 0, kDown = 1, kUpBwd = 2, kWgrad = 3;
 
 // Work of a weight-gradient workgroup: tile (mt, nt) of expert e, K slices of
@@ -295,7 +298,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const bf16_t* __restrict__ B1, bf16_t* __restrict__ C, int N, int K, int slots,
     float* __restrict__ part, const bf16_t* __restrict__ aux, bf16_t* __restrict__ C2, int M,
     const int32_t* __restrict__ a_exp = nullptr, const int32_t* __restrict__ b_exp0 = nullptr,
-    const int32_t* __restrict__ b_exp1 = nullptr) {
+    const int32_t* __restrict__ b_exp1 = nullptr, int a_row_off = 0) {
     constexpr bool GATEUP = MODE == kUp || MODE == kUpBwd;
     constexpr bool WG = MODE == kWgrad;
     static_assert(!F8 || MODE == kUp || MODE == kDown, "fp8 operands: forward GEMMs only");
@@ -327,8 +330,9 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 
     Work work;
     if (WG) {
-        // (K is the operands' row stride here; offsets are the padded
-        // offsets and sorted_assign the expert order, heaviest first)
+        // (K is the row count of A's per-expert blocks here; offsets are
+        // the padded offsets and sorted_assign the expert order, heaviest
+        // first)
         if (!find_wgrad_work(offsets, sorted_assign, E, M, N, work)) return;
     } else {
         build_tile_prefix(offsets, E, TM, s_prefix, s_off);
@@ -360,10 +364,14 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const char* a_src[WIDE ? LA : 1];
     uint32_t a_off[WIDE ? 1 : LA];
     const char* const Ab = reinterpret_cast<const char*>(A);
-    const int64_t RB = static_cast<int64_t>(K) * EB;  // bytes per operand row
-    // (the K range [work.kb, work.kb + work.nkl) of 128-byte slices is folded into the bases)
+    // bytes per operand row (weight gradients: the expert's K_e columns)
+    const int64_t RB = WG ? static_cast<int64_t>(work.nkl) * 128 : static_cast<int64_t>(K) * EB;
+    // (the K range [work.kb, work.kb + work.nkl) of 128-byte slices is folded
+    // into the bases; a weight-gradient tile starts at its expert's block,
+    // whose first column is poff[e] = 64 kb)
     const char* const a_base =
-        uniform_ptr((GATHER ? Ab : Ab + static_cast<int64_t>(tile.row0) * RB) + work.kb * 128);
+        uniform_ptr(WG ? Ab + static_cast<int64_t>(work.kb) * 128 * K + (a_row_off + tile.row0) * RB
+                       : (GATHER ? Ab : Ab + static_cast<int64_t>(tile.row0) * RB) + work.kb * 128);
     // (gathered rows need a lookup in sorted_assign: called after the first
     // weight loads are on their way)
     auto setup_a = [&]() {
@@ -388,7 +396,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const int rb0 = wave * (TN / 4);
     const char* const b_base =
         uniform_ptr(reinterpret_cast<const char*>(GATEUP && rb0 >= TN / 2 ? B1 : B0) +
-                    (WG ? 0 : static_cast<int64_t>(tile.e) * N * RB) + work.kb * 128);
+                    (WG ? static_cast<int64_t>(work.kb) * 128 * N : static_cast<int64_t>(tile.e) * N * RB + work.kb * 128));
     uint32_t b_off[LB];
 #pragma unroll
     for (int j = 0; j < LB; ++j) {
@@ -1024,16 +1032,18 @@ hipError_t launch_backward_dxperm(const moe_problem_t& p, const void* duv, const
 }
 
 // Weight gradient per expert: C[e] [M, N] = A_e B_e^T over the expert's padded
-// queue columns [poff[e], poff[e+1]) of A [M, ldk] and B [N, ldk]; order: the
-// experts by descending row count.
-hipError_t launch_backward_wgrad(const moe_problem_t& p, const void* A, int M, const void* B, int N,
-                                 int64_t ldk, const int32_t* poff, const int32_t* order, void* C,
+// queue columns [poff[e], poff[e+1]); A and B hold per-expert blocks (A:
+// a_rows rows, of which a_row_off .. + M are used; B: N rows; rows of the
+// expert's K_e columns); order: the experts by descending row count.
+hipError_t launch_backward_wgrad(const moe_problem_t& p, const void* A, int M, int a_rows, int a_row_off,
+                                 const void* B, int N, const int32_t* poff, const int32_t* order, void* C,
                                  hipStream_t s) {
     const int64_t tiles = static_cast<int64_t>(p.E) * ceil_div(M, kBM) * ceil_div(N, kDownCols);
     const unsigned g = static_cast<unsigned>(tiles);
     grouped_gemm_bf16_kernel<kWgrad, false, false><<<g, 256, 0, s>>>(
         static_cast<const bf16_t*>(A), order, p.k, poff, p.E, static_cast<const bf16_t*>(B), nullptr,
-        static_cast<bf16_t*>(C), N, static_cast<int>(ldk), 0, nullptr, nullptr, nullptr, M);
+        static_cast<bf16_t*>(C), N, a_rows, 0, nullptr, nullptr, nullptr, M, nullptr, nullptr, nullptr,
+        a_row_off);
     return hipGetLastError();
 }
 

@@ -426,10 +426,10 @@ moe_status_t moe_backward(const moe_problem_t* p, const void* x, const void* w_r
                                              xT, dsel, w_router != nullptr ? wr_part : nullptr, s));
     }
     // weight gradients (an expert with no rows gets zeros)
-    MOE_LAUNCH(launch_backward_wgrad(*p, dyT, p->d, hT, p->f, kp, poff, order, out->dw_down, s));
-    MOE_LAUNCH(launch_backward_wgrad(*p, duvT, p->f, xT, p->d, kp, poff, order, out->dw_gate, s));
-    MOE_LAUNCH(launch_backward_wgrad(*p, static_cast<char*>(duvT) + static_cast<size_t>(p->f) * kp * 2, p->f,
-                                     xT, p->d, kp, poff, order, out->dw_up, s));
+    // (du^T and dv^T are rows 0 .. f and f .. 2f of each expert's block of (du|dv)^T)
+    MOE_LAUNCH(launch_backward_wgrad(*p, dyT, p->d, p->d, 0, hT, p->f, poff, order, out->dw_down, s));
+    MOE_LAUNCH(launch_backward_wgrad(*p, duvT, p->f, 2 * p->f, 0, xT, p->d, poff, order, out->dw_gate, s));
+    MOE_LAUNCH(launch_backward_wgrad(*p, duvT, p->f, 2 * p->f, p->f, xT, p->d, poff, order, out->dw_up, s));
     if (w_router != nullptr)
         MOE_LAUNCH(launch_backward_dwr(*p, wr_part, poff, out->dw_router, s));
     return MOE_OK;

@@ -133,8 +133,8 @@ hipError_t launch_backward_recompute(const moe_problem_t& p, const void* x, cons
                                      const void* dh, void* duv, void* h, hipStream_t s);
 hipError_t launch_backward_dxperm(const moe_problem_t& p, const void* duv, const int32_t* offsets,
                                   const void* w_gu_t, void* dx_perm, float* part, hipStream_t s);
-hipError_t launch_backward_wgrad(const moe_problem_t& p, const void* A, int M, const void* B, int N,
-                                 int64_t ldk, const int32_t* poff, const int32_t* order, void* C,
+hipError_t launch_backward_wgrad(const moe_problem_t& p, const void* A, int M, int a_rows, int a_row_off,
+                                 const void* B, int N, const int32_t* poff, const int32_t* order, void* C,
                                  hipStream_t s);
 
 }  // namespace moe
