@@ -52,7 +52,7 @@ def parse():
     ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 expert-FFN timing")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run a plain 1 GiB device copy (for HBM counter calibration)")
+                    help="also run moe_stream_copy over 1 GiB (the plain copy that calibrates HBM counters)")
     ap.add_argument("--library-gemm", action="store_true",
                     help="also time the vendor library's dense bf16 GEMM (torch.mm, hipBLASLt) on the "
                          "shapes of the two expert GEMMs with all T*k rows as one matrix (a measured ceiling)")
@@ -162,12 +162,15 @@ def main():
         return a.elapsed_time(b) / reps  # ms
 
     def timed_cold(fn, reps):
-        """Median of single calls, each after writing a 1 GiB buffer (more than
-        the 256 MB Infinity Cache), so that the call's inputs come from HBM."""
-        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        """Median of single calls, each after reading a 1 GiB buffer (four
+        times the 256 MB Infinity Cache), so that the call's inputs come from
+        HBM.  The buffer is only read between calls: the lines it leaves in
+        the caches are clean, so the call's own writes evict nothing that has
+        to be written back first."""
+        flush = torch.ones((1 << 30) // 4, dtype=torch.int32, device=dev)
         out = []
         for _ in range(reps + 1):
-            flush.fill_(1)
+            flush.max()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
             fn()
@@ -199,6 +202,8 @@ def main():
     comb_bytes = (p.k + 1) * p.T * p.d * s + 8 * n
     disp_gbs = disp_bytes / (ms_disp * 1e-3) / 1e9
     comb_gbs = comb_bytes / (ms_comb * 1e-3) / 1e9
+    disp_gbs_cold = disp_bytes / (ms_disp_cold * 1e-3) / 1e9
+    comb_gbs_cold = comb_bytes / (ms_comb_cold * 1e-3) / 1e9
 
     counts = inter["counts"].cpu().numpy()
 
@@ -220,20 +225,19 @@ def main():
         del dyg, wt, bws, gout
 
     if args.copy_calibration:
-        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        b = torch.empty_like(a)
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        del a, b
+        # six moe_stream_copy launches of exactly 1 GiB each (one untimed):
+        # the reference that scales the HBM byte counters
+        moe.stream_copy_gbs(dev)
 
-    # ---- measured ceilings: MFMA-only kernel, device copy ----
+    # ---- measured ceilings: MFMA-only kernel, device copies ----
     mfma_meas = moe.mfma_peak_tflops(dev)
+    copy_gbs = moe.stream_copy_gbs(dev)          # this library's copy kernel
     ca = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     cb = torch.empty_like(ca)
     ms_copy = timed(lambda: cb.copy_(ca), 5)
-    copy_gbs = 2.0 * ca.numel() / (ms_copy * 1e-3) / 1e9
+    torch_copy_gbs = 2.0 * ca.numel() / (ms_copy * 1e-3) / 1e9
     del ca, cb
+    stream_gbs = max(copy_gbs, torch_copy_gbs)
 
     # ---- the vendor library's dense GEMM on the expert GEMMs' shapes (bf16 only) ----
     lib_gemm = None
@@ -284,21 +288,60 @@ def main():
     if not args.no_cpu_baseline:
         del x_perm, y_perm, ffn_ws, disp_ws
         import oracle
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         S = min(args.cpu_tokens, p.T)
         f32 = lambda a: mi.as_f32(a, p.dtype)  # noqa: E731
         xs = f32(L["x"][:S])
         wgs, wus, wds = f32(L["w_gate"]), f32(L["w_up"]), f32(L["w_down"])
+        wrs = f32(L["w_router"]) if L["w_router"] is not None else None
         tc = time.perf_counter()
         if L["logits"] is not None:
             oracle.forward(xs, p.k, wgs, wus, wds, logits=L["logits"][:S])
         else:
-            oracle.forward(xs, p.k, wgs, wus, wds, w_router=f32(L["w_router"]))
+            oracle.forward(xs, p.k, wgs, wus, wds, w_router=wrs)
         tc = time.perf_counter() - tc
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        del xs
+        # the same oracle on one pinned core: routing and queues over all T
+        # tokens, the per-token FFN and combine on a seeded token subset,
+        # extrapolated linearly (the per-token work does not depend on T)
+        S1 = min(64 if p.d * p.f >= (1 << 25) else 256, p.T)
+        aff = os.sched_getaffinity(0)
+        core = min(aff)
+        x_all = f32(L["x"])
+        os.sched_setaffinity(0, {core})
+        try:
+            with threadpool_limits(1):
+                t1 = time.perf_counter()
+                lg_all = L["logits"] if L["logits"] is not None else oracle.router_logits(x_all, wrs)
+                ids_all, _ = oracle.topk_route(lg_all, p.k)
+                oracle.dispatch(ids_all, p.E)
+                t_route = time.perf_counter() - t1
+                tok = mi.sample_tokens(p.T, S1, seed=0)
+                t1 = time.perf_counter()
+                oracle.forward_tokens(tok, x_all, lg_all, p.k, wgs, wus, wds)
+                t_tok = time.perf_counter() - t1
+        finally:
+            os.sched_setaffinity(0, aff)
+        del x_all
+        single = {"value": round(p.T / (t_route + t_tok * p.T / S1), 2), "unit": "tokens/s", "cores": 1,
+                  "pinned_cpu": core, "route_dispatch_all_tokens_s": round(t_route, 3),
+                  "ffn_combine_tokens": S1, "ffn_combine_s": round(t_tok, 3),
+                  "extrapolation": "T / (t_route+dispatch(all T) + t_ffn+combine(S tokens) * T / S)"}
+        model_name = "unknown"
+        try:
+            for line in open("/proc/cpuinfo"):
+                if line.startswith("model name"):
+                    model_name = line.split(":", 1)[1].strip()
+                    break
+        except OSError:
+            pass
         cpu = {"value": round(S / tc, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
                "sample": f"first {S} of {p.T} tokens, whole layer (router GEMM, top-k, queues, "
-                         f"SwiGLU FFN, combine) in float64 numpy; {tc:.1f} s"}
+                         f"SwiGLU FFN, combine) in float64 numpy with {threads} BLAS threads; {tc:.1f} s",
+               "host": {"cpu_model": model_name, "logical_cpus": os.cpu_count(),
+                        "cpus_in_affinity": len(aff)},
+               "single_thread": single}
 
     traffic = measured_traffic()
     out = {
@@ -325,25 +368,29 @@ def main():
         "measured_peaks": {
             "mfma_bf16_tflops": round(mfma_meas, 1),
             "note": "moe_mfma_peak: register-operand MFMAs only, at the clock this GPU holds under full matrix "
-                    "load; copy: 1 GiB device copy, read + write bytes",
+                    "load; copies of 1 GiB, read + write bytes: moe_stream_copy (this library's copy kernel) "
+                    "and torch's copy_; the stream ceiling is the faster of the two",
             "copy_gbs": round(copy_gbs, 1),
+            "torch_copy_gbs": round(torch_copy_gbs, 1),
+            "stream_ceiling_gbs": round(stream_gbs, 1),
             "expert_gemm_frac_of_measured_mfma": round(ffn_tflops / mfma_meas, 4) if p.dtype == "bf16" else None,
-            "dispatch_frac_of_copy": round(disp_gbs / copy_gbs, 4),
-            "combine_frac_of_copy": round(comb_gbs / copy_gbs, 4),
+            "dispatch_frac_of_stream_ceiling": round(disp_gbs_cold / stream_gbs, 4),
+            "combine_frac_of_stream_ceiling": round(comb_gbs_cold / stream_gbs, 4),
             "library_gemm": lib_gemm},
         "expert_gemm_tflops": round(ffn_tflops, 2),
         "expert_gemm_frac_mfma_peak": round(ffn_tflops / peak, 4),
-        "dispatch_gbs": round(disp_gbs, 1),
-        "dispatch_frac_hbm_peak": round(disp_gbs / PEAK_HBM_GBS, 4),
-        "combine_gbs": round(comb_gbs, 1),
-        "combine_frac_hbm_peak": round(comb_gbs / PEAK_HBM_GBS, 4),
-        "stage_ms": {"route": round(ms_route, 4), "dispatch_with_x_perm": round(ms_disp, 4),
-                     "expert_ffn": round(ms_ffn, 4), "combine": round(ms_comb, 4)},
-        "cold_cache": {"note": "median single call after a 1 GiB write (inputs from HBM, not the Infinity Cache)",
-                       "dispatch_with_x_perm_ms": round(ms_disp_cold, 4),
-                       "dispatch_gbs": round(disp_bytes / (ms_disp_cold * 1e-3) / 1e9, 1),
-                       "combine_ms": round(ms_comb_cold, 4),
-                       "combine_gbs": round(comb_bytes / (ms_comb_cold * 1e-3) / 1e9, 1)},
+        "dispatch_gbs": round(disp_gbs_cold, 1),
+        "dispatch_frac_hbm_peak": round(disp_gbs_cold / PEAK_HBM_GBS, 4),
+        "combine_gbs": round(comb_gbs_cold, 1),
+        "combine_frac_hbm_peak": round(comb_gbs_cold / PEAK_HBM_GBS, 4),
+        "stage_ms": {"route": round(ms_route, 4), "dispatch_with_x_perm": round(ms_disp_cold, 4),
+                     "expert_ffn": round(ms_ffn, 4), "combine": round(ms_comb_cold, 4)},
+        "cold_cache_note": "dispatch and combine: median single call after a 1 GiB read, so that x and y_perm "
+                           "come from HBM and not from the 256 MB Infinity Cache (dispatch: histogram, scatter "
+                           "and gather launches, with the gaps between them)",
+        "warm_cache": {"note": "back-to-back calls; x, x_perm and y_perm partly stay in the Infinity Cache",
+                       "dispatch_with_x_perm_ms": round(ms_disp, 4), "dispatch_gbs": round(disp_gbs, 1),
+                       "combine_ms": round(ms_comb, 4), "combine_gbs": round(comb_gbs, 1)},
         "expert_counts": {"min": int(counts.min()), "max": int(counts.max()),
                           "empty": int((counts == 0).sum())},
         "backward": bwd,

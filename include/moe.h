@@ -47,8 +47,10 @@
  *     kernel launch returns MOE_ERR_HIP; faults during execution surface on
  *     the stream.  Logits must be finite (not checked).
  *   - Limits: 1 <= E <= MOE_MAX_EXPERTS, 1 <= k <= min(E, MOE_MAX_TOPK),
- *     T*k <= 2^31 - 1; bf16 needs d and f to be multiples of 64 and
- *     d*f <= 2^31 - 1 (one expert's weight matrix below 4 GiB).
+ *     T*k <= 2^31 - 1 and T <= 2^24 - 1 (a kernel launch counts its
+ *     work-items in 32 bits, and the per-token kernels run 256 lanes per
+ *     token); bf16 needs d and f to be multiples of 64 and d*f <= 2^31 - 1
+ *     (one expert's weight matrix below 4 GiB).
  */
 #ifndef MOE_H
 #define MOE_H
@@ -244,9 +246,10 @@ moe_status_t moe_backward_weights(const moe_problem_t* p, const void* w_gate, co
 
 /*
  * moe_backward -- gradients of the layer for the output gradient dy [T, d]
- * (MoEBlaze summary, Methodology 2: the backward runs on the forward's
- * dispatch queues; item 3: the SwiGLU intermediates are recomputed from x,
- * not stored).  Given the forward state `fw` (ids, gates, queues, y_perm)
+ * (MoEBlaze summary, Methodology item 2: the backward runs on the
+ * forward's dispatch queues; its checkpoint bullet and Key contributions
+ * bullet 3: intermediates are recomputed rather than stored, here the SwiGLU
+ * ones, from x).  Given the forward state `fw` (ids, gates, queues, y_perm)
  * it computes, with the routing held fixed:
  *   slot gradients dg = <dy[t], y_perm[pos]>, the queue rows' gradient
  *   g dy[t], per expert dh = dy_perm W_down, the recomputed u = x W_gate^T,
@@ -278,8 +281,8 @@ moe_status_t moe_backward(const moe_problem_t* p, const void* x, const void* w_r
  * power-of-two scale 2^exps[r], the smallest with max|row| <= 448 * 2^exps[r]
  * (0 for an all-zero row), and codes[r, c] = E4M3(src[r, c] / 2^exps[r]),
  * OCP FP8 E4M3, rounded to nearest even.  cols must be a positive multiple
- * of 16 (MOE_ERR_UNSUPPORTED otherwise); src, codes and exps 16-byte
- * aligned.  rows = 0 is a no-op.
+ * of 16 and rows at most 2^24 - 1 (MOE_ERR_UNSUPPORTED otherwise); src,
+ * codes and exps 16-byte aligned.  rows = 0 is a no-op.
  */
 moe_status_t moe_quantize_rows_fp8(const void* src, int64_t rows, int32_t cols, void* codes, int32_t* exps,
                                    void* stream);
@@ -317,6 +320,17 @@ moe_status_t moe_expert_ffn_fp8(const moe_problem_t* p, const void* x, const int
  * positive.
  */
 moe_status_t moe_mfma_peak(int32_t workgroups, int32_t iters, float* sink, void* stream);
+
+/*
+ * moe_stream_copy -- measurement kernel, not part of the layer: dst[i] =
+ * src[i] for `bytes` bytes, read and written once in 16-byte words
+ * (non-overlapping device buffers, 16-byte aligned, bytes a multiple of 16:
+ * MOE_ERR_UNSUPPORTED otherwise; bytes = 0 is a no-op).  Timed by the
+ * caller, 2 * bytes / time is the streaming bandwidth this GPU sustains, the
+ * ceiling the dispatch and combine bandwidths are also reported against,
+ * and the plain copy of known size that calibrates HBM byte counters.
+ */
+moe_status_t moe_stream_copy(const void* src, void* dst, size_t bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -75,6 +75,7 @@ SIGNATURES = {
     "moe_backward_weights": (_i32, [_PP, _p, _p, _p, _p, _p, _p]),
     "moe_quantize_rows_fp8": (_i32, [_p, ctypes.c_int64, _i32, _p, _p, _p]),
     "moe_mfma_peak": (_i32, [_i32, _i32, _p, _p]),
+    "moe_stream_copy": (_i32, [_p, _p, _sz, _p]),
     "moe_quantize_weights_fp8": (_i32, [_PP, _p, _p, _p, ctypes.POINTER(MoeFp8Weights), _p]),
     "moe_expert_ffn_fp8": (_i32, [_PP, _p, _p, _p, ctypes.POINTER(MoeFp8Weights), _p, _p, _sz, _p]),
     "moe_backward": (_i32, [_PP, _p, _p, _p, _p, _p, _p, ctypes.POINTER(MoeForwardState), _p,

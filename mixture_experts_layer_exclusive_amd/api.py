@@ -17,6 +17,39 @@ from . import _lib as L
 _DTYPES = {torch.float32: L.MOE_DTYPE_F32, torch.bfloat16: L.MOE_DTYPE_BF16}
 
 
+def _expect(name: str, t: Optional[torch.Tensor], shape, dtype, device=None, required: bool = True):
+    """Checks one tensor argument against the problem before anything reaches
+    the C ABI (which sees only pointers: a wrong shape or dtype there would
+    make the kernels read or write out of bounds)."""
+    if t is None:
+        if required:
+            raise ValueError(f"{name} is required")
+        return
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(int(v) for v in shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(int(v) for v in shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _expect_ws(ws: Optional[torch.Tensor], device):
+    if ws is None:
+        return
+    if not isinstance(ws, torch.Tensor) or ws.device != device or not ws.is_contiguous():
+        raise ValueError(f"ws must be a contiguous tensor on {device}")
+
+
+def _float_dtype(name: str, t: torch.Tensor):
+    if t.dtype not in _DTYPES:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected float32 or bfloat16")
+    return t.dtype
+
+
 def _ptr(t: Optional[torch.Tensor]):
     if t is None:
         return None
@@ -57,18 +90,27 @@ def route(k: int, x: Optional[torch.Tensor] = None, w_router: Optional[torch.Ten
     """Router GEMM (unless ``logits`` [T, E] fp32 is given) and top-k gating.
     Returns (topk_ids int32 [T, k], topk_gates fp32 [T, k], logits fp32 [T, E])."""
     if logits is not None:
+        if logits.dim() != 2:
+            raise ValueError("logits must be [T, E]")
         T, E = logits.shape
         dev = logits.device
-        d = x.shape[1] if x is not None else 64
-        dt = x.dtype if x is not None else torch.bfloat16
+        _expect("logits", logits, (T, E), torch.float32)
+        d = x.shape[1] if x is not None and x.dim() == 2 else 64
+        dt = _float_dtype("x", x) if x is not None else torch.bfloat16
         logits_out = logits
     else:
+        if x is None or w_router is None or x.dim() != 2 or w_router.dim() != 2:
+            raise ValueError("without logits, x [T, d] and w_router [E, d] are required")
         T, d = x.shape
         E = w_router.shape[0]
         dev = x.device
-        dt = x.dtype
+        dt = _float_dtype("x", x)
+        _expect("w_router", w_router, (E, d), dt, dev)
+        _expect("logits_out", logits_out, (T, E), torch.float32, dev, required=False)
         if logits_out is None:
             logits_out = torch.empty(T, E, dtype=torch.float32, device=dev)
+    _expect("ids", ids, (T, k), torch.int32, dev, required=False)
+    _expect("gates", gates, (T, k), torch.float32, dev, required=False)
     p = problem(T, d, E, k, 64, dt)
     if ids is None:
         ids = torch.empty(T, k, dtype=torch.int32, device=dev)
@@ -86,11 +128,26 @@ def dispatch(topk_ids: torch.Tensor, E: int, x: Optional[torch.Tensor] = None,
     """Dispatch queues of ``topk_ids`` [T, k]: counts, offsets, sorted_assign,
     assign_pos and (with ``with_x_perm``) the gathered rows x_perm.  ``out``
     may supply any of these tensors."""
+    if topk_ids.dim() != 2:
+        raise ValueError("topk_ids must be [T, k]")
     T, k = topk_ids.shape
     dev = topk_ids.device
+    _expect("topk_ids", topk_ids, (T, k), torch.int32)
+    if with_x_perm and x is None:
+        raise ValueError("with_x_perm needs x")
+    if x is not None:
+        if x.dim() != 2:
+            raise ValueError("x must be [T, d]")
+        _expect("x", x, (T, x.shape[1]), _float_dtype("x", x), dev)
     d = x.shape[1] if x is not None else 64
     dt = x.dtype if x is not None else torch.bfloat16
+    _expect_ws(ws, dev)
     p = problem(T, d, E, k, 64, dt)
+    given = dict(out or {})
+    for key, shape, tdt in (("counts", (E,), torch.int32), ("offsets", (E + 1,), torch.int32),
+                            ("sorted_assign", (T * k,), torch.int32), ("assign_pos", (T * k,), torch.int32),
+                            ("x_perm", (T * k, d), dt)):
+        _expect(key, given.get(key), shape, tdt, dev, required=False)
     res = dict(out or {})
     res.setdefault("counts", torch.empty(E, dtype=torch.int32, device=dev))
     res.setdefault("offsets", torch.empty(E + 1, dtype=torch.int32, device=dev))
@@ -113,9 +170,25 @@ def expert_ffn(offsets: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor,
                x: Optional[torch.Tensor] = None, sorted_assign: Optional[torch.Tensor] = None,
                ws: Optional[torch.Tensor] = None, y_perm: Optional[torch.Tensor] = None):
     """Grouped SwiGLU FFN over the queues; returns y_perm [T*k, d]."""
+    if w_gate.dim() != 3:
+        raise ValueError("w_gate must be [E, f, d]")
     E, f, d = w_gate.shape
     src = x_perm if x_perm is not None else x
+    if src is None:
+        raise ValueError("x_perm, or x with sorted_assign, is required")
     dev = src.device
+    dt = _float_dtype("w_gate", w_gate)
+    if x_perm is not None:
+        _expect("x_perm", x_perm, (T * k, d), dt, dev)
+    else:
+        _expect("x", x, (T, d), dt, dev)
+        _expect("sorted_assign", sorted_assign, (T * k,), torch.int32, dev)
+    _expect("offsets", offsets, (E + 1,), torch.int32, dev)
+    _expect("w_gate", w_gate, (E, f, d), dt, dev)
+    _expect("w_up", w_up, (E, f, d), dt, dev)
+    _expect("w_down", w_down, (E, d, f), dt, dev)
+    _expect("y_perm", y_perm, (T * k, d), dt, dev, required=False)
+    _expect_ws(ws, dev)
     p = problem(T, d, E, k, f, src.dtype)
     if y_perm is None:
         y_perm = torch.empty(T * k, d, dtype=src.dtype, device=dev)
@@ -130,9 +203,16 @@ def expert_ffn(offsets: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor,
 def combine(y_perm: torch.Tensor, assign_pos: torch.Tensor, gates: torch.Tensor,
             y: Optional[torch.Tensor] = None):
     """Gate-weighted combine back to token order; returns y [T, d]."""
+    if gates.dim() != 2 or y_perm.dim() != 2:
+        raise ValueError("gates must be [T, k] and y_perm [T*k, d]")
     T, k = gates.shape
     d = y_perm.shape[1]
     dev = y_perm.device
+    dt = _float_dtype("y_perm", y_perm)
+    _expect("y_perm", y_perm, (T * k, d), dt)
+    _expect("assign_pos", assign_pos, (T * k,), torch.int32, dev)
+    _expect("gates", gates, (T, k), torch.float32, dev)
+    _expect("y", y, (T, d), dt, dev, required=False)
     p = problem(T, d, 1 if k == 1 else k, k, 64, y_perm.dtype)
     if y is None:
         y = torch.empty(T, d, dtype=y_perm.dtype, device=dev)
@@ -148,9 +228,21 @@ def forward(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor, w_down: t
     """The whole layer in one call.  Returns y [T, d], or (y, dict of
     intermediates) with ``intermediates=True``; the intermediates include
     the forward state ``backward`` reads."""
+    if x.dim() != 2 or w_gate.dim() != 3:
+        raise ValueError("x must be [T, d] and w_gate [E, f, d]")
     T, d = x.shape
     E, f, _ = w_gate.shape
     dev = x.device
+    dt = _float_dtype("x", x)
+    _expect("w_gate", w_gate, (E, f, d), dt, dev)
+    _expect("w_up", w_up, (E, f, d), dt, dev)
+    _expect("w_down", w_down, (E, d, f), dt, dev)
+    if w_router is None and logits is None:
+        raise ValueError("w_router or logits is required")
+    _expect("w_router", w_router, (E, d), dt, dev, required=False)
+    _expect("logits", logits, (T, E), torch.float32, dev, required=False)
+    _expect("y", y, (T, d), dt, dev, required=False)
+    _expect_ws(ws, dev)
     p = problem(T, d, E, k, f, x.dtype)
     if y is None:
         y = torch.empty(T, d, dtype=x.dtype, device=dev)
@@ -180,8 +272,15 @@ def backward_weights(w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Ten
                      w_down_t: Optional[torch.Tensor] = None, w_gu_t: Optional[torch.Tensor] = None):
     """The weight layouts the backward GEMMs read: (w_down_t [E, f, d],
     w_gu_t [E, d, 2f]).  Recompute after every change of the weights."""
+    if w_gate.dim() != 3:
+        raise ValueError("w_gate must be [E, f, d]")
     E, f, d = w_gate.shape
     dev = w_gate.device
+    dt = _float_dtype("w_gate", w_gate)
+    _expect("w_up", w_up, (E, f, d), dt, dev)
+    _expect("w_down", w_down, (E, d, f), dt, dev)
+    _expect("w_down_t", w_down_t, (E, f, d), dt, dev, required=False)
+    _expect("w_gu_t", w_gu_t, (E, d, 2 * f), dt, dev, required=False)
     p = problem(0, d, E, 1, f, w_gate.dtype)
     if w_down_t is None:
         w_down_t = torch.empty(E, f, d, dtype=w_gate.dtype, device=dev)
@@ -205,11 +304,32 @@ def backward(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor, k: int, 
     ``backward_weights``.  Returns dx, dw_gate, dw_up, dw_down, dw_router
     (None without a router) and dlogits (None unless ``with_dlogits``).
     ``out`` may supply any of these tensors."""
+    if x.dim() != 2 or w_gate.dim() != 3:
+        raise ValueError("x must be [T, d] and w_gate [E, f, d]")
     T, d = x.shape
     E, f, _ = w_gate.shape
     dev = x.device
-    p = problem(T, d, E, k, f, x.dtype)
+    dt = _float_dtype("x", x)
     w_down_t, w_gu_t = weights_t
+    _expect("w_gate", w_gate, (E, f, d), dt, dev)
+    _expect("w_up", w_up, (E, f, d), dt, dev)
+    _expect("w_down_t", w_down_t, (E, f, d), dt, dev)
+    _expect("w_gu_t", w_gu_t, (E, d, 2 * f), dt, dev)
+    _expect("w_router", w_router, (E, d), dt, dev, required=False)
+    _expect("dy", dy, (T, d), dt, dev)
+    n = T * k
+    if T > 0:
+        for key, shape, tdt in (("topk_ids", (T, k), torch.int32), ("topk_gates", (T, k), torch.float32),
+                                ("offsets", (E + 1,), torch.int32), ("sorted_assign", (n,), torch.int32),
+                                ("assign_pos", (n,), torch.int32), ("y_perm", (n, d), dt)):
+            _expect(f"state[{key!r}]", state.get(key), shape, tdt, dev)
+    given = dict(out or {})
+    for key, shape, tdt in (("dx", (T, d), dt), ("dw_gate", (E, f, d), dt), ("dw_up", (E, f, d), dt),
+                            ("dw_down", (E, d, f), dt), ("dw_router", (E, d), dt),
+                            ("dlogits", (T, E), torch.float32)):
+        _expect(key, given.get(key), shape, tdt, dev, required=False)
+    _expect_ws(ws, dev)
+    p = problem(T, d, E, k, f, x.dtype)
     res = dict(out or {})
     res.setdefault("dx", torch.empty(T, d, dtype=x.dtype, device=dev))
     res.setdefault("dw_gate", torch.empty(E, f, d, dtype=x.dtype, device=dev))
@@ -240,8 +360,13 @@ def quantize_rows_fp8(src: torch.Tensor, codes: Optional[torch.Tensor] = None,
                       exps: Optional[torch.Tensor] = None):
     """Per-row FP8 E4M3 codes (uint8) and power-of-two scale exponents
     (int32) of a bf16 matrix [rows, cols]."""
+    if src.dim() != 2:
+        raise ValueError("src must be [rows, cols]")
     rows, cols = src.shape
     dev = src.device
+    _expect("src", src, (rows, cols), torch.bfloat16)
+    _expect("codes", codes, (rows, cols), torch.uint8, dev, required=False)
+    _expect("exps", exps, (rows,), torch.int32, dev, required=False)
     if codes is None:
         codes = torch.empty(rows, cols, dtype=torch.uint8, device=dev)
     if exps is None:
@@ -255,8 +380,13 @@ def quantize_rows_fp8(src: torch.Tensor, codes: Optional[torch.Tensor] = None,
 def quantize_weights_fp8(w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor) -> dict:
     """The expert weights as FP8 codes with per-row scale exponents (for
     ``expert_ffn_fp8``)."""
+    if w_gate.dim() != 3:
+        raise ValueError("w_gate must be [E, f, d]")
     E, f, d = w_gate.shape
     dev = w_gate.device
+    _expect("w_gate", w_gate, (E, f, d), torch.bfloat16)
+    _expect("w_up", w_up, (E, f, d), torch.bfloat16, dev)
+    _expect("w_down", w_down, (E, d, f), torch.bfloat16, dev)
     p = problem(1, d, E, 1, f, w_gate.dtype)
     q = dict(w_gate=torch.empty(E, f, d, dtype=torch.uint8, device=dev),
              w_gate_exp=torch.empty(E, f, dtype=torch.int32, device=dev),
@@ -274,9 +404,20 @@ def expert_ffn_fp8(offsets: torch.Tensor, wq: dict, k: int, x: torch.Tensor, sor
                    ws: Optional[torch.Tensor] = None, y_perm: Optional[torch.Tensor] = None):
     """Grouped SwiGLU FFN on FP8 MFMA (weights from ``quantize_weights_fp8``,
     x bf16 quantised per token inside); returns y_perm [T*k, d] bf16."""
+    if x.dim() != 2 or wq.get("w_gate") is None or wq["w_gate"].dim() != 3:
+        raise ValueError("x must be [T, d] and wq['w_gate'] [E, f, d]")
     T, d = x.shape
     E, f, _ = wq["w_gate"].shape
     dev = x.device
+    _expect("x", x, (T, d), torch.bfloat16)
+    for key, shape, tdt in (("w_gate", (E, f, d), torch.uint8), ("w_gate_exp", (E, f), torch.int32),
+                            ("w_up", (E, f, d), torch.uint8), ("w_up_exp", (E, f), torch.int32),
+                            ("w_down", (E, d, f), torch.uint8), ("w_down_exp", (E, d), torch.int32)):
+        _expect(f"wq[{key!r}]", wq.get(key), shape, tdt, dev)
+    _expect("offsets", offsets, (E + 1,), torch.int32, dev)
+    _expect("sorted_assign", sorted_assign, (T * k,), torch.int32, dev)
+    _expect("y_perm", y_perm, (T * k, d), torch.bfloat16, dev, required=False)
+    _expect_ws(ws, dev)
     p = problem(T, d, E, k, f, x.dtype)
     if y_perm is None:
         y_perm = torch.empty(T * k, d, dtype=x.dtype, device=dev)
@@ -304,4 +445,25 @@ def mfma_peak_tflops(device=None, workgroups: int = 1024, iters: int = 4000, rep
         torch.cuda.synchronize(dev)
         if r > 0:
             best = max(best, workgroups * 4 * iters * 8 * 32768.0 / (a.elapsed_time(b) * 1e-3) / 1e12)
+    return best
+
+
+def stream_copy_gbs(device=None, nbytes: int = 1 << 30, reps: int = 5) -> float:
+    """The streaming bandwidth this GPU sustains in a plain device copy of
+    ``nbytes`` (``moe_stream_copy``, read + write bytes), in GB/s: the best of
+    ``reps`` timed launches after one warm-up."""
+    dev = torch.device(device or "cuda:0")
+    a = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(1)
+    stream = torch.cuda.current_stream(dev)
+    best = 0.0
+    for r in range(reps + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        L.check(L.load().moe_stream_copy(_ptr(a), _ptr(b), nbytes, _stream(dev)), "moe_stream_copy")
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+        if r > 0:
+            best = max(best, 2.0 * nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
     return best

@@ -2,8 +2,9 @@
 //
 // The MoEBlaze summary (euno.news, "MoEBlaze: breaking the memory wall for
 // efficient MoE training on modern GPUs"), Methodology item 2, has the
-// backward run on the forward's compact dispatch queues; item 3 recomputes
-// the SwiGLU intermediates instead of storing them.  Here:
+// backward run on the forward's compact dispatch queues; the checkpoint
+// bullet of the same item (and Key contributions, bullet 3) recomputes
+// intermediates instead of storing them: here the SwiGLU ones.  Here:
 //   1. per token: slot gradients dg = <dy[t], y_perm[pos]>, the queue rows'
 //      output gradient dy_perm[pos] = g dy[t], and the logit gradient of the
 //      renormalised top-k softmax, dl_j = g_j (dg_j - sum_i g_i dg_i);

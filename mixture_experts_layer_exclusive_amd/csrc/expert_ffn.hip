@@ -22,7 +22,6 @@
 // tile, so the weight tile and the activation tiles a workgroup needs are
 // mostly already in its XCD's L2.
 #include <algorithm>
-#include <atomic>
 #include <type_traits>
 
 #include "device_util.h"
@@ -917,21 +916,15 @@ int64_t expert_ffn_grid_bound(const moe_problem_t& p) {
     return m * std::max(ceil_div(p.f, kF32BN), ceil_div(p.d, kF32BN)) + NUM_XCD;
 }
 
-// Workgroups of the bf16 GEMM that run at once on the current device: one
-// per CU (each takes 160 KB of LDS), at most kSplitWGs; 0 if unknown.
-int resident_slots() {
-    static std::atomic<int> cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    int v = cache[dev].load(std::memory_order_relaxed);
-    if (v == 0) {
-        int cus = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-            return 0;
-        v = std::min(cus, kSplitWGs);
-        cache[dev].store(v, std::memory_order_relaxed);
-    }
-    return v;
+// Workgroups of the bf16 GEMM that run at once on the device of stream s:
+// one per CU (each takes 160 KB of LDS), at most kSplitWGs; 0 if unknown.
+int resident_slots(hipStream_t s) {
+    hipDevice_t dev = 0;
+    int cus = 0;
+    if (hipStreamGetDevice(s, &dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        return 0;
+    return std::min(cus, kSplitWGs);
 }
 
 hipError_t launch_expert_ffn(const moe_problem_t& p, const void* x_perm, const void* x,
@@ -957,7 +950,7 @@ hipError_t launch_expert_ffn(const moe_problem_t& p, const void* x_perm, const v
                 a, sorted_assign, p.k, offsets, p.E, static_cast<const bf16_t*>(w_gate),
                 static_cast<const bf16_t*>(w_up), static_cast<bf16_t*>(h), p.f, p.d, 0, nullptr, nullptr, nullptr, 0);
         const unsigned g2 = grid_for(n, p.E, kBM, static_cast<int>(ceil_div(p.d, kDownCols)));
-        const int slots = ffn_can_split(p) ? resident_slots() : 0;
+        const int slots = ffn_can_split(p) ? resident_slots(s) : 0;
         float* part = slots > 0 ? reinterpret_cast<float*>(static_cast<char*>(ffn_ws) + ffn_h_bytes(p)) : nullptr;
         grouped_gemm_bf16_kernel<kDown, false, false><<<g2 + (slots > 0 ? kSplitWGs : 0), 256, 0, s>>>(
             static_cast<const bf16_t*>(h), sorted_assign, p.k, offsets, p.E,
@@ -1021,7 +1014,7 @@ hipError_t launch_backward_dxperm(const moe_problem_t& p, const void* duv, const
                                   const void* w_gu_t, void* dx_perm, float* part, hipStream_t s) {
     const int64_t n = p.T * p.k;
     const unsigned g = grid_for(n, p.E, kBM, static_cast<int>(ceil_div(p.d, kDownCols)));
-    const int slots = (part != nullptr && bwd_can_split(p)) ? resident_slots() : 0;
+    const int slots = (part != nullptr && bwd_can_split(p)) ? resident_slots(s) : 0;
     grouped_gemm_bf16_kernel<kDown, false, false><<<g + (slots > 0 ? kSplitWGs : 0), 256, 0, s>>>(
         static_cast<const bf16_t*>(duv), nullptr, p.k, offsets, p.E, static_cast<const bf16_t*>(w_gu_t),
         nullptr, static_cast<bf16_t*>(dx_perm), p.d, 2 * p.f, slots, part, nullptr, nullptr, 0);
@@ -1068,7 +1061,7 @@ hipError_t launch_expert_ffn_fp8(const moe_problem_t& p, const void* x_q, const 
     if (err != hipSuccess) return err;
     const unsigned g2 = grid_for(n, p.E, kBM, static_cast<int>(ceil_div(p.d, kDownCols)));
     const int nk2 = p.f / 128;
-    const int slots = (part != nullptr && fp8_can_split(p)) ? resident_slots() : 0;
+    const int slots = (part != nullptr && fp8_can_split(p)) ? resident_slots(s) : 0;
     grouped_gemm_bf16_kernel<kDown, false, false, true><<<g2 + (slots > 0 ? kSplitWGs : 0), 256, 0, s>>>(
         static_cast<const bf16_t*>(h_q), sorted_assign, p.k, offsets, p.E, static_cast<const bf16_t*>(wd_q),
         nullptr, static_cast<bf16_t*>(y_perm), p.d, p.f, slots, part, nullptr, nullptr, 0, h_exp, wd_exp,

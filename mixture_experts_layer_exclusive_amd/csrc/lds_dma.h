@@ -25,14 +25,18 @@ __device__ __forceinline__ void wait_vmcnt_lgkm0() {
 // 16 bytes per lane from global memory straight into LDS: lane i's bytes land
 // at LDS address lds_base + 16 * i.  Issued as inline assembly so that the
 // compiler does not treat every later LDS read as dependent on it; the caller
-// orders it with wait_vmcnt and the workgroup barrier.
+// orders it with wait_vmcnt and the workgroup barrier.  The LDS address is
+// read from M0; it is an input operand bound to M0, so the compiler itself
+// writes M0 before the statement (and knows what M0 then holds) instead of
+// the statement overwriting a register the compiler may be using.  The load
+// reads M0 one wait state after a scalar write of it at the earliest (the
+// s_nop: the compiler's hazard checks do not look inside the statement).
 __device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_base) {
     asm volatile(
-        "s_mov_b32 m0, %1\n\t"
         "s_nop 0\n\t"
         "global_load_lds_dwordx4 %0, off"
         :
-        : "v"(gptr), "s"(lds_base)
+        : "v"(gptr), "{m0}"(lds_base)
         : "memory");
 }
 
@@ -40,11 +44,10 @@ __device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_base) {
 // offset (the scalar-base form of the load).
 __device__ __forceinline__ void lds_dma16_s(const void* sbase, uint32_t voff, uint32_t lds_base) {
     asm volatile(
-        "s_mov_b32 m0, %2\n\t"
         "s_nop 0\n\t"
         "global_load_lds_dwordx4 %0, %1"
         :
-        : "v"(voff), "s"(sbase), "s"(lds_base)
+        : "v"(voff), "s"(sbase), "{m0}"(lds_base)
         : "memory");
 }
 

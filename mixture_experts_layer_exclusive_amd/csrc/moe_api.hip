@@ -26,10 +26,13 @@ moe_status_t check_problem(const moe_problem_t* p) {
     if (p->dtype != MOE_DTYPE_F32 && p->dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARGUMENT;
     if (p->E > MOE_MAX_EXPERTS || p->k > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
     if (p->T > INT32_MAX / p->k) return MOE_ERR_UNSUPPORTED;
+    // a launch counts its work-items in 32 bits: the per-token kernels run
+    // up to 256 lanes per token, the expert FFN 256 per workgroup
+    if (p->T > kMaxLaunchItems / 256) return MOE_ERR_UNSUPPORTED;
     if (p->dtype == MOE_DTYPE_BF16 && (p->d % 64 != 0 || p->f % 64 != 0)) return MOE_ERR_UNSUPPORTED;
     // the bf16 GEMMs address one expert's weight matrix with 32-bit byte offsets
     if (p->dtype == MOE_DTYPE_BF16 && static_cast<int64_t>(p->d) * p->f > INT32_MAX) return MOE_ERR_UNSUPPORTED;
-    if (expert_ffn_grid_bound(*p) > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+    if (expert_ffn_grid_bound(*p) > kMaxLaunchItems / 256) return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
 
@@ -126,6 +129,8 @@ moe_status_t check_fp8(const moe_problem_t* p) {
     if (p->dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
     if (p->d % 128 != 0 || p->f % 128 != 0) return MOE_ERR_UNSUPPORTED;
     if (p->T * static_cast<int64_t>(p->d) > UINT32_MAX) return MOE_ERR_UNSUPPORTED;
+    // the weight quantisation takes every weight row as one row of a launch
+    if (static_cast<int64_t>(p->E) * std::max(p->d, p->f) > kMaxLaunchItems / 256) return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
 
@@ -437,9 +442,9 @@ moe_status_t moe_backward(const moe_problem_t* p, const void* x, const void* w_r
 
 moe_status_t moe_quantize_rows_fp8(const void* src, int64_t rows, int32_t cols, void* codes, int32_t* exps,
                                    void* stream) {
-    if (rows < 0 || cols <= 0 || rows > INT32_MAX) return rows < 0 || cols <= 0 ? MOE_ERR_INVALID_ARGUMENT
-                                                                              : MOE_ERR_UNSUPPORTED;
-    if (cols % 16 != 0) return MOE_ERR_UNSUPPORTED;
+    if (rows < 0 || cols <= 0) return MOE_ERR_INVALID_ARGUMENT;
+    // (one 256-lane workgroup per row at most: 32-bit work-item count)
+    if (rows > kMaxLaunchItems / 256 || cols % 16 != 0) return MOE_ERR_UNSUPPORTED;
     if (rows == 0) return MOE_OK;
     MOE_TRY(need(src));
     MOE_TRY(need(codes));
@@ -505,6 +510,16 @@ moe_status_t moe_expert_ffn_fp8(const moe_problem_t* p, const void* x, const int
     MOE_LAUNCH(launch_quant_rows_fp8(x, p->T, p->d, x_q, x_exp, s));
     MOE_LAUNCH(launch_expert_ffn_fp8(*p, x_q, x_exp, sorted_assign, offsets, w->w_gate, w->w_gate_exp, w->w_up,
                                      w->w_up_exp, w->w_down, w->w_down_exp, h, h_q, h_exp, part, y_perm, s));
+    return MOE_OK;
+}
+
+moe_status_t moe_stream_copy(const void* src, void* dst, size_t bytes, void* stream) {
+    if (bytes % 16 != 0) return MOE_ERR_UNSUPPORTED;
+    if (bytes == 0) return MOE_OK;
+    MOE_TRY(need(src));
+    MOE_TRY(need(dst));
+    clear_hip_error();
+    MOE_LAUNCH(launch_stream_copy(src, dst, bytes, static_cast<hipStream_t>(stream)));
     return MOE_OK;
 }
 

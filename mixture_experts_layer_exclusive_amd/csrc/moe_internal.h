@@ -28,6 +28,10 @@ constexpr int kSplitWGs = 256;
 constexpr int kSplitMax = 8;
 constexpr int kSplitMinSlices = 8;
 
+// A kernel launch counts its work-items (workgroups x threads) per grid
+// dimension in 32 bits.
+constexpr int64_t kMaxLaunchItems = 0xffffffffLL;
+
 // ---- small host helpers ------------------------------------------------------
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -59,8 +63,8 @@ inline int64_t dispatch_blocks(int64_t n_assign) { return ceil_div(n_assign, dis
 // Upper bound of sum_e ceil(count_e / bm) over any routing of n rows to E experts.
 inline int64_t max_m_tiles(int64_t n_rows, int E, int bm) { return n_rows / bm + E; }
 
-// Largest 1-D grid the expert FFN launches for problem p (validated against
-// the hardware limit before any launch).
+// Largest 1-D grid, in 256-thread workgroups, the expert FFN launches for
+// problem p (validated against the launch limit before any launch).
 int64_t expert_ffn_grid_bound(const moe_problem_t& p);
 
 // ---- launchers (return the launch status) ------------------------------------
@@ -103,6 +107,7 @@ inline int64_t backward_kpad(const moe_problem_t& p) {
 }
 
 hipError_t launch_mfma_peak(int workgroups, int iters, float* sink, hipStream_t s);
+hipError_t launch_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 hipError_t launch_quant_rows_fp8(const void* src, int64_t rows, int cols, void* codes, int32_t* exps,
                                  hipStream_t s);
 hipError_t launch_expert_ffn_fp8(const moe_problem_t& p, const void* x_q, const int32_t* x_exp,

@@ -8,9 +8,10 @@ The pages state the training side only in outline.  The MoEBlaze summary
 (euno.news, "MoEBlaze: breaking the memory wall for efficient MoE training
 on modern GPUs"), Methodology item 2, has the backward reuse the forward's
 compact dispatch queues for the gradients: reverse dispatch of the output
-gradient, the expert backward, dispatch of the input gradient.  Its item 3
-(activation checkpointing with smart recomputation) recomputes the SwiGLU
-intermediates instead of storing them.  Everything else is the derivative
+gradient, the expert backward, dispatch of the input gradient.  The
+checkpoint bullet of the same item (and Key contributions, bullet 3: smart
+activation checkpointing) stores only what the backward needs and recomputes
+the rest: here the SwiGLU intermediates are recomputed instead of stored.  Everything else is the derivative
 of the forward in ``moe_oracle``, taken by the chain rule:
 
 * slot gradients ``dg[t, j] = <dy[t], y_perm[pos(t, j)]>``;

@@ -78,6 +78,9 @@ def ws_size(lib, p, op):
     (dict(d=100), L.MOE_ERR_UNSUPPORTED),           # bf16 needs d % 64 == 0
     (dict(f=96), L.MOE_ERR_UNSUPPORTED),
     (dict(T=2 ** 30, k=2), L.MOE_ERR_UNSUPPORTED),  # T*k >= 2^31
+    # one 256-lane workgroup per token would exceed the 32-bit work-item count
+    (dict(T=2 ** 25, d=64, E=8, k=1), L.MOE_ERR_UNSUPPORTED),
+    (dict(T=2 ** 24, d=64, E=8, k=1), L.MOE_ERR_UNSUPPORTED),
     (dict(d=65536, f=32768), L.MOE_ERR_UNSUPPORTED),  # bf16 d*f >= 2^31
 ])
 def test_problem_validation(lib, bad, status):
@@ -88,6 +91,11 @@ def test_problem_validation(lib, bad, status):
     assert lib.moe_expert_ffn(ctypes.byref(p), A, None, A, A, A, A, A, A, A, 1 << 40, None) == status
     assert lib.moe_combine(ctypes.byref(p), A, A, A, A, None) == status
     assert lib.moe_forward(ctypes.byref(p), A, A, None, A, A, A, A, None, A, 1 << 40, None) == status
+
+
+def test_largest_token_count_is_accepted(lib):
+    # 2^24 - 1 tokens: 256 lanes per token still fit the 32-bit work-item count
+    assert ws_size(lib, prob(T=2 ** 24 - 1, d=64, E=8, k=1), L.MOE_OP_FORWARD)[0] == L.MOE_OK
 
 
 def test_f32_allows_any_width(lib):
@@ -257,6 +265,8 @@ def test_fp8_validation(lib):
     assert lib.moe_quantize_rows_fp8(A, -1, 16, A, A, None) == E
     assert lib.moe_quantize_rows_fp8(None, 0, 16, None, None, None) == L.MOE_OK
     assert lib.moe_quantize_rows_fp8(A, 4, 16, MIS, A, None) == U
+    # one workgroup per row: 2^24 rows of 256 lanes exceed the 32-bit work-item count
+    assert lib.moe_quantize_rows_fp8(A, 2 ** 24, 4096, A, A, None) == U
 
 
 def test_mfma_peak_validation(lib):
@@ -264,3 +274,10 @@ def test_mfma_peak_validation(lib):
     assert lib.moe_mfma_peak(4, 0, A, None) == L.MOE_ERR_INVALID_ARGUMENT
     assert lib.moe_mfma_peak(4, 10, None, None) == L.MOE_ERR_INVALID_ARGUMENT
     assert lib.moe_mfma_peak(4, 10, MIS, None) == L.MOE_ERR_UNSUPPORTED
+
+
+def test_stream_copy_validation(lib):
+    assert lib.moe_stream_copy(A, A, 24, None) == L.MOE_ERR_UNSUPPORTED   # not a multiple of 16
+    assert lib.moe_stream_copy(None, A, 32, None) == L.MOE_ERR_INVALID_ARGUMENT
+    assert lib.moe_stream_copy(A, MIS, 32, None) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_stream_copy(None, None, 0, None) == L.MOE_OK

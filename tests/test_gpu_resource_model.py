@@ -7,9 +7,12 @@ call and the backward call of the four full-size workloads, whose shapes it
 has not seen.  Inputs are random (timing does not depend on values); the
 routing comes from Gaussian logits, or Zipf-skewed ones for the skewed
 workload, and the model is given the resulting expert counts.  Each
-prediction must land within 15 % of the measured time (the target is 10 %;
-the errors are printed).
+prediction must land within 10 % of the measured time (Piper's validation
+bound); the errors are printed.  Every measured time is the median of
+several timed blocks of calls, so that one slow block does not decide it.
 """
+import statistics
+
 import pytest
 import torch
 
@@ -21,17 +24,21 @@ DEV = "cuda:0"
 BF = torch.bfloat16
 
 
-def event_us(fn, reps):
+def event_us(fn, reps, blocks=5):
+    """Median over `blocks` timed blocks of `reps` calls, in us per call."""
     for _ in range(2):
         fn()
     torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(reps):
-        fn()
-    b.record()
-    torch.cuda.synchronize()
-    return a.elapsed_time(b) * 1e3 / reps
+    per_call = []
+    for _ in range(blocks):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        per_call.append(a.elapsed_time(b) * 1e3 / reps)
+    return statistics.median(per_call)
 
 
 class Bench:
@@ -72,7 +79,7 @@ class Bench:
         ws = torch.empty(moe.workspace_size(p, 4), dtype=torch.uint8, device=DEV)
         out = {key: v for key, v in moe.backward(self.x, self.wg, self.wu, L.k, self.st, dy, wt, ws=ws).items()
                if v is not None}
-        return event_us(lambda: moe.backward(self.x, self.wg, self.wu, L.k, self.st, dy, wt, ws=ws, out=out), 5)
+        return event_us(lambda: moe.backward(self.x, self.wg, self.wu, L.k, self.st, dy, wt, ws=ws, out=out), 3)
 
 
 WORKLOADS = [("mixtral", RM.Layer(8192, 4096, 8, 2, 14336), False),
@@ -118,4 +125,4 @@ def test_time_model_predicts_unseen_workloads():
               f"({errs[name][1]:+.1%})", flush=True)
         del b
     for name, (e1, e2) in errs.items():
-        assert abs(e1) <= 0.15 and abs(e2) <= 0.15, (name, e1, e2)
+        assert abs(e1) <= 0.10 and abs(e2) <= 0.10, (name, e1, e2)
