@@ -34,8 +34,9 @@
  *   - Device pointers must be 16-byte aligned.
  *   - `stream` is a hipStream_t (NULL = the null stream).  All work is
  *     enqueued on it; no entry point synchronises, allocates or frees, and
- *     the library keeps no mutable global state, so calls on different
- *     streams with different buffers may run concurrently.
+ *     apart from moe_dispatch_no_alloc's static scratch the library keeps no
+ *     mutable global state, so calls on different streams with different
+ *     buffers may run concurrently.
  *   - Workspace `ws` (device, >= the size from moe_workspace_size) is
  *     scratch whose contents are undefined before and after the call; it
  *     must not be shared by calls that may overlap.
@@ -192,6 +193,31 @@ moe_status_t moe_dispatch(const moe_problem_t* p, const int32_t* topk_ids, const
                           int32_t* counts, int32_t* offsets,
                           int32_t* sorted_assign, int32_t* assign_pos, void* x_perm,
                           void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of the static device scratch moe_dispatch_no_alloc uses on each GPU. */
+#define MOE_NO_ALLOC_SCRATCH_BYTES (1u << 20)
+
+/*
+ * moe_dispatch_no_alloc -- moe_dispatch for callers that cannot allocate
+ * device memory or pass a workspace: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  Same arguments as
+ * moe_dispatch without ws / ws_bytes, and the same outputs, bit for bit.
+ * Its scratch (the per-block expert count table, whose size
+ * moe_workspace_size(p, MOE_OP_DISPATCH) gives) lives in a static device
+ * array of MOE_NO_ALLOC_SCRATCH_BYTES that each GPU holds until the process
+ * ends; the call allocates and frees nothing.  A problem whose table does
+ * not fit returns MOE_ERR_UNSUPPORTED before any HIP call (with 256
+ * experts, up to about 8.4 M assignments T*k fit; with 128, twice that).
+ * The first call on a GPU looks up the array's address there (once per
+ * device, briefly making that device current); a failed lookup returns
+ * MOE_ERR_HIP.  Every call on one GPU uses that GPU's one array, which keeps
+ * the last call's contents (each call writes all it reads): calls that may
+ * overlap on one GPU, on different streams or from unsynchronised threads,
+ * race and must not be issued.
+ */
+moe_status_t moe_dispatch_no_alloc(const moe_problem_t* p, const int32_t* topk_ids, const void* x,
+                                   int32_t* counts, int32_t* offsets, int32_t* sorted_assign,
+                                   int32_t* assign_pos, void* x_perm, void* stream);
 
 /*
  * moe_expert_ffn -- grouped SwiGLU expert FFN over the queues (the

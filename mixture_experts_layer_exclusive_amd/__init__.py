@@ -8,6 +8,6 @@ only binds them to torch tensors and streams.
 """
 from ._lib import MoeError, load  # noqa: F401
 from .api import (  # noqa: F401
-    backward, backward_weights, combine, dispatch, expert_ffn, expert_ffn_fp8, forward, mfma_peak_tflops,
+    backward, backward_weights, combine, dispatch, dispatch_no_alloc, expert_ffn, expert_ffn_fp8, forward, mfma_peak_tflops,
     problem, quantize_rows_fp8, quantize_weights_fp8, route, stream_copy_gbs, workspace_size,
 )

@@ -28,6 +28,7 @@ MOE_OP_EXPERT_FFN_FP8 = 5
 
 MOE_MAX_EXPERTS = 256
 MOE_MAX_TOPK = 32
+MOE_NO_ALLOC_SCRATCH_BYTES = 1 << 20
 
 # every function the header declares, with its ctypes signature
 _p = ctypes.c_void_p
@@ -68,6 +69,7 @@ SIGNATURES = {
     "moe_workspace_size": (_i32, [_PP, _i32, ctypes.POINTER(_sz)]),
     "moe_route": (_i32, [_PP, _p, _p, _p, _p, _p, _p, _p]),
     "moe_dispatch": (_i32, [_PP, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "moe_dispatch_no_alloc": (_i32, [_PP, _p, _p, _p, _p, _p, _p, _p, _p]),
     "moe_expert_ffn": (_i32, [_PP, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "moe_combine": (_i32, [_PP, _p, _p, _p, _p, _p]),
     "moe_forward": (_i32, [_PP, _p, _p, _p, _p, _p, _p, _p, ctypes.POINTER(MoeForwardOutputs),

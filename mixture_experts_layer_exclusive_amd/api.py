@@ -165,6 +165,41 @@ def dispatch(topk_ids: torch.Tensor, E: int, x: Optional[torch.Tensor] = None,
     return res
 
 
+def dispatch_no_alloc(topk_ids: torch.Tensor, E: int, x: Optional[torch.Tensor] = None,
+                      with_x_perm: bool = False, out: Optional[dict] = None) -> dict:
+    """``dispatch`` through ``moe_dispatch_no_alloc``: the library's static
+    per-GPU scratch instead of a workspace (no device allocation inside the
+    call; outputs are allocated here unless ``out`` supplies them)."""
+    if topk_ids.dim() != 2:
+        raise ValueError("topk_ids must be [T, k]")
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    _expect("topk_ids", topk_ids, (T, k), torch.int32)
+    if with_x_perm and x is None:
+        raise ValueError("with_x_perm needs x")
+    if x is not None:
+        if x.dim() != 2:
+            raise ValueError("x must be [T, d]")
+        _expect("x", x, (T, x.shape[1]), _float_dtype("x", x), dev)
+    d = x.shape[1] if x is not None else 64
+    dt = x.dtype if x is not None else torch.bfloat16
+    p = problem(T, d, E, k, 64, dt)
+    res = dict(out or {})
+    for key, shape, tdt in (("counts", (E,), torch.int32), ("offsets", (E + 1,), torch.int32),
+                            ("sorted_assign", (T * k,), torch.int32), ("assign_pos", (T * k,), torch.int32),
+                            ("x_perm", (T * k, d), dt)):
+        _expect(key, res.get(key), shape, tdt, dev, required=False)
+        if key != "x_perm" or with_x_perm:
+            res.setdefault(key, torch.empty(shape, dtype=tdt, device=dev))
+    if not with_x_perm:
+        res["x_perm"] = None
+    L.check(L.load().moe_dispatch_no_alloc(ctypes.byref(p), _ptr(topk_ids), _ptr(x), _ptr(res["counts"]),
+                                           _ptr(res["offsets"]), _ptr(res["sorted_assign"]),
+                                           _ptr(res["assign_pos"]), _ptr(res["x_perm"]), _stream(dev)),
+            "moe_dispatch_no_alloc")
+    return res
+
+
 def expert_ffn(offsets: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor,
                w_down: torch.Tensor, k: int, T: int, x_perm: Optional[torch.Tensor] = None,
                x: Optional[torch.Tensor] = None, sorted_assign: Optional[torch.Tensor] = None,

@@ -3,15 +3,26 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 #include "moe.h"
 #include "moe_internal.h"
 
 using namespace moe;
 
+// Scratch of moe_dispatch_no_alloc: the dispatch's per-block expert count
+// table (dispatch_blocks(T*k) x E int32), in a device array of its own so
+// that the call needs no workspace argument.  Each GPU the library runs on
+// holds one copy, at its own address, until the process ends.  Host code
+// never passes `scratch` itself to a kernel (on the host the name stands
+// for a host-side shadow, not a device address): it uses the address
+// hipGetSymbolAddress returns for the device (scratch_address below).
+static __device__ __align__(256) int32_t scratch[MOE_NO_ALLOC_SCRATCH_BYTES / 4];
+
 namespace {
 
-constexpr int32_t kAbiVersion = 3;
+constexpr int32_t kAbiVersion = 4;
 constexpr size_t kAlign = 256;
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
@@ -149,6 +160,40 @@ size_t forward_ws(const moe_problem_t& p) {
 
 void clear_hip_error() { (void)hipGetLastError(); }
 
+// Device address of `scratch` on the device of stream s: looked up once per
+// device, with that device current (the caller's current device is restored),
+// then kept.
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+hipError_t scratch_address(hipStream_t s, void** out) {
+    hipDevice_t dev = 0;
+    hipError_t e = hipStreamGetDevice(s, &dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void* addr = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (addr == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mutex);
+        addr = g_scratch_addr[dev].load(std::memory_order_relaxed);
+        if (addr == nullptr) {
+            int cur = 0;
+            if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+            if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+            e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+            if (cur != dev) {
+                const hipError_t e2 = hipSetDevice(cur);
+                if (e == hipSuccess) e = e2;
+            }
+            if (e != hipSuccess) return e;
+            if (addr == nullptr) return hipErrorInvalidSymbol;
+            g_scratch_addr[dev].store(addr, std::memory_order_release);
+        }
+    }
+    *out = addr;
+    return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -231,6 +276,32 @@ moe_status_t moe_dispatch(const moe_problem_t* p, const int32_t* topk_ids, const
     clear_hip_error();
     MOE_LAUNCH(launch_dispatch_queues(*p, topk_ids, counts, offsets, sorted_assign, assign_pos,
                                       static_cast<int32_t*>(ws), s));
+    if (x_perm != nullptr) MOE_LAUNCH(launch_gather_rows(*p, x, assign_pos, x_perm, s));
+    return MOE_OK;
+}
+
+moe_status_t moe_dispatch_no_alloc(const moe_problem_t* p, const int32_t* topk_ids, const void* x,
+                                   int32_t* counts, int32_t* offsets, int32_t* sorted_assign,
+                                   int32_t* assign_pos, void* x_perm, void* stream) {
+    MOE_TRY(check_problem(p));
+    if (p->T == 0) return MOE_OK;
+    MOE_TRY(need(topk_ids));
+    MOE_TRY(need(counts));
+    MOE_TRY(need(offsets));
+    MOE_TRY(need(sorted_assign));
+    MOE_TRY(need(assign_pos));
+    MOE_TRY(optional(x_perm));
+    if (x_perm != nullptr) MOE_TRY(need(x));
+    // the count table must fit the static scratch
+    if (dispatch_ws(*p) > MOE_NO_ALLOC_SCRATCH_BYTES) return MOE_ERR_UNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    clear_hip_error();
+    void* table = nullptr;
+    if (scratch_address(s, &table) != hipSuccess) return MOE_ERR_HIP;
+    // (the histogram writes every entry of the table that the scatter reads,
+    // so nothing in it has to start at zero)
+    MOE_LAUNCH(launch_dispatch_queues(*p, topk_ids, counts, offsets, sorted_assign, assign_pos,
+                                      static_cast<int32_t*>(table), s));
     if (x_perm != nullptr) MOE_LAUNCH(launch_gather_rows(*p, x, assign_pos, x_perm, s));
     return MOE_OK;
 }

@@ -46,6 +46,8 @@ def test_header_constants_match_binding():
     text = open(HEADER).read()
     assert int(re.search(r"#define MOE_MAX_EXPERTS (\d+)", text).group(1)) == L.MOE_MAX_EXPERTS
     assert int(re.search(r"#define MOE_MAX_TOPK (\d+)", text).group(1)) == L.MOE_MAX_TOPK
+    assert 1 << int(re.search(r"#define MOE_NO_ALLOC_SCRATCH_BYTES \(1u << (\d+)\)", text).group(1)) == \
+        L.MOE_NO_ALLOC_SCRATCH_BYTES
     for name in ("MOE_OK", "MOE_ERR_INVALID_ARGUMENT", "MOE_ERR_UNSUPPORTED",
                  "MOE_ERR_WORKSPACE_TOO_SMALL", "MOE_ERR_HIP", "MOE_DTYPE_F32", "MOE_DTYPE_BF16",
                  "MOE_OP_DISPATCH", "MOE_OP_EXPERT_FFN", "MOE_OP_FORWARD", "MOE_OP_BACKWARD",
@@ -281,3 +283,23 @@ def test_stream_copy_validation(lib):
     assert lib.moe_stream_copy(None, A, 32, None) == L.MOE_ERR_INVALID_ARGUMENT
     assert lib.moe_stream_copy(A, MIS, 32, None) == L.MOE_ERR_UNSUPPORTED
     assert lib.moe_stream_copy(None, None, 0, None) == L.MOE_OK
+
+
+def test_dispatch_no_alloc_validation(lib):
+    def call(p, *ptrs):
+        return lib.moe_dispatch_no_alloc(ctypes.byref(p), *ptrs, None)
+
+    good = prob(T=4096, d=64, E=128, k=8)
+    assert call(prob(k=9), A, None, A, A, A, A, None) == L.MOE_ERR_INVALID_ARGUMENT
+    assert call(good, None, None, A, A, A, A, None) == L.MOE_ERR_INVALID_ARGUMENT
+    assert call(good, A, None, A, MIS, A, A, None) == L.MOE_ERR_UNSUPPORTED
+    assert call(good, A, None, A, A, A, A, A) == L.MOE_ERR_INVALID_ARGUMENT  # x_perm without x
+    assert call(prob(T=0), None, None, None, None, None, None, None) == L.MOE_OK
+    # the count table of the largest problems does not fit the static scratch:
+    # rejected before any HIP call (the workspace size says how large it is)
+    big = prob(T=2 ** 21, d=64, E=256, k=8)
+    st, table = ws_size(lib, big, L.MOE_OP_DISPATCH)
+    assert st == L.MOE_OK and table > L.MOE_NO_ALLOC_SCRATCH_BYTES
+    assert call(big, A, None, A, A, A, A, None) == L.MOE_ERR_UNSUPPORTED
+    st, table = ws_size(lib, prob(T=65536, d=2048, E=128, k=8), L.MOE_OP_DISPATCH)
+    assert st == L.MOE_OK and table <= L.MOE_NO_ALLOC_SCRATCH_BYTES
