@@ -32,3 +32,22 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+@pytest.fixture
+def poison_workspaces(monkeypatch):
+    """Every workspace the binding allocates or is handed is filled with 0xFF
+    bytes before the call (its contents are undefined by contract), so a
+    kernel that reads workspace memory it has not written in the same call
+    (a stale table, a split-K partial) sees NaN or -1 instead of leftovers
+    that happen to be right."""
+    from mixture_experts_layer_exclusive_amd import api
+
+    real = api._workspace
+
+    def poisoned(p, op, device, ws):
+        ws, nbytes = real(p, op, device, ws)
+        ws.view(-1).view(api.torch.uint8).fill_(0xFF)
+        return ws, nbytes
+
+    monkeypatch.setattr(api, "_workspace", poisoned)

@@ -21,7 +21,7 @@ import oracle as O
 import mixture_experts_layer_exclusive_amd as moe
 from oracle import moe_backward as B
 
-pytestmark = pytest.mark.gpu
+pytestmark = [pytest.mark.gpu, pytest.mark.usefixtures("poison_workspaces")]
 DEV = "cuda:0"
 TOL = 1e-2
 

@@ -25,7 +25,7 @@ import oracle as O
 import mixture_experts_layer_exclusive_amd as moe
 from oracle import moe_fp8 as F
 
-pytestmark = pytest.mark.gpu
+pytestmark = [pytest.mark.gpu, pytest.mark.usefixtures("poison_workspaces")]
 DEV = "cuda:0"
 
 

@@ -23,7 +23,7 @@ import moe_inputs as mi
 import oracle as O
 import mixture_experts_layer_exclusive_amd as moe
 
-pytestmark = pytest.mark.gpu
+pytestmark = [pytest.mark.gpu, pytest.mark.usefixtures("poison_workspaces")]
 DEV = "cuda:0"
 TOL = {"f32": 1e-5, "bf16": 1e-2}
 
@@ -371,26 +371,33 @@ def test_zero_tokens_noop():
 # full-size workloads, in the benchmark's launch configuration
 # --------------------------------------------------------------------------
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["mixtral_8x_bf16", "deepseek_moe_bf16", "qwen3_moe_bf16", "zipf_skewed_bf16"])
-def test_full_size_workload_sampled(name):
+def test_full_size_workload(name):
+    """The whole layer at full size, in the benchmark's launch configuration,
+    with every workspace filled with 0xFF first: routing (bit-exact on
+    supplied logits, else the margin protocol), the queues (bit-exact), the
+    materialised row gather x_perm at the full width (bitwise), and y for
+    every token against the oracle's whole layer."""
     print(f"full-size {name}: generating inputs", flush=True)
     L = mi.make_layer(name, seed=0)
     p = L["problem"]
     dt = p.dtype
-    sample = mi.sample_tokens(p.T, 48, seed=0)
+    n = p.T * p.k
     xg = dev(L["x"])
     wg, wu, wd = dev(L["w_gate"]), dev(L["w_up"]), dev(L["w_down"])
     wr = dev(L["w_router"]) if L["w_router"] is not None else None
     lg = dev(L["logits"]) if L["logits"] is not None else None
-    ws = torch.empty(moe.workspace_size(moe.problem(p.T, p.d, p.E, p.k, p.f, torch.bfloat16), 3),
-                     dtype=torch.uint8, device=DEV)
+    prob = moe.problem(p.T, p.d, p.E, p.k, p.f, torch.bfloat16)
+    ws = torch.full((moe.workspace_size(prob, 3),), 0xFF, dtype=torch.uint8, device=DEV)
     y = poison((p.T, p.d), torch.bfloat16)
     print(f"full-size {name}: forward", flush=True)
     _, inter = moe.forward(xg, wg, wu, wd, p.k, w_router=wr, logits=lg, intermediates=True, ws=ws, y=y)
     torch.cuda.synchronize()
-    del xg, wg, wu, wd
+    del wg, wu, wd, ws
     ids_gpu = host(inter["topk_ids"])
     yh = host(y)
+    del y
     assert np.all(np.isfinite(yh))
 
     # routing: exact on supplied logits, else the margin protocol over all tokens
@@ -419,18 +426,49 @@ def test_full_size_workload_sampled(name):
             assert np.array_equal(v, q[key]), key
     else:
         flat = ids_gpu.reshape(-1)
-        assert counts.sum() == p.T * p.k and offsets[-1] == p.T * p.k
+        assert counts.sum() == n and offsets[-1] == n
         assert np.array_equal(np.diff(offsets), counts)
-        assert np.array_equal(ap[sa], np.arange(p.T * p.k))
+        assert np.array_equal(ap[sa], np.arange(n))
         for e in range(p.E):
             seg = sa[offsets[e]:offsets[e + 1]]
             assert np.all(flat[seg] == e) and np.all(np.diff(seg) > 0)
 
-    # values on the sampled tokens, one token at a time in the oracle
-    tok = sample[safe[sample]]
-    get = {n: (lambda a: (lambda e: f32_of(a[e], dt)))(L[n]) for n in ("w_gate", "w_up", "w_down")}
-    print(f"full-size {name}: oracle on {len(tok)} sampled tokens", flush=True)
-    ref = O.forward_tokens(tok, x32, l_ref, p.k, get["w_gate"], get["w_up"], get["w_down"])
-    err = rel(yh[tok], ref["y"])
-    print(f"full-size {name}: max|dy|/max|y| on sample = {err:.3e}", flush=True)
+    # moe_dispatch with the row gather, as the benchmark times it: the same
+    # queues, and x_perm a bitwise copy of the source rows at the full width
+    print(f"full-size {name}: dispatch with x_perm", flush=True)
+    dws = torch.full((max(256, moe.workspace_size(prob, 1)),), 0xFF, dtype=torch.uint8, device=DEV)
+    out = dict(counts=poison_i32(p.E), offsets=poison_i32(p.E + 1), sorted_assign=poison_i32(n),
+               assign_pos=poison_i32(n), x_perm=poison((n, p.d), torch.bfloat16))
+    moe.dispatch(inter["topk_ids"], p.E, x=xg, with_x_perm=True, ws=dws, out=out)
+    torch.cuda.synchronize()
+    del xg, dws
+    for key, v in (("counts", counts), ("offsets", offsets), ("sorted_assign", sa), ("assign_pos", ap)):
+        assert np.array_equal(host(out[key]), v), key
+    xp = out["x_perm"].view(torch.int16).cpu().numpy().view(np.uint16)
+    del out
+    assert np.array_equal(xp, O.gather_rows(L["x"], sa, p.k))
+    del xp
+
+    # y of every token against the oracle's whole layer, routed from the
+    # oracle's logits (tokens on a near tie excluded)
+    print(f"full-size {name}: oracle on all {p.T} tokens", flush=True)
+    wf = {nm: f32_of(L[nm], dt) for nm in ("w_gate", "w_up", "w_down")}
+    ref = O.forward(x32, p.k, wf["w_gate"], wf["w_up"], wf["w_down"], logits=l_ref)
+    err = rel(yh[safe], ref["y"][safe])
+    print(f"full-size {name}: max|dy|/max|y| over {int(safe.sum())} of {p.T} tokens = {err:.3e}", flush=True)
     assert err <= TOL[dt]
+
+
+def test_stream_copy_is_exact():
+    # the measurement copy kernel: ragged tail past the last whole 32 KB block
+    import ctypes
+    from mixture_experts_layer_exclusive_amd import _lib as LB
+    nbytes = (3 << 20) + 16 * 777
+    src = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device=DEV)
+    dst = torch.zeros(nbytes + 64, dtype=torch.uint8, device=DEV)
+    st = LB.load().moe_stream_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), nbytes,
+                                   ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == LB.MOE_OK
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:nbytes], src)
+    assert int(dst[nbytes:].count_nonzero()) == 0
