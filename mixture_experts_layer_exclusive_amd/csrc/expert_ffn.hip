@@ -936,29 +936,37 @@ hipError_t launch_expert_ffn(const moe_problem_t& p, const void* x_perm, const v
     void* h = ffn_ws;
     if (p.dtype == MOE_DTYPE_BF16) {
         const bf16_t* a = static_cast<const bf16_t*>(gather ? x : x_perm);
-        const unsigned g1 = grid_for(n, p.E, kBM, static_cast<int>(ceil_div(p.f, kGateUpCols)));
-        if (gather && p.T * p.d >= (int64_t{1} << 31))
-            grouped_gemm_bf16_kernel<kUp, true, true><<<g1, 256, 0, s>>>(
-                a, sorted_assign, p.k, offsets, p.E, static_cast<const bf16_t*>(w_gate),
-                static_cast<const bf16_t*>(w_up), static_cast<bf16_t*>(h), p.f, p.d, 0, nullptr, nullptr, nullptr, 0);
-        else if (gather)
-            grouped_gemm_bf16_kernel<kUp, true, false><<<g1, 256, 0, s>>>(
-                a, sorted_assign, p.k, offsets, p.E, static_cast<const bf16_t*>(w_gate),
-                static_cast<const bf16_t*>(w_up), static_cast<bf16_t*>(h), p.f, p.d, 0, nullptr, nullptr, nullptr, 0);
-        else
-            grouped_gemm_bf16_kernel<kUp, false, false><<<g1, 256, 0, s>>>(
-                a, sorted_assign, p.k, offsets, p.E, static_cast<const bf16_t*>(w_gate),
-                static_cast<const bf16_t*>(w_up), static_cast<bf16_t*>(h), p.f, p.d, 0, nullptr, nullptr, nullptr, 0);
-        const unsigned g2 = grid_for(n, p.E, kBM, static_cast<int>(ceil_div(p.d, kDownCols)));
-        const int slots = ffn_can_split(p) ? resident_slots(s) : 0;
-        float* part = slots > 0 ? reinterpret_cast<float*>(static_cast<char*>(ffn_ws) + ffn_h_bytes(p)) : nullptr;
-        grouped_gemm_bf16_kernel<kDown, false, false><<<g2 + (slots > 0 ? kSplitWGs : 0), 256, 0, s>>>(
-            static_cast<const bf16_t*>(h), sorted_assign, p.k, offsets, p.E,
-            static_cast<const bf16_t*>(w_down), nullptr, static_cast<bf16_t*>(y_perm), p.d, p.f, slots,
-            part, nullptr, nullptr, 0);
-        if (slots > 0)
-            split_reduce_kernel<<<kSplitWGs * 16, 256, 0, s>>>(part, offsets, p.E, p.d, p.f / 64, slots,
-                                                          static_cast<bf16_t*>(y_perm));
+        const bf16_t* wg = static_cast<const bf16_t*>(w_gate);
+        const bf16_t* wu = static_cast<const bf16_t*>(w_up);
+        const bf16_t* wd = static_cast<const bf16_t*>(w_down);
+        bf16_t* hb = static_cast<bf16_t*>(h);
+        bf16_t* yb = static_cast<bf16_t*>(y_perm);
+        // (a gathered x of 2^31 elements or more needs 64-bit row addresses)
+        const bool wide = gather && p.T * p.d >= (int64_t{1} << 31);
+        // GEMM1 (K = d): gate and up, SwiGLU epilogue -> h
+        {
+            const unsigned g = grid_for(n, p.E, kBM, static_cast<int>(ceil_div(p.f, kGateUpCols)));
+            if (wide)
+                grouped_gemm_bf16_kernel<kUp, true, true><<<g, 256, 0, s>>>(
+                    a, sorted_assign, p.k, offsets, p.E, wg, wu, hb, p.f, p.d, 0, nullptr, nullptr, nullptr, 0);
+            else if (gather)
+                grouped_gemm_bf16_kernel<kUp, true, false><<<g, 256, 0, s>>>(
+                    a, sorted_assign, p.k, offsets, p.E, wg, wu, hb, p.f, p.d, 0, nullptr, nullptr, nullptr, 0);
+            else
+                grouped_gemm_bf16_kernel<kUp, false, false><<<g, 256, 0, s>>>(
+                    a, sorted_assign, p.k, offsets, p.E, wg, wu, hb, p.f, p.d, 0, nullptr, nullptr, nullptr, 0);
+        }
+        // GEMM2 (K = f): down projection -> y_perm, its tail split in K
+        {
+            const unsigned g = grid_for(n, p.E, kBM, static_cast<int>(ceil_div(p.d, kDownCols)));
+            const int slots = ffn_can_split(p) ? resident_slots(s) : 0;
+            float* part =
+                slots > 0 ? reinterpret_cast<float*>(static_cast<char*>(ffn_ws) + ffn_h_bytes(p)) : nullptr;
+            grouped_gemm_bf16_kernel<kDown, false, false><<<g + (slots > 0 ? kSplitWGs : 0), 256, 0, s>>>(
+                hb, sorted_assign, p.k, offsets, p.E, wd, nullptr, yb, p.d, p.f, slots, part, nullptr, nullptr, 0);
+            if (slots > 0)
+                split_reduce_kernel<<<kSplitWGs * 16, 256, 0, s>>>(part, offsets, p.E, p.d, p.f / 64, slots, yb);
+        }
     } else {
         const float* a = static_cast<const float*>(gather ? x : x_perm);
         const unsigned g1 = grid_for(n, p.E, kF32BM, static_cast<int>(ceil_div(p.f, kF32BN)));

@@ -171,6 +171,10 @@ FFN_CASES = [
     (1024, 256, 4, 2, 2048, "bf16", "gauss"),  # few tiles: the down projection splits K (S = 4)
     (700, 320, 8, 2, 1088, "bf16", "gauss"),   # uneven split ranges (17 slices), column tail
     (160, 64, 256, 32, 128, "bf16", "gauss"),  # the largest E and k: 256 experts of about 20 rows
+    # long K in both GEMMs, the down projection's tail split (72 tiles: S = 3)
+    (1024, 2112, 4, 2, 4096, "bf16", "gauss"),
+    (600, 2176, 8, 2, 2240, "bf16", "zipf"),   # full tiles, skewed, column tails
+    (900, 2048, 16, 4, 2112, "bf16", "gauss"),  # the down projection at K = 2112: 33 slices
 ]
 
 
