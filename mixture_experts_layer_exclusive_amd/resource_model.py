@@ -199,10 +199,10 @@ class Hardware:
     (the micro-benchmarks of ``tests/test_gpu_resource_model.py``)."""
 
     cus: int = 256
-    slice_us: float = 1.39
-    tile_us: float = 12.7
-    upbwd_tile_us: float = 6.8
-    stream_bw: float = 4.27e6
+    slice_us: float = 1.374
+    tile_us: float = 10.81
+    upbwd_tile_us: float = 17.19
+    stream_bw: float = 5.09e6
     launch_us: float = 4.0
 
 
@@ -258,13 +258,32 @@ def list_time(hw: Hardware, tile_us: Sequence[float], xcds: int = 8) -> float:
     return worst
 
 
-def wgrad_time(hw: Hardware, counts: Sequence[int], M: int, N: int) -> float:
+def xcd_list_time(hw: Hardware, lists: Sequence[Sequence[float]]) -> float:
+    """Makespan when XCD x runs the tiles of lists[x] in order, each on the
+    CU of that XCD that frees first."""
+    per = hw.cus // len(lists)
+    worst = 0.0
+    for tiles in lists:
+        heap = [0.0] * per
+        for t in tiles:
+            heapq.heappush(heap, heapq.heappop(heap) + t)
+        worst = max(worst, max(heap))
+    return worst
+
+
+def wgrad_time(hw: Hardware, counts: Sequence[int], M: int, N: int, xcds: int = 8) -> float:
     """One weight-gradient launch: per expert ceil(M/256) * ceil(N/256) tiles
-    of K = its padded row count, experts taken heaviest first."""
+    of K = its padded row count.  Whole experts go to XCDs, heaviest first
+    (ties: lower id) in a snake order (XCD 0 to 7, then 7 to 0, ...), and
+    each XCD runs its experts' tiles in that order on its CUs."""
     per_e = _cdiv(M, TM) * _cdiv(N, DOWN_COLS)
-    pc = sorted(((_cdiv(int(c), BK), -e) for e, c in enumerate(counts)), reverse=True)
-    times = [hw.slice_us * nk + hw.tile_us for nk, _ in pc for _ in range(per_e)]
-    return list_time(hw, times)
+    nks = [_cdiv(int(c), BK) for c in counts]
+    order = sorted(range(len(counts)), key=lambda e: (-nks[e], e))
+    lists = [[] for _ in range(xcds)]
+    for r, e in enumerate(order):
+        j, i = divmod(r, xcds)
+        lists[xcds - 1 - i if j % 2 else i].extend([hw.slice_us * nks[e] + hw.tile_us] * per_e)
+    return xcd_list_time(hw, lists)
 
 
 def _backward_parts(L: Layer, counts: Sequence[int], hw: Hardware) -> Dict[str, float]:

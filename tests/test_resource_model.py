@@ -115,6 +115,14 @@ def test_list_schedule():
     assert RM.list_time(hw, [1.0] * 32) == 2.0
     # one long tile bounds its XCD; the others finish earlier
     assert RM.list_time(hw, [10.0] + [1.0] * 15) == 10.0
-    # a heavy expert's tiles are spread over the XCDs, not given to one
+    # whole experts per XCD: the heavy expert's one tile bounds its XCD
     t = RM.wgrad_time(RM.Hardware(slice_us=1.0, tile_us=0.0), [64 * 100] + [64] * 15, 256, 256)
     assert t == 100.0
+    # snake order: 16 experts of 16 tiles each on 16 CUs (2 per XCD); ranks 0
+    # and 15 share XCD 0, ranks 7 and 8 XCD 7: 16 tiles of 8 slices per CU pair
+    counts = [64 * (16 - e) for e in range(16)]
+    t = RM.wgrad_time(RM.Hardware(cus=16, slice_us=1.0, tile_us=0.0), counts, 4 * 256, 4 * 256)
+    assert t == (16 + 1) * 16 / 2
+    # one expert's tiles (16 here) never leave its XCD
+    t = RM.wgrad_time(RM.Hardware(cus=16, slice_us=1.0, tile_us=0.0), [64] + [0] * 7, 4 * 256, 4 * 256)
+    assert t == 16 / 2
