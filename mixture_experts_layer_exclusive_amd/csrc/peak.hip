@@ -42,25 +42,35 @@ __global__ __launch_bounds__(256) void mfma_peak_kernel(int iters, float* __rest
     if (threadIdx.x == 0) sink[blockIdx.x] = s;
 }
 
-// dst[i] = src[i] over n16 16-byte words: each workgroup copies 2048-word
-// (32 KB) blocks, 8 loads in flight per thread, blocks strided by the grid.
-constexpr int kCopyUnroll = 8;
+// dst[i] = src[i] over n16 16-byte words.  A workgroup copies 1024-word
+// (16 KB) blocks strided by the grid: each thread first loads its 4 words
+// (all in flight together), then stores them, with non-temporal loads and
+// stores (the data is touched once).  Measured on one MI355X, 1 GiB: 6.0
+// TB/s on 4096 workgroups, against 5.3 TB/s for hipMemcpyAsync and 5.3-5.6
+// TB/s with 8 or 16 words per thread or temporal accesses.
+constexpr int kCopyUnroll = 4;
 constexpr int64_t kCopyBlockWords = 256 * kCopyUnroll;
+constexpr int64_t kCopyGrid = 4096;
 
-__global__ __launch_bounds__(256) void stream_copy_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+__global__ __launch_bounds__(256) void stream_copy_kernel(const u32x4_t* __restrict__ src, u32x4_t* __restrict__ dst,
                                                           int64_t n16) {
     const int64_t step = static_cast<int64_t>(gridDim.x) * kCopyBlockWords;
-    for (int64_t base = static_cast<int64_t>(blockIdx.x) * kCopyBlockWords; base < n16; base += step) {
-        uint4 v[kCopyUnroll];
+    int64_t base = static_cast<int64_t>(blockIdx.x) * kCopyBlockWords;
+    // whole blocks: no bounds checks between the loads, so all 4 are in flight
+    for (; base + kCopyBlockWords <= n16; base += step) {
+        const u32x4_t* s = src + base + threadIdx.x;
+        u32x4_t* d = dst + base + threadIdx.x;
+        u32x4_t v[kCopyUnroll];
 #pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u) v[u] = __builtin_nontemporal_load(s + u * 256);
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u) __builtin_nontemporal_store(v[u], d + u * 256);
+    }
+    // the last, partial block
+    if (base < n16) {
         for (int u = 0; u < kCopyUnroll; ++u) {
             const int64_t i = base + u * 256 + threadIdx.x;
-            if (i < n16) v[u] = src[i];
-        }
-#pragma unroll
-        for (int u = 0; u < kCopyUnroll; ++u) {
-            const int64_t i = base + u * 256 + threadIdx.x;
-            if (i < n16) dst[i] = v[u];
+            if (i < n16) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
         }
     }
 }
@@ -70,8 +80,8 @@ __global__ __launch_bounds__(256) void stream_copy_kernel(const uint4* __restric
 hipError_t launch_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t s) {
     const int64_t n16 = static_cast<int64_t>(bytes / 16);
     const int64_t blocks = ceil_div(n16, kCopyBlockWords);
-    const unsigned grid = static_cast<unsigned>(blocks < 65536 ? blocks : 65536);
-    stream_copy_kernel<<<grid, 256, 0, s>>>(static_cast<const uint4*>(src), static_cast<uint4*>(dst), n16);
+    const unsigned grid = static_cast<unsigned>(blocks < kCopyGrid ? blocks : kCopyGrid);
+    stream_copy_kernel<<<grid, 256, 0, s>>>(static_cast<const u32x4_t*>(src), static_cast<u32x4_t*>(dst), n16);
     return hipGetLastError();
 }
 
