@@ -175,6 +175,10 @@ FFN_CASES = [
     (1024, 2112, 4, 2, 4096, "bf16", "gauss"),
     (600, 2176, 8, 2, 2240, "bf16", "zipf"),   # full tiles, skewed, column tails
     (900, 2048, 16, 4, 2112, "bf16", "gauss"),  # the down projection at K = 2112: 33 slices
+    # pairs of column tiles: an odd number of them (the last pair has one
+    # tile) and a ragged last column tile, in both GEMMs
+    (700, 1216, 8, 2, 704, "bf16", "zipf"),
+    (500, 1280, 16, 4, 384, "bf16", "gauss"),
 ]
 
 
