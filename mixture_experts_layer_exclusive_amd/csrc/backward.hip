@@ -146,7 +146,9 @@ __global__ __launch_bounds__(64) void bwd_poff_kernel(const int32_t* __restrict_
 // sorted_assign[pos] / k of src.  Tiles of 64 columns x 64 rows through LDS.
 // With GATHER and wr_part, block b = q / 64 also yields the router-gradient
 // partial sums wr_part[b, c] = sum over its columns q of dsel[a_q] src[c]
-// (a_q = sorted_assign[pos]; zero for padding), in a fixed order.
+// (a_q = sorted_assign[pos]; zero for padding), in a fixed order.  With dst
+// NULL only the partial sums are written (the weight gradients read their
+// operands in queue order and need no transposed copy).
 template <bool GATHER>
 __global__ __launch_bounds__(256) void bwd_transpose_kernel(const bf16_t* __restrict__ src,
                                                            int64_t ld_src, int C,
@@ -186,7 +188,7 @@ __global__ __launch_bounds__(256) void bwd_transpose_kernel(const bf16_t* __rest
     __syncthreads();
     const int eb = s_e;
     const int64_t ke = poff[eb + 1] - poff[eb];
-    bf16_t* const dst_e = dst + static_cast<int64_t>(poff[eb]) * C + (q0 - poff[eb]);
+    bf16_t* const dst_e = dst == nullptr ? nullptr : dst + static_cast<int64_t>(poff[eb]) * C + (q0 - poff[eb]);
     // load: thread -> (row i = tid / 4, 16 columns (tid % 4) * 16 ..)
     {
         const int i = threadIdx.x >> 2;
@@ -225,8 +227,9 @@ __global__ __launch_bounds__(256) void bwd_transpose_kernel(const bf16_t* __rest
                         part = fmaf(s_dsel[qq + u + 2 * h + 1], bf16_to_f32(hi), part);
                     }
                 }
-                *reinterpret_cast<uint4*>(dst_e + static_cast<int64_t>(c0 + c) * ke + qq + u) =
-                    make_uint4(w[0], w[1], w[2], w[3]);
+                if (dst != nullptr)
+                    *reinterpret_cast<uint4*>(dst_e + static_cast<int64_t>(c0 + c) * ke + qq + u) =
+                        make_uint4(w[0], w[1], w[2], w[3]);
             }
         }
         if (GATHER && wr_part != nullptr) {

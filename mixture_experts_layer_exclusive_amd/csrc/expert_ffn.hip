@@ -143,6 +143,7 @@ __device__ __forceinline__ SplitPlan split_plan(int total, int slots, int nk) {
 struct Work {
     Tile t;
     int kb, nkl, j;
+    int kv = 64;  // weight gradients: valid K rows of the last slice
 };
 __device__ __forceinline__ bool find_work(const int* s_off, int E, int bm, int n_tiles,
                                           const int* s_prefix, int nk, int slots, Work& w) {
@@ -227,6 +228,12 @@ __device__ __forceinline__ float sigmoid_fast(float u) {
 // LDS slot of chunk c of tile row r: c ^ slot_swizzle(r).
 __device__ __forceinline__ int slot_swizzle(int r) { return (r >> 1) & 7; }
 
+// Weight gradients (512-byte LDS rows of 32 chunks): slot of chunk c of row r
+// is c ^ wg_swizzle(r).  The transposing reads of one instruction touch 8
+// rows (r & 3 = 0..3, twice) of 64 bytes each; flipping chunk bits 2-3 by
+// r & 3 puts rows with different r & 3 on different 16-bank groups.
+__device__ __forceinline__ int wg_swizzle(int r) { return (r & 3) << 2; }
+
 // A pointer that is wave-uniform but not provably so to the compiler, moved
 // to scalar registers.
 template <typename T>
@@ -242,12 +249,11 @@ __device__ __forceinline__ const T* uniform_ptr(const T* p) {
 //   kDown  C = A B^T over the queue rows (forward GEMM2; the backward's dh and dx)
 //   kUpBwd the backward's recompute of gate and up, with an epilogue that
 //          takes dh and writes du, dv (side by side, [rows, 2f]) and h
-//   kWgrad weight gradients: per expert e, C_e[M, N] = A_e B_e^T over the
-//          expert's K_e = poff[e+1] - poff[e] padded queue columns.  The
-//          operands are transposed, padding zero, and stored per expert:
-//          expert e's block of A (K rows, of which rows a_row_off ..
-//          a_row_off + M are used) starts at element poff[e] * K, that of B
-//          (N rows) at poff[e] * N, each row K_e elements long
+//   kWgrad weight gradients: per expert e, C_e[M, N] = sum over the
+//          expert's queue rows q of A[q, a_row_off + m] B[q, n], with A and
+//          B in queue order ([rows, K] and [rows, N]: K is A's row length
+//          here) and read through transposing LDS reads, so no transposed
+//          copy of either operand is made
 constexpr int kUp = 0, kDown = 1, kUpBwd = 2, kWgrad = 3;
 
 // Work of a weight-gradient workgroup: tile (mt, nt) of expert e, K slices of
@@ -268,7 +274,7 @@ constexpr int kUp = 0, kDown = 1, kUpBwd = 2, kWgrad = 3;
 __host__ __device__ __forceinline__ int wgrad_tiles_per_expert(int M, int N) {
     return ((M + kBM - 1) / kBM) * ((N + kDownCols - 1) / kDownCols);
 }
-__device__ __forceinline__ bool find_wgrad_work(const int32_t* __restrict__ poff,
+__device__ __forceinline__ bool find_wgrad_work(const int32_t* __restrict__ offsets,
                                                 const int32_t* __restrict__ order, int E, int M, int N,
                                                 Work& w) {
     const int mtn = (M + kBM - 1) / kBM;
@@ -297,9 +303,12 @@ __device__ __forceinline__ bool find_wgrad_work(const int32_t* __restrict__ poff
     w.t.nt = l2 / gsz;
     w.t.row0 = mt * kBM;
     w.t.row1 = min(M, w.t.row0 + kBM);
-    const int k0 = poff[e], k1 = poff[e + 1];
-    w.kb = k0 / 64;
-    w.nkl = (k1 - k0) / 64;
+    // (K runs over the expert's queue rows in slices of 64; the rows past
+    // its end in the last slice are read but zeroed)
+    const int k0 = offsets[e], cnt = offsets[e + 1] - k0;
+    w.kb = k0;
+    w.nkl = (cnt + 63) / 64;
+    w.kv = cnt - 64 * (w.nkl - 1);
     w.j = -1;
     return true;
 }
@@ -348,9 +357,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 
     Work work;
     if (WG) {
-        // (K is the row count of A's per-expert blocks here; offsets are
-        // the padded offsets and sorted_assign the expert order, heaviest
-        // first)
+        // (sorted_assign is the expert order, heaviest first, here)
         if (!find_wgrad_work(offsets, sorted_assign, E, M, N, work)) return;
     } else {
         build_tile_prefix(offsets, E, TM, s_prefix, s_off);
@@ -382,17 +389,34 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const char* a_src[WIDE ? LA : 1];
     uint32_t a_off[WIDE ? 1 : LA];
     const char* const Ab = reinterpret_cast<const char*>(A);
-    // bytes per operand row (weight gradients: the expert's K_e columns)
-    const int64_t RB = WG ? static_cast<int64_t>(work.nkl) * 128 : static_cast<int64_t>(K) * EB;
+    // bytes per operand row (weight gradients: A's rows of K elements)
+    const int64_t RB = static_cast<int64_t>(K) * EB;
     // (the K range [work.kb, work.kb + work.nkl) of 128-byte slices is folded
-    // into the bases; a weight-gradient tile starts at its expert's block,
-    // whose first column is poff[e] = 64 kb)
+    // into the bases; a weight-gradient tile starts at its expert's first
+    // queue row work.kb, at column a_row_off + its first output row)
     const char* const a_base =
-        uniform_ptr(WG ? Ab + static_cast<int64_t>(work.kb) * 128 * K + (a_row_off + tile.row0) * RB
+        uniform_ptr(WG ? Ab + static_cast<int64_t>(work.kb) * RB + (a_row_off + tile.row0) * 2
                        : (GATHER ? Ab : Ab + static_cast<int64_t>(tile.row0) * RB) + work.kb * 128);
+    // Weight gradients stage a slice as 64 queue rows x 256 channels of each
+    // operand (512-byte LDS rows: the same 32 KB per operand, at the same LDS
+    // places as the other modes).  Load j of wave w covers queue rows w*16 +
+    // 2j and + 1 (lane -> row lane >> 5, slot lane & 31); slot s of row r
+    // holds channel chunk s ^ wg_swizzle(r).  One slice advances 64 rows.
+    const int64_t RBB = WG ? static_cast<int64_t>(N) * 2 : RB;  // bytes per B row
+    const int64_t a_step = WG ? 64 * RB : 128;
+    const int64_t b_step = WG ? 64 * RBB : 128;
     // (gathered rows need a lookup in sorted_assign: called after the first
     // weight loads are on their way)
     auto setup_a = [&]() {
+        if constexpr (WG) {
+#pragma unroll
+            for (int j = 0; j < LA; ++j) {
+                const int r = wave * 16 + 2 * j + (lane >> 5);
+                a_off[0 * WIDE + j] = static_cast<uint32_t>(r) * static_cast<uint32_t>(RB) +
+                                      static_cast<uint32_t>(((lane & 31) ^ wg_swizzle(r)) * 16);
+            }
+            return;
+        }
 #pragma unroll
         for (int j = 0; j < LA; ++j) {
             const int r = wave * 64 + j * 8 + lrow;
@@ -414,10 +438,17 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const int rb0 = wave * (TN / 4);
     const char* const b_base =
         uniform_ptr(reinterpret_cast<const char*>(GATEUP && rb0 >= TN / 2 ? B1 : B0) +
-                    (WG ? static_cast<int64_t>(work.kb) * 128 * N : static_cast<int64_t>(tile.e) * N * RB + work.kb * 128));
+                    (WG ? static_cast<int64_t>(work.kb) * RBB + static_cast<int64_t>(n0) * 2
+                        : static_cast<int64_t>(tile.e) * N * RB + work.kb * 128));
     uint32_t b_off[LB];
 #pragma unroll
     for (int j = 0; j < LB; ++j) {
+        if (WG) {
+            const int r = wave * 16 + 2 * j + (lane >> 5);
+            b_off[j] = static_cast<uint32_t>(r) * static_cast<uint32_t>(RBB) +
+                       static_cast<uint32_t>(((lane & 31) ^ wg_swizzle(r)) * 16);
+            continue;
+        }
         const int r = rb0 + j * 8 + lrow;
         const int chunk = lslot ^ slot_swizzle(r);
         int n = n0 + (GATEUP && r >= TN / 2 ? r - TN / 2 : r);
@@ -431,11 +462,11 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     auto dma_a = [&](int j, int kt) {
         const uint32_t so = static_cast<uint32_t>((kt & 1) * STAGE_BYTES);
         if (WIDE) lds_dma16(a_src[WIDE ? j : 0] + kt * 128, lds_a + so + j * 8 * ROWB);
-        else lds_dma16_s(a_base + kt * 128, a_off[WIDE ? 0 : j], lds_a + so + j * 8 * ROWB);
+        else lds_dma16_s(a_base + kt * a_step, a_off[WIDE ? 0 : j], lds_a + so + j * 8 * ROWB);
     };
     auto dma_b = [&](int j, int kt) {
         const uint32_t so = static_cast<uint32_t>((kt & 1) * STAGE_BYTES);
-        lds_dma16_s(b_base + kt * 128, b_off[j], lds_b + so + j * 8 * ROWB);
+        lds_dma16_s(b_base + kt * b_step, b_off[j], lds_b + so + j * 8 * ROWB);
     };
     // load q (< NL) of slice kt, in the GEMM's load order
     auto dma = [&](int q, int kt) {
@@ -460,6 +491,28 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     uint32_t foff[KS];
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) foff[kk] = l32 * ROWB + (((2 * kk + khalf) ^ slot_swizzle(l32)) * 16);
+    // Weight gradients: a fragment (32 channels x 16 K values) is two
+    // transposing reads (ds_read_b64_tr_b16) of the [K][channel] stage.  In
+    // each 16-lane group g (lanes 16g + i), lane i addresses queue row
+    // (g >> 1) * 8 + (i >> 2) (and + 4 for the second read) and channels
+    // (g & 1) * 16 + 4 (i & 3) .. + 4 of the block, and receives channel
+    // (g & 1) * 16 + i at the 4 rows from there: element t of the fragment
+    // is K row (g >> 1) * 8 + t of the step (lane mapping checked on gfx950).
+    // The swizzle flips bits 2-3 of the chunk, so the block's offset depends
+    // on the lane's row: one offset per block (A: 0..3, B: 4..7).
+    constexpr int WROWB = 512;  // bytes per LDS row of a weight-gradient slice
+    static_assert(SA_BYTES == 64 * WROWB, "64 queue rows of 256 channels per operand and stage");
+    uint32_t wofs[WG ? NR : 1];
+    if constexpr (WG) {
+        const int g = lane >> 4, i = lane & 15, q = (i >> 2) & 3;
+        const uint32_t rb = static_cast<uint32_t>(((g >> 1) * 8 + (i >> 2)) * WROWB);
+        const int low = (g & 1) * 2 + ((i & 3) >> 1);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            wofs[b] = rb + ((wm * 16 + ((b ^ q) << 2) + low) << 4) + 8 * (i & 1);
+            wofs[4 + b] = SA_BYTES + rb + ((wn * 16 + ((b ^ q) << 2) + low) << 4) + 8 * (i & 1);
+        }
+    }
     const char* const sa_w = smem + wm * 128 * ROWB;
     const char* const sb_w = smem + SA_BYTES;
     auto b_row0 = [&](int nb) {
@@ -468,6 +521,24 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     };
 
     const int nk = work.nkl;
+    // Weight gradients: in an expert's last slice the queue rows from work.kv
+    // on are not the expert's (the next expert's rows, or padding rows past
+    // the last queue row).  Each wave zeroes its own rows among them, in
+    // both operands, once its loads of that slice have landed and before
+    // the barrier that publishes the slice; then the waits that barrier needs.
+    auto zero_tail_rows = [&](int kt) {
+        if constexpr (WG) {
+            if (kt == nk - 1 && work.kv < 64) {
+                char* const st = smem + (kt & 1) * STAGE_BYTES + (lane < 32 ? 0 : SA_BYTES) + (lane & 31) * 16;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const int r = wave * 16 + j;
+                    if (r >= work.kv) *reinterpret_cast<i32x4_t*>(st + r * WROWB) = i32x4_t{0, 0, 0, 0};
+                }
+                wait_vmcnt_lgkm0<0>();
+            }
+        }
+    };
     // All fragments of one slice: step kk's activation blocks f[kk][0..3] and
     // weight blocks f[kk][4..7].
     bf16x8_t f[F8 ? 1 : KS][NR];
@@ -477,6 +548,15 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // index)
     i32x8_t g[F8 ? 2 : 1][NR];
     auto read_frag = [&](int kk, int i, uint32_t so) {
+        if constexpr (WG) {
+            typedef short ws4_t __attribute__((ext_vector_type(4)));
+            typedef __attribute__((address_space(3))) ws4_t* lds_ws4_t;
+            const uint32_t a = lds_addr(smem) + so + wofs[i] + kk * 16 * WROWB;
+            const ws4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_ws4_t>(a));
+            const ws4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_ws4_t>(a + 4 * WROWB));
+            f[kk][i] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            return;
+        }
         const char* base = i < 4 ? sa_w + so + i * 32 * ROWB : sb_w + so + b_row0(i - 4) * ROWB;
         if constexpr (F8) {
             const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(base + foff[2 * kk]);
@@ -551,6 +631,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             wait_vmcnt_lgkm0<LA>();
         } else {
             wait_vmcnt_lgkm0<0>();
+            zero_tail_rows(0);
         }
         barrier_lds();
 #pragma unroll
@@ -565,22 +646,25 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         const uint32_t so = static_cast<uint32_t>((kt & 1) * STAGE_BYTES);
         const uint32_t nso = static_cast<uint32_t>(((kt + 1) & 1) * STAGE_BYTES);
         // step 0: the reads of the remaining steps (bf16: 24 over 16 MFMAs;
-        // fp8: 16 over 8)
+        // fp8: 16 over 8; weight gradients: 48 transposing reads over 16)
+        {
 #pragma unroll
-        for (int kk = KPRE; kk < KREAD; ++kk)
+            for (int kk = KPRE; kk < KREAD; ++kk)
 #pragma unroll
-            for (int i = 0; i < NR; ++i) read_frag(kk, i, so);
+                for (int i = 0; i < NR; ++i) read_frag(kk, i, so);
 #pragma unroll
-        for (int q = 0; q < NM; ++q) MOE_MFMA(0, q);
+            for (int q = 0; q < NM; ++q) MOE_MFMA(0, q);
+            constexpr int RPM = WG ? 3 : 2;  // LDS reads per MFMA in the first half
 #pragma unroll
-        for (int i = 0; i < NR; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        }
+            for (int i = 0; i < NR; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);
+            }
 #pragma unroll
-        for (int i = NR; i < NM; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            for (int i = NR; i < NM; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, WG ? 3 : 1, 0);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
         wait_vmcnt_lgkm0<63>();
@@ -601,6 +685,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             barrier_lds();
         } else if (kt + 1 < nk) {
             wait_vmcnt<0>();
+            zero_tail_rows(kt + 1);
             barrier_lds();
         }
         // step 3 (after the last slice the reads fetch a stale, in-bounds
@@ -1051,21 +1136,20 @@ hipError_t launch_backward_dxperm(const moe_problem_t& p, const void* duv, const
     return hipGetLastError();
 }
 
-// Weight gradient per expert: C[e] [M, N] = A_e B_e^T over the expert's padded
-// queue columns [poff[e], poff[e+1]); A and B hold per-expert blocks (A:
-// a_rows rows, of which a_row_off .. + M are used; B: N rows; rows of the
-// expert's K_e columns); order: the experts by descending row count.
-hipError_t launch_backward_wgrad(const moe_problem_t& p, const void* A, int M, int a_rows, int a_row_off,
-                                 const void* B, int N, const int32_t* poff, const int32_t* order, void* C,
+// Weight gradient per expert: C[e] [M, N] = sum over the expert's queue rows
+// q in [offsets[e], offsets[e+1]) of A[q, a_col_off + m] B[q, n], with A
+// [rows, lda] and B [rows, N] in queue order (each with kWgradPadRows rows
+// after the last queue row); order: the experts by descending row count.
+hipError_t launch_backward_wgrad(const moe_problem_t& p, const void* A, int lda, int a_col_off, int M,
+                                 const void* B, int N, const int32_t* offsets, const int32_t* order, void* C,
                                  hipStream_t s) {
     // (every XCD's list is sized for the most experts one XCD receives)
     const int64_t tiles =
         ceil_div(p.E, NUM_XCD) * NUM_XCD * static_cast<int64_t>(wgrad_tiles_per_expert(M, N));
     const unsigned g = static_cast<unsigned>(tiles);
     grouped_gemm_bf16_kernel<kWgrad, false, false><<<g, 256, 0, s>>>(
-        static_cast<const bf16_t*>(A), order, p.k, poff, p.E, static_cast<const bf16_t*>(B), nullptr,
-        static_cast<bf16_t*>(C), N, a_rows, 0, nullptr, nullptr, nullptr, M, nullptr, nullptr, nullptr,
-        a_row_off);
+        static_cast<const bf16_t*>(A), order, p.k, offsets, p.E, static_cast<const bf16_t*>(B), nullptr,
+        static_cast<bf16_t*>(C), N, lda, 0, nullptr, nullptr, nullptr, M, nullptr, nullptr, nullptr, a_col_off);
     return hipGetLastError();
 }
 

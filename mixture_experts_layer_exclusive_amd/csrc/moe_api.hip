@@ -89,38 +89,39 @@ size_t dispatch_ws(const moe_problem_t& p) {
 
 size_t ffn_ws(const moe_problem_t& p) { return ffn_h_bytes(p) + ffn_split_bytes(p); }
 
-// Backward workspace: dsel [T*k] fp32, dy_perm and dx_perm [T*k, d], dh and
-// h [T*k, f], duv [T*k, 2f], poff [E+1], the expert order [E], the transposed operands of the
-// weight gradients dy_perm^T and x_perm^T [d, kpad], h^T [f, kpad],
-// duv^T [2f, kpad], the router-gradient partial sums [kpad / 64, d] fp32
-// and the split-K partial tiles of the dx_perm GEMM.
+// Backward workspace: dsel [T*k] fp32; dy_perm [T*k + pad, d]; dx_perm
+// [T*k, d]; dh [T*k, f]; h [T*k + pad, f]; du|dv [T*k + pad, 2f]; padded
+// offsets [E+1] and the expert order [E]; x_perm [T*k + pad, d] (x gathered
+// into queue order); the router-gradient partial sums [kpad / 64, d] fp32;
+// the split-K partial tiles of the dx_perm GEMM.  dy_perm, h, du|dv and
+// x_perm are the weight gradients' queue-order operands (pad =
+// kWgradPadRows rows after the last queue row).
 size_t backward_ws(const moe_problem_t& p) {
     const size_t n = static_cast<size_t>(p.T) * p.k;
+    const size_t np = n + static_cast<size_t>(kWgradPadRows);
     const size_t kp = static_cast<size_t>(backward_kpad(p));
     size_t b = align_up(n * 4, kAlign);
-    b += align_up(n * p.d * 2, kAlign) * 2;          // dy_perm, dx_perm
-    b += align_up(n * p.f * 2, kAlign) * 2;          // dh, h
-    b += align_up(n * 2 * p.f * 2, kAlign);          // duv
+    b += align_up(np * p.d * 2, kAlign);             // dy_perm
+    b += align_up(n * p.d * 2, kAlign);              // dx_perm
+    b += align_up(n * p.f * 2, kAlign);              // dh
+    b += align_up(np * p.f * 2, kAlign);             // h
+    b += align_up(np * 2 * p.f * 2, kAlign);         // du|dv
     b += align_up(static_cast<size_t>(p.E + 1) * 4, kAlign);
     b += align_up(static_cast<size_t>(p.E) * 4, kAlign);           // expert order
-    b += align_up(static_cast<size_t>(p.d) * kp * 2, kAlign) * 2;  // dy^T, x^T
-    b += align_up(static_cast<size_t>(p.f) * kp * 2, kAlign);      // h^T
-    b += align_up(static_cast<size_t>(2 * p.f) * kp * 2, kAlign);  // duv^T
+    b += align_up(np * p.d * 2, kAlign);             // x_perm
     b += align_up(static_cast<size_t>(kp / 64) * p.d * 4, kAlign);
     b += align_up(bwd_split_bytes(p), kAlign);
     return b;
 }
 
 // Limits of the bf16 backward (beyond check_problem): the GEMMs address
-// [E, d, 2f] weight rows and the padded transposed operands with 32-bit
-// byte offsets (which also keeps T * d below 2^31, so the recompute's
-// gather of x needs no 64-bit addresses).
+// [E, d, 2f] weight rows with 32-bit byte offsets, and the recompute's gather
+// of x takes 32-bit offsets too (T * d below 2^31).
 moe_status_t check_backward(const moe_problem_t* p) {
     if (p->dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
     if (static_cast<int64_t>(p->d) * p->f >= (int64_t{1} << 30)) return MOE_ERR_UNSUPPORTED;
-    const int64_t kp = backward_kpad(*p);
-    if (kp > INT32_MAX || static_cast<int64_t>(p->d > p->f ? p->d : p->f) * kp * 2 > UINT32_MAX)
-        return MOE_ERR_UNSUPPORTED;
+    if (p->T * static_cast<int64_t>(p->d) >= (int64_t{1} << 31)) return MOE_ERR_UNSUPPORTED;
+    if (backward_kpad(*p) > INT32_MAX) return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
 
@@ -461,20 +462,18 @@ moe_status_t moe_backward(const moe_problem_t* p, const void* x, const void* w_r
     if (ws_bytes < backward_ws(*p)) return MOE_ERR_WORKSPACE_TOO_SMALL;
 
     const size_t n = static_cast<size_t>(p->T) * p->k;
+    const size_t np = n + static_cast<size_t>(kWgradPadRows);
     const int64_t kp = backward_kpad(*p);
     Carver c(ws);
     float* dsel = c.take<float>(n * 4);
-    void* dy_perm = c.take<char>(n * p->d * 2);
+    void* dy_perm = c.take<char>(np * p->d * 2);
     void* dx_perm = c.take<char>(n * p->d * 2);
     void* dh = c.take<char>(n * p->f * 2);
-    void* h = c.take<char>(n * p->f * 2);
-    void* duv = c.take<char>(n * 2 * p->f * 2);
+    void* h = c.take<char>(np * p->f * 2);
+    void* duv = c.take<char>(np * 2 * p->f * 2);
     int32_t* poff = c.take<int32_t>(static_cast<size_t>(p->E + 1) * 4);
     int32_t* order = c.take<int32_t>(static_cast<size_t>(p->E) * 4);
-    void* dyT = c.take<char>(static_cast<size_t>(p->d) * kp * 2);
-    void* xT = c.take<char>(static_cast<size_t>(p->d) * kp * 2);
-    void* hT = c.take<char>(static_cast<size_t>(p->f) * kp * 2);
-    void* duvT = c.take<char>(static_cast<size_t>(2 * p->f) * kp * 2);
+    void* x_perm = c.take<char>(np * p->d * 2);
     float* wr_part = c.take<float>(static_cast<size_t>(kp / 64) * p->d * 4);
     float* split = bwd_split_bytes(*p) > 0 ? c.take<float>(bwd_split_bytes(*p)) : nullptr;
 
@@ -491,21 +490,20 @@ moe_status_t moe_backward(const moe_problem_t* p, const void* x, const void* w_r
         MOE_LAUNCH(launch_backward_dxperm(*p, duv, fw->offsets, w_gu_t, dx_perm, split, s));
         MOE_LAUNCH(launch_backward_dx(*p, dx_perm, fw->assign_pos, fw->topk_ids, dsel, w_router, out->dx,
                                       s));
-        MOE_LAUNCH(launch_backward_transpose(*p, dy_perm, p->d, p->d, false, fw->offsets, poff, nullptr, kp,
-                                             dyT, nullptr, nullptr, s));
-        MOE_LAUNCH(launch_backward_transpose(*p, h, p->f, p->f, false, fw->offsets, poff, nullptr, kp, hT,
-                                             nullptr, nullptr, s));
-        MOE_LAUNCH(launch_backward_transpose(*p, duv, 2 * p->f, 2 * p->f, false, fw->offsets, poff, nullptr,
-                                             kp, duvT, nullptr, nullptr, s));
-        // (with a router, the transpose of x also yields the router gradient's partial sums)
-        MOE_LAUNCH(launch_backward_transpose(*p, x, p->d, p->d, true, fw->offsets, poff, fw->sorted_assign, kp,
-                                             xT, dsel, w_router != nullptr ? wr_part : nullptr, s));
+        // x gathered into queue order, the weight gradients' operand
+        MOE_LAUNCH(launch_gather_rows(*p, x, fw->assign_pos, x_perm, s));
+        // the router gradient's partial sums over 64-row blocks of each queue
+        if (w_router != nullptr)
+            MOE_LAUNCH(launch_backward_transpose(*p, x, p->d, p->d, true, fw->offsets, poff, fw->sorted_assign, kp,
+                                                 nullptr, dsel, wr_part, s));
     }
-    // weight gradients (an expert with no rows gets zeros)
-    // (du^T and dv^T are rows 0 .. f and f .. 2f of each expert's block of (du|dv)^T)
-    MOE_LAUNCH(launch_backward_wgrad(*p, dyT, p->d, p->d, 0, hT, p->f, poff, order, out->dw_down, s));
-    MOE_LAUNCH(launch_backward_wgrad(*p, duvT, p->f, 2 * p->f, 0, xT, p->d, poff, order, out->dw_gate, s));
-    MOE_LAUNCH(launch_backward_wgrad(*p, duvT, p->f, 2 * p->f, p->f, xT, p->d, poff, order, out->dw_up, s));
+    // weight gradients from the queue-order operands (an expert with no rows
+    // gets zeros; with no tokens every count, from poff, is zero)
+    // (du and dv are columns 0 .. f and f .. 2f of du|dv)
+    const int32_t* qoff = p->T > 0 ? fw->offsets : poff;
+    MOE_LAUNCH(launch_backward_wgrad(*p, dy_perm, p->d, 0, p->d, h, p->f, qoff, order, out->dw_down, s));
+    MOE_LAUNCH(launch_backward_wgrad(*p, duv, 2 * p->f, 0, p->f, x_perm, p->d, qoff, order, out->dw_gate, s));
+    MOE_LAUNCH(launch_backward_wgrad(*p, duv, 2 * p->f, p->f, p->f, x_perm, p->d, qoff, order, out->dw_up, s));
     if (w_router != nullptr)
         MOE_LAUNCH(launch_backward_dwr(*p, wr_part, poff, out->dw_router, s));
     return MOE_OK;

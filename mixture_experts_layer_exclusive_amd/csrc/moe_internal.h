@@ -102,6 +102,11 @@ inline bool bwd_can_split(const moe_problem_t& p) { return (2 * p.f) / 64 >= 2 *
 inline size_t bwd_split_bytes(const moe_problem_t& p) {
     return bwd_can_split(p) ? static_cast<size_t>(kSplitWGs) * kBM * kDownCols * 4 : 0;
 }
+// Extra rows after each queue-order operand of the weight-gradient GEMMs: a
+// tile reads whole 64-row slices, up to 63 rows past an expert's last row
+// (those values are zeroed after the read), plus one row for the channel
+// range of a tile that passes a row's end.
+constexpr int64_t kWgradPadRows = 65;
 inline int64_t backward_kpad(const moe_problem_t& p) {
     return static_cast<int64_t>(align_up(static_cast<size_t>(p.T * p.k + 63 * static_cast<int64_t>(p.E)), 64));
 }
@@ -138,8 +143,8 @@ hipError_t launch_backward_recompute(const moe_problem_t& p, const void* x, cons
                                      const void* dh, void* duv, void* h, hipStream_t s);
 hipError_t launch_backward_dxperm(const moe_problem_t& p, const void* duv, const int32_t* offsets,
                                   const void* w_gu_t, void* dx_perm, float* part, hipStream_t s);
-hipError_t launch_backward_wgrad(const moe_problem_t& p, const void* A, int M, int a_rows, int a_row_off,
-                                 const void* B, int N, const int32_t* poff, const int32_t* order, void* C,
+hipError_t launch_backward_wgrad(const moe_problem_t& p, const void* A, int lda, int a_col_off, int M,
+                                 const void* B, int N, const int32_t* offsets, const int32_t* order, void* C,
                                  hipStream_t s);
 
 }  // namespace moe

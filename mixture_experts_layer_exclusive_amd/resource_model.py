@@ -94,9 +94,13 @@ def _ffn_ws(L: Layer) -> int:
 
 
 def kpad(L: Layer) -> int:
-    """Columns of the backward's transposed operands: each expert's queue
-    padded to a multiple of 64."""
+    """Rows of the backward's padded queue (each expert's queue rounded up to
+    64 rows): the router gradient's partial sums take one row per 64."""
     return _align(L.n + 63 * L.E, 64)
+
+
+# Rows after each queue-order operand of the weight-gradient GEMMs.
+WGRAD_PAD_ROWS = 65
 
 
 def workspace(L: Layer, op: int) -> int:
@@ -110,9 +114,12 @@ def workspace(L: Layer, op: int) -> int:
                 + _dispatch_ws(L) + _ffn_ws(L) + _align(L.n * L.d * L.s))
     if op == OP_BACKWARD:
         kp = kpad(L)
-        return (_align(L.n * 4) + 2 * _align(L.n * L.d * 2) + 2 * _align(L.n * L.f * 2) + _align(L.n * 2 * L.f * 2)
-                + _align((L.E + 1) * 4) + _align(L.E * 4) + 2 * _align(L.d * kp * 2) + _align(L.f * kp * 2)
-                + _align(2 * L.f * kp * 2) + _align(kp // 64 * L.d * 4) + _align(_split_bytes(2 * L.f, 2)))
+        npad = L.n + WGRAD_PAD_ROWS
+        # dsel, dy_perm, dx_perm, dh, h, du|dv, poff, order, x_perm, router
+        # partial sums, split-K partials
+        return (_align(L.n * 4) + _align(npad * L.d * 2) + _align(L.n * L.d * 2) + _align(L.n * L.f * 2)
+                + _align(npad * L.f * 2) + _align(npad * 2 * L.f * 2) + _align((L.E + 1) * 4) + _align(L.E * 4)
+                + _align(npad * L.d * 2) + _align(kp // 64 * L.d * 4) + _align(_split_bytes(2 * L.f, 2)))
     raise ValueError(f"unknown op {op}")
 
 
@@ -174,7 +181,10 @@ def hbm_bytes(L: Layer) -> Dict[str, float]:
         "router_read": L.T * L.d * s + L.E * L.d * s + 4.0 * L.T * L.E,
         "backward_dy": (2 * L.k + 1) * L.T * L.d * 2.0,
         "backward_dx": (L.k + 1) * L.T * L.d * 2.0,
-        "backward_transposes": 2.0 * L.n * (2 * L.d + 3 * L.f) * 2,
+        # x gathered into queue order (read once per token, written per row)
+        "backward_x_gather": L.T * L.d * 2.0 + L.n * L.d * 2.0,
+        # the router gradient's partial sums: every queue row's x row read
+        "backward_router_partials": L.n * L.d * 2.0,
     }
 
 
@@ -293,15 +303,18 @@ def _backward_parts(L: Layer, counts: Sequence[int], hw: Hardware) -> Dict[str, 
     t["bwd_recompute"] = gemm_time(hw, R * _cdiv(L.f, GATEUP_COLS), L.d / BK, extra_us=hw.upbwd_tile_us)
     t["bwd_dx_perm"] = gemm_time(hw, R * _cdiv(L.d, DOWN_COLS), 2 * L.f / BK, split=_split_bytes(2 * L.f, 2) > 0)
     t["bwd_wgrad"] = wgrad_time(hw, counts, L.d, L.f) + 2 * wgrad_time(hw, counts, L.f, L.d)
-    t["bwd_streaming"] = 8 * hw.launch_us + backward_stream_bytes(L) / hw.stream_bw
+    # (launches: offsets and order, dy, dx, the gather of x; no router)
+    t["bwd_streaming"] = 4 * hw.launch_us + backward_stream_bytes(L) / hw.stream_bw
     return t
 
 
-def backward_stream_bytes(L: Layer) -> float:
+def backward_stream_bytes(L: Layer, router: bool = False) -> float:
     """Bytes of the backward's bandwidth-bound kernels: slot gradients and
-    reverse dispatch of dy, the dx sum, the four transposes."""
+    reverse dispatch of dy, the dx sum, x gathered into queue order and, with
+    a router, its gradient's partial sums."""
     b = hbm_bytes(L)
-    return b["backward_dy"] + b["backward_dx"] + b["backward_transposes"]
+    return (b["backward_dy"] + b["backward_dx"] + b["backward_x_gather"]
+            + (b["backward_router_partials"] if router else 0.0))
 
 
 def predict_times(L: Layer, counts: Sequence[int], hw: Optional[Hardware] = None) -> Dict[str, float]:
