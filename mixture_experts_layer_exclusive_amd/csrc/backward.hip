@@ -147,8 +147,9 @@ __global__ __launch_bounds__(64) void bwd_poff_kernel(const int32_t* __restrict_
 // With GATHER and wr_part, block b = q / 64 also yields the router-gradient
 // partial sums wr_part[b, c] = sum over its columns q of dsel[a_q] src[c]
 // (a_q = sorted_assign[pos]; zero for padding), in a fixed order.  With dst
-// NULL only the partial sums are written (the weight gradients read their
-// operands in queue order and need no transposed copy).
+// NULL no transposed block is written (the weight gradients read their
+// operands in queue order); with rows (GATHER) the gathered rows are also
+// written in queue order, rows[pos] = src row of pos (row stride C).
 template <bool GATHER>
 __global__ __launch_bounds__(256) void bwd_transpose_kernel(const bf16_t* __restrict__ src,
                                                            int64_t ld_src, int C,
@@ -157,9 +158,11 @@ __global__ __launch_bounds__(256) void bwd_transpose_kernel(const bf16_t* __rest
                                                            const int32_t* __restrict__ sorted_assign,
                                                            int k, bf16_t* __restrict__ dst,
                                                            const float* __restrict__ dsel,
-                                                           float* __restrict__ wr_part) {
+                                                           float* __restrict__ wr_part,
+                                                           bf16_t* __restrict__ rows = nullptr) {
     __shared__ bf16_t tile[64][64 + 2];
     __shared__ int64_t s_row[64];
+    __shared__ int s_pos[64];
     __shared__ float s_dsel[64];
     __shared__ int s_e;
     const int q0 = blockIdx.x * 64;
@@ -181,6 +184,7 @@ __global__ __launch_bounds__(256) void bwd_transpose_kernel(const bf16_t* __rest
             if (GATHER && wr_part != nullptr) ds = dsel[a];
         }
         s_row[threadIdx.x] = row;
+        s_pos[threadIdx.x] = row >= 0 ? pos : -1;
         s_dsel[threadIdx.x] = ds;
         // (poff is a multiple of 64: the block's 64 columns share one expert)
         if (threadIdx.x == 0) s_e = lo;
@@ -194,11 +198,14 @@ __global__ __launch_bounds__(256) void bwd_transpose_kernel(const bf16_t* __rest
         const int i = threadIdx.x >> 2;
         const int cc = (threadIdx.x & 3) * 16;
         const int64_t row = s_row[i];
+        const int pos_i = s_pos[i];
 #pragma unroll
         for (int u = 0; u < 16; u += 8) {
             const int c = c0 + cc + u;
             uint4 v = make_uint4(0u, 0u, 0u, 0u);
             if (row >= 0 && c < C) v = *reinterpret_cast<const uint4*>(src + row * ld_src + c);
+            if (GATHER && rows != nullptr && pos_i >= 0 && c < C)
+                *reinterpret_cast<uint4*>(rows + static_cast<int64_t>(pos_i) * C + c) = v;
             const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
             for (int h = 0; h < 4; ++h) {
@@ -381,12 +388,13 @@ hipError_t launch_backward_poff(const moe_problem_t& p, const int32_t* offsets, 
 hipError_t launch_backward_transpose(const moe_problem_t& p, const void* src, int64_t ld_src, int C,
                                      bool gather, const int32_t* offsets, const int32_t* poff,
                                      const int32_t* sorted_assign, int64_t kpad, void* dst,
-                                     const float* dsel, float* wr_part, hipStream_t s) {
+                                     const float* dsel, float* wr_part, hipStream_t s, void* rows) {
     const dim3 grid(static_cast<unsigned>(kpad / 64), static_cast<unsigned>(ceil_div(C, 64)));
     if (gather)
         bwd_transpose_kernel<true><<<grid, 256, 0, s>>>(static_cast<const bf16_t*>(src), ld_src, C, offsets,
                                                         poff, p.E, sorted_assign, p.k,
-                                                        static_cast<bf16_t*>(dst), dsel, wr_part);
+                                                        static_cast<bf16_t*>(dst), dsel, wr_part,
+                                                        static_cast<bf16_t*>(rows));
     else
         bwd_transpose_kernel<false><<<grid, 256, 0, s>>>(static_cast<const bf16_t*>(src), ld_src, C, offsets,
                                                          poff, p.E, sorted_assign, p.k,

@@ -490,12 +490,14 @@ moe_status_t moe_backward(const moe_problem_t* p, const void* x, const void* w_r
         MOE_LAUNCH(launch_backward_dxperm(*p, duv, fw->offsets, w_gu_t, dx_perm, split, s));
         MOE_LAUNCH(launch_backward_dx(*p, dx_perm, fw->assign_pos, fw->topk_ids, dsel, w_router, out->dx,
                                       s));
-        // x gathered into queue order, the weight gradients' operand
-        MOE_LAUNCH(launch_gather_rows(*p, x, fw->assign_pos, x_perm, s));
-        // the router gradient's partial sums over 64-row blocks of each queue
+        // x gathered into queue order, the weight gradients' operand; with a
+        // router the same pass over 64-row blocks of each queue also takes
+        // the router gradient's partial sums
         if (w_router != nullptr)
             MOE_LAUNCH(launch_backward_transpose(*p, x, p->d, p->d, true, fw->offsets, poff, fw->sorted_assign, kp,
-                                                 nullptr, dsel, wr_part, s));
+                                                 nullptr, dsel, wr_part, s, x_perm));
+        else
+            MOE_LAUNCH(launch_gather_rows(*p, x, fw->assign_pos, x_perm, s));
     }
     // weight gradients from the queue-order operands (an expert with no rows
     // gets zeros; with no tokens every count, from poff, is zero)

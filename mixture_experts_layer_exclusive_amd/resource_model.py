@@ -311,10 +311,12 @@ def _backward_parts(L: Layer, counts: Sequence[int], hw: Hardware) -> Dict[str, 
 def backward_stream_bytes(L: Layer, router: bool = False) -> float:
     """Bytes of the backward's bandwidth-bound kernels: slot gradients and
     reverse dispatch of dy, the dx sum, x gathered into queue order and, with
-    a router, its gradient's partial sums."""
+    a router, its gradient's partial sums (taken in the same pass)."""
     b = hbm_bytes(L)
+    # (with a router the queue-ordered pass that takes the partial sums also
+    # writes x_perm: x rows read per queue row instead of once per token)
     return (b["backward_dy"] + b["backward_dx"] + b["backward_x_gather"]
-            + (b["backward_router_partials"] if router else 0.0))
+            + (b["backward_router_partials"] - L.T * L.d * 2.0 if router else 0.0))
 
 
 def predict_times(L: Layer, counts: Sequence[int], hw: Optional[Hardware] = None) -> Dict[str, float]:
