@@ -9,7 +9,9 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libmoe.so")
+# MOE_LIBRARY names another build of the same library (the host-sanitizer
+# build, for instance); by default the in-tree libmoe.so is loaded
+LIB_PATH = os.environ.get("MOE_LIBRARY") or os.path.join(PKG, "libmoe.so")
 
 MOE_OK = 0
 MOE_ERR_INVALID_ARGUMENT = 1
