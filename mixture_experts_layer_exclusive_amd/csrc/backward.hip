@@ -9,14 +9,13 @@
 //      output gradient dy_perm[pos] = g dy[t], and the logit gradient of the
 //      renormalised top-k softmax, dl_j = g_j (dg_j - sum_i g_i dg_i);
 //   2. grouped GEMMs over the queues (dh, the recompute of gate/up with the
-//      SwiGLU backward, dx_perm) and the weight gradients, whose operands are
-//      first transposed here into per-expert column segments padded to a
-//      multiple of 64 with zeros;
+//      SwiGLU backward, dx_perm) and the weight gradients, which read their
+//      operands in queue order (x gathered into queue order here);
 //   3. per token: dx[t] = sum_j dx_perm[pos(t, j)] + sum_j dl_j W_r[id_j];
 //   4. router weight gradient dW_r[e] = sum over expert e's queue of dl x:
-//      partial sums over each 64-column block of the padded queue (one
-//      expert per block) come out of the transpose of x, and a second
-//      kernel adds an expert's blocks in order.
+//      partial sums over each 64-row block of the padded queue (one expert
+//      per block) come out of the gather of x, and a second kernel adds an
+//      expert's blocks in order.
 // All reductions run in a fixed order (deterministic); accumulation is fp32,
 // storage bf16.
 #include "device_util.h"
@@ -97,76 +96,68 @@ __global__ __launch_bounds__(256) void bwd_dy_kernel(const uint4* __restrict__ d
 // Padded offsets: expert e's queue columns start at poff[e], each expert's
 // count rounded up to a multiple of 64 (all zero when offsets is null: no
 // tokens).  Also the experts in descending order of padded count, ties by
-// lower id: order[rank] = e.  One wave, E <= 256.
-__global__ __launch_bounds__(64) void bwd_poff_kernel(const int32_t* __restrict__ offsets, int E,
-                                                     int32_t* __restrict__ poff, int32_t* __restrict__ order) {
-    __shared__ int s_c[MOE_MAX_EXPERTS];
-    const int lane = threadIdx.x;
-    int c[4], local = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int e = lane * 4 + i;
-        c[i] = (e < E && offsets != nullptr) ? ((offsets[e + 1] - offsets[e] + 63) / 64) * 64 : 0;
-        local += c[i];
-    }
-    int incl = local;
+// lower id: order[rank] = e.  One thread per expert.
+static_assert(MOE_MAX_EXPERTS == 256, "bwd_poff_kernel runs one 256-thread workgroup, a thread per expert");
+__global__ __launch_bounds__(256) void bwd_poff_kernel(const int32_t* __restrict__ offsets, int E,
+                                                      int32_t* __restrict__ poff, int32_t* __restrict__ order) {
+    __shared__ __align__(16) int s_c[MOE_MAX_EXPERTS];
+    __shared__ int s_wave[4];
+    const int e = threadIdx.x;
+    const int c = (e < E && offsets != nullptr) ? ((offsets[e + 1] - offsets[e] + 63) / 64) * 64 : 0;
+    s_c[e] = c;
+    int incl = c;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
         const int o = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += o;
+        if ((e & 63) >= off) incl += o;
     }
-    int run = incl - local;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int e = lane * 4 + i;
-        if (e < E) poff[e] = run;
-        run += c[i];
-    }
-    if (lane == 63) poff[E] = incl;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s_c[lane * 4 + i] = c[i];
+    if ((e & 63) == 63) s_wave[e >> 6] = incl;
     __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int e = lane * 4 + i;
-        if (e >= E) continue;
-        int rank = 0;
-        for (int o = 0; o < E; ++o) rank += (s_c[o] > c[i] || (s_c[o] == c[i] && o < e)) ? 1 : 0;
-        order[rank] = e;
+    for (int w = 0; w < (e >> 6); ++w) incl += s_wave[w];
+    if (e < E) poff[e] = incl - c;
+    if (e == E - 1) poff[E] = incl;
+    if (e >= E) return;
+    // (entries past E hold 0 and never outrank a count >= 0)
+    int rank = 0;
+    const int4* s4 = reinterpret_cast<const int4*>(s_c);
+#pragma unroll 8
+    for (int o4 = 0; o4 < MOE_MAX_EXPERTS / 4; ++o4) {
+        const int4 v = s4[o4];
+        const int o = o4 * 4;
+        rank += (v.x > c || (v.x == c && o < e)) ? 1 : 0;
+        rank += (v.y > c || (v.y == c && o + 1 < e)) ? 1 : 0;
+        rank += (v.z > c || (v.z == c && o + 2 < e)) ? 1 : 0;
+        rank += (v.w > c || (v.w == c && o + 3 < e)) ? 1 : 0;
     }
+    order[rank] = e;
 }
 
-// Transpose of queue rows into padded per-expert blocks: expert e's block
-// [C, K_e] (K_e = poff[e+1] - poff[e]) starts at element poff[e] * C and
-//   block_e[c, q - poff[e]] = src_row(q)[c] for c < C, poff[e] <= q < poff[e+1],
-// where padded column q is queue row pos = offsets[e] + q - poff[e] when
-// pos < offsets[e+1], else zero.  Compact blocks keep the rows a weight-
-// gradient tile reads K_e (not all Kpad) columns apart.  The
-// source row is src[pos] (row stride ld_src), or, with GATHER, row
-// sorted_assign[pos] / k of src.  Tiles of 64 columns x 64 rows through LDS.
-// With GATHER and wr_part, block b = q / 64 also yields the router-gradient
-// partial sums wr_part[b, c] = sum over its columns q of dsel[a_q] src[c]
-// (a_q = sorted_assign[pos]; zero for padding), in a fixed order.  With dst
-// NULL no transposed block is written (the weight gradients read their
-// operands in queue order); with rows (GATHER) the gathered rows are also
-// written in queue order, rows[pos] = src row of pos (row stride C).
-template <bool GATHER>
-__global__ __launch_bounds__(256) void bwd_transpose_kernel(const bf16_t* __restrict__ src,
-                                                           int64_t ld_src, int C,
-                                                           const int32_t* __restrict__ offsets,
-                                                           const int32_t* __restrict__ poff, int E,
-                                                           const int32_t* __restrict__ sorted_assign,
-                                                           int k, bf16_t* __restrict__ dst,
-                                                           const float* __restrict__ dsel,
-                                                           float* __restrict__ wr_part,
-                                                           bf16_t* __restrict__ rows = nullptr) {
-    __shared__ bf16_t tile[64][64 + 2];
+// x gathered into queue order for the weight gradients, x_perm[pos] =
+// x[sorted_assign[pos] / k] (x_perm has at least one row past its n_rows
+// queue rows), together with the router gradient's partial
+// sums.  The grid walks each expert's queue in 64-row blocks of the padded
+// queue (expert e's rows start at padded row poff[e], a multiple of 64, so a
+// block belongs to one expert; padded row q is queue row pos = offsets[e] +
+// q - poff[e] while pos < offsets[e+1], else padding) and kGatherXCols
+// columns at a time.  Block b = q / 64 yields wr_part[b, c] = sum over its
+// rows of dsel[a] x[a / k, c] (a = sorted_assign[pos]; padding adds
+// nothing), in a fixed order: wave w adds rows 16w .. 16w + 15 in turn (each
+// lane 8 columns, its 16 row loads in flight first), then (s0 + s1) +
+// (s2 + s3) over the waves.
+constexpr int kGatherXCols = 512;
+__global__ __launch_bounds__(256) void bwd_gather_x_kernel(const bf16_t* __restrict__ x, int d,
+                                                          const int32_t* __restrict__ offsets,
+                                                          const int32_t* __restrict__ poff, int E,
+                                                          const int32_t* __restrict__ sorted_assign,
+                                                          int k, const float* __restrict__ dsel,
+                                                          float* __restrict__ wr_part,
+                                                          bf16_t* __restrict__ x_perm, int64_t n_rows) {
     __shared__ int64_t s_row[64];
     __shared__ int s_pos[64];
     __shared__ float s_dsel[64];
-    __shared__ int s_e;
+    __shared__ float s_part[4][kGatherXCols];
     const int q0 = blockIdx.x * 64;
-    const int c0 = blockIdx.y * 64;
+    const int c0 = blockIdx.y * kGatherXCols;
     if (q0 >= poff[E]) return;
     if (threadIdx.x < 64) {
         const int q = q0 + threadIdx.x;
@@ -178,73 +169,52 @@ __global__ __launch_bounds__(256) void bwd_transpose_kernel(const bf16_t* __rest
         const int pos = offsets[lo] + (q - poff[lo]);
         int64_t row = -1;
         float ds = 0.f;
-        if (q < poff[E] && pos < offsets[lo + 1]) {
-            const int a = GATHER ? sorted_assign[pos] : pos;
-            row = GATHER ? a / k : pos;
-            if (GATHER && wr_part != nullptr) ds = dsel[a];
+        if (pos < offsets[lo + 1]) {
+            const int a = sorted_assign[pos];
+            row = a / k;
+            ds = dsel[a];
         }
         s_row[threadIdx.x] = row;
         s_pos[threadIdx.x] = row >= 0 ? pos : -1;
         s_dsel[threadIdx.x] = ds;
-        // (poff is a multiple of 64: the block's 64 columns share one expert)
-        if (threadIdx.x == 0) s_e = lo;
     }
     __syncthreads();
-    const int eb = s_e;
-    const int64_t ke = poff[eb + 1] - poff[eb];
-    bf16_t* const dst_e = dst == nullptr ? nullptr : dst + static_cast<int64_t>(poff[eb]) * C + (q0 - poff[eb]);
-    // load: thread -> (row i = tid / 4, 16 columns (tid % 4) * 16 ..)
-    {
-        const int i = threadIdx.x >> 2;
-        const int cc = (threadIdx.x & 3) * 16;
-        const int64_t row = s_row[i];
-        const int pos_i = s_pos[i];
+    const int w = threadIdx.x >> 6;
+    const int cl = (threadIdx.x & 63) * 8;  // the lane's 8 columns within the strip
+    const int c = c0 + cl;
+    float part[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (c < d) {
+        // branch-free: a padding row loads x row 0 and keeps zeros, and
+        // stores them to row n_rows of x_perm, a pad row past the queue
+        // whose contents are never used
+        uint4 v[16];
 #pragma unroll
-        for (int u = 0; u < 16; u += 8) {
-            const int c = c0 + cc + u;
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (row >= 0 && c < C) v = *reinterpret_cast<const uint4*>(src + row * ld_src + c);
-            if (GATHER && rows != nullptr && pos_i >= 0 && c < C)
-                *reinterpret_cast<uint4*>(rows + static_cast<int64_t>(pos_i) * C + c) = v;
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        for (int r = 0; r < 16; ++r) {
+            const int64_t row = s_row[w * 16 + r];
+            const uint4 t = *reinterpret_cast<const uint4*>(x + (row >= 0 ? row : 0) * d + c);
+            v[r] = row >= 0 ? t : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int pos = s_pos[w * 16 + r];
+            const int64_t dst = pos >= 0 ? pos : n_rows;
+            *reinterpret_cast<uint4*>(x_perm + dst * d + c) = v[r];
+            const float ds = s_dsel[w * 16 + r];
+            const uint32_t u[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
 #pragma unroll
             for (int h = 0; h < 4; ++h) {
-                tile[i][cc + u + 2 * h] = static_cast<bf16_t>(w[h] & 0xffffu);
-                tile[i][cc + u + 2 * h + 1] = static_cast<bf16_t>(w[h] >> 16);
+                part[2 * h] = fmaf(ds, __uint_as_float(u[h] << 16), part[2 * h]);
+                part[2 * h + 1] = fmaf(ds, __uint_as_float(u[h] & 0xffff0000u), part[2 * h + 1]);
             }
         }
     }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s_part[w][cl + i] = part[i];
     __syncthreads();
-    // store: thread -> (column c = tid / 4, 16 padded positions (tid % 4) * 16 ..)
-    {
-        const int c = threadIdx.x >> 2;
-        const int qq = (threadIdx.x & 3) * 16;
-        float part = 0.f;
-        if (c0 + c < C) {
-#pragma unroll
-            for (int u = 0; u < 16; u += 8) {
-                uint32_t w[4];
-#pragma unroll
-                for (int h = 0; h < 4; ++h) {
-                    const uint16_t lo = tile[qq + u + 2 * h][c];
-                    const uint16_t hi = tile[qq + u + 2 * h + 1][c];
-                    w[h] = static_cast<uint32_t>(lo) | (static_cast<uint32_t>(hi) << 16);
-                    if (GATHER) {
-                        part = fmaf(s_dsel[qq + u + 2 * h], bf16_to_f32(lo), part);
-                        part = fmaf(s_dsel[qq + u + 2 * h + 1], bf16_to_f32(hi), part);
-                    }
-                }
-                if (dst != nullptr)
-                    *reinterpret_cast<uint4*>(dst_e + static_cast<int64_t>(c0 + c) * ke + qq + u) =
-                        make_uint4(w[0], w[1], w[2], w[3]);
-            }
-        }
-        if (GATHER && wr_part != nullptr) {
-            // the 4 threads of column c are adjacent lanes: (s0 + s1) + (s2 + s3)
-            part += __shfl_xor(part, 1, 64);
-            part += __shfl_xor(part, 2, 64);
-            if ((threadIdx.x & 3) == 0 && c0 + c < C) wr_part[static_cast<int64_t>(q0 / 64) * C + c0 + c] = part;
-        }
+    for (int i = threadIdx.x; i < kGatherXCols; i += 256) {
+        if (c0 + i < d)
+            wr_part[static_cast<int64_t>(q0 / 64) * d + c0 + i] =
+                (s_part[0][i] + s_part[1][i]) + (s_part[2][i] + s_part[3][i]);
     }
 }
 
@@ -381,24 +351,17 @@ hipError_t launch_backward_dy(const moe_problem_t& p, const void* dy, const void
 
 hipError_t launch_backward_poff(const moe_problem_t& p, const int32_t* offsets, int32_t* poff,
                                 int32_t* order, hipStream_t s) {
-    bwd_poff_kernel<<<1, 64, 0, s>>>(offsets, p.E, poff, order);
+    bwd_poff_kernel<<<1, 256, 0, s>>>(offsets, p.E, poff, order);
     return hipGetLastError();
 }
 
-hipError_t launch_backward_transpose(const moe_problem_t& p, const void* src, int64_t ld_src, int C,
-                                     bool gather, const int32_t* offsets, const int32_t* poff,
-                                     const int32_t* sorted_assign, int64_t kpad, void* dst,
-                                     const float* dsel, float* wr_part, hipStream_t s, void* rows) {
-    const dim3 grid(static_cast<unsigned>(kpad / 64), static_cast<unsigned>(ceil_div(C, 64)));
-    if (gather)
-        bwd_transpose_kernel<true><<<grid, 256, 0, s>>>(static_cast<const bf16_t*>(src), ld_src, C, offsets,
-                                                        poff, p.E, sorted_assign, p.k,
-                                                        static_cast<bf16_t*>(dst), dsel, wr_part,
-                                                        static_cast<bf16_t*>(rows));
-    else
-        bwd_transpose_kernel<false><<<grid, 256, 0, s>>>(static_cast<const bf16_t*>(src), ld_src, C, offsets,
-                                                         poff, p.E, sorted_assign, p.k,
-                                                         static_cast<bf16_t*>(dst), nullptr, nullptr);
+hipError_t launch_backward_gather_x(const moe_problem_t& p, const void* x, const int32_t* offsets,
+                                    const int32_t* poff, const int32_t* sorted_assign, int64_t kpad,
+                                    const float* dsel, float* wr_part, void* x_perm, hipStream_t s) {
+    const dim3 grid(static_cast<unsigned>(kpad / 64), static_cast<unsigned>(ceil_div(p.d, kGatherXCols)));
+    bwd_gather_x_kernel<<<grid, 256, 0, s>>>(static_cast<const bf16_t*>(x), p.d, offsets, poff, p.E,
+                                             sorted_assign, p.k, dsel, wr_part, static_cast<bf16_t*>(x_perm),
+                                             p.T * p.k);
     return hipGetLastError();
 }
 

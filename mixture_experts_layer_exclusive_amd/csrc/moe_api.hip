@@ -494,8 +494,8 @@ moe_status_t moe_backward(const moe_problem_t* p, const void* x, const void* w_r
         // router the same pass over 64-row blocks of each queue also takes
         // the router gradient's partial sums
         if (w_router != nullptr)
-            MOE_LAUNCH(launch_backward_transpose(*p, x, p->d, p->d, true, fw->offsets, poff, fw->sorted_assign, kp,
-                                                 nullptr, dsel, wr_part, s, x_perm));
+            MOE_LAUNCH(launch_backward_gather_x(*p, x, fw->offsets, poff, fw->sorted_assign, kp, dsel, wr_part,
+                                                x_perm, s));
         else
             MOE_LAUNCH(launch_gather_rows(*p, x, fw->assign_pos, x_perm, s));
     }

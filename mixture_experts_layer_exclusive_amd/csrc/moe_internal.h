@@ -127,10 +127,9 @@ hipError_t launch_backward_dy(const moe_problem_t& p, const void* dy, const void
                               void* dy_perm, float* dsel, float* dlogits, hipStream_t s);
 hipError_t launch_backward_poff(const moe_problem_t& p, const int32_t* offsets, int32_t* poff,
                                 int32_t* order, hipStream_t s);
-hipError_t launch_backward_transpose(const moe_problem_t& p, const void* src, int64_t ld_src, int C,
-                                     bool gather, const int32_t* offsets, const int32_t* poff,
-                                     const int32_t* sorted_assign, int64_t kpad, void* dst,
-                                     const float* dsel, float* wr_part, hipStream_t s, void* rows = nullptr);
+hipError_t launch_backward_gather_x(const moe_problem_t& p, const void* x, const int32_t* offsets,
+                                    const int32_t* poff, const int32_t* sorted_assign, int64_t kpad,
+                                    const float* dsel, float* wr_part, void* x_perm, hipStream_t s);
 hipError_t launch_backward_dx(const moe_problem_t& p, const void* dx_perm, const int32_t* assign_pos,
                               const int32_t* ids, const float* dsel, const void* w_router, void* dx,
                               hipStream_t s);
