@@ -53,6 +53,17 @@ def parse():
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 expert-FFN timing")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run moe_stream_copy over 1 GiB (the plain copy that calibrates HBM counters)")
+    ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV",
+                    help="no GPU: summarise a rocprofv3 kernel trace (--output-format csv) of a bench.py run, "
+                         "per timed region (needs --bench-json)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU: HBM-side bytes per expert-FFN call from two rocprofv3 --pmc runs of bench.py "
+                         "--copy-calibration (FETCH_SIZE, then WRITE_SIZE); needs --bench-json")
+    ap.add_argument("--summarize-mfma", metavar="PMC_CSV",
+                    help="no GPU: MFMA utilisation per kernel from a rocprofv3 --pmc MfmaUtil "
+                         "SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE run of bench.py; needs --bench-json")
+    ap.add_argument("--bench-json", help="the JSON line that the traced bench.py run printed")
+    ap.add_argument("--traffic-json", help="with --summarize-pmc: also write the traffic record here")
     ap.add_argument("--library-gemm", action="store_true",
                     help="also time the vendor library's dense bf16 GEMM (torch.mm, hipBLASLt) on the "
                          "shapes of the two expert GEMMs with all T*k rows as one matrix (a measured ceiling)")
@@ -74,9 +85,227 @@ def measured_traffic():
         return None
     return rec.get("hbm_bytes_per_call")
 
+# Region markers for kernel traces: a tiny moe_stream_copy launch whose
+# workgroup count is the marker's number (copies of 16384 * m bytes run on m
+# workgroups), issued on the stream outside the timed windows, so that a
+# trace summary can pick out exactly the kernels of each timed loop.
+REGIONS = {1: "forward steps (the timed moe_forward calls)",
+           3: "expert FFN timing loop (the roofline's launches)",
+           5: "backward timing loop (moe_backward calls)",
+           7: "fp8 expert FFN timing loop (moe_expert_ffn_fp8 calls)"}
+MARK_BYTES = 16384
+COPY_CAL_WORKGROUPS = 4096  # moe_stream_copy over 1 GiB (--copy-calibration)
+
+
+class Marker:
+    def __init__(self, torch, dev, stream):
+        from mixture_experts_layer_exclusive_amd import _lib
+        self.lib = _lib.load()
+        self.src = torch.zeros(MARK_BYTES * 8, dtype=torch.uint8, device=dev)
+        self.dst = torch.empty_like(self.src)
+        self.stream = stream
+
+    def __call__(self, m):
+        rc = self.lib.moe_stream_copy(self.src.data_ptr(), self.dst.data_ptr(), MARK_BYTES * m,
+                                      self.stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"trace marker {m}: status {rc}")
+
+
+def _short(name):
+    import re
+    name = name.replace("void ", "").replace("moe::(anonymous namespace)::", "")
+    return re.sub(r"\(.*$", "", name)
+
+
+def _regions(rows, wg_of, name_of):
+    """rows in dispatch order -> {first marker: rows strictly between it and the next}"""
+    marks = [(i, wg_of(r)) for i, r in enumerate(rows)
+             if name_of(r).startswith("stream_copy_kernel") and wg_of(r) <= 8]
+    out = {}
+    for (i, m), (j, m2) in zip(marks, marks[1:]):
+        if m in REGIONS and m2 == m + 1:
+            out[m] = rows[i + 1:j]
+    return out
+
+
+def summarize_trace(path, bench):
+    import csv
+    import statistics as st
+    rows = list(csv.DictReader(open(path)))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    wg = lambda r: int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"])  # noqa: E731
+    reg = _regions(rows, wg, lambda r: _short(r["Kernel_Name"]))
+    cfg = bench["config"]
+    out = [f"Workload: {cfg['workload']} (T={cfg['tokens']}, d={cfg['d']}, E={cfg['experts']}, k={cfg['top_k']}, "
+           f"f={cfg['ffn_width']}); the bench line: ms_per_step {bench['ms_per_step']}, roofline.frac "
+           f"{bench['roofline']['frac']}.", ""]
+    per_call = {}
+    for m, name in REGIONS.items():
+        if m not in reg:
+            continue
+        ks = {}
+        for r in reg[m]:
+            key = (_short(r["Kernel_Name"]), wg(r), int(r["Grid_Size_Y"]) // int(r["Workgroup_Size_Y"]))
+            ks.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        calls = {1: bench["steps"]}.get(m, None)
+        tot = sum(sum(v) for v in ks.values())
+        out += [f"### {name}", "",
+                "| kernel | workgroups | launches | min us | median us | mean us | share % |",
+                "|---|---|---|---|---|---|---|"]
+        for (kn, gx, gy), v in sorted(ks.items(), key=lambda kv: -sum(kv[1])):
+            out.append(f"| {kn} | {gx}x{gy} | {len(v)} | {min(v):.1f} | {st.median(v):.1f} | "
+                       f"{sum(v) / len(v):.1f} | {100 * sum(v) / tot:.2f} |")
+        # launches per call: the least frequent kernel runs once per call
+        n_calls = calls or min(len(v) for v in ks.values())
+        med = sum(st.median(v) * len(v) / n_calls for v in ks.values())
+        mean = tot / n_calls
+        per_call[m] = (n_calls, med, mean)
+        out += ["", f"{n_calls} calls; kernel time per call: {med:.1f} us from the medians, {mean:.1f} us mean "
+                f"(launch gaps not included).", ""]
+    pk = bench["roofline"]["peak"]
+    if 1 in per_call:
+        n_, med, mean = per_call[1]
+        out.append(f"Forward step: {mean / 1e3:.4f} ms of kernel time per step against ms_per_step "
+                   f"{bench['ms_per_step']} (wall clock, launches included).")
+    if 3 in per_call:
+        n_, med, mean = per_call[3]
+        fl = bench["roofline"]["flops_per_launch"]
+        out.append(f"Expert FFN call: {fl / 1e12:.4f} TFLOP (6*T*k*d*f) / {med:.1f} us (sum of the kernels' medians) / "
+                   f"{pk:.0f} TFLOP/s = frac {fl / (med * 1e-6) / 1e12 / pk:.4f}; with the mean, "
+                   f"{fl / (mean * 1e-6) / 1e12 / pk:.4f}; the bench line (HIP events around the loop): "
+                   f"{bench['roofline']['frac']}.")
+    if 5 in per_call and bench.get("backward"):
+        n_, med, mean = per_call[5]
+        fl = bench["backward"]["gemm_flops_per_call"]
+        out.append(f"Backward call: {fl / 1e12:.4f} TFLOP (16*T*k*d*f) / {med:.1f} us / {pk:.0f} = frac "
+                   f"{fl / (med * 1e-6) / 1e12 / pk:.4f}; the bench line: {bench['backward']['frac_mfma_peak']}.")
+    if 7 in per_call and bench.get("fp8_expert_ffn"):
+        n_, med, mean = per_call[7]
+        fl = bench["fp8_expert_ffn"]["flops_per_call"]
+        p8 = bench["fp8_expert_ffn"]["peak"]
+        out.append(f"fp8 expert FFN call: {fl / 1e12:.4f} TFLOP / {med:.1f} us / {p8:.0f} = frac "
+                   f"{fl / (med * 1e-6) / 1e12 / p8:.4f}; the bench line: {bench['fp8_expert_ffn']['frac_mfma_peak']}.")
+    return "\n".join(out) + "\n"
+
+
+def _pmc_dispatches(path):
+    """rocprofv3 --pmc CSV -> one dict per dispatch, in dispatch order: short
+    kernel name, workgroups, duration (us) and {counter: value}."""
+    import csv
+    by = {}
+    for r in csv.DictReader(open(path)):
+        d = int(r["Dispatch_Id"])
+        e = by.setdefault(d, {"name": _short(r["Kernel_Name"]),
+                              "wg": int(r["Grid_Size"]) // int(r["Workgroup_Size"]),
+                              "us": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3, "c": {}})
+        e["c"][r["Counter_Name"]] = e["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return [v for _, v in sorted(by.items())]
+
+
+def summarize_pmc(fetch_csv, write_csv, bench):
+    """HBM-side bytes per launch: FETCH_SIZE and WRITE_SIZE (KiB) per
+    dispatch, each scaled by what it reads for the 1 GiB moe_stream_copy
+    launches of --copy-calibration (read and written bytes known exactly),
+    for the expert FFN and backward timing loops."""
+    fr, wr = _pmc_dispatches(fetch_csv), _pmc_dispatches(write_csv)
+    if [(a["name"], a["wg"]) for a in fr] != [(a["name"], a["wg"]) for a in wr]:
+        raise SystemExit("the two counter runs dispatched different kernels")
+    cal = [i for i, a in enumerate(fr) if a["name"].startswith("stream_copy_kernel") and a["wg"] == COPY_CAL_WORKGROUPS]
+    if not cal:
+        raise SystemExit("no 1 GiB moe_stream_copy launches: run bench.py with --copy-calibration")
+    gib_kib = (1 << 30) / 1024
+    ff = sum(fr[i]["c"]["FETCH_SIZE"] for i in cal) / len(cal) / gib_kib
+    wf = sum(wr[i]["c"]["WRITE_SIZE"] for i in cal) / len(cal) / gib_kib
+    reg = _regions(list(range(len(fr))), lambda i: fr[i]["wg"], lambda i: fr[i]["name"])
+    if 3 not in reg:
+        raise SystemExit("no expert FFN timing loop between markers 3 and 4")
+    lines = [f"Calibration: {len(cal)} moe_stream_copy launches of exactly 1 GiB; FETCH_SIZE reads {ff:.4f} x the "
+             f"bytes they read, WRITE_SIZE {wf:.4f} x the bytes they write. Scaled bytes = counter / factor; "
+             "FETCH counts reads that miss the L2 (served by the Infinity Cache or HBM).", ""]
+    totals = {}
+    for m in (3, 5):
+        if m not in reg:
+            continue
+        agg = {}
+        for i in reg[m]:
+            e = agg.setdefault((fr[i]["name"], fr[i]["wg"]), [0, 0.0, 0.0])
+            e[0] += 1
+            e[1] += fr[i]["c"]["FETCH_SIZE"] * 1024 / ff
+            e[2] += wr[i]["c"]["WRITE_SIZE"] * 1024 / wf
+        n_calls = min(c for c, _, _ in agg.values())
+        totals[m] = (n_calls, sum(e[1] for e in agg.values()) / n_calls, sum(e[2] for e in agg.values()) / n_calls)
+        lines += [f"### {REGIONS[m]}", "", "| kernel | workgroups | launches | read MB per launch | written MB per launch |",
+                  "|---|---|---|---|---|"]
+        for (kn, g), (c, rd, wt) in sorted(agg.items(), key=lambda kv: -(kv[1][1] + kv[1][2])):
+            lines.append(f"| {kn} | {g} | {c} | {rd / c / 1e6:.1f} | {wt / c / 1e6:.1f} |")
+        lines += ["", f"{n_calls} calls: {totals[m][1] / 1e9:.3f} GB read and {totals[m][2] / 1e9:.3f} GB written "
+                  "beyond the L2 per call.", ""]
+    cfg = bench["config"]
+    T, d, E, k, f = cfg["tokens"], cfg["d"], cfg["experts"], cfg["top_k"], cfg["ffn_width"]
+    es = 2 if bench["dtype"] == "bf16" else 4
+    alg = (3 * E * d * f + T * d + 2 * T * k * f + T * k * d) * es
+    n_calls, read, written = totals[3]
+    lines.append(f"Expert FFN call: {(read + written) / 1e9:.3f} GB beyond the L2 per call against {alg / 1e9:.3f} GB "
+                 f"algorithmic (each expert weight once, x once, h written and read, y_perm written): "
+                 f"{(read + written) / alg:.2f} x.")
+    rec = {"hbm_bytes_per_call": int(read + written), "read_bytes_per_call": int(read),
+           "written_bytes_per_call": int(written), "algorithmic_bytes_per_call": int(alg),
+           "fetch_factor": round(ff, 4), "write_factor": round(wf, 4), "workload": cfg["workload"]}
+    return "\n".join(lines) + "\n", rec
+
+
+def summarize_mfma(path):
+    """MfmaUtil (rocprofv3's derived counter: SQ_VALU_MFMA_BUSY_CYCLES over
+    all SIMDs / (GRBM_GUI_ACTIVE x SIMDs)) per kernel of the forward steps,
+    the expert FFN loop and the backward loop, and of the register-only MFMA
+    kernel; the clock is GRBM_GUI_ACTIVE (summed over the 8 XCDs) / 8 / the
+    kernel's duration, given for kernels of 500 us or more."""
+    ds = _pmc_dispatches(path)
+    reg = _regions(ds, lambda a: a["wg"], lambda a: a["name"])
+    reg["peak"] = [a for a in ds if a["name"].startswith("mfma_peak_kernel")]
+    lines = []
+    for m, title in [(1, REGIONS[1]), (3, REGIONS[3]), (5, REGIONS[5]),
+                     ("peak", "register-operand MFMA kernel (moe_mfma_peak)")]:
+        if not reg.get(m):
+            continue
+        agg = {}
+        for a in reg[m]:
+            e = agg.setdefault((a["name"], a["wg"]), [0, 0.0, 0.0, 0.0])
+            e[0] += 1
+            e[1] += a["us"]
+            e[2] += a["c"].get("MfmaUtil", 0.0)
+            e[3] += a["c"].get("GRBM_GUI_ACTIVE", 0.0)
+        lines += [f"### {title}", "", "| kernel | workgroups | launches | mean us | MfmaUtil % | clock GHz |",
+                  "|---|---|---|---|---|---|"]
+        for (kn, g), (c, us, mu, ga) in sorted(agg.items(), key=lambda kv: -kv[1][1]):
+            clk = f"{ga / 8 / (us * 1e3):.2f}" if us / c >= 500 else "-"
+            lines.append(f"| {kn} | {g} | {c} | {us / c:.1f} | {mu / c:.1f} | {clk} |")
+        lines.append("")
+    return "\n".join(lines)
+
+
+def summary_mode(args):
+    if not args.bench_json:
+        raise SystemExit("--bench-json is required")
+    bench = json.loads([l for l in open(args.bench_json).read().splitlines() if l.startswith("{")][-1])
+    if args.summarize_trace:
+        sys.stdout.write(summarize_trace(args.summarize_trace, bench))
+    if args.summarize_mfma:
+        sys.stdout.write(summarize_mfma(args.summarize_mfma))
+    if args.summarize_pmc:
+        text, rec = summarize_pmc(*args.summarize_pmc, bench)
+        sys.stdout.write(text)
+        if args.traffic_json:
+            rec["kernel_src_sha"] = src_sha(FFN_SRC)
+            json.dump(rec, open(args.traffic_json, "w"), indent=1)
+
 
 def main():
     args = parse()
+    if args.summarize_trace or args.summarize_pmc or args.summarize_mfma:
+        summary_mode(args)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this library has no multi-GPU path "
               "(each GPU would run this same layer on its own token shard); use --gpus 1.",
@@ -114,11 +343,14 @@ def main():
     y = torch.empty(p.T, p.d, dtype=tdt, device=dev)
     stream = torch.cuda.current_stream(dev)
 
+    mark = Marker(torch, dev, stream)
+
     def step():
         moe.forward(x, wg, wu, wd, p.k, w_router=wr, logits=lg, ws=ws, y=y)
 
     for _ in range(args.warmup):
         step()
+    mark(1)
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -128,6 +360,7 @@ def main():
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    mark(2)
     ms_step = wall * 1e3 / args.steps
     ms_step_ev = ev0.elapsed_time(ev1) / args.steps
     tokens_s = p.T / (ms_step / 1e3)
@@ -149,9 +382,11 @@ def main():
                     x_perm=x_perm)
     y2 = torch.empty_like(y)
 
-    def timed(fn, reps):
+    def timed(fn, reps, region=None):
         for _ in range(2):
             fn()
+        if region:
+            mark(region)
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
@@ -159,6 +394,8 @@ def main():
             fn()
         b.record(stream)
         torch.cuda.synchronize()
+        if region:
+            mark(region + 1)
         return a.elapsed_time(b) / reps  # ms
 
     def timed_cold(fn, reps):
@@ -182,7 +419,7 @@ def main():
 
     reps = max(5, args.steps)
     ms_ffn = timed(lambda: moe.expert_ffn(offsets, wg, wu, wd, p.k, p.T, x=x, sorted_assign=sa,
-                                          ws=ffn_ws, y_perm=y_perm), reps)
+                                          ws=ffn_ws, y_perm=y_perm), reps, region=3)
     ms_disp = timed(lambda: moe.dispatch(ids, p.E, x=x, with_x_perm=True, ws=disp_ws, out=disp_out), reps)
     ms_comb = timed(lambda: moe.combine(y_perm, apos, gates, y=y2), reps)
     ms_disp_cold = timed_cold(lambda: moe.dispatch(ids, p.E, x=x, with_x_perm=True, ws=disp_ws, out=disp_out),
@@ -215,7 +452,8 @@ def main():
         bws = torch.empty(moe.workspace_size(prob, 4), dtype=torch.uint8, device=dev)
         gout = moe.backward(x, wg, wu, p.k, inter, dyg, wt, w_router=wr, ws=bws)
         gout = {key: v for key, v in gout.items() if v is not None}
-        ms_bwd = timed(lambda: moe.backward(x, wg, wu, p.k, inter, dyg, wt, w_router=wr, ws=bws, out=gout), reps)
+        ms_bwd = timed(lambda: moe.backward(x, wg, wu, p.k, inter, dyg, wt, w_router=wr, ws=bws, out=gout), reps,
+                       region=5)
         bwd_flops = 16.0 * p.T * p.k * p.d * p.f
         bwd = {"ms_per_call": round(ms_bwd, 4), "gemm_flops_per_call": bwd_flops,
                "gemm_tflops": round(bwd_flops / (ms_bwd * 1e-3) / 1e12, 2),
@@ -260,7 +498,7 @@ def main():
     if p.dtype == "bf16" and p.d % 128 == 0 and p.f % 128 == 0 and not args.no_fp8:
         wq = moe.quantize_weights_fp8(wg, wu, wd)
         ws8 = torch.empty(moe.workspace_size(prob, 5), dtype=torch.uint8, device=dev)
-        ms_fp8 = timed(lambda: moe.expert_ffn_fp8(offsets, wq, p.k, x, sa, ws=ws8, y_perm=y_perm), reps)
+        ms_fp8 = timed(lambda: moe.expert_ffn_fp8(offsets, wq, p.k, x, sa, ws=ws8, y_perm=y_perm), reps, region=7)
         fp8_tflops = ffn_flops / (ms_fp8 * 1e-3) / 1e12
         fp8 = {"ms_per_call": round(ms_fp8, 4), "flops_per_call": ffn_flops, "tflops": round(fp8_tflops, 2),
                "peak": PEAK_FP8_TFLOPS, "frac_mfma_peak": round(fp8_tflops / PEAK_FP8_TFLOPS, 4),
