@@ -264,9 +264,11 @@ def summarize_mfma(path):
     ds = _pmc_dispatches(path)
     reg = _regions(ds, lambda a: a["wg"], lambda a: a["name"])
     reg["peak"] = [a for a in ds if a["name"].startswith("mfma_peak_kernel")]
+    reg["lib"] = [dict(a, name="vendor library GEMM (" + a["name"][:24] + "...)") for a in ds if "Cijk" in a["name"]]
     lines = []
     for m, title in [(1, REGIONS[1]), (3, REGIONS[3]), (5, REGIONS[5]),
-                     ("peak", "register-operand MFMA kernel (moe_mfma_peak)")]:
+                     ("peak", "register-operand MFMA kernel (moe_mfma_peak)"),
+                     ("lib", "the vendor library's dense GEMM on the expert GEMMs' shapes (--library-gemm)")]:
         if not reg.get(m):
             continue
         agg = {}

@@ -287,9 +287,10 @@ moe_status_t moe_backward_weights(const moe_problem_t* p, const void* w_gate, co
  *   and, with a router, dW_r = dl^T x and dx += dl W_r.
  * w_down_t and w_gu_t come from moe_backward_weights.  w_router is NULL
  * when the forward took supplied logits (then no router gradients).
- * bf16 only; needs d*f < 2^30 and max(d, f) * Kpad * 2 < 2^32 bytes
- * (Kpad = T*k + 63*E rounded up to 64: the padded queue length of the
- * weight gradients' operands).  With T = 0 neither x, dy, dx nor the
+ * bf16 only; needs d*f < 2^30, T*d < 2^31 and Kpad <= 2^31 - 1
+ * (Kpad = T*k + 63*E rounded up to 64: the queues with each expert's start
+ * padded to a multiple of 64, the blocks of the router gradient's partial
+ * sums); MOE_ERR_UNSUPPORTED otherwise.  With T = 0 neither x, dy, dx nor the
  * fields of fw are read and the weight gradients come out zero.  Workspace:
  * moe_workspace_size(p, MOE_OP_BACKWARD).  Deterministic: every reduction
  * runs in a fixed order.
