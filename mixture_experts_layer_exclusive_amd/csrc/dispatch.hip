@@ -245,11 +245,24 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(const int32_t* __
     __shared__ int s_ids[kMaxDispatchChunk];
     const int64_t a0 = static_cast<int64_t>(blockIdx.x) * chunk;
     const int64_t a1 = (a0 + chunk < n) ? a0 + chunk : n;
-    stage_ids<256>(ids, a0, static_cast<int>(a1 - a0), s_ids);
-    // (wcur[0] doubles as the totals' scratch until the scatter clears it;
-    // block_bases synchronises the workgroup before s_ids is read)
+    const int cnt = static_cast<int>(a1 - a0);
+    // the first 8 * 256 ids are loaded into registers before the block-count
+    // table, so the two round trips to memory overlap; they reach LDS after
+    // the table is reduced
+    constexpr int U = 8;
+    int v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = ids[a0 + min(u * 256 + static_cast<int>(threadIdx.x), cnt - 1)];
+    // (wcur[0] doubles as the totals' scratch until the scatter clears it)
     block_bases(block_counts, E, nblk, static_cast<int>(blockIdx.x), block_base, wcur[0], counts,
                 offsets);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int i = u * 256 + static_cast<int>(threadIdx.x);
+        if (i < cnt) s_ids[i] = v[u];
+    }
+    if (cnt > U * 256) stage_ids<256>(ids, a0 + U * 256, cnt - U * 256, s_ids + U * 256);
+    __syncthreads();
     scatter_chunk<4>(s_ids, a0, a1, E, nbits, block_base, wcur, sorted_assign, assign_pos);
 }
 
