@@ -20,6 +20,7 @@ import moe_inputs as mi
 import oracle as O
 import mixture_experts_layer_exclusive_amd as moe
 from oracle import moe_backward as B
+from routing_helpers import exact_count_logits
 
 pytestmark = [pytest.mark.gpu, pytest.mark.usefixtures("poison_workspaces")]
 DEV = "cuda:0"
@@ -123,6 +124,62 @@ def test_backward_with_router(T, d, E, k, f):
     st, g = run_layer(L, dy)
     # the oracle routes on the GPU's logits (routing on equal fp32 logits is
     # bit-exact), and the router gradient flows through W_r on both sides
+    ref = oracle_grads(L, dy, host(st["logits"]), router=True)
+    assert np.array_equal(host(st["topk_ids"]), ref["forward"]["ids"])
+    check(g, ref, router=True)
+
+
+def run_layer_supplied_with_router(L, dy, logits):
+    """GPU forward on supplied logits, then the backward with the router
+    weight as well (the logits stand for the router's output: routing reads
+    them, the router gradient flows through W_r)."""
+    p = L["problem"]
+    x = dev(L["x"])
+    wg, wu, wd, wr = dev(L["w_gate"]), dev(L["w_up"]), dev(L["w_down"]), dev(L["w_router"])
+    _, st = moe.forward(x, wg, wu, wd, p.k, logits=dev(logits), intermediates=True)
+    wt = moe.backward_weights(wg, wu, wd)
+    g = moe.backward(x, wg, wu, p.k, st, dev(dy), wt, w_router=wr, with_dlogits=True,
+                     out=poisoned_outputs(p, True))
+    torch.cuda.synchronize()
+    return st, g
+
+
+# rows per expert around the 64-row slices of the weight-gradient GEMMs and
+# the 64-row blocks of the router gradient's partial sums: empty, one row,
+# one short of, at and one past a slice, and a few slices with a ragged end
+EXACT_COUNTS = [0, 1, 63, 64, 65, 127, 128, 129, 191, 193, 256, 3]
+
+
+def test_backward_exact_expert_counts():
+    """Top-2 logits that give every expert an exact row count (EXACT_COUNTS),
+    with the router gradient: the queue-order operands of the weight
+    gradients end at every offset within a 64-row slice, and so do the
+    64-row blocks of the router gradient's partial sums."""
+    E, k, d, f = len(EXACT_COUNTS), 2, 128, 192
+    T = sum(EXACT_COUNTS) // 2
+    print(f"backward exact counts T={T} d={d} E={E} k={k} f={f}", flush=True)
+    p = mi.Problem(T, d, E, k, f, "bf16")
+    L = mi.make_layer(p, seed=11)
+    logits = exact_count_logits(EXACT_COUNTS, seed=5)
+    dy = mi.make_grad_output(p, seed=3)
+    st, g = run_layer_supplied_with_router(L, dy, logits)
+    assert np.array_equal(host(st["counts"]), np.array(EXACT_COUNTS))
+    ref = oracle_grads(L, dy, logits, router=True)
+    check(g, ref, router=True)
+    # an expert with no rows gets exactly zero weight gradients
+    for key in ("dw_gate", "dw_up", "dw_down", "dw_router"):
+        assert np.all(host(g[key])[0] == 0.0), key
+
+
+@pytest.mark.parametrize("T,d,E,k,f", [(400, 640, 16, 2, 128), (257, 1088, 4, 3, 64)])
+def test_backward_with_router_wide_rows(T, d, E, k, f):
+    """Router gradient with d above one 512-column strip of the x gather,
+    the last strip ragged."""
+    print(f"backward router wide T={T} d={d} E={E} k={k} f={f}", flush=True)
+    p = mi.Problem(T, d, E, k, f, "bf16")
+    L = mi.make_layer(p, seed=d)
+    dy = mi.make_grad_output(p, seed=d)
+    st, g = run_layer(L, dy)
     ref = oracle_grads(L, dy, host(st["logits"]), router=True)
     assert np.array_equal(host(st["topk_ids"]), ref["forward"]["ids"])
     check(g, ref, router=True)

@@ -220,6 +220,36 @@ def test_expert_ffn_and_combine(T, d, E, k, f, dtype, kind, fused_gather):
     assert rel(host(y), y_ref) <= (1e-6 if dtype == "f32" else 4e-3)
 
 
+# rows per expert around the 256-row tiles of the grouped GEMMs: empty, one
+# row, one short of, at and one past one, two and three tiles
+FFN_EXACT_COUNTS = [0, 1, 255, 256, 257, 511, 512, 513, 767, 4]
+
+
+@pytest.mark.parametrize("fused_gather", [True, False])
+def test_expert_ffn_exact_tile_counts(fused_gather):
+    from routing_helpers import exact_count_logits
+    E, k, d, f = len(FFN_EXACT_COUNTS), 2, 192, 320
+    T = sum(FFN_EXACT_COUNTS) // 2
+    print(f"ffn exact counts T={T} d={d} E={E} k={k} f={f} fused={fused_gather}", flush=True)
+    p = mi.Problem(T, d, E, k, f, "bf16")
+    L = mi.make_layer(p, seed=17)
+    ids, gates = O.topk_route(exact_count_logits(FFN_EXACT_COUNTS, seed=7), k)
+    q = O.dispatch(ids, E)
+    assert np.array_equal(q["counts"], np.array(FFN_EXACT_COUNTS))
+    wg, wu, wd = (f32_of(L[n], "bf16") for n in ("w_gate", "w_up", "w_down"))
+    yp_ref = O.expert_ffn(f32_of(L["x"], "bf16"), q["sorted_assign"], q["offsets"], k, wg, wu, wd)
+    y_perm = poison((T * k, d), torch.bfloat16)
+    if fused_gather:
+        moe.expert_ffn(dev(q["offsets"]), dev(L["w_gate"]), dev(L["w_up"]), dev(L["w_down"]), k, T,
+                       x=dev(L["x"]), sorted_assign=dev(q["sorted_assign"]), y_perm=y_perm)
+    else:
+        xp = dev(O.gather_rows(L["x"], q["sorted_assign"], k))
+        moe.expert_ffn(dev(q["offsets"]), dev(L["w_gate"]), dev(L["w_up"]), dev(L["w_down"]), k, T, x_perm=xp,
+                       y_perm=y_perm)
+    torch.cuda.synchronize()
+    assert rel(host(y_perm), yp_ref) <= TOL["bf16"]
+
+
 def test_expert_ffn_gather_from_x_beyond_4gib():
     # x with 2^31 or more elements: the fused gather addresses its rows with
     # 64-bit offsets.  x repeats a seeded block of R rows, so the oracle
