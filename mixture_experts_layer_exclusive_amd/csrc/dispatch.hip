@@ -20,6 +20,8 @@
 // Up to 4096 assignments both passes run in one 1024-thread workgroup.
 // The scatter stages its chunk's ids in LDS first (one bulk load).
 // Ids outside [0, E) are skipped (their assign_pos is -1).
+#include <algorithm>
+
 #include "device_util.h"
 #include "moe_internal.h"
 
@@ -363,6 +365,149 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const W* __restrict__ 
     }
 }
 
+// Scatter and gather in one pass, for small problems with x_perm: chunks of
+// 256 assignments and an expert-major block-count table of at most
+// kFusedMaxTable entries (written by dispatch_hist_kernel).  Each workgroup
+// copies the rows of TPB tokens as gather_rows_kernel does, and first works
+// out the queue positions of their assignments itself, by the scatter's own
+// rule: pos(a) = offsets[e] + (count of e in the blocks below a's block) +
+// (count of e at a' < a in a's block), e = ids[a].  Its row loads are issued
+// before the table is read, so the copy's memory latency overlaps the
+// position work; it writes sorted_assign and assign_pos for its assignments,
+// workgroup 0 also counts and offsets.  Every workgroup reduces the whole
+// table (E x blocks entries, from L2).
+constexpr int kFusedMaxTable = 4096;
+constexpr int kFusedChunk = 256;
+// assignments per workgroup: at most one chunk, so they lie in at most two
+// consecutive blocks (b_lo and b_lo + 1)
+constexpr int kFusedMaxAssign = kFusedChunk;
+
+template <int U>
+__global__ __launch_bounds__(256) void dispatch_fused_gather_kernel(
+    const int32_t* __restrict__ ids, int E, int k, int nblk, const int32_t* __restrict__ block_counts,
+    const uint4* __restrict__ x, int64_t T, int64_t words_per_row, int tpb, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_assign, int32_t* __restrict__ assign_pos,
+    uint4* __restrict__ x_perm) {
+    __shared__ int s_off[MOE_MAX_EXPERTS];     // offsets, then offsets + counts below block b_lo
+    __shared__ int s_off1[MOE_MAX_EXPERTS];    // ... below block b_lo + 1
+    __shared__ int s_ids[kFusedChunk + kFusedMaxAssign];
+    __shared__ int s_pos[kFusedMaxAssign];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * tpb;
+    const int64_t nt = (t0 + tpb <= T) ? tpb : T - t0;
+    const int64_t total = nt * words_per_row;
+    const uint4* src = x + t0 * words_per_row;
+    // the first pass of row loads, before anything else
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t i = tid + u * 256;
+        if (i < total) v[u] = load_nt(src + i);
+    }
+    const int64_t a_lo = t0 * k;
+    const int m = static_cast<int>(nt * k);
+    const int b_lo = static_cast<int>(a_lo / kFusedChunk);
+    const int64_t cs = static_cast<int64_t>(b_lo) * kFusedChunk;
+    const int nid = static_cast<int>(a_lo + m - cs);
+    for (int i = tid; i < nid; i += 256) s_ids[i] = ids[cs + i];
+    // per expert (one thread each): its total and its counts below blocks
+    // b_lo and b_lo + 1
+    int tot = 0, pre0 = 0, pre1 = 0;
+    if (tid < E) {
+        const int32_t* row = block_counts + static_cast<int64_t>(tid) * nblk;
+#pragma unroll 8
+        for (int b = 0; b < nblk; ++b) {
+            const int c = row[b];
+            tot += c;
+            pre0 += b < b_lo ? c : 0;
+            pre1 += b <= b_lo ? c : 0;
+        }
+        s_off[tid] = tot;
+    }
+    __syncthreads();
+    if (tid < 64) {
+        // exclusive scan of the totals over E <= 256 experts, 4 per lane
+        int c[4], local = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = tid * 4 + i;
+            c[i] = e < E ? s_off[e] : 0;
+            local += c[i];
+        }
+        int incl = local;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int o = __shfl_up(incl, off, 64);
+            if (tid >= off) incl += o;
+        }
+        int run = incl - local;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = tid * 4 + i;
+            if (e < E) {
+                s_off1[e] = run;  // (offsets, for now)
+                if (blockIdx.x == 0) {
+                    offsets[e] = run;
+                    counts[e] = c[i];
+                }
+            }
+            run += c[i];
+        }
+        if (blockIdx.x == 0 && tid == 63) offsets[E] = incl;
+    }
+    __syncthreads();
+    if (tid < E) {
+        const int o = s_off1[tid];
+        s_off[tid] = o + pre0;
+        s_off1[tid] = o + pre1;
+    }
+    __syncthreads();
+    // positions: wave w takes assignments w, w + 4, ...; its lanes count the
+    // matching ids below a in a's block 64 at a time
+    for (int i = wave; i < m; i += 4) {
+        const int64_t a = a_lo + i;
+        const int e = s_ids[a - cs];
+        int pos = -1;
+        if (static_cast<unsigned>(e) < static_cast<unsigned>(E)) {
+            const int64_t start = (a / kFusedChunk) * kFusedChunk;
+            int rank = 0;
+            for (int64_t j0 = start; j0 < a; j0 += 64) {
+                const int64_t j = j0 + lane;
+                rank += __popcll(__ballot(j < a && s_ids[j - cs] == e));
+            }
+            pos = (start == cs ? s_off[e] : s_off1[e]) + rank;
+        }
+        if (lane == 0) {
+            s_pos[i] = pos;
+            assign_pos[a] = pos;
+            if (pos >= 0) sorted_assign[pos] = static_cast<int32_t>(a);
+        }
+    }
+    __syncthreads();
+    for (int64_t i0 = tid; i0 < total; i0 += 256 * U) {
+        if (i0 != tid) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t i = i0 + u * 256;
+                if (i < total) v[u] = load_nt(src + i);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = i0 + u * 256;
+            if (i >= total) break;
+            const int64_t tl = i / words_per_row;
+            const int64_t w = i % words_per_row;
+            for (int j = 0; j < k; ++j) {
+                const int pos = s_pos[tl * k + j];
+                if (pos >= 0) x_perm[static_cast<int64_t>(pos) * words_per_row + w] = v[u];
+            }
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_dispatch_queues(const moe_problem_t& p, const int32_t* ids, int32_t* counts,
@@ -380,6 +525,30 @@ hipError_t launch_dispatch_queues(const moe_problem_t& p, const int32_t* ids, in
     dispatch_scatter_kernel<<<nblk, 256, 0, s>>>(ids, n, chunk, p.E, id_bits(p.E), nblk, block_counts,
                                                  counts, offsets, sorted_assign, assign_pos);
     return hipGetLastError();
+}
+
+hipError_t launch_dispatch(const moe_problem_t& p, const int32_t* ids, const void* x, int32_t* counts,
+                           int32_t* offsets, int32_t* sorted_assign, int32_t* assign_pos, int32_t* block_counts,
+                           void* x_perm, hipStream_t s) {
+    const int64_t n = p.T * p.k;
+    const int64_t row_bytes = static_cast<int64_t>(p.d) * (p.dtype == MOE_DTYPE_F32 ? 4 : 2);
+    if (x_perm != nullptr && n > SMALL_SORT_MAX && dispatch_chunk(n) == kFusedChunk &&
+        static_cast<int64_t>(p.E) * dispatch_blocks(n) <= kFusedMaxTable && row_bytes % 16 == 0) {
+        const int nblk = static_cast<int>(dispatch_blocks(n));
+        dispatch_hist_kernel<<<nblk, 256, 0, s>>>(ids, n, kFusedChunk, p.E, nblk, block_counts);
+        // rows per workgroup as in the gather (about 32 KB), at most
+        // kFusedMaxAssign assignments
+        int tpb = static_cast<int>(row_bytes >= 32768 ? 1 : 32768 / row_bytes);
+        tpb = std::max(1, std::min(tpb, kFusedMaxAssign / p.k));
+        const unsigned grid = static_cast<unsigned>(ceil_div(p.T, tpb));
+        dispatch_fused_gather_kernel<8><<<grid, 256, 0, s>>>(
+            ids, p.E, p.k, nblk, block_counts, static_cast<const uint4*>(x), p.T, row_bytes / 16, tpb, counts,
+            offsets, sorted_assign, assign_pos, static_cast<uint4*>(x_perm));
+        return hipGetLastError();
+    }
+    const hipError_t e = launch_dispatch_queues(p, ids, counts, offsets, sorted_assign, assign_pos, block_counts, s);
+    if (e != hipSuccess || x_perm == nullptr) return e;
+    return launch_gather_rows(p, x, assign_pos, x_perm, s);
 }
 
 hipError_t launch_gather_rows(const moe_problem_t& p, const void* x, const int32_t* assign_pos,

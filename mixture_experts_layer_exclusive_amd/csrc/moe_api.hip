@@ -275,9 +275,8 @@ moe_status_t moe_dispatch(const moe_problem_t* p, const int32_t* topk_ids, const
     if (ws_bytes < dispatch_ws(*p)) return MOE_ERR_WORKSPACE_TOO_SMALL;
     hipStream_t s = static_cast<hipStream_t>(stream);
     clear_hip_error();
-    MOE_LAUNCH(launch_dispatch_queues(*p, topk_ids, counts, offsets, sorted_assign, assign_pos,
-                                      static_cast<int32_t*>(ws), s));
-    if (x_perm != nullptr) MOE_LAUNCH(launch_gather_rows(*p, x, assign_pos, x_perm, s));
+    MOE_LAUNCH(launch_dispatch(*p, topk_ids, x, counts, offsets, sorted_assign, assign_pos,
+                               static_cast<int32_t*>(ws), x_perm, s));
     return MOE_OK;
 }
 
@@ -299,11 +298,11 @@ moe_status_t moe_dispatch_no_alloc(const moe_problem_t* p, const int32_t* topk_i
     clear_hip_error();
     void* table = nullptr;
     if (scratch_address(s, &table) != hipSuccess) return MOE_ERR_HIP;
-    // (the histogram writes every entry of the table that the scatter reads,
-    // so nothing in it has to start at zero)
-    MOE_LAUNCH(launch_dispatch_queues(*p, topk_ids, counts, offsets, sorted_assign, assign_pos,
-                                      static_cast<int32_t*>(table), s));
-    if (x_perm != nullptr) MOE_LAUNCH(launch_gather_rows(*p, x, assign_pos, x_perm, s));
+    // (the histogram writes every entry of the table that the scatter, or
+    // the one-pass scatter and gather, reads, so nothing in it has to start
+    // at zero)
+    MOE_LAUNCH(launch_dispatch(*p, topk_ids, x, counts, offsets, sorted_assign, assign_pos,
+                               static_cast<int32_t*>(table), x_perm, s));
     return MOE_OK;
 }
 

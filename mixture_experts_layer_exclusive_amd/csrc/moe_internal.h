@@ -77,6 +77,11 @@ hipError_t launch_route_topk(const moe_problem_t& p, const float* logits, int32_
 hipError_t launch_dispatch_queues(const moe_problem_t& p, const int32_t* ids, int32_t* counts,
                                   int32_t* offsets, int32_t* sorted_assign, int32_t* assign_pos,
                                   int32_t* block_counts, hipStream_t s);
+// The dispatch: queues, and with x_perm the rows gathered into queue order
+// (small problems: one pass does the scatter and the gather).
+hipError_t launch_dispatch(const moe_problem_t& p, const int32_t* ids, const void* x, int32_t* counts,
+                           int32_t* offsets, int32_t* sorted_assign, int32_t* assign_pos, int32_t* block_counts,
+                           void* x_perm, hipStream_t s);
 hipError_t launch_gather_rows(const moe_problem_t& p, const void* x, const int32_t* assign_pos,
                               void* x_perm, hipStream_t s);
 

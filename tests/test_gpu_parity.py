@@ -116,6 +116,46 @@ def test_route_and_dispatch_bit_exact(T, E, k, kind):
     assert np.array_equal(xp, O.gather_rows(x, q["sorted_assign"], k))
 
 
+@pytest.mark.parametrize("T,E,k,with_x", [(100, 8, 2, True), (5000, 8, 2, True), (5000, 8, 2, False),
+                                          (30000, 16, 2, True), (700, 40, 7, True), (10000, 128, 4, True)])
+def test_dispatch_skips_ids_outside_range(T, E, k, with_x):
+    """Ids outside [0, E) take no queue row (assign_pos = -1) and leave the
+    other assignments' stable order as it is, on every dispatch path (one
+    workgroup; histogram + scatter; histogram + one-pass scatter and gather).
+    The oracle defines only valid ids, so the expectation is the counting
+    sort of the valid assignments alone: pos(a) = offsets[e] + the number of
+    valid a' < a with the same expert."""
+    print(f"dispatch with out-of-range ids T={T} E={E} k={k} x_perm={with_x}", flush=True)
+    p = mi.Problem(T, 64, E, k, 64, "bf16")
+    ids, _ = O.topk_route(mi.make_gaussian_logits(p, seed=T), k)
+    rng = np.random.default_rng(T)
+    bad = rng.random(ids.shape) < 0.03
+    ids = np.where(bad, rng.choice(np.array([-1, E, E + 7, -1000], dtype=np.int32), ids.shape), ids).astype(np.int32)
+    flat = ids.reshape(-1)
+    valid = (flat >= 0) & (flat < E)
+    counts = np.bincount(flat[valid], minlength=E).astype(np.int32)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    apos = np.full(T * k, -1, dtype=np.int32)
+    seen = offsets[:-1].copy()
+    for a in np.nonzero(valid)[0]:
+        apos[a] = seen[flat[a]]
+        seen[flat[a]] += 1
+    nv = int(valid.sum())
+    x = mi.make_x(p, seed=1)
+    out = dict(counts=poison_i32(E), offsets=poison_i32(E + 1), sorted_assign=poison_i32(T * k),
+               assign_pos=poison_i32(T * k), x_perm=poison((T * k, 64), torch.bfloat16) if with_x else None)
+    moe.dispatch(dev(ids), E, x=dev(x) if with_x else None, with_x_perm=with_x, out=out)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(out["counts"]), counts)
+    assert np.array_equal(host(out["offsets"]), offsets)
+    assert np.array_equal(host(out["assign_pos"]), apos)
+    sa = host(out["sorted_assign"])[:nv]
+    assert np.array_equal(sa, np.nonzero(valid)[0][np.argsort(apos[valid], kind="stable")])
+    if with_x:
+        xp = out["x_perm"].view(torch.int16).cpu().numpy().view(np.uint16)[:nv]
+        assert np.array_equal(xp, np.asarray(x)[sa // k])
+
+
 def test_dispatch_f32_rows_and_odd_width():
     p = mi.Problem(300, 3, 5, 2, 7, "f32")
     ids_ref, _ = O.topk_route(mi.make_tie_logits(p, 3), 2)
