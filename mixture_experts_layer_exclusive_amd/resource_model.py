@@ -80,9 +80,24 @@ class Layer:
 
 # ---- memory -----------------------------------------------------------------
 
+def _dispatch_chunk(n: int) -> int:
+    return min(max(_cdiv(_cdiv(n, 256), 256) * 256, 256), MAX_DISPATCH_CHUNK)
+
+
 def _dispatch_ws(L: Layer) -> int:
-    chunk = min(max(_cdiv(_cdiv(L.n, 256), 256) * 256, 256), MAX_DISPATCH_CHUNK)
-    return _align(_cdiv(L.n, chunk) * L.E * 4)
+    return _align(_cdiv(L.n, _dispatch_chunk(L.n)) * L.E * 4)
+
+
+def dispatch_launches(L: Layer) -> int:
+    """Kernel launches of a dispatch with x_perm: one workgroup for up to 4096
+    assignments, plus the gather; histogram and one pass of scatter and
+    gather for chunks of 256 ids with at most 4096 block counts; else
+    histogram, scatter and gather."""
+    if L.n <= 4096:
+        return 2
+    if _dispatch_chunk(L.n) == 256 and _cdiv(L.n, 256) * L.E <= 4096 and (L.d * L.s) % 16 == 0:
+        return 2
+    return 3
 
 
 def _split_bytes(K: int, s: int) -> int:
@@ -330,7 +345,7 @@ def predict_times(L: Layer, counts: Sequence[int], hw: Optional[Hardware] = None
     t["gemm2"] = gemm_time(hw, R * _cdiv(L.d, DOWN_COLS), L.f / BK, split=_split_bytes(L.f, L.s) > 0)
     t["expert_ffn"] = t["gemm1"] + t["gemm2"]
     t["combine"] = hw.launch_us + b["combine"] / hw.stream_bw
-    t["dispatch_with_x_perm"] = 3 * hw.launch_us + b["dispatch_with_x_perm"] / hw.stream_bw
+    t["dispatch_with_x_perm"] = dispatch_launches(L) * hw.launch_us + b["dispatch_with_x_perm"] / hw.stream_bw
     bw = _backward_parts(L, counts, hw)
     t.update(bw)
     t["backward"] = sum(bw.values())

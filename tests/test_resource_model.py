@@ -126,3 +126,17 @@ def test_list_schedule():
     # one expert's tiles (16 here) never leave its XCD
     t = RM.wgrad_time(RM.Hardware(cus=16, slice_us=1.0, tile_us=0.0), [64] + [0] * 7, 4 * 256, 4 * 256)
     assert t == 16 / 2
+
+
+def test_dispatch_launches_follow_the_library_paths():
+    # one workgroup (+ gather) up to 4096 assignments; histogram + one pass of
+    # scatter and gather for chunks of 256 ids and at most 4096 block counts;
+    # else histogram, scatter, gather
+    L = lambda T, E, k, d=4096: RM.Layer(T, d, E, k, 1024, 2)  # noqa: E731
+    assert RM.dispatch_launches(L(2048, 8, 2)) == 2
+    assert RM.dispatch_launches(L(8192, 8, 2)) == 2          # 64 blocks x 8 experts
+    assert RM.dispatch_launches(L(2048, 64, 6)) == 2         # 48 blocks x 64 experts
+    assert RM.dispatch_launches(L(32768, 16, 2)) == 2        # 256 blocks x 16 experts
+    assert RM.dispatch_launches(L(32768, 32, 2)) == 3        # 8192 block counts
+    assert RM.dispatch_launches(L(40000, 8, 2)) == 3         # chunks of 512 ids
+    assert RM.dispatch_launches(L(16384, 64, 6)) == 3
