@@ -121,6 +121,34 @@ def test_fp8_expert_ffn(T, d, E, k, f, kind):
     assert err <= 3e-2 and rms <= 3e-3
 
 
+def test_fp8_expert_ffn_exact_tile_counts():
+    """Expert row counts around the 256-row tiles (empty, 1, 255/256/257,
+    511/512/513 and 767 rows), on the fp8 path (d and f multiples of 128;
+    f = 1024 also takes the down projection's split-K tail)."""
+    from routing_helpers import exact_count_logits
+    counts = [0, 1, 255, 256, 257, 511, 512, 513, 767, 4]
+    E, k, d, f = len(counts), 2, 256, 1024
+    T = sum(counts) // 2
+    print(f"fp8 ffn exact counts T={T} d={d} E={E} k={k} f={f}", flush=True)
+    p = mi.Problem(T, d, E, k, f, "bf16")
+    L = mi.make_layer(p, seed=23)
+    ids, _ = O.topk_route(exact_count_logits(counts, seed=9), k)
+    q = O.dispatch(ids, E)
+    assert np.array_equal(q["counts"], np.array(counts))
+    f32 = lambda n: mi.bf16_bits_to_f32(L[n])  # noqa: E731
+    ref = F.fp8_expert_ffn(f32("x"), q["sorted_assign"], q["offsets"], k, f32("w_gate"), f32("w_up"),
+                           f32("w_down"))
+    wq = moe.quantize_weights_fp8(dev(L["w_gate"]), dev(L["w_up"]), dev(L["w_down"]))
+    y_perm = torch.full((T * k, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+    moe.expert_ffn_fp8(dev(q["offsets"]), wq, k, dev(L["x"]), dev(q["sorted_assign"]), y_perm=y_perm)
+    torch.cuda.synchronize()
+    got = y_perm.float().cpu().numpy()
+    err = rel(got, ref["y_perm"])
+    rms = float(np.sqrt(np.mean((got - ref["y_perm"]) ** 2) / np.mean(ref["y_perm"] ** 2)))
+    print(f"fp8 ffn exact counts: max|dy|/max|y| = {err:.2e}, rms {rms:.2e}", flush=True)
+    assert err <= 3e-2 and rms <= 3e-3
+
+
 def test_fp8_expert_ffn_twice_is_bitwise_identical():
     p = mi.Problem(2000, 256, 8, 2, 2048, "bf16")
     L = mi.make_layer(p, seed=9)
