@@ -156,6 +156,23 @@ def test_dispatch_skips_ids_outside_range(T, E, k, with_x):
         assert np.array_equal(xp, np.asarray(x)[sa // k])
 
 
+@pytest.mark.parametrize("T,E,k,d", [(5000, 8, 2, 64), (3000, 16, 3, 100)])
+def test_dispatch_f32_rows_one_pass(T, E, k, d):
+    """fp32 rows whose width is a multiple of 16 bytes take the one-pass
+    scatter and gather too (the copy is of raw 16-byte words)."""
+    p = mi.Problem(T, d, E, k, 64, "f32")
+    ids_ref, _ = O.topk_route(mi.make_gaussian_logits(p, 4), k)
+    q = O.dispatch(ids_ref, E)
+    x = mi.make_x(p, 4)
+    out = moe.dispatch(dev(ids_ref), E, x=dev(x), with_x_perm=True,
+                       out=dict(x_perm=poison((T * k, d), torch.float32), sorted_assign=poison_i32(T * k),
+                                assign_pos=poison_i32(T * k), counts=poison_i32(E), offsets=poison_i32(E + 1)))
+    torch.cuda.synchronize()
+    for key in ("counts", "offsets", "sorted_assign", "assign_pos"):
+        assert np.array_equal(host(out[key]), q[key]), key
+    assert np.array_equal(host(out["x_perm"]).view(np.uint32), O.gather_rows(x, q["sorted_assign"], k).view(np.uint32))
+
+
 def test_dispatch_f32_rows_and_odd_width():
     p = mi.Problem(300, 3, 5, 2, 7, "f32")
     ids_ref, _ = O.topk_route(mi.make_tie_logits(p, 3), 2)
