@@ -288,3 +288,44 @@ def test_full_size_backward_sampled(name):
         e_wr = rel(host(g["dw_router"]), dl.T @ x32.astype(np.float64))
         print(f"full-size backward {name}: dW_r vs dlogits^T x {e_wr:.2e}", flush=True)
         assert e_wr <= TOL
+
+
+def bwd_fuzz_cases(n=24, seed=77):
+    """Seeded random backward shapes: T in [1, 400], E in {1, 2, 3, 5, 8, 16,
+    64, 128}, k in [1, min(E, 8)], d and f multiples of 64 (some above one
+    512-column strip of the x gather, some with several 64-row weight-
+    gradient slices), Gaussian, Zipf-skewed or tie-heavy supplied logits, or
+    the router on the GPU."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        E = int(rng.choice([1, 2, 3, 5, 8, 16, 64, 128]))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        T = int(rng.integers(1, 401))
+        d = int(rng.choice([64, 128, 192, 320, 576]))
+        f = int(rng.choice([64, 128, 192, 320, 1088]))
+        kind = str(rng.choice(["gauss", "zipf", "ties", "router"]))
+        cases.append((T, d, E, k, f, kind))
+    return cases
+
+
+@pytest.mark.parametrize("T,d,E,k,f,kind", bwd_fuzz_cases())
+def test_fuzz_backward(T, d, E, k, f, kind):
+    print(f"backward fuzz T={T} d={d} E={E} k={k} f={f} {kind}", flush=True)
+    p = mi.Problem(T, d, E, k, f, "bf16")
+    L = mi.make_layer(p, seed=T * 7 + E)
+    dy = mi.make_grad_output(p, seed=T + d)
+    if kind == "router":
+        st, g = run_layer(L, dy)
+        ref = oracle_grads(L, dy, host(st["logits"]), router=True)
+        assert np.array_equal(host(st["topk_ids"]), ref["forward"]["ids"])
+        check(g, ref, router=True)
+        return
+    if kind == "gauss":
+        logits = mi.make_gaussian_logits(p, seed=d)
+    elif kind == "zipf":
+        logits = mi.make_zipf_logits(p, seed=d)
+    else:
+        logits = mi.make_tie_logits(p, seed=d)
+    _, g = run_layer(L, dy, logits=logits)
+    check(g, oracle_grads(L, dy, logits, router=False), router=False)
