@@ -219,7 +219,10 @@ __global__ __launch_bounds__(256) void bwd_gather_x_kernel(const bf16_t* __restr
 }
 
 // Step 3: dx[t] = sum_j dx_perm[pos(t, j)] (+ sum_j dl_j W_r[id_j]), fp32 in
-// ascending j, one rounding.
+// ascending j, one rounding.  KM > 0: k <= KM, the token's positions (ids,
+// logit gradients) read once into LDS and a chunk's k row loads issued
+// together; KM = 0: any k, one row at a time.  Same sums either way.
+template <int KM>
 __global__ __launch_bounds__(256) void bwd_dx_kernel(const uint4* __restrict__ dx_perm,
                                                     const int32_t* __restrict__ assign_pos,
                                                     const int32_t* __restrict__ ids,
@@ -227,6 +230,68 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(const uint4* __restrict__ d
                                                     const uint4* __restrict__ w_router, int k, int E,
                                                     int chunks, uint4* __restrict__ dx) {
     const int64_t t = blockIdx.x;
+    if constexpr (KM > 0) {
+        __shared__ int s_pos[KM];
+        __shared__ int s_e[KM];
+        __shared__ float s_dl[KM];
+        if (threadIdx.x < KM) {
+            const int j = threadIdx.x;
+            s_pos[j] = j < k ? assign_pos[t * k + j] : -1;
+            const int e = j < k && w_router != nullptr ? ids[t * k + j] : -1;
+            s_e[j] = static_cast<unsigned>(e) < static_cast<unsigned>(E) ? e : -1;
+            s_dl[j] = j < k && w_router != nullptr ? dsel[t * k + j] : 0.f;
+        }
+        __syncthreads();
+        int pos[KM], ex[KM];
+        float dl[KM];
+#pragma unroll
+        for (int j = 0; j < KM; ++j) {
+            pos[j] = s_pos[j];
+            ex[j] = s_e[j];
+            dl[j] = s_dl[j];
+        }
+        for (int c = threadIdx.x; c < chunks; c += 256) {
+            uint4 v[KM];
+#pragma unroll
+            for (int j = 0; j < KM; ++j)
+                v[j] = pos[j] >= 0 ? load_nt(dx_perm + static_cast<int64_t>(pos[j]) * chunks + c)
+                                   : make_uint4(0u, 0u, 0u, 0u);
+            uint4 wr[KM];
+            if (w_router != nullptr) {
+#pragma unroll
+                for (int j = 0; j < KM; ++j)
+                    wr[j] = ex[j] >= 0 ? w_router[static_cast<int64_t>(ex[j]) * chunks + c] : make_uint4(0u, 0u, 0u, 0u);
+            }
+            float acc[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+#pragma unroll
+            for (int j = 0; j < KM; ++j) {
+                if (pos[j] < 0) continue;
+                const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    acc[2 * i] += lo_bf16(w[i]);
+                    acc[2 * i + 1] += hi_bf16(w[i]);
+                }
+            }
+            if (w_router != nullptr) {
+#pragma unroll
+                for (int j = 0; j < KM; ++j) {
+                    if (ex[j] < 0) continue;
+                    const uint32_t w[4] = {wr[j].x, wr[j].y, wr[j].z, wr[j].w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        acc[2 * i] = fmaf(dl[j], lo_bf16(w[i]), acc[2 * i]);
+                        acc[2 * i + 1] = fmaf(dl[j], hi_bf16(w[i]), acc[2 * i + 1]);
+                    }
+                }
+            }
+            dx[t * chunks + c] = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                                            pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
+        }
+        return;
+    }
     for (int c = threadIdx.x; c < chunks; c += 256) {
         float acc[8];
 #pragma unroll
@@ -368,9 +433,18 @@ hipError_t launch_backward_gather_x(const moe_problem_t& p, const void* x, const
 hipError_t launch_backward_dx(const moe_problem_t& p, const void* dx_perm, const int32_t* assign_pos,
                               const int32_t* ids, const float* dsel, const void* w_router, void* dx,
                               hipStream_t s) {
-    bwd_dx_kernel<<<static_cast<unsigned>(p.T), 256, 0, s>>>(
-        static_cast<const uint4*>(dx_perm), assign_pos, ids, dsel, static_cast<const uint4*>(w_router),
-        p.k, p.E, p.d / 8, static_cast<uint4*>(dx));
+    const unsigned grid = static_cast<unsigned>(p.T);
+    const uint4* src = static_cast<const uint4*>(dx_perm);
+    const uint4* wr = static_cast<const uint4*>(w_router);
+    uint4* out = static_cast<uint4*>(dx);
+    if (p.k <= 2)
+        bwd_dx_kernel<2><<<grid, 256, 0, s>>>(src, assign_pos, ids, dsel, wr, p.k, p.E, p.d / 8, out);
+    else if (p.k <= 4)
+        bwd_dx_kernel<4><<<grid, 256, 0, s>>>(src, assign_pos, ids, dsel, wr, p.k, p.E, p.d / 8, out);
+    else if (p.k <= 8)
+        bwd_dx_kernel<8><<<grid, 256, 0, s>>>(src, assign_pos, ids, dsel, wr, p.k, p.E, p.d / 8, out);
+    else
+        bwd_dx_kernel<0><<<grid, 256, 0, s>>>(src, assign_pos, ids, dsel, wr, p.k, p.E, p.d / 8, out);
     return hipGetLastError();
 }
 
