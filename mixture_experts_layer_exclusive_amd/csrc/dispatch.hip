@@ -19,6 +19,9 @@
 //      makes the sort stable.
 // Up to 4096 assignments both passes run in one 1024-thread workgroup.
 // The scatter stages its chunk's ids in LDS first (one bulk load).
+// With x_perm, the rows follow in token order (gather_rows_kernel); for
+// chunks of 256 ids and a block-count table of at most 4096 entries the
+// scatter and the gather are one pass (dispatch_fused_gather_kernel).
 // Ids outside [0, E) are skipped (their assign_pos is -1).
 #include <algorithm>
 
