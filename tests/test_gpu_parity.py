@@ -117,7 +117,8 @@ def test_route_and_dispatch_bit_exact(T, E, k, kind):
 
 
 @pytest.mark.parametrize("T,E,k,with_x", [(100, 8, 2, True), (5000, 8, 2, True), (5000, 8, 2, False),
-                                          (30000, 16, 2, True), (700, 40, 7, True), (10000, 128, 4, True)])
+                                          (30000, 16, 2, True), (700, 40, 7, True), (10000, 128, 4, True),
+                                          (1100, 200, 4, True), (1030, 256, 4, False)])
 def test_dispatch_skips_ids_outside_range(T, E, k, with_x):
     """Ids outside [0, E) take no queue row (assign_pos = -1) and leave the
     other assignments' stable order as it is, on every dispatch path (one
