@@ -16,7 +16,11 @@ here (every step is a definition, written out below):
 * GEMM1 sums code products exactly (float64 here) and applies the two
   scales: u = 2^(a_t + b_j) sum_c q(x)[t, c] q(W_gate)[j, c], likewise v;
 * h = silu(u) * v is rounded to bf16 (round to nearest even), then
-  quantised per queue row, and GEMM2 gives y_perm the same way.
+  quantised per block of 32 consecutive columns of each queue row: each
+  block takes the smallest power-of-two scale that fits it, as above, but
+  not below 2^-127, the smallest scale an E8M0 byte (OCP MX) holds;
+* GEMM2 gives y_perm the same way, each code product scaled by its h
+  block's and its W_down row's scales.
 
 The combine and the routing are those of ``moe_oracle``.
 
@@ -99,6 +103,52 @@ def quantize_rows(a: np.ndarray):
     return codes, exps
 
 
+H_BLOCK = 32        # h columns per scale
+E8M0_MIN_EXP = -127  # the smallest scale exponent an E8M0 byte holds
+
+
+def pow2_scale_exponents(amax: np.ndarray) -> np.ndarray:
+    """``pow2_scale_exponent`` of every element of ``amax`` (int64)."""
+    amax = np.asarray(amax, dtype=np.float64)
+    m, e = np.frexp(amax)
+    a = np.where(m <= 0.875, e - 9, e - 8)
+    return np.where(amax == 0.0, 0, a).astype(np.int64)
+
+
+def quantize_blocks(a: np.ndarray, block: int = H_BLOCK):
+    """Power-of-two scaled E4M3 codes of each block of ``block``
+    consecutive columns of each row of a 2-D array (a row's last block may
+    be shorter): the block's exponent is the row rule of ``quantize_rows``
+    applied to the block alone, raised to at least -127.  Returns (codes
+    uint8 [R, C], exponents int32 [R, ceil(C / block)]) with
+    a[r, c] ~= 2^exp[r, c // block] * decode(codes[r, c])."""
+    a = np.asarray(a)
+    R, C = a.shape
+    nb = -(-C // block)
+    codes = np.zeros((R, C), dtype=np.uint8)
+    exps = np.zeros((R, nb), dtype=np.int32)
+    for r0 in range(0, R, 256):  # blocks of rows (the rows are independent)
+        rows = np.asarray(a[r0:r0 + 256], dtype=np.float64)
+        for b in range(nb):
+            c0, c1 = b * block, min(C, (b + 1) * block)
+            sub = rows[:, c0:c1]
+            ex = np.maximum(pow2_scale_exponents(np.max(np.abs(sub), axis=1)), E8M0_MIN_EXP)
+            codes[r0:r0 + 256, c0:c1] = e4m3_encode(np.ldexp(sub, -ex[:, None]))
+            exps[r0:r0 + 256, b] = ex
+    return codes, exps
+
+
+def dequantize_blocks(codes: np.ndarray, exps: np.ndarray, block: int = H_BLOCK) -> np.ndarray:
+    """2^exps[r, c // block] * value(codes[r, c]), float64."""
+    codes = np.asarray(codes)
+    exps = np.asarray(exps, dtype=np.int64)
+    cols = np.arange(codes.shape[1]) // block
+    out = np.empty(codes.shape, dtype=np.float64)
+    for r0 in range(0, codes.shape[0], 256):
+        out[r0:r0 + 256] = np.ldexp(e4m3_decode(codes[r0:r0 + 256]), exps[r0:r0 + 256][:, cols])
+    return out
+
+
 def dequantize_rows(codes: np.ndarray, exps: np.ndarray) -> np.ndarray:
     """2^exps[r] * value(codes[r, c]), float64 (in blocks of rows)."""
     codes = np.asarray(codes)
@@ -129,7 +179,8 @@ def fp8_expert_ffn(x: np.ndarray, sorted_assign: np.ndarray, offsets: np.ndarray
                    w_gate: np.ndarray, w_up: np.ndarray, w_down: np.ndarray) -> dict:
     """The fp8 expert FFN over the dispatch queues (definition above).
     Returns y_perm (float64 [T*k, d]), h (the bf16-rounded values, float64
-    [T*k, f]) and the codes and exponents of x, h and the weights."""
+    [T*k, f]) and the codes and exponents of x, h (one exponent per block of
+    32 columns) and the weights."""
     sa = np.asarray(sorted_assign, dtype=np.int64)
     off = np.asarray(offsets, dtype=np.int64)
     xq, xe = quantize_rows(x)
@@ -149,8 +200,8 @@ def fp8_expert_ffn(x: np.ndarray, sorted_assign: np.ndarray, offsets: np.ndarray
         u = xr @ dequantize_rows(wg[e], ge[e]).T
         v = xr @ dequantize_rows(wu[e], ue[e]).T
         h[lo:hi] = round_bf16(silu(u) * v)
-    hq, he = quantize_rows(h)
-    hdq = dequantize_rows(hq, he)
+    hq, he = quantize_blocks(h)
+    hdq = dequantize_blocks(hq, he)
     y = np.zeros((n, d), dtype=np.float64)
     for e in range(E):
         lo, hi = int(off[e]), int(off[e + 1])
@@ -162,7 +213,8 @@ def fp8_expert_ffn(x: np.ndarray, sorted_assign: np.ndarray, offsets: np.ndarray
 
 def fp8_ffn_rows(x_rows: np.ndarray, experts: np.ndarray, w_gate, w_up, w_down) -> np.ndarray:
     """The fp8 FFN of single queue rows (every quantisation above is per
-    row, so a row's output depends only on its token and expert): row i is
+    row or per block of a row, so a row's output depends only on its token
+    and expert): row i is
     token row x_rows[i] through expert experts[i].  Weights may be callables
     ``w(e)`` returning one expert's matrix; each expert used is quantised
     once.  Returns float64 [n, d]."""
@@ -180,7 +232,7 @@ def fp8_ffn_rows(x_rows: np.ndarray, experts: np.ndarray, w_gate, w_up, w_down) 
         wd = dequantize_rows(*quantize_rows(get(w_down, e)))
         xr = xdq[rows]
         h = round_bf16(silu(xr @ wg.T) * (xr @ wu.T))
-        y = dequantize_rows(*quantize_rows(h)) @ wd.T
+        y = dequantize_blocks(*quantize_blocks(h)) @ wd.T
         if out is None:
             out = np.zeros((len(experts), y.shape[1]), dtype=np.float64)
         out[rows] = y

@@ -102,6 +102,45 @@ def test_quantize_rows_scale_invariance():
     assert np.all(np.abs(dq - a) <= np.ldexp(np.abs(a), -4) + np.ldexp(1.0, e[:, None] - 10))
 
 
+def test_vector_scale_exponents_match_the_scalar_rule():
+    rng = np.random.default_rng(11)
+    amax = np.concatenate([[0.0, 448.0, 449.0, 2.0 ** -133, 3.0e38], np.abs(rng.standard_normal(2000)) *
+                           2.0 ** rng.integers(-140, 120, 2000).astype(np.float64)])
+    assert np.array_equal(F.pow2_scale_exponents(amax), [F.pow2_scale_exponent(m) for m in amax])
+
+
+def test_quantize_blocks_is_the_row_rule_on_each_block():
+    # every block of 32 columns (and the shorter last one) quantised as a row
+    # of its own gives the same codes and exponents
+    rng = np.random.default_rng(12)
+    a = rng.standard_normal((9, 32 * 3 + 7)) * 2.0 ** rng.integers(-20, 20, (9, 1))
+    a[2, 32:64] = 0.0                       # one all-zero block: exponent 0, codes 0
+    a[4, :32] *= 2.0 ** 30                  # blocks of one row far apart in scale
+    c, e = F.quantize_blocks(a)
+    assert c.shape == a.shape and e.shape == (9, 4)
+    for b in range(4):
+        cb, eb = F.quantize_rows(a[:, 32 * b:32 * (b + 1)])
+        assert np.array_equal(c[:, 32 * b:32 * (b + 1)], cb) and np.array_equal(e[:, b], eb)
+    assert e[2, 1] == 0 and np.all(c[2, 32:64] == 0)
+    # dequantised within half a code step of the input
+    dq = F.dequantize_blocks(c, e)
+    step = np.ldexp(1.0, np.repeat(e, 32, axis=1)[:, :a.shape[1]] - 10)
+    assert np.all(np.abs(dq - a) <= np.ldexp(np.abs(a), -4) + step)
+
+
+def test_quantize_blocks_floor_of_the_e8m0_range():
+    # blocks below about 2^-118 would want an exponent under -127: they take
+    # -127, and their codes are those of the values times 2^127 (0.125 is
+    # E4M3 0x20, -0.0625 is 0x98, 2^-9 the smallest subnormal 0x01)
+    a = np.zeros((1, 64))
+    a[0, :4] = [2.0 ** -130, -(2.0 ** -131), 0.0, 2.0 ** -136]
+    a[0, 32] = 1.0
+    c, e = F.quantize_blocks(a)
+    assert e[0, 0] == -127 and e[0, 1] == F.pow2_scale_exponent(1.0) == -8
+    assert list(c[0, :4]) == [0x20, 0x98, 0x00, 0x01]
+    assert np.array_equal(F.e4m3_decode(c[0, :4]) * 2.0 ** -127, a[0, :4])
+
+
 def test_round_bf16_matches_torch():
     v = np.random.default_rng(4).standard_normal(5000) * 10.0 ** np.random.default_rng(5).integers(-5, 5, 5000)
     ref = torch.tensor(v, dtype=torch.float64).to(torch.bfloat16).double().numpy()
@@ -131,7 +170,7 @@ def test_fp8_ffn_is_exact_on_representable_inputs():
         h = F.round_bf16(O.silu(xr @ wg[e].T) * (xr @ wu[e].T))
         assert np.array_equal(r["h"][lo:hi], h)
         # and GEMM2 is exact on the quantised h
-        hq = F.dequantize_rows(r["h_codes"][lo:hi], r["h_exp"][lo:hi])
+        hq = F.dequantize_blocks(r["h_codes"][lo:hi], r["h_exp"][lo:hi])
         assert np.allclose(r["y_perm"][lo:hi], hq @ wd[e].T, rtol=1e-14, atol=0)
     # every x code equals the input's own code (no rounding happened)
     assert np.array_equal(F.dequantize_rows(r["x_codes"], r["x_exp"]), x)
