@@ -505,8 +505,9 @@ def main():
         fp8 = {"ms_per_call": round(ms_fp8, 4), "flops_per_call": ffn_flops, "tflops": round(fp8_tflops, 2),
                "peak": PEAK_FP8_TFLOPS, "frac_mfma_peak": round(fp8_tflops / PEAK_FP8_TFLOPS, 4),
                "speedup_vs_bf16": round(ms_ffn / ms_fp8, 3),
-               "scheme": "OCP E4M3 codes, power-of-two scale per token (x), per queue row (h) and per "
-                         "weight row; fp32 accumulation; quantisation of x and h included"}
+               "scheme": "OCP E4M3 codes, power-of-two scale per token (x), per 32 columns of a queue row "
+                         "(h, E8M0, applied by the block-scaled MFMA) and per weight row; fp32 accumulation; "
+                         "quantisation of x and h included"}
         print(f"# fp8 expert FFN: {ms_fp8:.3f} ms/call", file=sys.stderr, flush=True)
         del wq, ws8
 

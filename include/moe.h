@@ -326,9 +326,12 @@ moe_status_t moe_quantize_weights_fp8(const moe_problem_t* p, const void* w_gate
  * moe_expert_ffn_fp8 -- moe_expert_ffn with fp8 GEMMs: x [T, d] bf16 is
  * quantised per token, GEMM1 multiplies its codes (gathered through
  * sorted_assign) with the codes of W_gate and W_up on FP8 MFMA with fp32
- * accumulation, applies both scales exactly and the SwiGLU, and rounds h to
- * bf16; h is quantised per queue row and GEMM2 does the same with W_down,
- * writing y_perm [T*k, d] bf16.  Weights from moe_quantize_weights_fp8.
+ * accumulation, applies both scales exactly and the SwiGLU, rounds h to
+ * bf16 and quantises it in its epilogue, one power-of-two scale per block of
+ * 32 columns of a queue row (an E8M0 byte, so at least 2^-127); GEMM2
+ * multiplies the h codes with the codes of W_down on the block-scaled FP8
+ * MFMA, which applies the h scales, then the W_down row scales, writing
+ * y_perm [T*k, d] bf16.  Weights from moe_quantize_weights_fp8.
  * bf16 problems with d and f multiples of 128 and T*d < 2^32 only.
  * Workspace: moe_workspace_size(p, MOE_OP_EXPERT_FFN_FP8).
  */

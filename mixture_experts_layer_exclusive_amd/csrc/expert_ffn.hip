@@ -334,12 +334,18 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     constexpr int TN = 256;                  // weight rows per tile
     constexpr int BK = 128 / EB;             // K slice width (one 128-byte line per row)
     constexpr int BN_OUT = GATEUP ? TN / 2 : TN;
+    // fp8 GEMM2 (MXS): the activation operand is h, E4M3 codes with one
+    // E8M0 scale per 32 columns of a row, which the block-scaled MFMA
+    // applies; a slice's scales (4 bytes per row) ride in each stage after
+    // the operands, one 4-byte load per lane of one instruction per wave.
+    constexpr bool MXS = F8 && MODE == kDown;
     constexpr int LA = TM / 32;              // activation loads per wave per slice (8 rows each)
     constexpr int LB = TN / 32;              // weight loads per wave per slice
-    constexpr int NL = LA + LB;
+    constexpr int NL = LA + LB + (MXS ? 1 : 0);
     constexpr int ROWB = 128;                // bytes per row of a slice
     constexpr int SA_BYTES = TM * ROWB;
-    constexpr int STAGE_BYTES = (TM + TN) * ROWB;
+    constexpr int SC_OFF = (TM + TN) * ROWB;  // (MXS) the scales within a stage
+    constexpr int STAGE_BYTES = (TM + TN) * ROWB + (MXS ? TM * 4 : 0);
     constexpr int NR = 8;                    // fragment reads per K step (4 activation, 4 weight)
     constexpr int NM = F8 ? 8 : 16;          // MFMAs per K step (fp8: each twice as long)
     constexpr int KS = 4;                    // K steps per slice (32 bytes of each row per step)
@@ -348,7 +354,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     constexpr bool A_FIRST = GATEUP;
     static_assert(2 * STAGE_BYTES <= 160 * 1024, "two stages must fit the 160 KB of LDS");
     static_assert(BK * EB == ROWB, "a slice is one 128-byte line per row");
-    static_assert(F8 ? 3 * NL <= 2 * (KS - 1) * NM : 3 * NL <= (KS - 1) * NM,
+    static_assert(F8 ? 3 * (LA + LB) <= 2 * (KS - 1) * NM : 3 * NL <= (KS - 1) * NM,
                   "the refill spreads one load per 3 MFMAs (fp8: two per 3)");
     __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE_BYTES];
     // The tile prefix and offsets tables live in stage 0 until the first load.
@@ -468,8 +474,31 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         const uint32_t so = static_cast<uint32_t>((kt & 1) * STAGE_BYTES);
         lds_dma16_s(b_base + kt * b_step, b_off[j], lds_b + so + j * 8 * ROWB);
     };
-    // load q (< NL) of slice kt, in the GEMM's load order
+    // (MXS) the scales: LDS dword w*64 + i of the stage (lane i of wave w)
+    // holds tile row ((s & 7) << 5) | (s >> 3), s = w*64 + i, so that the
+    // rows wm*128 + mb*32 + l (mb = 0..3) of a lane's fragments are 4
+    // consecutive dwords; aux holds the scales slice by slice, [K/128][M
+    // queue rows][4 bytes]
+    uint32_t sc_off = 0;
+    const char* sc_base = nullptr;
+    if constexpr (MXS) {
+        const int sl = wave * 64 + lane;
+        int pos = tile.row0 + (((sl & 7) << 5) | (sl >> 3));
+        if (pos >= tile.row1) pos = tile.row1 - 1;
+        sc_off = static_cast<uint32_t>(pos) * 4u;
+        sc_base = uniform_ptr(reinterpret_cast<const char*>(aux) + static_cast<int64_t>(work.kb) * M * 4);
+    }
+    auto dma_sc = [&](int kt) {
+        const uint32_t so = static_cast<uint32_t>((kt & 1) * STAGE_BYTES);
+        lds_dma4_s(sc_base + static_cast<int64_t>(kt) * M * 4, sc_off, lds0 + so + SC_OFF + wave * 256);
+    };
+    // load q (< NL) of slice kt, in the GEMM's load order (MXS: the scales
+    // last)
     auto dma = [&](int q, int kt) {
+        if (MXS && q == LA + LB) {
+            dma_sc(kt);
+            return;
+        }
         const bool a_op = A_FIRST ? q < LA : q >= LB;
         if (a_op) dma_a(A_FIRST ? q : q - LB, kt);
         else dma_b(A_FIRST ? q - LA : q, kt);
@@ -569,12 +598,34 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 #define MOE_MFMA_BF16(KK, Q)                                                                    \
     acc[(Q) / 4][(Q) % 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                           \
         f[KK][4 + (Q) / 4], f[KK][(Q) % 4], acc[(Q) / 4][(Q) % 4], 0, 0, 0)
+    // (MXS) this slice's scale dwords of the lane's 4 activation rows,
+    // shifted so that byte 2s is the lane's K block of fp8 K step s (lanes
+    // 32..63 hold the upper 32 of the step's 64 K values), and the next
+    // slice's, read during step 3
+    uint32_t scv[MXS ? 4 : 1] = {}, scv_n[MXS ? 4 : 1] = {};
+    auto read_sc = [&](uint32_t so, uint32_t* dst) {
+        if constexpr (MXS) {
+            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(smem + so + SC_OFF + (l32 * 8 + wm * 4) * 4);
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) dst[mb] = v[mb] >> (8 * khalf);
+        }
+    };
     // fp8: step S of a slice runs blocks (S & 1) * 8 .. + 8 of fp8 K step S >> 1
+    // (MXS: the h operand scaled by its E8M0 byte 2 (S >> 1), the weights by
+    // 2^0 = E8M0 127; their row scales follow after the loop)
 #define MOE_MFMA_F8(S, J)                                                                       \
-    acc[(((S) & 1) * 8 + (J)) / 4][(((S) & 1) * 8 + (J)) % 4] =                                   \
-        __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                                        \
-            g[(S) >> 1][4 + (((S) & 1) * 8 + (J)) / 4], g[(S) >> 1][(((S) & 1) * 8 + (J)) % 4],   \
-            acc[(((S) & 1) * 8 + (J)) / 4][(((S) & 1) * 8 + (J)) % 4], 0, 0, 0, 0, 0, 0)
+    do {                                                                                        \
+        constexpr int i_ = ((S) & 1) * 8;                                                       \
+        if constexpr (MXS)                                                                      \
+            acc[(i_ + (J)) / 4][(i_ + (J)) % 4] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4( \
+                g[(S) >> 1][4 + (i_ + (J)) / 4], g[(S) >> 1][(i_ + (J)) % 4],                     \
+                acc[(i_ + (J)) / 4][(i_ + (J)) % 4], 0, 0, 0, 0x7F7F7F7F, 2 * ((S) >> 1),         \
+                scv[MXS ? (i_ + (J)) % 4 : 0]);                                                 \
+        else                                                                                    \
+            acc[(i_ + (J)) / 4][(i_ + (J)) % 4] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4( \
+                g[(S) >> 1][4 + (i_ + (J)) / 4], g[(S) >> 1][(i_ + (J)) % 4],                     \
+                acc[(i_ + (J)) / 4][(i_ + (J)) % 4], 0, 0, 0, 0, 0, 0);                         \
+    } while (0)
 #define MOE_MFMA(KK, Q)                                                                         \
     do {                                                                                        \
         if constexpr (F8) MOE_MFMA_F8(KK, Q);                                                   \
@@ -592,9 +643,12 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // Loads complete in issue order, so each wait leaves pending exactly the
     // loads of slice kt + 2 issued before it.
     // (fp8: MFMAs twice as long, half as many: two loads per 3 MFMAs)
+    // (MXS: the scale load goes out with the first operand load)
     auto refill = [&](int step, int q, int kt) {  // MFMA q of step 1..3
         const int p = (step - 1) * NM + q;
-        const bool issue = F8 ? (p % 3 != 2 && p - p / 3 < NL) : (p % 3 == 0 && p / 3 < NL);
+        constexpr int NOP = LA + LB;  // operand loads
+        const bool issue = F8 ? (p % 3 != 2 && p - p / 3 < NOP) : (p % 3 == 0 && p / 3 < NOP);
+        if (MXS && p == 0) dma(NOP, kt + 2);
         if (issue) {
             dma(F8 ? p - p / 3 : p / 3, kt + 2);
             // keep each load between its MFMAs (the scheduler would
@@ -603,7 +657,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         }
     };
     // loads issued in steps 1..2
-    constexpr int BEFORE3_ = F8 ? 2 * NM - (2 * NM) / 3 : (2 * NM + 2) / 3;
+    constexpr int BEFORE3_ = (F8 ? 2 * NM - (2 * NM) / 3 : (2 * NM + 2) / 3) + (MXS ? 1 : 0);
     constexpr int BEFORE3 = BEFORE3_ < NL ? BEFORE3_ : NL;
     // fragments read ahead of a slice: bf16 step 0; fp8 step 0 (a register
     // pair per block, used by the slice's first two quarter steps)
@@ -625,10 +679,12 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         setup_a();
 #pragma unroll
         for (int j = 0; j < LA; ++j) dma_a(j, 0);
+        if constexpr (MXS) dma_sc(0);
         if (nk > 1) {
 #pragma unroll
             for (int j = 0; j < LA; ++j) dma_a(j, 1);
-            wait_vmcnt_lgkm0<LA>();
+            if constexpr (MXS) dma_sc(1);
+            wait_vmcnt_lgkm0<LA + (MXS ? 1 : 0)>();
         } else {
             wait_vmcnt_lgkm0<0>();
             zero_tail_rows(0);
@@ -636,6 +692,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         barrier_lds();
 #pragma unroll
         for (int i = 0; i < NR; ++i) read_frag(0, i, 0);
+        read_sc(0, scv);
         __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -696,11 +753,16 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             if (MORE) refill(3, q, kt);
             if (F8) {
                 read_frag(0, q, nso);  // two 16-byte reads
+                if (MXS && q == 0) read_sc(nso, scv_n);
             } else if ((q & 1) && (q >> 1) < NR) {
                 read_frag(0, q >> 1, nso);
             }
         }
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (MXS) {
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) scv[mb] = scv_n[mb];
+        }
     };
     int kt = 0;
     for (; kt + 2 < nk; ++kt) slice(kt, std::true_type{});
@@ -718,7 +780,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         for (int mb = 0; mb < 4; ++mb) {
             int pos = tile.row0 + wm * 128 + mb * 32 + l32;
             if (pos >= tile.row1) pos = tile.row1 - 1;
-            ea[mb] = a_exp[GATHER ? sorted_assign[pos] / topk : pos];
+            ea[mb] = MXS ? 0 : a_exp[GATHER ? sorted_assign[pos] / topk : pos];
         }
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
@@ -803,6 +865,75 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             *reinterpret_cast<uint4*>(out + static_cast<int64_t>(pos) * ldo + col) = v;
         }
     };
+
+    if constexpr (F8 && GATEUP) {
+        // fp8 GEMM1: h = silu(gate) * up rounded to bf16 and quantised for
+        // GEMM2 per block of 32 columns of a row: the block's exponent a is
+        // the smallest with max|block| <= 448 * 2^a (0 for a zero block), at
+        // least -127, stored as the E8M0 byte a + 127, and each value becomes
+        // the E4M3 code of value / 2^a (round to nearest even).  A block's 32
+        // values sit in lanes l and l + 32 of the wave (16 each).  The codes
+        // are staged as 256 rows of 128 bytes (16-byte chunk ch of row r at
+        // chunk ch ^ (r & 7)), the 4 scale bytes of each row after them; C
+        // receives the codes [M rows, N], C2 the scales, slice by slice
+        // ([N / 128][M][4]: tile column nt is GEMM2's K slice nt).
+        char* const s_codes = smem;
+        unsigned char* const s_sc = reinterpret_cast<unsigned char*>(smem + TM * 128);
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+            const int r = wm * 128 + mb * 32 + l32;
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+                float v[16];
+                float am = 0.f;
+#pragma unroll
+                for (int i = 0; i < 16; i += 2) {
+                    const uint32_t w = pack_bf16x2(silu_mul_fast(acc[nb][mb][i], acc[nb + 2][mb][i]),
+                                                   silu_mul_fast(acc[nb][mb][i + 1], acc[nb + 2][mb][i + 1]));
+                    v[i] = lo_bf16(w);
+                    v[i + 1] = hi_bf16(w);
+                    am = fmaxf(am, fmaxf(fabsf(v[i]), fabsf(v[i + 1])));
+                }
+                am = fmaxf(am, __shfl_xor(am, 32, 64));
+                // am = mm 2^e with mm in [0.5, 1); 448 = 0.875 * 2^9
+                int a = 0;
+                if (am > 0.f) {
+                    int e = 0;
+                    const float mm = frexpf(am, &e);
+                    a = mm <= 0.875f ? e - 9 : e - 8;
+                }
+                a = max(a, -127);
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    int w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(v[4 * g], -a),
+                                                            __builtin_amdgcn_ldexpf(v[4 * g + 1], -a), 0, false);
+                    w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(v[4 * g + 2], -a),
+                                                        __builtin_amdgcn_ldexpf(v[4 * g + 3], -a), w, true);
+                    const int c = wn * 64 + nb * 32 + 8 * g + 4 * khalf;  // byte column of the tile
+                    *reinterpret_cast<int*>(s_codes + r * 128 + (((c >> 4) ^ (r & 7)) << 4) + (c & 15)) = w;
+                }
+                if (khalf == 0) s_sc[r * 4 + wn * 2 + nb] = static_cast<unsigned char>(a + 127);
+            }
+        }
+        __syncthreads();
+        unsigned char* const hq = reinterpret_cast<unsigned char*>(C);
+#pragma unroll 4
+        for (int idx = tid; idx < TM * 8; idx += 256) {
+            const int r = idx >> 3;
+            const int ch = idx & 7;
+            const int pos = tile.row0 + r;
+            const int col = n0 + ch * 16;
+            if (pos >= tile.row1 || col >= N) continue;
+            *reinterpret_cast<uint4*>(hq + static_cast<int64_t>(pos) * N + col) =
+                *reinterpret_cast<const uint4*>(s_codes + r * 128 + ((ch ^ (r & 7)) << 4));
+        }
+        const int pos = tile.row0 + tid;
+        if (pos < tile.row1)
+            *reinterpret_cast<uint32_t*>(reinterpret_cast<unsigned char*>(C2) +
+                                         (static_cast<int64_t>(tile.nt) * M + pos) * 4) =
+                *reinterpret_cast<const uint32_t*>(s_sc + tid * 4);
+        return;
+    }
 
     if (MODE == kUpBwd) {
         // The backward of SwiGLU from the recomputed gate u and up v and the
@@ -1156,29 +1287,29 @@ hipError_t launch_backward_wgrad(const moe_problem_t& p, const void* A, int lda,
 // ---- fp8 expert FFN ------------------------------------------------------
 
 // GEMM1 on fp8 codes of x (gathered per queue row) and of W_gate / W_up, with
-// the SwiGLU epilogue, writes h in bf16; h is quantised per queue row; GEMM2
-// on the codes of h and W_down writes y_perm.  The down projection splits its
-// tail like the bf16 one (part: kSplitWGs partial tiles, or null).
+// the SwiGLU epilogue, writes h as E4M3 codes h_q [T*k, f] with one E8M0
+// scale per 32 columns (h_sc, [f / 128][T*k][4] bytes); GEMM2 on the codes of
+// h and W_down, on the block-scaled MFMA, writes y_perm.  The down projection
+// splits its tail like the bf16 one (part: kSplitWGs partial tiles, or null).
 hipError_t launch_expert_ffn_fp8(const moe_problem_t& p, const void* x_q, const int32_t* x_exp,
                                  const int32_t* sorted_assign, const int32_t* offsets, const void* wg_q,
                                  const int32_t* wg_exp, const void* wu_q, const int32_t* wu_exp,
-                                 const void* wd_q, const int32_t* wd_exp, void* h, void* h_q, int32_t* h_exp,
-                                 float* part, void* y_perm, hipStream_t s) {
+                                 const void* wd_q, const int32_t* wd_exp, void* h_q, void* h_sc, float* part,
+                                 void* y_perm, hipStream_t s) {
     const int64_t n = p.T * p.k;
+    const int mrows = static_cast<int>(n);  // (queue rows: the scales' row count)
     const unsigned g1 = grid_for(n, p.E, kBM, static_cast<int>(ceil_div(p.f, kGateUpCols)));
     grouped_gemm_bf16_kernel<kUp, true, false, true><<<g1, 256, 0, s>>>(
         static_cast<const bf16_t*>(x_q), sorted_assign, p.k, offsets, p.E, static_cast<const bf16_t*>(wg_q),
-        static_cast<const bf16_t*>(wu_q), static_cast<bf16_t*>(h), p.f, p.d, 0, nullptr, nullptr, nullptr, 0,
-        x_exp, wg_exp, wu_exp);
-    hipError_t err = launch_quant_rows_fp8(h, n, p.f, h_q, h_exp, s);
-    if (err != hipSuccess) return err;
+        static_cast<const bf16_t*>(wu_q), static_cast<bf16_t*>(h_q), p.f, p.d, 0, nullptr, nullptr,
+        static_cast<bf16_t*>(h_sc), mrows, x_exp, wg_exp, wu_exp);
     const unsigned g2 = grid_for(n, p.E, kBM, static_cast<int>(ceil_div(p.d, kDownCols)));
     const int nk2 = p.f / 128;
     const int slots = (part != nullptr && fp8_can_split(p)) ? resident_slots(s) : 0;
     grouped_gemm_bf16_kernel<kDown, false, false, true><<<g2 + (slots > 0 ? kSplitWGs : 0), 256, 0, s>>>(
         static_cast<const bf16_t*>(h_q), sorted_assign, p.k, offsets, p.E, static_cast<const bf16_t*>(wd_q),
-        nullptr, static_cast<bf16_t*>(y_perm), p.d, p.f, slots, part, nullptr, nullptr, 0, h_exp, wd_exp,
-        nullptr);
+        nullptr, static_cast<bf16_t*>(y_perm), p.d, p.f, slots, part, static_cast<const bf16_t*>(h_sc), nullptr,
+        mrows, nullptr, wd_exp, nullptr);
     if (slots > 0)
         split_reduce_kernel<<<kSplitWGs * 16, 256, 0, s>>>(part, offsets, p.E, p.d, nk2, slots,
                                                           static_cast<bf16_t*>(y_perm));

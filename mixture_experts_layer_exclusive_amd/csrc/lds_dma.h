@@ -51,6 +51,17 @@ __device__ __forceinline__ void lds_dma16_s(const void* sbase, uint32_t voff, ui
         : "memory");
 }
 
+// 4 bytes per lane from a wave-uniform base plus a 32-bit per-lane byte
+// offset into LDS: lane i's dword lands at lds_base + 4 * i.
+__device__ __forceinline__ void lds_dma4_s(const void* sbase, uint32_t voff, uint32_t lds_base) {
+    asm volatile(
+        "s_nop 0\n\t"
+        "global_load_lds_dword %0, %1"
+        :
+        : "v"(voff), "s"(sbase), "{m0}"(lds_base)
+        : "memory");
+}
+
 // Workgroup barrier without a memory fence (the LDS traffic it orders is
 // waited for explicitly); the empty asm statements keep the compiler from
 // moving memory accesses across it.

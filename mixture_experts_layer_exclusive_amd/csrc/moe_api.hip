@@ -125,13 +125,13 @@ moe_status_t check_backward(const moe_problem_t* p) {
     return MOE_OK;
 }
 
-// fp8 expert FFN workspace: x codes [T, d] and exponents [T], h [T*k, f]
-// bf16, h codes [T*k, f] and exponents [T*k], split-K partial tiles.
+// fp8 expert FFN workspace: x codes [T, d] and exponents [T], h codes
+// [T*k, f] and their E8M0 scales (one byte per 32 columns), split-K partial
+// tiles.
 size_t ffn_fp8_ws(const moe_problem_t& p) {
     const size_t n = static_cast<size_t>(p.T) * p.k;
     return align_up(static_cast<size_t>(p.T) * p.d, kAlign) + align_up(static_cast<size_t>(p.T) * 4, kAlign) +
-           align_up(n * p.f * 2, kAlign) + align_up(n * p.f, kAlign) + align_up(n * 4, kAlign) +
-           align_up(fp8_split_bytes(p), kAlign);
+           align_up(n * p.f, kAlign) + align_up(n * (p.f / 32), kAlign) + align_up(fp8_split_bytes(p), kAlign);
 }
 
 // Limits of the fp8 path (beyond check_problem): bf16 weights and
@@ -571,15 +571,14 @@ moe_status_t moe_expert_ffn_fp8(const moe_problem_t* p, const void* x, const int
     Carver c(ws);
     void* x_q = c.take<char>(static_cast<size_t>(p->T) * p->d);
     int32_t* x_exp = c.take<int32_t>(static_cast<size_t>(p->T) * 4);
-    void* h = c.take<char>(n * p->f * 2);
     void* h_q = c.take<char>(n * p->f);
-    int32_t* h_exp = c.take<int32_t>(n * 4);
+    void* h_sc = c.take<char>(n * (p->f / 32));
     float* part = fp8_split_bytes(*p) > 0 ? c.take<float>(fp8_split_bytes(*p)) : nullptr;
     hipStream_t s = static_cast<hipStream_t>(stream);
     clear_hip_error();
     MOE_LAUNCH(launch_quant_rows_fp8(x, p->T, p->d, x_q, x_exp, s));
     MOE_LAUNCH(launch_expert_ffn_fp8(*p, x_q, x_exp, sorted_assign, offsets, w->w_gate, w->w_gate_exp, w->w_up,
-                                     w->w_up_exp, w->w_down, w->w_down_exp, h, h_q, h_exp, part, y_perm, s));
+                                     w->w_up_exp, w->w_down, w->w_down_exp, h_q, h_sc, part, y_perm, s));
     return MOE_OK;
 }
 

@@ -123,8 +123,8 @@ hipError_t launch_quant_rows_fp8(const void* src, int64_t rows, int cols, void* 
 hipError_t launch_expert_ffn_fp8(const moe_problem_t& p, const void* x_q, const int32_t* x_exp,
                                  const int32_t* sorted_assign, const int32_t* offsets, const void* wg_q,
                                  const int32_t* wg_exp, const void* wu_q, const int32_t* wu_exp,
-                                 const void* wd_q, const int32_t* wd_exp, void* h, void* h_q, int32_t* h_exp,
-                                 float* part, void* y_perm, hipStream_t s);
+                                 const void* wd_q, const int32_t* wd_exp, void* h_q, void* h_sc, float* part,
+                                 void* y_perm, hipStream_t s);
 hipError_t launch_backward_weights(const moe_problem_t& p, const void* w_gate, const void* w_up,
                                    const void* w_down, void* w_down_t, void* w_gu_t, hipStream_t s);
 hipError_t launch_backward_dy(const moe_problem_t& p, const void* dy, const void* y_perm,

@@ -246,7 +246,8 @@ def test_fp8_validation(lib):
     st, need = ws_size(lib, good, L.MOE_OP_EXPERT_FFN_FP8)
     assert st == L.MOE_OK
     n = 64 * 2
-    assert need >= 64 * 256 + 64 * 4 + n * 512 * 2 + n * 512 + n * 4
+    # x codes and exponents, h codes and one scale byte per 32 columns
+    assert need >= 64 * 256 + 64 * 4 + n * 512 + n * 512 // 32
     w = L.MoeFp8Weights(w_gate=A, w_gate_exp=A, w_up=A, w_up_exp=A, w_down=A, w_down_exp=A)
     for bad in (dict(d=192), dict(f=320), dict(dtype=L.MOE_DTYPE_F32), dict(T=2 ** 22, d=2048)):
         p = prob(T=64, d=256, E=8, k=2, f=512)

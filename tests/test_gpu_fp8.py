@@ -5,7 +5,8 @@
   must be bit-exact (ties, subnormal codes, zero rows and signed zeros
   included).
 * The fp8 expert FFN must agree with the oracle's fp8 FFN, which quantises
-  the same bf16 inputs the same way and sums in float64.  The bound follows
+  the same bf16 inputs the same way (h with one E8M0 scale per 32 columns)
+  and sums in float64.  The bound follows
   from where the two may differ.  The GPU sums in fp32 and computes the
   SwiGLU in fp32 before rounding h to bf16, so about one h element in 2000
   lands one bf16 unit away from the oracle's.  About one in 16 of those
@@ -147,6 +148,44 @@ def test_fp8_expert_ffn_exact_tile_counts():
     rms = float(np.sqrt(np.mean((got - ref["y_perm"]) ** 2) / np.mean(ref["y_perm"] ** 2)))
     print(f"fp8 ffn exact counts: max|dy|/max|y| = {err:.2e}, rms {rms:.2e}", flush=True)
     assert err <= 3e-2 and rms <= 3e-3
+
+
+def test_fp8_h_scales_are_per_block():
+    """One block of 32 h columns 2^16 times larger than the rest of its row
+    (its W_up rows scaled), and zero W_down columns there, so that y depends
+    on the other blocks only: with one scale per block they keep E4M3's
+    relative precision, with one scale per row they would fall into E4M3's
+    subnormals.  The GPU follows the per-block oracle, and the two schemes
+    are far apart on this input."""
+    p = mi.Problem(256, 256, 4, 2, 512, "bf16")
+    L = mi.make_layer(p, seed=31)
+    f32 = {n: mi.bf16_bits_to_f32(L[n]) for n in ("x", "w_gate", "w_up", "w_down")}
+    f32["w_up"][:, 64:96, :] *= 2.0 ** 16
+    f32["w_down"][:, :, 64:96] = 0.0
+    bits = {n: torch.from_numpy(f32[n]).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+            for n in ("w_up", "w_down")}
+    ids, _ = O.topk_route(mi.make_gaussian_logits(p, 31), 2)
+    q = O.dispatch(ids, 4)
+    ref = F.fp8_expert_ffn(f32["x"], q["sorted_assign"], q["offsets"], 2, f32["w_gate"], f32["w_up"],
+                           f32["w_down"])
+    wd_c, wd_e = F.quantize_weights(f32["w_down"])
+    h_row = F.dequantize_rows(*F.quantize_rows(ref["h"]))
+    off = q["offsets"]
+    y_row = np.zeros_like(ref["y_perm"])
+    for e in range(4):
+        y_row[off[e]:off[e + 1]] = h_row[off[e]:off[e + 1]] @ F.dequantize_rows(wd_c[e], wd_e[e]).T
+    wq = moe.quantize_weights_fp8(dev(L["w_gate"]), dev(bits["w_up"]), dev(bits["w_down"]))
+    y_perm = torch.full((p.T * 2, p.d), float("nan"), dtype=torch.bfloat16, device=DEV)
+    moe.expert_ffn_fp8(dev(off), wq, 2, dev(L["x"]), dev(q["sorted_assign"]), y_perm=y_perm)
+    torch.cuda.synchronize()
+    got = y_perm.float().cpu().numpy()
+    err = rel(got, ref["y_perm"])
+    rms = float(np.sqrt(np.mean((got - ref["y_perm"]) ** 2) / np.mean(ref["y_perm"] ** 2)))
+    apart = rel(y_row, ref["y_perm"])
+    print(f"fp8 h block scales: GPU vs per-block max {err:.2e} rms {rms:.2e}; per-row vs per-block {apart:.2e}",
+          flush=True)
+    assert err <= 3e-2 and rms <= 3e-3
+    assert apart >= 0.1
 
 
 def test_fp8_expert_ffn_twice_is_bitwise_identical():
