@@ -37,10 +37,7 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
-#ifndef GEMM_GROUP_M
-#define GEMM_GROUP_M 8
-#endif
-constexpr int GROUP_M = GEMM_GROUP_M;
+constexpr int GROUP_M = 8;  // row tiles per group of the tile order (8 measured best)
 constexpr int NUM_XCD = 8;
 
 // Per-expert tile prefix in LDS: s_prefix[e] = sum_{e' < e} ceil(rows_e' / bm),
@@ -268,9 +265,6 @@ constexpr int kUp = 0, kDown = 1, kUpBwd = 2, kWgrad = 3;
 // permutation of the experts by descending count) in a snake order, XCD 0
 // to 7 and back, which keeps the XCDs' loads even under a skewed routing.
 // Within an expert, groups of GROUP_M row tiles walk the column tiles.
-#ifndef MOE_WGRAD_BY_XCD
-#define MOE_WGRAD_BY_XCD 1
-#endif
 __host__ __device__ __forceinline__ int wgrad_tiles_per_expert(int M, int N) {
     return ((M + kBM - 1) / kBM) * ((N + kDownCols - 1) / kDownCols);
 }
@@ -280,7 +274,6 @@ __device__ __forceinline__ bool find_wgrad_work(const int32_t* __restrict__ offs
     const int mtn = (M + kBM - 1) / kBM;
     const int ntn = (N + kDownCols - 1) / kDownCols;
     const int per_e = mtn * ntn;
-#if MOE_WGRAD_BY_XCD
     const int x = blockIdx.x % NUM_XCD;
     const int place = blockIdx.x / NUM_XCD;
     const int j = place / per_e;  // the XCD's j-th expert
@@ -288,12 +281,6 @@ __device__ __forceinline__ bool find_wgrad_work(const int32_t* __restrict__ offs
     if (rank >= E) return false;
     const int e = order[rank];
     const int local = place % per_e;
-#else
-    const int pid = blockIdx.x;
-    if (pid >= E * per_e) return false;
-    const int e = order[pid / per_e];
-    const int local = pid % per_e;
-#endif
     const int group = local / (GROUP_M * ntn);
     const int first_m = group * GROUP_M;
     const int gsz = min(GROUP_M, mtn - first_m);
