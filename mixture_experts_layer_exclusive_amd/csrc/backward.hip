@@ -5,17 +5,19 @@
 // backward run on the forward's compact dispatch queues; the checkpoint
 // bullet of the same item (and Key contributions, bullet 3) recomputes
 // intermediates instead of storing them: here the SwiGLU ones.  Here:
-//   1. per token: slot gradients dg = <dy[t], y_perm[pos]>, the queue rows'
-//      output gradient dy_perm[pos] = g dy[t], and the logit gradient of the
-//      renormalised top-k softmax, dl_j = g_j (dg_j - sum_i g_i dg_i);
-//   2. grouped GEMMs over the queues (dh, the recompute of gate/up with the
-//      SwiGLU backward, dx_perm) and the weight gradients, which read their
-//      operands in queue order (x gathered into queue order here);
+//   1. per token: slot gradients dg = <dy[t], y_perm[pos]>, the logit
+//      gradient of the renormalised top-k softmax, dl_j = g_j (dg_j - sum_i
+//      g_i dg_i), and for each queue row its token and gate (qtok, qgate);
+//   2. grouped GEMMs over the queues: dh_raw = dy W_down with dy's rows
+//      gathered by token (the queue rows' output gradient g dy[t] is never
+//      stored: the gate comes in the next epilogue), the recompute of
+//      gate/up with the SwiGLU backward of dh = g dh_raw, dx_perm; and the
+//      weight gradients, which read x and dy by token through qtok and the
+//      rest in queue order;
 //   3. per token: dx[t] = sum_j dx_perm[pos(t, j)] + sum_j dl_j W_r[id_j];
 //   4. router weight gradient dW_r[e] = sum over expert e's queue of dl x:
 //      partial sums over each 64-row block of the padded queue (one expert
-//      per block) come out of the gather of x, and a second kernel adds an
-//      expert's blocks in order.
+//      per block), then a second kernel adds an expert's blocks in order.
 // All reductions run in a fixed order (deterministic); accumulation is fp32,
 // storage bf16.
 #include "device_util.h"
@@ -41,8 +43,8 @@ __global__ __launch_bounds__(256) void bwd_dy_kernel(const uint4* __restrict__ d
                                                     const int32_t* __restrict__ ids,
                                                     const float* __restrict__ gates,
                                                     const int32_t* __restrict__ assign_pos, int k,
-                                                    int E, int chunks, uint4* __restrict__ dy_perm,
-                                                    float* __restrict__ dsel,
+                                                    int E, int chunks, int32_t* __restrict__ qtok,
+                                                    float* __restrict__ qgate, float* __restrict__ dsel,
                                                     float* __restrict__ dlogits) {
     __shared__ float s_part[4];
     __shared__ float s_dg[MOE_MAX_TOPK];
@@ -50,22 +52,22 @@ __global__ __launch_bounds__(256) void bwd_dy_kernel(const uint4* __restrict__ d
     const uint4* dyr = dy + t * chunks;
     for (int j = 0; j < k; ++j) {
         const int pos = assign_pos[t * k + j];
-        const float g = gates[t * k + j];
+        if (pos >= 0 && threadIdx.x == 0) {
+            qtok[pos] = static_cast<int32_t>(t);
+            qgate[pos] = gates[t * k + j];
+        }
         float acc = 0.f;
         for (int c = threadIdx.x; c < chunks; c += 256) {
-            const uint4 a = dyr[c];
-            const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
-            uint32_t o[4] = {0u, 0u, 0u, 0u};
             if (pos >= 0) {
+                const uint4 a = dyr[c];
+                const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
                 const uint4 b = load_nt(y_perm + static_cast<int64_t>(pos) * chunks + c);
                 const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     acc = fmaf(lo_bf16(aw[i]), lo_bf16(bw[i]), acc);
                     acc = fmaf(hi_bf16(aw[i]), hi_bf16(bw[i]), acc);
-                    o[i] = pack_bf16x2(g * lo_bf16(aw[i]), g * hi_bf16(aw[i]));
                 }
-                dy_perm[static_cast<int64_t>(pos) * chunks + c] = make_uint4(o[0], o[1], o[2], o[3]);
             }
         }
         const float dg = block_sum(acc, s_part);
@@ -96,13 +98,18 @@ __global__ __launch_bounds__(256) void bwd_dy_kernel(const uint4* __restrict__ d
 // Padded offsets: expert e's queue columns start at poff[e], each expert's
 // count rounded up to a multiple of 64 (all zero when offsets is null: no
 // tokens).  Also the experts in descending order of padded count, ties by
-// lower id: order[rank] = e.  One thread per expert.
+// lower id: order[rank] = e.  One thread per expert.  And token 0 in the 64
+// entries of qtok after the last queue row (a weight gradient's last slice of
+// an expert reads up to 63 rows past its end; their values are zeroed, but
+// their addresses must be valid).
 static_assert(MOE_MAX_EXPERTS == 256, "bwd_poff_kernel runs one 256-thread workgroup, a thread per expert");
 __global__ __launch_bounds__(256) void bwd_poff_kernel(const int32_t* __restrict__ offsets, int E,
-                                                      int32_t* __restrict__ poff, int32_t* __restrict__ order) {
+                                                      int32_t* __restrict__ poff, int32_t* __restrict__ order,
+                                                      int32_t* __restrict__ qtok) {
     __shared__ __align__(16) int s_c[MOE_MAX_EXPERTS];
     __shared__ int s_wave[4];
     const int e = threadIdx.x;
+    if (offsets != nullptr && e < 64) qtok[offsets[E] + e] = 0;
     const int c = (e < E && offsets != nullptr) ? ((offsets[e + 1] - offsets[e] + 63) / 64) * 64 : 0;
     s_c[e] = c;
     int incl = c;
@@ -132,28 +139,23 @@ __global__ __launch_bounds__(256) void bwd_poff_kernel(const int32_t* __restrict
     order[rank] = e;
 }
 
-// x gathered into queue order for the weight gradients, x_perm[pos] =
-// x[sorted_assign[pos] / k] (x_perm has at least one row past its n_rows
-// queue rows), together with the router gradient's partial
-// sums.  The grid walks each expert's queue in 64-row blocks of the padded
-// queue (expert e's rows start at padded row poff[e], a multiple of 64, so a
-// block belongs to one expert; padded row q is queue row pos = offsets[e] +
-// q - poff[e] while pos < offsets[e+1], else padding) and kGatherXCols
-// columns at a time.  Block b = q / 64 yields wr_part[b, c] = sum over its
-// rows of dsel[a] x[a / k, c] (a = sorted_assign[pos]; padding adds
-// nothing), in a fixed order: wave w adds rows 16w .. 16w + 15 in turn (each
-// lane 8 columns, its 16 row loads in flight first), then (s0 + s1) +
-// (s2 + s3) over the waves.
+// The router gradient's partial sums over the queues.  The grid walks each
+// expert's queue in 64-row blocks of the padded queue (expert e's rows start
+// at padded row poff[e], a multiple of 64, so a block belongs to one expert;
+// padded row q is queue row pos = offsets[e] + q - poff[e] while pos <
+// offsets[e+1], else padding) and kGatherXCols columns at a time.  Block b =
+// q / 64 yields wr_part[b, c] = sum over its rows of dsel[a] x[a / k, c] (a =
+// sorted_assign[pos]; padding adds nothing), in a fixed order: wave w adds
+// rows 16w .. 16w + 15 in turn (each lane 8 columns, its 16 row loads in
+// flight first), then (s0 + s1) + (s2 + s3) over the waves.
 constexpr int kGatherXCols = 512;
-__global__ __launch_bounds__(256) void bwd_gather_x_kernel(const bf16_t* __restrict__ x, int d,
-                                                          const int32_t* __restrict__ offsets,
-                                                          const int32_t* __restrict__ poff, int E,
-                                                          const int32_t* __restrict__ sorted_assign,
-                                                          int k, const float* __restrict__ dsel,
-                                                          float* __restrict__ wr_part,
-                                                          bf16_t* __restrict__ x_perm, int64_t n_rows) {
+__global__ __launch_bounds__(256) void bwd_router_partials_kernel(const bf16_t* __restrict__ x, int d,
+                                                                 const int32_t* __restrict__ offsets,
+                                                                 const int32_t* __restrict__ poff, int E,
+                                                                 const int32_t* __restrict__ sorted_assign,
+                                                                 int k, const float* __restrict__ dsel,
+                                                                 float* __restrict__ wr_part) {
     __shared__ int64_t s_row[64];
-    __shared__ int s_pos[64];
     __shared__ float s_dsel[64];
     __shared__ float s_part[4][kGatherXCols];
     const int q0 = blockIdx.x * 64;
@@ -175,7 +177,6 @@ __global__ __launch_bounds__(256) void bwd_gather_x_kernel(const bf16_t* __restr
             ds = dsel[a];
         }
         s_row[threadIdx.x] = row;
-        s_pos[threadIdx.x] = row >= 0 ? pos : -1;
         s_dsel[threadIdx.x] = ds;
     }
     __syncthreads();
@@ -184,9 +185,7 @@ __global__ __launch_bounds__(256) void bwd_gather_x_kernel(const bf16_t* __restr
     const int c = c0 + cl;
     float part[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (c < d) {
-        // branch-free: a padding row loads x row 0 and keeps zeros, and
-        // stores them to row n_rows of x_perm, a pad row past the queue
-        // whose contents are never used
+        // branch-free: a padding row loads x row 0 and keeps zeros
         uint4 v[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -196,9 +195,6 @@ __global__ __launch_bounds__(256) void bwd_gather_x_kernel(const bf16_t* __restr
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int pos = s_pos[w * 16 + r];
-            const int64_t dst = pos >= 0 ? pos : n_rows;
-            *reinterpret_cast<uint4*>(x_perm + dst * d + c) = v[r];
             const float ds = s_dsel[w * 16 + r];
             const uint32_t u[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
 #pragma unroll
@@ -407,26 +403,25 @@ hipError_t launch_backward_weights(const moe_problem_t& p, const void* w_gate, c
 
 hipError_t launch_backward_dy(const moe_problem_t& p, const void* dy, const void* y_perm,
                               const int32_t* ids, const float* gates, const int32_t* assign_pos,
-                              void* dy_perm, float* dsel, float* dlogits, hipStream_t s) {
+                              int32_t* qtok, float* qgate, float* dsel, float* dlogits, hipStream_t s) {
     bwd_dy_kernel<<<static_cast<unsigned>(p.T), 256, 0, s>>>(
         static_cast<const uint4*>(dy), static_cast<const uint4*>(y_perm), ids, gates, assign_pos, p.k,
-        p.E, p.d / 8, static_cast<uint4*>(dy_perm), dsel, dlogits);
+        p.E, p.d / 8, qtok, qgate, dsel, dlogits);
     return hipGetLastError();
 }
 
 hipError_t launch_backward_poff(const moe_problem_t& p, const int32_t* offsets, int32_t* poff,
-                                int32_t* order, hipStream_t s) {
-    bwd_poff_kernel<<<1, 256, 0, s>>>(offsets, p.E, poff, order);
+                                int32_t* order, int32_t* qtok, hipStream_t s) {
+    bwd_poff_kernel<<<1, 256, 0, s>>>(offsets, p.E, poff, order, qtok);
     return hipGetLastError();
 }
 
-hipError_t launch_backward_gather_x(const moe_problem_t& p, const void* x, const int32_t* offsets,
-                                    const int32_t* poff, const int32_t* sorted_assign, int64_t kpad,
-                                    const float* dsel, float* wr_part, void* x_perm, hipStream_t s) {
+hipError_t launch_backward_router_partials(const moe_problem_t& p, const void* x, const int32_t* offsets,
+                                           const int32_t* poff, const int32_t* sorted_assign, int64_t kpad,
+                                           const float* dsel, float* wr_part, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(kpad / 64), static_cast<unsigned>(ceil_div(p.d, kGatherXCols)));
-    bwd_gather_x_kernel<<<grid, 256, 0, s>>>(static_cast<const bf16_t*>(x), p.d, offsets, poff, p.E,
-                                             sorted_assign, p.k, dsel, wr_part, static_cast<bf16_t*>(x_perm),
-                                             p.T * p.k);
+    bwd_router_partials_kernel<<<grid, 256, 0, s>>>(static_cast<const bf16_t*>(x), p.d, offsets, poff, p.E,
+                                                    sorted_assign, p.k, dsel, wr_part);
     return hipGetLastError();
 }
 

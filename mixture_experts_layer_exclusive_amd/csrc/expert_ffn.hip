@@ -305,14 +305,19 @@ __device__ __forceinline__ bool find_wgrad_work(const int32_t* __restrict__ offs
 // GATHER, else per queue row), b_exp0 / b_exp1 per weight row of B0 / B1
 // (indexed e * N + row).  The MFMA is v_mfma_f32_32x32x64_f8f6f4; the scales
 // are applied exactly (ldexp) to the fp32 sums before the epilogue.
-template <int MODE, bool GATHER, bool WIDE, bool F8 = false>
+// Weight gradients with GATHER: one operand (A, or B when GB) is token-major,
+// [T, row length], and queue row q reads its token's row qtok[q] (so neither
+// x nor dy is copied into queue order).  kUpBwd: row_scale holds each queue
+// row's gate.
+template <int MODE, bool GATHER, bool WIDE, bool F8 = false, bool GB = false>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void grouped_gemm_bf16_kernel(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ sorted_assign, int topk,
     const int32_t* __restrict__ offsets, int E, const bf16_t* __restrict__ B0,
     const bf16_t* __restrict__ B1, bf16_t* __restrict__ C, int N, int K, int slots,
     float* __restrict__ part, const bf16_t* __restrict__ aux, bf16_t* __restrict__ C2, int M,
     const int32_t* __restrict__ a_exp = nullptr, const int32_t* __restrict__ b_exp0 = nullptr,
-    const int32_t* __restrict__ b_exp1 = nullptr, int a_row_off = 0) {
+    const int32_t* __restrict__ b_exp1 = nullptr, int a_row_off = 0,
+    const int32_t* __restrict__ qtok = nullptr, const float* __restrict__ row_scale = nullptr) {
     constexpr bool GATEUP = MODE == kUp || MODE == kUpBwd;
     constexpr bool WG = MODE == kWgrad;
     static_assert(!F8 || MODE == kUp || MODE == kDown, "fp8 operands: forward GEMMs only");
@@ -326,9 +331,17 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // applies; a slice's scales (4 bytes per row) ride in each stage after
     // the operands, one 4-byte load per lane of one instruction per wave.
     constexpr bool MXS = F8 && MODE == kDown;
+    // Weight gradients with a token-major operand (G_A: A, G_B: B): each
+    // wave loads the token ids of its 16 rows of a slice into LDS (one
+    // 4-byte load per lane, 4 slices ahead of the rows' own loads, a ring of
+    // 4 slots), and reads those of the slice it refills at the slice's start.
+    constexpr bool WGG = WG && GATHER;
+    constexpr bool G_A = WGG && !GB;
+    constexpr bool G_B = WGG && GB;
+    static_assert(!GB || WGG, "GB selects the gathered operand of a weight gradient");
     constexpr int LA = TM / 32;              // activation loads per wave per slice (8 rows each)
     constexpr int LB = TN / 32;              // weight loads per wave per slice
-    constexpr int NL = LA + LB + (MXS ? 1 : 0);
+    constexpr int NL = LA + LB + ((MXS || WGG) ? 1 : 0);
     constexpr int ROWB = 128;                // bytes per row of a slice
     constexpr int SA_BYTES = TM * ROWB;
     constexpr int SC_OFF = (TM + TN) * ROWB;  // (MXS) the scales within a stage
@@ -341,9 +354,10 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     constexpr bool A_FIRST = GATEUP;
     static_assert(2 * STAGE_BYTES <= 160 * 1024, "two stages must fit the 160 KB of LDS");
     static_assert(BK * EB == ROWB, "a slice is one 128-byte line per row");
-    static_assert(F8 ? 3 * (LA + LB) <= 2 * (KS - 1) * NM : 3 * NL <= (KS - 1) * NM,
+    static_assert(F8 ? 3 * (LA + LB) <= 2 * (KS - 1) * NM : 3 * (LA + LB) <= (KS - 1) * NM,
                   "the refill spreads one load per 3 MFMAs (fp8: two per 3)");
-    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE_BYTES];
+    constexpr int IDS_OFF = 2 * STAGE_BYTES;  // (WGG) the token-id ring: [slot][wave][64 dwords]
+    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE_BYTES + (WGG ? 4 * 4 * 256 : 0)];
     // The tile prefix and offsets tables live in stage 0 until the first load.
     int* const s_prefix = reinterpret_cast<int*>(smem);
     int* const s_off = s_prefix + MOE_MAX_EXPERTS + 1;
@@ -386,9 +400,10 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const int64_t RB = static_cast<int64_t>(K) * EB;
     // (the K range [work.kb, work.kb + work.nkl) of 128-byte slices is folded
     // into the bases; a weight-gradient tile starts at its expert's first
-    // queue row work.kb, at column a_row_off + its first output row)
+    // queue row work.kb, at column a_row_off + its first output row; a
+    // token-major operand's rows are found per slice instead)
     const char* const a_base =
-        uniform_ptr(WG ? Ab + static_cast<int64_t>(work.kb) * RB + (a_row_off + tile.row0) * 2
+        uniform_ptr(WG ? Ab + (G_A ? 0 : static_cast<int64_t>(work.kb) * RB) + (a_row_off + tile.row0) * 2
                        : (GATHER ? Ab : Ab + static_cast<int64_t>(tile.row0) * RB) + work.kb * 128);
     // Weight gradients stage a slice as 64 queue rows x 256 channels of each
     // operand (512-byte LDS rows: the same 32 KB per operand, at the same LDS
@@ -398,6 +413,16 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const int64_t RBB = WG ? static_cast<int64_t>(N) * 2 : RB;  // bytes per B row
     const int64_t a_step = WG ? 64 * RB : 128;
     const int64_t b_step = WG ? 64 * RBB : 128;
+    // (weight gradients) byte offset of the lane's 16-byte chunk of row r of
+    // a slice, for a channel range starting col_bytes into rows of row_bytes.
+    // A range that passes the row's end (M or N not a multiple of 256) reads
+    // the row's last chunk instead: those channels' results are never
+    // stored, and a token-major operand has no padding past its last row.
+    auto wg_chunk = [&](int r, int64_t col_bytes, int64_t row_bytes) {
+        int64_t c = ((lane & 31) ^ wg_swizzle(r)) * 16;
+        if (WGG && col_bytes + c >= row_bytes) c = row_bytes - 16 - col_bytes;
+        return static_cast<uint32_t>(c);
+    };
     // (gathered rows need a lookup in sorted_assign: called after the first
     // weight loads are on their way)
     auto setup_a = [&]() {
@@ -405,8 +430,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 #pragma unroll
             for (int j = 0; j < LA; ++j) {
                 const int r = wave * 16 + 2 * j + (lane >> 5);
-                a_off[0 * WIDE + j] = static_cast<uint32_t>(r) * static_cast<uint32_t>(RB) +
-                                      static_cast<uint32_t>(((lane & 31) ^ wg_swizzle(r)) * 16);
+                a_off[0 * WIDE + j] = (G_A ? 0u : static_cast<uint32_t>(r) * static_cast<uint32_t>(RB)) +
+                                      wg_chunk(r, (a_row_off + tile.row0) * 2, RB);
             }
             return;
         }
@@ -431,15 +456,15 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const int rb0 = wave * (TN / 4);
     const char* const b_base =
         uniform_ptr(reinterpret_cast<const char*>(GATEUP && rb0 >= TN / 2 ? B1 : B0) +
-                    (WG ? static_cast<int64_t>(work.kb) * RBB + static_cast<int64_t>(n0) * 2
+                    (WG ? (G_B ? 0 : static_cast<int64_t>(work.kb) * RBB) + static_cast<int64_t>(n0) * 2
                         : static_cast<int64_t>(tile.e) * N * RB + work.kb * 128));
     uint32_t b_off[LB];
 #pragma unroll
     for (int j = 0; j < LB; ++j) {
         if (WG) {
             const int r = wave * 16 + 2 * j + (lane >> 5);
-            b_off[j] = static_cast<uint32_t>(r) * static_cast<uint32_t>(RBB) +
-                       static_cast<uint32_t>(((lane & 31) ^ wg_swizzle(r)) * 16);
+            b_off[j] = (G_B ? 0u : static_cast<uint32_t>(r) * static_cast<uint32_t>(RBB)) +
+                       wg_chunk(r, n0 * 2, RBB);
             continue;
         }
         const int r = rb0 + j * 8 + lrow;
@@ -452,14 +477,51 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const uint32_t lds_a = lds0 + wave * 64 * ROWB;
     const uint32_t lds_b = lds0 + SA_BYTES + rb0 * ROWB;
     // activation load j (< LA) and weight load j (< LB) of slice kt
+    // (WGG: gid[j] is the token of load j's row in the slice being loaded)
+    uint32_t gid[WGG ? LA : 1] = {};
+    static_assert(!WGG || LA == LB, "one token id per load of either operand");
     auto dma_a = [&](int j, int kt) {
         const uint32_t so = static_cast<uint32_t>((kt & 1) * STAGE_BYTES);
         if (WIDE) lds_dma16(a_src[WIDE ? j : 0] + kt * 128, lds_a + so + j * 8 * ROWB);
+        else if (G_A)
+            lds_dma16_s(a_base, gid[WGG ? j : 0] * static_cast<uint32_t>(RB) + a_off[WIDE ? 0 : j],
+                        lds_a + so + j * 8 * ROWB);
         else lds_dma16_s(a_base + kt * a_step, a_off[WIDE ? 0 : j], lds_a + so + j * 8 * ROWB);
     };
     auto dma_b = [&](int j, int kt) {
         const uint32_t so = static_cast<uint32_t>((kt & 1) * STAGE_BYTES);
-        lds_dma16_s(b_base + kt * b_step, b_off[j], lds_b + so + j * 8 * ROWB);
+        if (G_B)
+            lds_dma16_s(b_base, gid[WGG ? j : 0] * static_cast<uint32_t>(RBB) + b_off[j], lds_b + so + j * 8 * ROWB);
+        else lds_dma16_s(b_base + kt * b_step, b_off[j], lds_b + so + j * 8 * ROWB);
+    };
+    // (WGG) token ids: lane i of wave w loads the id of row w*16 + 2*(i & 7)
+    // + ((i >> 3) & 1) of slice kt (lanes 16..63 repeat lanes 0..15), into
+    // dword i of the wave's 256-byte region of ring slot kt & 3; a lane then
+    // finds the ids of its loads j = 0..7 (rows w*16 + 2j + (lane >> 5)) as
+    // 8 consecutive dwords.  Slices past the last load the last one's ids
+    // (the expert's rows end within the padding qtok carries).
+    const char* id_base = nullptr;
+    uint32_t id_voff = 0;
+    if constexpr (WGG) {
+        id_base = uniform_ptr(reinterpret_cast<const char*>(qtok) + static_cast<int64_t>(work.kb) * 4);
+        id_voff = static_cast<uint32_t>(wave * 16 + 2 * (lane & 7) + ((lane >> 3) & 1)) * 4u;
+    }
+    auto dma_id = [&](int kt) {
+        const int kc = min(kt, work.nkl - 1);
+        lds_dma4_s(id_base + static_cast<int64_t>(kc) * 256, id_voff,
+                   lds0 + IDS_OFF + static_cast<uint32_t>(((kt & 3) * 4 + wave) * 256));
+    };
+    auto read_ids = [&](int kt) {
+        if constexpr (WGG) {
+            const char* const src = smem + IDS_OFF + ((kt & 3) * 4 + wave) * 256 + (lane >> 5) * 32;
+            const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(src);
+            const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(src + 16);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                gid[WGG ? j : 0] = lo[j];
+                gid[WGG ? 4 + j : 0] = hi[j];
+            }
+        }
     };
     // (MXS) the scales: LDS dword w*64 + i of the stage (lane i of wave w)
     // holds tile row ((s & 7) << 5) | (s >> 3), s = w*64 + i, so that the
@@ -484,6 +546,10 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     auto dma = [&](int q, int kt) {
         if (MXS && q == LA + LB) {
             dma_sc(kt);
+            return;
+        }
+        if (WGG && q == LA + LB) {  // (the ids of the slice two later)
+            dma_id(kt + 2);
             return;
         }
         const bool a_op = A_FIRST ? q < LA : q >= LB;
@@ -635,7 +701,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         const int p = (step - 1) * NM + q;
         constexpr int NOP = LA + LB;  // operand loads
         const bool issue = F8 ? (p % 3 != 2 && p - p / 3 < NOP) : (p % 3 == 0 && p / 3 < NOP);
-        if (MXS && p == 0) dma(NOP, kt + 2);
+        if ((MXS || WGG) && p == 0) dma(NOP, kt + 2);
         if (issue) {
             dma(F8 ? p - p / 3 : p / 3, kt + 2);
             // keep each load between its MFMAs (the scheduler would
@@ -644,7 +710,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         }
     };
     // loads issued in steps 1..2
-    constexpr int BEFORE3_ = (F8 ? 2 * NM - (2 * NM) / 3 : (2 * NM + 2) / 3) + (MXS ? 1 : 0);
+    constexpr int BEFORE3_ = (F8 ? 2 * NM - (2 * NM) / 3 : (2 * NM + 2) / 3) + ((MXS || WGG) ? 1 : 0);
     constexpr int BEFORE3 = BEFORE3_ < NL ? BEFORE3_ : NL;
     // fragments read ahead of a slice: bf16 step 0; fp8 step 0 (a register
     // pair per block, used by the slice's first two quarter steps)
@@ -656,7 +722,46 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // of A1 are pending.
     // (a weight-gradient tile of an expert with no rows has nk = 0: no loads,
     // and its zero accumulators are stored)
-    if (nk > 0) {
+    if (nk > 0 && WGG) {
+        // ids of slices 0..3, the queue-order operand's slices 0 and 1, then
+        // (once the ids have landed) the token-major operand's
+        setup_a();
+#pragma unroll
+        for (int kt0 = 0; kt0 < 4; ++kt0) dma_id(kt0);
+        auto dma_q = [&](int j, int kt0) {
+            if (G_A) dma_b(j, kt0);
+            else dma_a(j, kt0);
+        };
+        auto dma_t = [&](int j, int kt0) {
+            if (G_A) dma_a(j, kt0);
+            else dma_b(j, kt0);
+        };
+#pragma unroll
+        for (int j = 0; j < LA; ++j) dma_q(j, 0);
+        if (nk > 1) {
+#pragma unroll
+            for (int j = 0; j < LA; ++j) dma_q(j, 1);
+            wait_vmcnt<2 * LA>();
+        } else {
+            wait_vmcnt<LA>();
+        }
+        read_ids(0);
+#pragma unroll
+        for (int j = 0; j < LA; ++j) dma_t(j, 0);
+        if (nk > 1) {
+            read_ids(1);
+#pragma unroll
+            for (int j = 0; j < LA; ++j) dma_t(j, 1);
+            wait_vmcnt_lgkm0<LA>();
+        } else {
+            wait_vmcnt_lgkm0<0>();
+            zero_tail_rows(0);
+        }
+        barrier_lds();
+#pragma unroll
+        for (int i = 0; i < NR; ++i) read_frag(0, i, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    } else if (nk > 0) {
 #pragma unroll
         for (int j = 0; j < LB; ++j) dma_b(j, 0);
         if (nk > 1) {
@@ -692,12 +797,15 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         // step 0: the reads of the remaining steps (bf16: 24 over 16 MFMAs;
         // fp8: 16 over 8; weight gradients: 48 transposing reads over 16)
         {
+            // (WGG: the token ids of the slice this one refills, first)
+            if (MORE) read_ids(kt + 2);
 #pragma unroll
             for (int kk = KPRE; kk < KREAD; ++kk)
 #pragma unroll
                 for (int i = 0; i < NR; ++i) read_frag(kk, i, so);
 #pragma unroll
             for (int q = 0; q < NM; ++q) MOE_MFMA(0, q);
+            if (WGG && MORE) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             constexpr int RPM = WG ? 3 : 2;  // LDS reads per MFMA in the first half
 #pragma unroll
             for (int i = 0; i < NR; ++i) {
@@ -814,8 +922,18 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     static_assert(TM * ROWO <= 2 * STAGE_BYTES, "the staged tile must fit the ring");
     wait_vmcnt_lgkm0<0>();
     barrier_lds();
+    // (kUpBwd) the gate of each of the lane's 4 rows
+    float rs[4] = {1.f, 1.f, 1.f, 1.f};
+    if constexpr (MODE == kUpBwd) {
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+            const int pos = tile.row0 + wm * 128 + mb * 32 + l32;
+            rs[mb] = pos < tile.row1 ? row_scale[pos] : 0.f;
+        }
+    }
     // stage the tile's output (h = silu(gate) * up for the gate/up modes, the
-    // accumulators otherwise) and store it to out (row stride ldo)
+    // accumulators otherwise; kUpBwd: g h, the row's gate times h) and store
+    // it to out (row stride ldo)
     auto stage_and_store = [&](bf16_t* __restrict__ out, int64_t ldo) {
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
@@ -830,7 +948,10 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                     if (GATEUP) {
                         float v[4];
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) v[i] = silu_mul_fast(acc[nb][mb][4 * g + i], acc[nb + 2][mb][4 * g + i]);
+                        for (int i = 0; i < 4; ++i) {
+                            v[i] = silu_mul_fast(acc[nb][mb][4 * g + i], acc[nb + 2][mb][4 * g + i]);
+                            if (MODE == kUpBwd) v[i] *= rs[mb];
+                        }
                         o = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
                     } else {
                         const f32x16_t& a = acc[nb][mb];
@@ -924,12 +1045,13 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 
     if (MODE == kUpBwd) {
         // The backward of SwiGLU from the recomputed gate u and up v and the
-        // incoming dh (aux, [rows, f]): with sg = sigmoid(u), s = u sg,
+        // incoming dh = g dh_raw (aux holds dh_raw = dy W_down, [rows, f];
+        // g is the row's gate): with sg = sigmoid(u), s = u sg,
         // du = dh v sg (1 + u (1 - sg)) and dv = dh s.  Pass 1 stages du and
         // dv side by side (a 256-column row: chunks 0..15 du, 16..31 dv) and
         // stores them to C = [rows, 2f] (du in columns [0, f), dv in [f, 2f));
-        // pass 2 stores h = s v to C2 (the down projection's weight gradient
-        // reads it).
+        // pass 2 stores g h = g s v to C2 (the down projection's weight
+        // gradient sums dy[t] (g h) over the queue rows).
         constexpr int CPR2 = 32;
         constexpr int ROWO2 = CPR2 * 16;
         static_assert(TM * ROWO2 <= 2 * STAGE_BYTES, "the staged du/dv tile must fit the ring");
@@ -947,7 +1069,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                     uint2 dhw = make_uint2(0u, 0u);
                     if (pos < tile.row1 && col < N)
                         dhw = *reinterpret_cast<const uint2*>(aux + static_cast<int64_t>(pos) * N + col);
-                    const float dh[4] = {lo_bf16(dhw.x), hi_bf16(dhw.x), lo_bf16(dhw.y), hi_bf16(dhw.y)};
+                    const float dh[4] = {rs[mb] * lo_bf16(dhw.x), rs[mb] * hi_bf16(dhw.x), rs[mb] * lo_bf16(dhw.y),
+                                         rs[mb] * hi_bf16(dhw.y)};
                     float du[4], dv[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
@@ -1210,30 +1333,35 @@ hipError_t launch_expert_ffn(const moe_problem_t& p, const void* x_perm, const v
 
 // ---- backward GEMMs (bf16) ----------------------------------------------
 
-// dh = dy_perm W_down over the queues (W_down_t = W_down transposed, [E, f, d]).
-hipError_t launch_backward_dh(const moe_problem_t& p, const void* dy_perm, const int32_t* offsets,
-                              const void* w_down_t, void* dh, hipStream_t s) {
+// dh_raw = dy W_down over the queues, dy's rows gathered by token like x in
+// GEMM1 (W_down_t = W_down transposed, [E, f, d]); the gate is applied in the
+// recompute's epilogue.
+hipError_t launch_backward_dh(const moe_problem_t& p, const void* dy, const int32_t* sorted_assign,
+                              const int32_t* offsets, const void* w_down_t, void* dh, hipStream_t s) {
     const int64_t n = p.T * p.k;
     const unsigned g = grid_for(n, p.E, kBM, static_cast<int>(ceil_div(p.f, kDownCols)));
-    grouped_gemm_bf16_kernel<kDown, false, false><<<g, 256, 0, s>>>(
-        static_cast<const bf16_t*>(dy_perm), nullptr, p.k, offsets, p.E,
+    // (the backward's limits keep T * d below 2^31: 32-bit gather offsets)
+    grouped_gemm_bf16_kernel<kDown, true, false><<<g, 256, 0, s>>>(
+        static_cast<const bf16_t*>(dy), sorted_assign, p.k, offsets, p.E,
         static_cast<const bf16_t*>(w_down_t), nullptr, static_cast<bf16_t*>(dh), p.f, p.d, 0, nullptr,
         nullptr, nullptr, 0);
     return hipGetLastError();
 }
 
 // Recompute of gate and up from x (gathered), with the SwiGLU backward in the
-// epilogue: du, dv -> duv [T*k, 2f], h -> h [T*k, f].
+// epilogue: dh = g dh_raw (qgate: each queue row's gate), du, dv -> duv
+// [T*k, 2f], g h -> hg [T*k, f].
 hipError_t launch_backward_recompute(const moe_problem_t& p, const void* x, const int32_t* sorted_assign,
                                      const int32_t* offsets, const void* w_gate, const void* w_up,
-                                     const void* dh, void* duv, void* h, hipStream_t s) {
+                                     const void* dh, const float* qgate, void* duv, void* hg, hipStream_t s) {
     const int64_t n = p.T * p.k;
     const unsigned g = grid_for(n, p.E, kBM, static_cast<int>(ceil_div(p.f, kGateUpCols)));
     // (the backward's limits keep T * d below 2^31: 32-bit gather offsets)
     grouped_gemm_bf16_kernel<kUpBwd, true, false><<<g, 256, 0, s>>>(
         static_cast<const bf16_t*>(x), sorted_assign, p.k, offsets, p.E, static_cast<const bf16_t*>(w_gate),
         static_cast<const bf16_t*>(w_up), static_cast<bf16_t*>(duv), p.f, p.d, 0, nullptr,
-        static_cast<const bf16_t*>(dh), static_cast<bf16_t*>(h), 0);
+        static_cast<const bf16_t*>(dh), static_cast<bf16_t*>(hg), 0, nullptr, nullptr, nullptr, 0, nullptr,
+        qgate);
     return hipGetLastError();
 }
 
@@ -1255,19 +1383,29 @@ hipError_t launch_backward_dxperm(const moe_problem_t& p, const void* duv, const
 }
 
 // Weight gradient per expert: C[e] [M, N] = sum over the expert's queue rows
-// q in [offsets[e], offsets[e+1]) of A[q, a_col_off + m] B[q, n], with A
-// [rows, lda] and B [rows, N] in queue order (each with kWgradPadRows rows
-// after the last queue row); order: the experts by descending row count.
+// q in [offsets[e], offsets[e+1]) of A[q, a_col_off + m] B[q, n]; order: the
+// experts by descending row count.  One operand is token-major (B when
+// gather_b, else A): queue row q is its row qtok[q] (qtok carries 64 valid
+// entries past the last queue row); the other is in queue order, [rows, lda]
+// or [rows, N], with kWgradPadRows rows after the last queue row.
 hipError_t launch_backward_wgrad(const moe_problem_t& p, const void* A, int lda, int a_col_off, int M,
-                                 const void* B, int N, const int32_t* offsets, const int32_t* order, void* C,
-                                 hipStream_t s) {
+                                 const void* B, int N, const int32_t* offsets, const int32_t* order,
+                                 const int32_t* qtok, bool gather_b, void* C, hipStream_t s) {
     // (every XCD's list is sized for the most experts one XCD receives)
     const int64_t tiles =
         ceil_div(p.E, NUM_XCD) * NUM_XCD * static_cast<int64_t>(wgrad_tiles_per_expert(M, N));
     const unsigned g = static_cast<unsigned>(tiles);
-    grouped_gemm_bf16_kernel<kWgrad, false, false><<<g, 256, 0, s>>>(
-        static_cast<const bf16_t*>(A), order, p.k, offsets, p.E, static_cast<const bf16_t*>(B), nullptr,
-        static_cast<bf16_t*>(C), N, lda, 0, nullptr, nullptr, nullptr, M, nullptr, nullptr, nullptr, a_col_off);
+    // (the backward's limits keep T * d below 2^31: 32-bit row offsets)
+    if (gather_b)
+        grouped_gemm_bf16_kernel<kWgrad, true, false, false, true><<<g, 256, 0, s>>>(
+            static_cast<const bf16_t*>(A), order, p.k, offsets, p.E, static_cast<const bf16_t*>(B), nullptr,
+            static_cast<bf16_t*>(C), N, lda, 0, nullptr, nullptr, nullptr, M, nullptr, nullptr, nullptr,
+            a_col_off, qtok);
+    else
+        grouped_gemm_bf16_kernel<kWgrad, true, false, false, false><<<g, 256, 0, s>>>(
+            static_cast<const bf16_t*>(A), order, p.k, offsets, p.E, static_cast<const bf16_t*>(B), nullptr,
+            static_cast<bf16_t*>(C), N, lda, 0, nullptr, nullptr, nullptr, M, nullptr, nullptr, nullptr,
+            a_col_off, qtok);
     return hipGetLastError();
 }
 

@@ -89,26 +89,27 @@ size_t dispatch_ws(const moe_problem_t& p) {
 
 size_t ffn_ws(const moe_problem_t& p) { return ffn_h_bytes(p) + ffn_split_bytes(p); }
 
-// Backward workspace: dsel [T*k] fp32; dy_perm [T*k + pad, d]; dx_perm
-// [T*k, d]; dh [T*k, f]; h [T*k + pad, f]; du|dv [T*k + pad, 2f]; padded
-// offsets [E+1] and the expert order [E]; x_perm [T*k + pad, d] (x gathered
-// into queue order); the router-gradient partial sums [kpad / 64, d] fp32;
-// the split-K partial tiles of the dx_perm GEMM.  dy_perm, h, du|dv and
-// x_perm are the weight gradients' queue-order operands (pad =
-// kWgradPadRows rows after the last queue row).
+// Backward workspace: dsel [T*k] fp32; each queue row's token qtok [T*k +
+// pad] and gate qgate [T*k] fp32; dx_perm [T*k, d]; dh_raw [T*k, f]; g h
+// [T*k + pad, f]; du|dv [T*k + pad, 2f]; padded offsets [E+1] and the expert
+// order [E]; the router-gradient partial sums [kpad / 64, d] fp32; the
+// split-K partial tiles of the dx_perm GEMM.  g h and du|dv are the weight
+// gradients' queue-order operands (pad = kWgradPadRows rows after the last
+// queue row); x and dy are read by token through qtok, never copied into
+// queue order.
 size_t backward_ws(const moe_problem_t& p) {
     const size_t n = static_cast<size_t>(p.T) * p.k;
     const size_t np = n + static_cast<size_t>(kWgradPadRows);
     const size_t kp = static_cast<size_t>(backward_kpad(p));
-    size_t b = align_up(n * 4, kAlign);
-    b += align_up(np * p.d * 2, kAlign);             // dy_perm
+    size_t b = align_up(n * 4, kAlign);              // dsel
+    b += align_up(np * 4, kAlign);                   // qtok
+    b += align_up(n * 4, kAlign);                    // qgate
     b += align_up(n * p.d * 2, kAlign);              // dx_perm
-    b += align_up(n * p.f * 2, kAlign);              // dh
-    b += align_up(np * p.f * 2, kAlign);             // h
+    b += align_up(n * p.f * 2, kAlign);              // dh_raw
+    b += align_up(np * p.f * 2, kAlign);             // g h
     b += align_up(np * 2 * p.f * 2, kAlign);         // du|dv
     b += align_up(static_cast<size_t>(p.E + 1) * 4, kAlign);
     b += align_up(static_cast<size_t>(p.E) * 4, kAlign);           // expert order
-    b += align_up(np * p.d * 2, kAlign);             // x_perm
     b += align_up(static_cast<size_t>(kp / 64) * p.d * 4, kAlign);
     b += align_up(bwd_split_bytes(p), kAlign);
     return b;
@@ -465,46 +466,47 @@ moe_status_t moe_backward(const moe_problem_t* p, const void* x, const void* w_r
     const int64_t kp = backward_kpad(*p);
     Carver c(ws);
     float* dsel = c.take<float>(n * 4);
-    void* dy_perm = c.take<char>(np * p->d * 2);
+    int32_t* qtok = c.take<int32_t>(np * 4);
+    float* qgate = c.take<float>(n * 4);
     void* dx_perm = c.take<char>(n * p->d * 2);
     void* dh = c.take<char>(n * p->f * 2);
-    void* h = c.take<char>(np * p->f * 2);
+    void* hg = c.take<char>(np * p->f * 2);
     void* duv = c.take<char>(np * 2 * p->f * 2);
     int32_t* poff = c.take<int32_t>(static_cast<size_t>(p->E + 1) * 4);
     int32_t* order = c.take<int32_t>(static_cast<size_t>(p->E) * 4);
-    void* x_perm = c.take<char>(np * p->d * 2);
     float* wr_part = c.take<float>(static_cast<size_t>(kp / 64) * p->d * 4);
     float* split = bwd_split_bytes(*p) > 0 ? c.take<float>(bwd_split_bytes(*p)) : nullptr;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     clear_hip_error();
     // (with no tokens fw is not read: every queue is empty)
-    MOE_LAUNCH(launch_backward_poff(*p, p->T > 0 ? fw->offsets : nullptr, poff, order, s));
+    MOE_LAUNCH(launch_backward_poff(*p, p->T > 0 ? fw->offsets : nullptr, poff, order, qtok, s));
     if (p->T > 0) {
-        MOE_LAUNCH(launch_backward_dy(*p, dy, fw->y_perm, fw->topk_ids, fw->topk_gates, fw->assign_pos,
-                                      dy_perm, dsel, out->dlogits, s));
-        MOE_LAUNCH(launch_backward_dh(*p, dy_perm, fw->offsets, w_down_t, dh, s));
-        MOE_LAUNCH(launch_backward_recompute(*p, x, fw->sorted_assign, fw->offsets, w_gate, w_up, dh, duv,
-                                             h, s));
+        MOE_LAUNCH(launch_backward_dy(*p, dy, fw->y_perm, fw->topk_ids, fw->topk_gates, fw->assign_pos, qtok,
+                                      qgate, dsel, out->dlogits, s));
+        MOE_LAUNCH(launch_backward_dh(*p, dy, fw->sorted_assign, fw->offsets, w_down_t, dh, s));
+        MOE_LAUNCH(launch_backward_recompute(*p, x, fw->sorted_assign, fw->offsets, w_gate, w_up, dh, qgate,
+                                             duv, hg, s));
         MOE_LAUNCH(launch_backward_dxperm(*p, duv, fw->offsets, w_gu_t, dx_perm, split, s));
         MOE_LAUNCH(launch_backward_dx(*p, dx_perm, fw->assign_pos, fw->topk_ids, dsel, w_router, out->dx,
                                       s));
-        // x gathered into queue order, the weight gradients' operand; with a
-        // router the same pass over 64-row blocks of each queue also takes
-        // the router gradient's partial sums
+        // with a router, its gradient's partial sums over 64-row blocks of
+        // each queue
         if (w_router != nullptr)
-            MOE_LAUNCH(launch_backward_gather_x(*p, x, fw->offsets, poff, fw->sorted_assign, kp, dsel, wr_part,
-                                                x_perm, s));
-        else
-            MOE_LAUNCH(launch_gather_rows(*p, x, fw->assign_pos, x_perm, s));
+            MOE_LAUNCH(launch_backward_router_partials(*p, x, fw->offsets, poff, fw->sorted_assign, kp, dsel,
+                                                       wr_part, s));
     }
-    // weight gradients from the queue-order operands (an expert with no rows
-    // gets zeros; with no tokens every count, from poff, is zero)
+    // weight gradients: dW_down from dy (by token) and g h, dW_gate and dW_up
+    // from du, dv and x (by token); an expert with no rows gets zeros (with
+    // no tokens every count, from poff, is zero, and qtok is not read)
     // (du and dv are columns 0 .. f and f .. 2f of du|dv)
     const int32_t* qoff = p->T > 0 ? fw->offsets : poff;
-    MOE_LAUNCH(launch_backward_wgrad(*p, dy_perm, p->d, 0, p->d, h, p->f, qoff, order, out->dw_down, s));
-    MOE_LAUNCH(launch_backward_wgrad(*p, duv, 2 * p->f, 0, p->f, x_perm, p->d, qoff, order, out->dw_gate, s));
-    MOE_LAUNCH(launch_backward_wgrad(*p, duv, 2 * p->f, p->f, p->f, x_perm, p->d, qoff, order, out->dw_up, s));
+    MOE_LAUNCH(launch_backward_wgrad(*p, dy, p->d, 0, p->d, hg, p->f, qoff, order, qtok, false, out->dw_down,
+                                     s));
+    MOE_LAUNCH(launch_backward_wgrad(*p, duv, 2 * p->f, 0, p->f, x, p->d, qoff, order, qtok, true, out->dw_gate,
+                                     s));
+    MOE_LAUNCH(launch_backward_wgrad(*p, duv, 2 * p->f, p->f, p->f, x, p->d, qoff, order, qtok, true, out->dw_up,
+                                     s));
     if (w_router != nullptr)
         MOE_LAUNCH(launch_backward_dwr(*p, wr_part, poff, out->dw_router, s));
     return MOE_OK;

@@ -129,26 +129,26 @@ hipError_t launch_backward_weights(const moe_problem_t& p, const void* w_gate, c
                                    const void* w_down, void* w_down_t, void* w_gu_t, hipStream_t s);
 hipError_t launch_backward_dy(const moe_problem_t& p, const void* dy, const void* y_perm,
                               const int32_t* ids, const float* gates, const int32_t* assign_pos,
-                              void* dy_perm, float* dsel, float* dlogits, hipStream_t s);
+                              int32_t* qtok, float* qgate, float* dsel, float* dlogits, hipStream_t s);
 hipError_t launch_backward_poff(const moe_problem_t& p, const int32_t* offsets, int32_t* poff,
-                                int32_t* order, hipStream_t s);
-hipError_t launch_backward_gather_x(const moe_problem_t& p, const void* x, const int32_t* offsets,
-                                    const int32_t* poff, const int32_t* sorted_assign, int64_t kpad,
-                                    const float* dsel, float* wr_part, void* x_perm, hipStream_t s);
+                                int32_t* order, int32_t* qtok, hipStream_t s);
+hipError_t launch_backward_router_partials(const moe_problem_t& p, const void* x, const int32_t* offsets,
+                                           const int32_t* poff, const int32_t* sorted_assign, int64_t kpad,
+                                           const float* dsel, float* wr_part, hipStream_t s);
 hipError_t launch_backward_dx(const moe_problem_t& p, const void* dx_perm, const int32_t* assign_pos,
                               const int32_t* ids, const float* dsel, const void* w_router, void* dx,
                               hipStream_t s);
 hipError_t launch_backward_dwr(const moe_problem_t& p, const float* wr_part, const int32_t* poff,
                                void* dw_router, hipStream_t s);
-hipError_t launch_backward_dh(const moe_problem_t& p, const void* dy_perm, const int32_t* offsets,
-                              const void* w_down_t, void* dh, hipStream_t s);
+hipError_t launch_backward_dh(const moe_problem_t& p, const void* dy, const int32_t* sorted_assign,
+                              const int32_t* offsets, const void* w_down_t, void* dh, hipStream_t s);
 hipError_t launch_backward_recompute(const moe_problem_t& p, const void* x, const int32_t* sorted_assign,
                                      const int32_t* offsets, const void* w_gate, const void* w_up,
-                                     const void* dh, void* duv, void* h, hipStream_t s);
+                                     const void* dh, const float* qgate, void* duv, void* hg, hipStream_t s);
 hipError_t launch_backward_dxperm(const moe_problem_t& p, const void* duv, const int32_t* offsets,
                                   const void* w_gu_t, void* dx_perm, float* part, hipStream_t s);
 hipError_t launch_backward_wgrad(const moe_problem_t& p, const void* A, int lda, int a_col_off, int M,
-                                 const void* B, int N, const int32_t* offsets, const int32_t* order, void* C,
-                                 hipStream_t s);
+                                 const void* B, int N, const int32_t* offsets, const int32_t* order,
+                                 const int32_t* qtok, bool gather_b, void* C, hipStream_t s);
 
 }  // namespace moe

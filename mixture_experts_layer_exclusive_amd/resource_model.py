@@ -130,11 +130,13 @@ def workspace(L: Layer, op: int) -> int:
     if op == OP_BACKWARD:
         kp = kpad(L)
         npad = L.n + WGRAD_PAD_ROWS
-        # dsel, dy_perm, dx_perm, dh, h, du|dv, poff, order, x_perm, router
-        # partial sums, split-K partials
-        return (_align(L.n * 4) + _align(npad * L.d * 2) + _align(L.n * L.d * 2) + _align(L.n * L.f * 2)
-                + _align(npad * L.f * 2) + _align(npad * 2 * L.f * 2) + _align((L.E + 1) * 4) + _align(L.E * 4)
-                + _align(npad * L.d * 2) + _align(kp // 64 * L.d * 4) + _align(_split_bytes(2 * L.f, 2)))
+        # dsel, the queue rows' tokens and gates, dx_perm, dh_raw, g h, du|dv,
+        # poff, order, router partial sums, split-K partials (x and dy are
+        # read by token, not copied into queue order)
+        return (_align(L.n * 4) + _align(npad * 4) + _align(L.n * 4) + _align(L.n * L.d * 2)
+                + _align(L.n * L.f * 2) + _align(npad * L.f * 2) + _align(npad * 2 * L.f * 2)
+                + _align((L.E + 1) * 4) + _align(L.E * 4) + _align(kp // 64 * L.d * 4)
+                + _align(_split_bytes(2 * L.f, 2)))
     raise ValueError(f"unknown op {op}")
 
 
@@ -194,10 +196,9 @@ def hbm_bytes(L: Layer) -> Dict[str, float]:
         "dispatch_with_x_perm": (1 + L.k) * L.T * L.d * s + 12.0 * L.n,
         "combine": (L.k + 1) * L.T * L.d * s + 8.0 * L.n,
         "router_read": L.T * L.d * s + L.E * L.d * s + 4.0 * L.T * L.E,
-        "backward_dy": (2 * L.k + 1) * L.T * L.d * 2.0,
+        # dy and the queue rows' y_perm (dy_perm is not stored)
+        "backward_dy": (L.k + 1) * L.T * L.d * 2.0,
         "backward_dx": (L.k + 1) * L.T * L.d * 2.0,
-        # x gathered into queue order (read once per token, written per row)
-        "backward_x_gather": L.T * L.d * 2.0 + L.n * L.d * 2.0,
         # the router gradient's partial sums: every queue row's x row read
         "backward_router_partials": L.n * L.d * 2.0,
     }
@@ -318,20 +319,16 @@ def _backward_parts(L: Layer, counts: Sequence[int], hw: Hardware) -> Dict[str, 
     t["bwd_recompute"] = gemm_time(hw, R * _cdiv(L.f, GATEUP_COLS), L.d / BK, extra_us=hw.upbwd_tile_us)
     t["bwd_dx_perm"] = gemm_time(hw, R * _cdiv(L.d, DOWN_COLS), 2 * L.f / BK, split=_split_bytes(2 * L.f, 2) > 0)
     t["bwd_wgrad"] = wgrad_time(hw, counts, L.d, L.f) + 2 * wgrad_time(hw, counts, L.f, L.d)
-    # (launches: offsets and order, dy, dx, the gather of x; no router)
-    t["bwd_streaming"] = 4 * hw.launch_us + backward_stream_bytes(L) / hw.stream_bw
+    # (launches: offsets and order, dy, dx; no router)
+    t["bwd_streaming"] = 3 * hw.launch_us + backward_stream_bytes(L) / hw.stream_bw
     return t
 
 
 def backward_stream_bytes(L: Layer, router: bool = False) -> float:
-    """Bytes of the backward's bandwidth-bound kernels: slot gradients and
-    reverse dispatch of dy, the dx sum, x gathered into queue order and, with
-    a router, its gradient's partial sums (taken in the same pass)."""
+    """Bytes of the backward's bandwidth-bound kernels: the slot gradients,
+    the dx sum and, with a router, its gradient's partial sums."""
     b = hbm_bytes(L)
-    # (with a router the queue-ordered pass that takes the partial sums also
-    # writes x_perm: x rows read per queue row instead of once per token)
-    return (b["backward_dy"] + b["backward_dx"] + b["backward_x_gather"]
-            + (b["backward_router_partials"] - L.T * L.d * 2.0 if router else 0.0))
+    return b["backward_dy"] + b["backward_dx"] + (b["backward_router_partials"] if router else 0.0)
 
 
 def predict_times(L: Layer, counts: Sequence[int], hw: Optional[Hardware] = None) -> Dict[str, float]:
@@ -380,7 +377,7 @@ def calibrate(measure, shapes: Optional[Sequence[Layer]] = None, hw: Optional[Ha
     bwd = [(L,) + tuple(measure_backward(L)) for L in shapes] if measure_backward is not None else []
     # the two fits share the split-K reduction's bandwidth term: refit a few
     # times on the stored measurements until the constants settle
-    for _ in range(4 if bwd else 1):
+    for _ in range(8 if bwd else 1):
         rows = []
         for L, us, counts in fwd:
             a, b, c = ffn_terms(L, counts, hw)

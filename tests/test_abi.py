@@ -221,19 +221,21 @@ def test_backward_validation(lib):
 
 
 def test_backward_workspace_size(lib):
-    # dsel; the weight gradients' queue-order operands dy_perm, h, du|dv and
-    # x_perm, each with 65 rows of padding (whole 64-row slices past an
-    # expert's end, one row for a channel range past a row's end); dx_perm and
-    # dh; the padded offsets and expert order; the router gradient's partial
-    # sums per 64-row block of the padded queue (Kpad = 64-aligned T*k + 63 E);
-    # and the split-K partial tiles of the dx_perm GEMM.  No transposed copy.
+    # dsel; each queue row's token (with 65 entries of padding) and gate; the
+    # weight gradients' queue-order operands g h and du|dv, each with 65 rows
+    # of padding (whole 64-row slices past an expert's end, one row for a
+    # channel range past a row's end); dx_perm and dh; the padded offsets and
+    # expert order; the router gradient's partial sums per 64-row block of
+    # the padded queue (Kpad = 64-aligned T*k + 63 E); and the split-K partial
+    # tiles of the dx_perm GEMM.  No transposed copy, and no copy of x or dy
+    # in queue order: the weight gradients read them by token.
     for T, d, E, k, f in [(8192, 4096, 8, 2, 14336), (16384, 2048, 64, 6, 1408), (64, 256, 8, 2, 512)]:
         n = T * k
         np_ = n + 65
         kp = -(-(n + 63 * E) // 64) * 64
         split = 256 * 256 * 256 * 4 if 2 * f // 64 >= 16 else 0
-        expect = n * 4 + np_ * d * 2 + n * d * 2 + n * f * 2 + np_ * f * 2 + np_ * 2 * f * 2 + (E + 1) * 4 + \
-            E * 4 + np_ * d * 2 + kp // 64 * d * 4 + split
+        expect = n * 4 + np_ * 4 + n * 4 + n * d * 2 + n * f * 2 + np_ * f * 2 + np_ * 2 * f * 2 + \
+            (E + 1) * 4 + E * 4 + kp // 64 * d * 4 + split
         st, nb = ws_size(lib, prob(T, d, E, k, f), L.MOE_OP_BACKWARD)
         assert st == L.MOE_OK
         assert expect <= nb <= expect + 12 * 256

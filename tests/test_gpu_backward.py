@@ -6,8 +6,8 @@ the whole layer in float64 from the same bf16 inputs.  Routing is held
 identical by supplying logits: either seeded ones, or, with the router on
 the GPU, the GPU's own logits handed to the oracle (the router's gradient
 then still flows through W_r in both).  The HIP path stores every
-intermediate (dy_perm, dh, du|dv, h, dx_perm) in bf16 with fp32
-accumulation, so each gradient must agree with the oracle within
+intermediate (dh, du|dv, g h, dx_perm) in bf16 with fp32 accumulation,
+so each gradient must agree with the oracle within
 max|err| / max|ref| <= 1e-2, the bf16 tolerance of the forward tests;
 the weight layouts of the backward are bit-exact transposes.
 Outputs are poisoned before each call so that an unwritten element fails.
