@@ -277,12 +277,14 @@ moe_status_t moe_backward_weights(const moe_problem_t* p, const void* w_gate, co
  * bullet 3: intermediates are recomputed rather than stored, here the SwiGLU
  * ones, from x).  Given the forward state `fw` (ids, gates, queues, y_perm)
  * it computes, with the routing held fixed:
- *   slot gradients dg = <dy[t], y_perm[pos]>, the queue rows' gradient
- *   g dy[t], per expert dh = dy_perm W_down, the recomputed u = x W_gate^T,
- *   v = x W_up^T with du = dh v silu'(u) and dv = dh silu(u), dx_perm =
+ *   slot gradients dg = <dy[t], y_perm[pos]>, per expert and queue row q
+ *   (token t, gate g) dh = g dy[t] W_down, the recomputed u = x[t] W_gate^T,
+ *   v = x[t] W_up^T with du = dh v silu'(u) and dv = dh silu(u), dx_perm =
  *   du W_gate + dv W_up, dx[t] = sum_j dx_perm[pos(t, j)] (+ the router
- *   term), dW_down = dy_perm^T h, dW_gate = du^T x_perm, dW_up = dv^T x_perm,
- *   the logit gradient of the renormalised top-k softmax
+ *   term), dW_down = sum_q (g dy[t])^T h, dW_gate = sum_q du^T x[t],
+ *   dW_up = sum_q dv^T x[t] (x and dy are read by token: no copy of either
+ *   is made in queue order), the logit gradient of the renormalised top-k
+ *   softmax
  *   dl_j = g_j (dg_j - sum_i g_i dg_i) (zero for experts outside the top k),
  *   and, with a router, dW_r = dl^T x and dx += dl W_r.
  * w_down_t and w_gu_t come from moe_backward_weights.  w_router is NULL

@@ -173,8 +173,10 @@ def test_backward_exact_expert_counts():
 
 @pytest.mark.parametrize("T,d,E,k,f", [(400, 640, 16, 2, 128), (257, 1088, 4, 3, 64)])
 def test_backward_with_router_wide_rows(T, d, E, k, f):
-    """Router gradient with d above one 512-column strip of the x gather,
-    the last strip ragged."""
+    """Router gradient with d above one 512-column strip of its partial-sum
+    kernel, the last strip ragged (and d not a multiple of 256: the weight
+    gradients' last channel range passes the end of the token-major x and
+    dy rows)."""
     print(f"backward router wide T={T} d={d} E={E} k={k} f={f}", flush=True)
     p = mi.Problem(T, d, E, k, f, "bf16")
     L = mi.make_layer(p, seed=d)
@@ -268,9 +270,9 @@ def test_full_size_backward(name):
 def bwd_fuzz_cases(n=24, seed=77):
     """Seeded random backward shapes: T in [1, 400], E in {1, 2, 3, 5, 8, 16,
     64, 128}, k in [1, min(E, 8)], d and f multiples of 64 (some above one
-    512-column strip of the x gather, some with several 64-row weight-
-    gradient slices), Gaussian, Zipf-skewed or tie-heavy supplied logits, or
-    the router on the GPU."""
+    512-column strip of the router's partial sums, some with several 64-row
+    weight-gradient slices), Gaussian, Zipf-skewed or tie-heavy supplied
+    logits, or the router on the GPU."""
     rng = np.random.default_rng(seed)
     cases = []
     for _ in range(n):
