@@ -109,7 +109,7 @@ typedef struct {
     int32_t* offsets;        /* [E + 1] */
     int32_t* sorted_assign;  /* [T*k] */
     int32_t* assign_pos;     /* [T*k] */
-    void* y_perm;            /* [T*k, d] expert outputs (moe_backward needs them) */
+    void* y_perm;            /* [T*k, d] expert outputs (moe_backward does not need them) */
 } moe_forward_outputs_t;
 
 /* The forward state moe_backward reads (from moe_forward's outputs). */
@@ -119,7 +119,7 @@ typedef struct {
     const int32_t* offsets;       /* [E + 1] */
     const int32_t* sorted_assign; /* [T*k] */
     const int32_t* assign_pos;    /* [T*k] */
-    const void* y_perm;           /* [T*k, d] */
+    const void* y_perm;           /* [T*k, d]; not read (may be NULL) */
 } moe_forward_state_t;
 
 /* Gradients moe_backward writes.  dx, dw_gate, dw_up and dw_down are
@@ -275,9 +275,11 @@ moe_status_t moe_backward_weights(const moe_problem_t* p, const void* w_gate, co
  * (MoEBlaze summary, Methodology item 2: the backward runs on the
  * forward's dispatch queues; its checkpoint bullet and Key contributions
  * bullet 3: intermediates are recomputed rather than stored, here the SwiGLU
- * ones, from x).  Given the forward state `fw` (ids, gates, queues, y_perm)
- * it computes, with the routing held fixed:
- *   slot gradients dg = <dy[t], y_perm[pos]>, per expert and queue row q
+ * ones, from x).  Given the forward state `fw` (ids, gates, queues; its
+ * y_perm is not read: the slot gradients come from the recompute) it
+ * computes, with the routing held fixed:
+ *   slot gradients dg = <dy[t], y_perm[pos]> (computed as <dy[t] W_down,
+ *   h> from the recomputed h), per expert and queue row q
  *   (token t, gate g) dh = g dy[t] W_down, the recomputed u = x[t] W_gate^T,
  *   v = x[t] W_up^T with du = dh v silu'(u) and dv = dh silu(u), dx_perm =
  *   du W_gate + dv W_up, dx[t] = sum_j dx_perm[pos(t, j)] (+ the router

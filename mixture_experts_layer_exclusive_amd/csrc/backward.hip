@@ -27,70 +27,58 @@ namespace moe {
 
 namespace {
 
-// Block-wide sum of 256 threads (fixed order: per wave, then the 4 waves).
-__device__ __forceinline__ float block_sum(float v, float* s_part) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) s_part[threadIdx.x >> 6] = v;
-    __syncthreads();
-    return (s_part[0] + s_part[1]) + (s_part[2] + s_part[3]);
+// Step 1: each queue row's token and gate, qtok[pos] = a / k and qgate[pos]
+// = gates[a] for assignment a at queue position pos; one thread per
+// assignment.
+__global__ __launch_bounds__(256) void bwd_rows_kernel(const int32_t* __restrict__ assign_pos,
+                                                      const float* __restrict__ gates, int k, int64_t n,
+                                                      int32_t* __restrict__ qtok, float* __restrict__ qgate) {
+    const int64_t a = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (a >= n) return;
+    const int pos = assign_pos[a];
+    if (pos < 0) return;
+    qtok[pos] = static_cast<int32_t>(a / k);
+    qgate[pos] = gates[a];
 }
 
-// Step 1, one workgroup per token.
-__global__ __launch_bounds__(256) void bwd_dy_kernel(const uint4* __restrict__ dy,
-                                                    const uint4* __restrict__ y_perm,
+// Step 3b, one wave per token: the gate-weighted slot gradients gdg_j =
+// g_j <dy[t], y_perm[pos]> from the recompute's partial sums (dg_part
+// [T*k][P], P per queue row, summed in a fixed order: lane c adds entries c,
+// c + 64, ..., then a butterfly over the lanes), and the logit gradient of
+// the renormalised top-k softmax, dsel[t, j] = dl_j = g_j (dg_j - sum_i g_i
+// dg_i) = gdg_j - g_j sum_i gdg_i; dlogits (if given) holds dl_j at expert
+// id_j and zero elsewhere.
+__global__ __launch_bounds__(256) void bwd_dl_kernel(const float* __restrict__ dg_part, int P,
                                                     const int32_t* __restrict__ ids,
                                                     const float* __restrict__ gates,
-                                                    const int32_t* __restrict__ assign_pos, int k,
-                                                    int E, int chunks, int32_t* __restrict__ qtok,
-                                                    float* __restrict__ qgate, float* __restrict__ dsel,
+                                                    const int32_t* __restrict__ assign_pos, int64_t T, int k,
+                                                    int E, float* __restrict__ dsel,
                                                     float* __restrict__ dlogits) {
-    __shared__ float s_part[4];
-    __shared__ float s_dg[MOE_MAX_TOPK];
-    const int64_t t = blockIdx.x;
-    const uint4* dyr = dy + t * chunks;
+    __shared__ float s_gdg[4][MOE_MAX_TOPK];
+    const int w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + w;
+    if (t >= T) return;
     for (int j = 0; j < k; ++j) {
         const int pos = assign_pos[t * k + j];
-        if (pos >= 0 && threadIdx.x == 0) {
-            qtok[pos] = static_cast<int32_t>(t);
-            qgate[pos] = gates[t * k + j];
-        }
-        float acc = 0.f;
-        for (int c = threadIdx.x; c < chunks; c += 256) {
-            if (pos >= 0) {
-                const uint4 a = dyr[c];
-                const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
-                const uint4 b = load_nt(y_perm + static_cast<int64_t>(pos) * chunks + c);
-                const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
+        float v = 0.f;
+        if (pos >= 0)
+            for (int c = lane; c < P; c += 64) v += dg_part[static_cast<int64_t>(pos) * P + c];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    acc = fmaf(lo_bf16(aw[i]), lo_bf16(bw[i]), acc);
-                    acc = fmaf(hi_bf16(aw[i]), hi_bf16(bw[i]), acc);
-                }
-            }
-        }
-        const float dg = block_sum(acc, s_part);
-        if (threadIdx.x == 0) s_dg[j] = pos >= 0 ? dg : 0.f;
+        for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+        if (lane == 0) s_gdg[w][j] = v;
     }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        float inner = 0.f;
-        for (int j = 0; j < k; ++j) inner = fmaf(gates[t * k + j], s_dg[j], inner);
-        for (int j = 0; j < k; ++j) dsel[t * k + j] = gates[t * k + j] * (s_dg[j] - inner);
-    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    float inner = 0.f;
+    for (int j = 0; j < k; ++j) inner += s_gdg[w][j];
+    for (int j = lane; j < k; j += 64) dsel[t * k + j] = s_gdg[w][j] - gates[t * k + j] * inner;
     if (dlogits != nullptr) {
-        __syncthreads();
-        for (int e = threadIdx.x; e < E; e += 256) dlogits[t * E + e] = 0.f;
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            float inner = 0.f;
-            for (int j = 0; j < k; ++j) inner = fmaf(gates[t * k + j], s_dg[j], inner);
-            for (int j = 0; j < k; ++j) {
-                const int e = ids[t * k + j];
-                if (static_cast<unsigned>(e) < static_cast<unsigned>(E))
-                    dlogits[t * E + e] = gates[t * k + j] * (s_dg[j] - inner);
-            }
+        for (int e = lane; e < E; e += 64) {
+            float v = 0.f;
+            for (int j = 0; j < k; ++j)
+                if (ids[t * k + j] == e) v = s_gdg[w][j] - gates[t * k + j] * inner;
+            dlogits[t * E + e] = v;
         }
     }
 }
@@ -401,12 +389,19 @@ hipError_t launch_backward_weights(const moe_problem_t& p, const void* w_gate, c
     return hipGetLastError();
 }
 
-hipError_t launch_backward_dy(const moe_problem_t& p, const void* dy, const void* y_perm,
-                              const int32_t* ids, const float* gates, const int32_t* assign_pos,
-                              int32_t* qtok, float* qgate, float* dsel, float* dlogits, hipStream_t s) {
-    bwd_dy_kernel<<<static_cast<unsigned>(p.T), 256, 0, s>>>(
-        static_cast<const uint4*>(dy), static_cast<const uint4*>(y_perm), ids, gates, assign_pos, p.k,
-        p.E, p.d / 8, qtok, qgate, dsel, dlogits);
+hipError_t launch_backward_rows(const moe_problem_t& p, const int32_t* assign_pos, const float* gates,
+                                int32_t* qtok, float* qgate, hipStream_t s) {
+    const int64_t n = p.T * p.k;
+    bwd_rows_kernel<<<static_cast<unsigned>(ceil_div(n, 256)), 256, 0, s>>>(assign_pos, gates, p.k, n, qtok,
+                                                                            qgate);
+    return hipGetLastError();
+}
+
+hipError_t launch_backward_dl(const moe_problem_t& p, const float* dg_part, const int32_t* ids,
+                              const float* gates, const int32_t* assign_pos, float* dsel, float* dlogits,
+                              hipStream_t s) {
+    bwd_dl_kernel<<<static_cast<unsigned>(ceil_div(p.T, 4)), 256, 0, s>>>(
+        dg_part, bwd_dg_parts(p), ids, gates, assign_pos, p.T, p.k, p.E, dsel, dlogits);
     return hipGetLastError();
 }
 

@@ -1051,16 +1051,23 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         // dv side by side (a 256-column row: chunks 0..15 du, 16..31 dv) and
         // stores them to C = [rows, 2f] (du in columns [0, f), dv in [f, 2f));
         // pass 2 stores g h = g s v to C2 (the down projection's weight
-        // gradient sums dy[t] (g h) over the queue rows).
+        // gradient sums dy[t] (g h) over the queue rows).  The gate times
+        // the slot gradient's share of the tile's columns, the sum of dv v =
+        // g dh_raw s v over them (g <dy[t], y_perm[pos]> = g <dy[t] W_down,
+        // h>), goes to part: [rows][2 * column tiles] fp32, one value per
+        // wave column half, summed in a fixed order (lane's 32 columns, then
+        // lane + 32's).
         constexpr int CPR2 = 32;
         constexpr int ROWO2 = CPR2 * 16;
         static_assert(TM * ROWO2 <= 2 * STAGE_BYTES, "the staged du/dv tile must fit the ring");
+        const int ptiles = 2 * ((N + BN_OUT - 1) / BN_OUT);
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
             const int r = wm * 128 + mb * 32 + l32;
             const int pos = tile.row0 + r;
             char* const srow = smem + r * ROWO2 + khalf * 8;
             const int sw = r & (CPR2 - 1);
+            float dgp = 0.f;
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
@@ -1069,8 +1076,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                     uint2 dhw = make_uint2(0u, 0u);
                     if (pos < tile.row1 && col < N)
                         dhw = *reinterpret_cast<const uint2*>(aux + static_cast<int64_t>(pos) * N + col);
-                    const float dh[4] = {rs[mb] * lo_bf16(dhw.x), rs[mb] * hi_bf16(dhw.x), rs[mb] * lo_bf16(dhw.y),
-                                         rs[mb] * hi_bf16(dhw.y)};
+                    const float dr[4] = {lo_bf16(dhw.x), hi_bf16(dhw.x), lo_bf16(dhw.y), hi_bf16(dhw.y)};
                     float du[4], dv[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
@@ -1078,8 +1084,10 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                         const float v = acc[nb + 2][mb][4 * g + i];
                         const float sg = sigmoid_fast(u);
                         const float su = u * sg;
-                        du[i] = dh[i] * v * sg * (1.f + u * (1.f - sg));
-                        dv[i] = dh[i] * su;
+                        const float dh = rs[mb] * dr[i];
+                        du[i] = dh * v * sg * (1.f + u * (1.f - sg));
+                        dv[i] = dh * su;
+                        dgp = fmaf(dv[i], v, dgp);
                     }
                     const int ch = wn * 8 + nb * 4 + g;
                     *reinterpret_cast<uint2*>(srow + ((ch ^ sw) * 16)) =
@@ -1087,6 +1095,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                     *reinterpret_cast<uint2*>(srow + (((ch + 16) ^ sw) * 16)) =
                         make_uint2(pack_bf16x2(dv[0], dv[1]), pack_bf16x2(dv[2], dv[3]));
                 }
+            const float tot = dgp + __shfl_xor(dgp, 32, 64);
+            if (khalf == 0 && pos < tile.row1) part[static_cast<int64_t>(pos) * ptiles + tile.nt * 2 + wn] = tot;
         }
         __syncthreads();
 #pragma unroll 4
@@ -1350,16 +1360,19 @@ hipError_t launch_backward_dh(const moe_problem_t& p, const void* dy, const int3
 
 // Recompute of gate and up from x (gathered), with the SwiGLU backward in the
 // epilogue: dh = g dh_raw (qgate: each queue row's gate), du, dv -> duv
-// [T*k, 2f], g h -> hg [T*k, f].
+// [T*k, 2f], g h -> hg [T*k, f], and the gate-weighted slot gradients'
+// partial sums dg_part [T*k][2 ceil(f / 128)] (sum of g dh_raw h over each
+// 64 columns).
 hipError_t launch_backward_recompute(const moe_problem_t& p, const void* x, const int32_t* sorted_assign,
                                      const int32_t* offsets, const void* w_gate, const void* w_up,
-                                     const void* dh, const float* qgate, void* duv, void* hg, hipStream_t s) {
+                                     const void* dh, const float* qgate, void* duv, void* hg, float* dg_part,
+                                     hipStream_t s) {
     const int64_t n = p.T * p.k;
     const unsigned g = grid_for(n, p.E, kBM, static_cast<int>(ceil_div(p.f, kGateUpCols)));
     // (the backward's limits keep T * d below 2^31: 32-bit gather offsets)
     grouped_gemm_bf16_kernel<kUpBwd, true, false><<<g, 256, 0, s>>>(
         static_cast<const bf16_t*>(x), sorted_assign, p.k, offsets, p.E, static_cast<const bf16_t*>(w_gate),
-        static_cast<const bf16_t*>(w_up), static_cast<bf16_t*>(duv), p.f, p.d, 0, nullptr,
+        static_cast<const bf16_t*>(w_up), static_cast<bf16_t*>(duv), p.f, p.d, 0, dg_part,
         static_cast<const bf16_t*>(dh), static_cast<bf16_t*>(hg), 0, nullptr, nullptr, nullptr, 0, nullptr,
         qgate);
     return hipGetLastError();

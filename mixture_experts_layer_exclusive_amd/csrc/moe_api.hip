@@ -90,10 +90,11 @@ size_t dispatch_ws(const moe_problem_t& p) {
 size_t ffn_ws(const moe_problem_t& p) { return ffn_h_bytes(p) + ffn_split_bytes(p); }
 
 // Backward workspace: dsel [T*k] fp32; each queue row's token qtok [T*k +
-// pad] and gate qgate [T*k] fp32; dx_perm [T*k, d]; dh_raw [T*k, f]; g h
-// [T*k + pad, f]; du|dv [T*k + pad, 2f]; padded offsets [E+1] and the expert
-// order [E]; the router-gradient partial sums [kpad / 64, d] fp32; the
-// split-K partial tiles of the dx_perm GEMM.  g h and du|dv are the weight
+// pad] and gate qgate [T*k] fp32; the slot gradients' partial sums [T*k,
+// bwd_dg_parts] fp32; dx_perm [T*k, d]; dh_raw [T*k, f]; g h [T*k + pad, f];
+// du|dv [T*k + pad, 2f]; padded offsets [E+1] and the expert order [E]; the
+// router-gradient partial sums [kpad / 64, d] fp32; the split-K partial
+// tiles of the dx_perm GEMM.  g h and du|dv are the weight
 // gradients' queue-order operands (pad = kWgradPadRows rows after the last
 // queue row); x and dy are read by token through qtok, never copied into
 // queue order.
@@ -104,6 +105,7 @@ size_t backward_ws(const moe_problem_t& p) {
     size_t b = align_up(n * 4, kAlign);              // dsel
     b += align_up(np * 4, kAlign);                   // qtok
     b += align_up(n * 4, kAlign);                    // qgate
+    b += align_up(n * bwd_dg_parts(p) * 4, kAlign);  // slot-gradient partial sums
     b += align_up(n * p.d * 2, kAlign);              // dx_perm
     b += align_up(n * p.f * 2, kAlign);              // dh_raw
     b += align_up(np * p.f * 2, kAlign);             // g h
@@ -456,7 +458,6 @@ moe_status_t moe_backward(const moe_problem_t* p, const void* x, const void* w_r
         MOE_TRY(need(fw->topk_gates));
         MOE_TRY(need(fw->sorted_assign));
         MOE_TRY(need(fw->assign_pos));
-        MOE_TRY(need(fw->y_perm));
     }
     MOE_TRY(need(ws));
     if (ws_bytes < backward_ws(*p)) return MOE_ERR_WORKSPACE_TOO_SMALL;
@@ -468,6 +469,7 @@ moe_status_t moe_backward(const moe_problem_t* p, const void* x, const void* w_r
     float* dsel = c.take<float>(n * 4);
     int32_t* qtok = c.take<int32_t>(np * 4);
     float* qgate = c.take<float>(n * 4);
+    float* dg_part = c.take<float>(n * bwd_dg_parts(*p) * 4);
     void* dx_perm = c.take<char>(n * p->d * 2);
     void* dh = c.take<char>(n * p->f * 2);
     void* hg = c.take<char>(np * p->f * 2);
@@ -482,11 +484,12 @@ moe_status_t moe_backward(const moe_problem_t* p, const void* x, const void* w_r
     // (with no tokens fw is not read: every queue is empty)
     MOE_LAUNCH(launch_backward_poff(*p, p->T > 0 ? fw->offsets : nullptr, poff, order, qtok, s));
     if (p->T > 0) {
-        MOE_LAUNCH(launch_backward_dy(*p, dy, fw->y_perm, fw->topk_ids, fw->topk_gates, fw->assign_pos, qtok,
-                                      qgate, dsel, out->dlogits, s));
+        MOE_LAUNCH(launch_backward_rows(*p, fw->assign_pos, fw->topk_gates, qtok, qgate, s));
         MOE_LAUNCH(launch_backward_dh(*p, dy, fw->sorted_assign, fw->offsets, w_down_t, dh, s));
         MOE_LAUNCH(launch_backward_recompute(*p, x, fw->sorted_assign, fw->offsets, w_gate, w_up, dh, qgate,
-                                             duv, hg, s));
+                                             duv, hg, dg_part, s));
+        MOE_LAUNCH(launch_backward_dl(*p, dg_part, fw->topk_ids, fw->topk_gates, fw->assign_pos, dsel,
+                                      out->dlogits, s));
         MOE_LAUNCH(launch_backward_dxperm(*p, duv, fw->offsets, w_gu_t, dx_perm, split, s));
         MOE_LAUNCH(launch_backward_dx(*p, dx_perm, fw->assign_pos, fw->topk_ids, dsel, w_router, out->dx,
                                       s));

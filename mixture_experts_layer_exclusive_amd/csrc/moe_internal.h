@@ -127,9 +127,14 @@ hipError_t launch_expert_ffn_fp8(const moe_problem_t& p, const void* x_q, const 
                                  void* y_perm, hipStream_t s);
 hipError_t launch_backward_weights(const moe_problem_t& p, const void* w_gate, const void* w_up,
                                    const void* w_down, void* w_down_t, void* w_gu_t, hipStream_t s);
-hipError_t launch_backward_dy(const moe_problem_t& p, const void* dy, const void* y_perm,
-                              const int32_t* ids, const float* gates, const int32_t* assign_pos,
-                              int32_t* qtok, float* qgate, float* dsel, float* dlogits, hipStream_t s);
+// Slot-gradient partial sums per queue row: one per 64 columns of f (two per
+// recompute tile).
+inline int bwd_dg_parts(const moe_problem_t& p) { return 2 * static_cast<int>(ceil_div(p.f, kGateUpCols)); }
+hipError_t launch_backward_rows(const moe_problem_t& p, const int32_t* assign_pos, const float* gates,
+                                int32_t* qtok, float* qgate, hipStream_t s);
+hipError_t launch_backward_dl(const moe_problem_t& p, const float* dg_part, const int32_t* ids,
+                              const float* gates, const int32_t* assign_pos, float* dsel, float* dlogits,
+                              hipStream_t s);
 hipError_t launch_backward_poff(const moe_problem_t& p, const int32_t* offsets, int32_t* poff,
                                 int32_t* order, int32_t* qtok, hipStream_t s);
 hipError_t launch_backward_router_partials(const moe_problem_t& p, const void* x, const int32_t* offsets,
@@ -144,7 +149,8 @@ hipError_t launch_backward_dh(const moe_problem_t& p, const void* dy, const int3
                               const int32_t* offsets, const void* w_down_t, void* dh, hipStream_t s);
 hipError_t launch_backward_recompute(const moe_problem_t& p, const void* x, const int32_t* sorted_assign,
                                      const int32_t* offsets, const void* w_gate, const void* w_up,
-                                     const void* dh, const float* qgate, void* duv, void* hg, hipStream_t s);
+                                     const void* dh, const float* qgate, void* duv, void* hg, float* dg_part,
+                                     hipStream_t s);
 hipError_t launch_backward_dxperm(const moe_problem_t& p, const void* duv, const int32_t* offsets,
                                   const void* w_gu_t, void* dx_perm, float* part, hipStream_t s);
 hipError_t launch_backward_wgrad(const moe_problem_t& p, const void* A, int lda, int a_col_off, int M,

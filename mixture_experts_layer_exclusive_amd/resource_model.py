@@ -130,10 +130,13 @@ def workspace(L: Layer, op: int) -> int:
     if op == OP_BACKWARD:
         kp = kpad(L)
         npad = L.n + WGRAD_PAD_ROWS
-        # dsel, the queue rows' tokens and gates, dx_perm, dh_raw, g h, du|dv,
-        # poff, order, router partial sums, split-K partials (x and dy are
-        # read by token, not copied into queue order)
-        return (_align(L.n * 4) + _align(npad * 4) + _align(L.n * 4) + _align(L.n * L.d * 2)
+        # dsel, the queue rows' tokens and gates, the slot gradients' partial
+        # sums, dx_perm, dh_raw, g h, du|dv, poff, order, router partial
+        # sums, split-K partials (x and dy are read by token, not copied into
+        # queue order; y_perm is not read)
+        parts = 2 * _cdiv(L.f, GATEUP_COLS)
+        return (_align(L.n * 4) + _align(npad * 4) + _align(L.n * 4) + _align(L.n * parts * 4)
+                + _align(L.n * L.d * 2)
                 + _align(L.n * L.f * 2) + _align(npad * L.f * 2) + _align(npad * 2 * L.f * 2)
                 + _align((L.E + 1) * 4) + _align(L.E * 4) + _align(kp // 64 * L.d * 4)
                 + _align(_split_bytes(2 * L.f, 2)))
@@ -196,8 +199,9 @@ def hbm_bytes(L: Layer) -> Dict[str, float]:
         "dispatch_with_x_perm": (1 + L.k) * L.T * L.d * s + 12.0 * L.n,
         "combine": (L.k + 1) * L.T * L.d * s + 8.0 * L.n,
         "router_read": L.T * L.d * s + L.E * L.d * s + 4.0 * L.T * L.E,
-        # dy and the queue rows' y_perm (dy_perm is not stored)
-        "backward_dy": (L.k + 1) * L.T * L.d * 2.0,
+        # the queue rows' tokens and gates, and the slot and logit gradients
+        # from the recompute's partial sums (y_perm is not read)
+        "backward_dy": L.n * (8.0 + 8.0 + 4.0 * 2 * _cdiv(L.f, GATEUP_COLS)) + 4.0 * L.T * L.E,
         "backward_dx": (L.k + 1) * L.T * L.d * 2.0,
         # the router gradient's partial sums: every queue row's x row read
         "backward_router_partials": L.n * L.d * 2.0,
@@ -319,8 +323,9 @@ def _backward_parts(L: Layer, counts: Sequence[int], hw: Hardware) -> Dict[str, 
     t["bwd_recompute"] = gemm_time(hw, R * _cdiv(L.f, GATEUP_COLS), L.d / BK, extra_us=hw.upbwd_tile_us)
     t["bwd_dx_perm"] = gemm_time(hw, R * _cdiv(L.d, DOWN_COLS), 2 * L.f / BK, split=_split_bytes(2 * L.f, 2) > 0)
     t["bwd_wgrad"] = wgrad_time(hw, counts, L.d, L.f) + 2 * wgrad_time(hw, counts, L.f, L.d)
-    # (launches: offsets and order, dy, dx; no router)
-    t["bwd_streaming"] = 3 * hw.launch_us + backward_stream_bytes(L) / hw.stream_bw
+    # (launches: offsets and order, the queue rows' tokens and gates, the
+    # slot and logit gradients, dx; no router)
+    t["bwd_streaming"] = 4 * hw.launch_us + backward_stream_bytes(L) / hw.stream_bw
     return t
 
 

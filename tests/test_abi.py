@@ -213,7 +213,9 @@ def test_backward_validation(lib):
     assert lib.moe_backward(pp, *bwd_args(out=False)) == E
     assert lib.moe_backward(pp, *bwd_args(dw_router=None)) == E      # a router needs its gradient
     assert lib.moe_backward(pp, *bwd_args(w_router=None)) == E       # a gradient needs the router
-    assert lib.moe_backward(pp, *bwd_args(y_perm=None)) == E
+    assert lib.moe_backward(pp, *bwd_args(assign_pos=None)) == E
+    # y_perm is not read: its absence passes the checks (up to the workspace's)
+    assert lib.moe_backward(pp, *bwd_args(y_perm=None, ws_bytes=need - 1)) == L.MOE_ERR_WORKSPACE_TOO_SMALL
     assert lib.moe_backward(pp, *bwd_args(offsets=MIS)) == U
     assert lib.moe_backward(pp, *bwd_args(dw_down=None)) == E
     assert lib.moe_backward(pp, *bwd_args(dlogits=MIS)) == U
@@ -222,7 +224,9 @@ def test_backward_validation(lib):
 
 def test_backward_workspace_size(lib):
     # dsel; each queue row's token (with 65 entries of padding) and gate; the
-    # weight gradients' queue-order operands g h and du|dv, each with 65 rows
+    # slot gradients' partial sums (one per 64 columns of each 128-column
+    # recompute tile); the weight gradients' queue-order operands g h and
+    # du|dv, each with 65 rows
     # of padding (whole 64-row slices past an expert's end, one row for a
     # channel range past a row's end); dx_perm and dh; the padded offsets and
     # expert order; the router gradient's partial sums per 64-row block of
@@ -234,8 +238,9 @@ def test_backward_workspace_size(lib):
         np_ = n + 65
         kp = -(-(n + 63 * E) // 64) * 64
         split = 256 * 256 * 256 * 4 if 2 * f // 64 >= 16 else 0
-        expect = n * 4 + np_ * 4 + n * 4 + n * d * 2 + n * f * 2 + np_ * f * 2 + np_ * 2 * f * 2 + \
-            (E + 1) * 4 + E * 4 + kp // 64 * d * 4 + split
+        parts = 2 * -(-f // 128)
+        expect = n * 4 + np_ * 4 + n * 4 + n * parts * 4 + n * d * 2 + n * f * 2 + np_ * f * 2 + \
+            np_ * 2 * f * 2 + (E + 1) * 4 + E * 4 + kp // 64 * d * 4 + split
         st, nb = ws_size(lib, prob(T, d, E, k, f), L.MOE_OP_BACKWARD)
         assert st == L.MOE_OK
         assert expect <= nb <= expect + 12 * 256
