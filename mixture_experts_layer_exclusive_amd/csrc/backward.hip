@@ -59,14 +59,26 @@ __global__ __launch_bounds__(256) void bwd_dl_kernel(const float* __restrict__ d
     const int lane = threadIdx.x & 63;
     const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + w;
     if (t >= T) return;
-    for (int j = 0; j < k; ++j) {
-        const int pos = assign_pos[t * k + j];
-        float v = 0.f;
-        if (pos >= 0)
-            for (int c = lane; c < P; c += 64) v += dg_part[static_cast<int64_t>(pos) * P + c];
+    // (four slots at a time, their loads in flight together)
+    for (int j0 = 0; j0 < k; j0 += 4) {
+        int pos[4];
+        float v[4];
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-        if (lane == 0) s_gdg[w][j] = v;
+        for (int u = 0; u < 4; ++u) {
+            pos[u] = j0 + u < k ? assign_pos[t * k + j0 + u] : -1;
+            v[u] = 0.f;
+        }
+        for (int c = lane; c < P; c += 64) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (pos[u] >= 0) v[u] += dg_part[static_cast<int64_t>(pos[u]) * P + c];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) v[u] += __shfl_xor(v[u], off, 64);
+            if (lane == 0 && j0 + u < k) s_gdg[w][j0 + u] = v[u];
+        }
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     __builtin_amdgcn_wave_barrier();

@@ -932,8 +932,9 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         }
     }
     // stage the tile's output (h = silu(gate) * up for the gate/up modes, the
-    // accumulators otherwise; kUpBwd: g h, the row's gate times h) and store
-    // it to out (row stride ldo)
+    // accumulators otherwise; kUpBwd: g h, the row's gate times h, which the
+    // SwiGLU backward has left in the gate block's registers) and store it to
+    // out (row stride ldo)
     auto stage_and_store = [&](bf16_t* __restrict__ out, int64_t ldo) {
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
@@ -949,8 +950,10 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                         float v[4];
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            v[i] = silu_mul_fast(acc[nb][mb][4 * g + i], acc[nb + 2][mb][4 * g + i]);
-                            if (MODE == kUpBwd) v[i] *= rs[mb];
+                            // (kUpBwd: the gate block's registers already
+                            // hold g h, left there by the SwiGLU backward)
+                            if (MODE == kUpBwd) v[i] = acc[nb][mb][4 * g + i];
+                            else v[i] = silu_mul_fast(acc[nb][mb][4 * g + i], acc[nb + 2][mb][4 * g + i]);
                         }
                         o = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
                     } else {
@@ -1088,6 +1091,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                         du[i] = dh * v * sg * (1.f + u * (1.f - sg));
                         dv[i] = dh * su;
                         dgp = fmaf(dv[i], v, dgp);
+                        // g h for pass 2, in place of u (no second exp)
+                        acc[nb][mb][4 * g + i] = rs[mb] * su * v;
                     }
                     const int ch = wn * 8 + nb * 4 + g;
                     *reinterpret_cast<uint2*>(srow + ((ch ^ sw) * 16)) =
