@@ -356,8 +356,10 @@ def backward(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor, k: int, 
     if T > 0:
         for key, shape, tdt in (("topk_ids", (T, k), torch.int32), ("topk_gates", (T, k), torch.float32),
                                 ("offsets", (E + 1,), torch.int32), ("sorted_assign", (n,), torch.int32),
-                                ("assign_pos", (n,), torch.int32), ("y_perm", (n, d), dt)):
+                                ("assign_pos", (n,), torch.int32)):
             _expect(f"state[{key!r}]", state.get(key), shape, tdt, dev)
+        # (y_perm is not read: the backward needs only the routing)
+        _expect("state['y_perm']", state.get("y_perm"), (n, d), dt, dev, required=False)
     given = dict(out or {})
     for key, shape, tdt in (("dx", (T, d), dt), ("dw_gate", (E, f, d), dt), ("dw_up", (E, f, d), dt),
                             ("dw_down", (E, d, f), dt), ("dw_router", (E, d), dt),
@@ -379,7 +381,7 @@ def backward(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor, k: int, 
     else:
         res["dlogits"] = None
     # (with no tokens the forward state is not read)
-    fw = L.MoeForwardState(**{key: (_ptr(state[key]) if T > 0 else None) for key in _STATE_KEYS})
+    fw = L.MoeForwardState(**{key: (_ptr(state.get(key)) if T > 0 else None) for key in _STATE_KEYS})
     o = L.MoeBackwardOutputs(**{key: (_ptr(res[key]) if res[key] is not None and res[key].numel() > 0
                                       else None)
                                 for key in ("dx", "dw_gate", "dw_up", "dw_down", "dw_router", "dlogits")})

@@ -208,6 +208,29 @@ def test_backward_twice_is_bitwise_identical():
         assert torch.equal(g1[key], g2[key]), key
 
 
+def test_backward_needs_only_the_routing():
+    """The backward reads from the forward state only its routing: with
+    y_perm left out of the state, or filled with NaN, every gradient is
+    bitwise the same as with the forward's y_perm (the slot gradients come
+    from the recompute)."""
+    p = mi.Problem(700, 320, 16, 4, 192, "bf16")
+    L = mi.make_layer(p, seed=11)
+    dy = dev(mi.make_grad_output(p, seed=11))
+    x = dev(L["x"])
+    wg, wu, wd, wr = (dev(L[n]) for n in ("w_gate", "w_up", "w_down", "w_router"))
+    _, st = moe.forward(x, wg, wu, wd, p.k, w_router=wr, intermediates=True)
+    wt = moe.backward_weights(wg, wu, wd)
+    ref = moe.backward(x, wg, wu, p.k, st, dy, wt, w_router=wr, with_dlogits=True)
+    routing = {key: v for key, v in st.items() if key != "y_perm"}
+    nan_state = dict(routing, y_perm=torch.full_like(st["y_perm"], float("nan")))
+    for state in (routing, nan_state):
+        g = moe.backward(x, wg, wu, p.k, state, dy, wt, w_router=wr, with_dlogits=True,
+                         out=poisoned_outputs(p, True))
+        torch.cuda.synchronize()
+        for key in ("dx", "dw_gate", "dw_up", "dw_down", "dw_router", "dlogits"):
+            assert torch.equal(g[key], ref[key]), key
+
+
 def test_backward_zero_tokens_gives_zero_weight_gradients():
     p = mi.Problem(1, 128, 8, 2, 64, "bf16")
     L = mi.make_layer(p, seed=1)
