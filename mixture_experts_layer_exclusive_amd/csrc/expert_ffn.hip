@@ -249,8 +249,9 @@ __device__ __forceinline__ const T* uniform_ptr(const T* p) {
 //   kWgrad weight gradients: per expert e, C_e[M, N] = sum over the
 //          expert's queue rows q of A[q, a_row_off + m] B[q, n], with A and
 //          B in queue order ([rows, K] and [rows, N]: K is A's row length
-//          here) and read through transposing LDS reads, so no transposed
-//          copy of either operand is made
+//          here), or one of them token-major (row qtok[q] for queue row q),
+//          read through transposing LDS reads, so no transposed copy of
+//          either operand is made
 constexpr int kUp = 0, kDown = 1, kUpBwd = 2, kWgrad = 3;
 
 // Work of a weight-gradient workgroup: tile (mt, nt) of expert e, K slices of
