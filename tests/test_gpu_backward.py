@@ -208,6 +208,29 @@ def test_backward_twice_is_bitwise_identical():
         assert torch.equal(g1[key], g2[key]), key
 
 
+def test_backward_long_weight_gradient_k():
+    """Weight gradients over long K ranges: experts of 33000 queue rows (516
+    slices of 64, the last of 40 rows), 32768 rows (exactly 512 slices),
+    4232 rows and none; top-1 routing on supplied logits.  Checked against
+    the oracle, and bitwise on a repeat."""
+    counts = [33000, 32768, 4232, 0]
+    T = sum(counts)
+    print(f"backward long weight-gradient K T={T} counts={counts}", flush=True)
+    p = mi.Problem(T, 64, 4, 1, 128, "bf16")
+    rng = np.random.default_rng(21)
+    owner = rng.permutation(np.repeat(np.arange(4), counts))
+    logits = (rng.standard_normal((T, 4)) * 0.5).astype(np.float32)
+    logits[np.arange(T), owner] = 4.0
+    L = mi.make_layer(p, seed=21)
+    dy = mi.make_grad_output(p, seed=21)
+    st, g = run_layer(L, dy, logits=logits)
+    assert host(st["counts"]).tolist() == counts
+    check(g, oracle_grads(L, dy, logits, router=False), router=False)
+    _, g2 = run_layer(L, dy, logits=logits)
+    for key in ("dx", "dw_gate", "dw_up", "dw_down"):
+        assert torch.equal(g[key], g2[key]), key
+
+
 def test_backward_needs_only_the_routing():
     """The backward reads from the forward state only its routing: with
     y_perm left out of the state, or filled with NaN, every gradient is
