@@ -265,13 +265,17 @@ constexpr int kUp = 0, kDown = 1, kUpBwd = 2, kWgrad = 3;
 // expert's row count, so the experts are dealt heaviest first (order[], a
 // permutation of the experts by descending count) in a snake order, XCD 0
 // to 7 and back, which keeps the XCDs' loads even under a skewed routing.
-// Within an expert, groups of GROUP_M row tiles walk the column tiles.
+// Within an expert, groups of GROUP_M row tiles walk the column tiles; with a
+// token-major A (dy), whose gathered rows cost more to fetch than the queue-
+// order B, groups of GROUP_M column tiles walk the row tiles instead, so that
+// the tiles running at once share fewer gathered row blocks (same-box: the
+// backward 0.3-0.6 % faster on three layers, unchanged on the fourth).
 __host__ __device__ __forceinline__ int wgrad_tiles_per_expert(int M, int N) {
     return ((M + kBM - 1) / kBM) * ((N + kDownCols - 1) / kDownCols);
 }
 __device__ __forceinline__ bool find_wgrad_work(const int32_t* __restrict__ offsets,
                                                 const int32_t* __restrict__ order, int E, int M, int N,
-                                                Work& w) {
+                                                bool group_n, Work& w) {
     const int mtn = (M + kBM - 1) / kBM;
     const int ntn = (N + kDownCols - 1) / kDownCols;
     const int per_e = mtn * ntn;
@@ -282,13 +286,16 @@ __device__ __forceinline__ bool find_wgrad_work(const int32_t* __restrict__ offs
     if (rank >= E) return false;
     const int e = order[rank];
     const int local = place % per_e;
-    const int group = local / (GROUP_M * ntn);
-    const int first_m = group * GROUP_M;
-    const int gsz = min(GROUP_M, mtn - first_m);
-    const int l2 = local - group * GROUP_M * ntn;
-    const int mt = first_m + l2 % gsz;
+    // (group_n: groups of GROUP_M column tiles walk the row tiles instead)
+    const int gm = group_n ? ntn : mtn, go = group_n ? mtn : ntn;
+    const int group = local / (GROUP_M * go);
+    const int first = group * GROUP_M;
+    const int gsz = min(GROUP_M, gm - first);
+    const int l2 = local - group * GROUP_M * go;
+    const int ig = first + l2 % gsz, io = l2 / gsz;
+    const int mt = group_n ? io : ig;
     w.t.e = e;
-    w.t.nt = l2 / gsz;
+    w.t.nt = group_n ? ig : io;
     w.t.row0 = mt * kBM;
     w.t.row1 = min(M, w.t.row0 + kBM);
     // (K runs over the expert's queue rows in slices of 64; the rows past
@@ -366,7 +373,9 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     Work work;
     if (WG) {
         // (sorted_assign is the expert order, heaviest first, here)
-        if (!find_wgrad_work(offsets, sorted_assign, E, M, N, work)) return;
+        // (a token-major A is the gathered side: its tiles are the fewer in
+        // each concurrent group)
+        if (!find_wgrad_work(offsets, sorted_assign, E, M, N, G_A, work)) return;
     } else {
         build_tile_prefix(offsets, E, TM, s_prefix, s_off);
         const int n_tiles = (N + BN_OUT - 1) / BN_OUT;
