@@ -926,10 +926,9 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // out in whole 16-byte chunks, consecutive lanes on consecutive chunks of
     // a row, so that every store instruction covers whole 128-byte lines
     // (8-byte stores into 32 rows each took 5-12 us per tile, measured).
-    // The stores are non-temporal: a tile's output is not read again by
-    // this launch, and marking it so keeps it from displacing the operand
-    // lines other tiles are still reading from the XCD's L2 (the expert FFN
-    // call 1.2-1.6 % faster at f = 768 and 1408, measured).
+    // The stores are non-temporal (no tile of the launch reads another's
+    // output): the expert FFN call measured 1.2-1.6 % faster at f = 768 and
+    // 1408, with the operand reads' L2 hit rates unchanged within a point.
     constexpr int OUTC = GATEUP ? TN / 2 : TN;  // output columns of a tile
     constexpr int CPR = OUTC / 8;               // 16-byte chunks per row
     constexpr int ROWO = OUTC * 2;              // bytes per staged row
