@@ -158,17 +158,22 @@ __global__ __launch_bounds__(256) void bwd_router_partials_kernel(const bf16_t* 
     __shared__ int64_t s_row[64];
     __shared__ float s_dsel[64];
     __shared__ float s_part[4][kGatherXCols];
+    __shared__ int s_poff[MOE_MAX_EXPERTS + 1];
     const int q0 = blockIdx.x * 64;
     const int c0 = blockIdx.y * kGatherXCols;
     if (q0 >= poff[E]) return;
+    // the padded offsets in LDS with one load per thread, so that the search
+    // below costs no global round trips
+    for (int i = threadIdx.x; i <= E; i += 256) s_poff[i] = poff[i];
+    __syncthreads();
     if (threadIdx.x < 64) {
         const int q = q0 + threadIdx.x;
         int lo = 0, hi = E;
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
-            if (poff[mid] <= q) lo = mid; else hi = mid;
+            if (s_poff[mid] <= q) lo = mid; else hi = mid;
         }
-        const int pos = offsets[lo] + (q - poff[lo]);
+        const int pos = offsets[lo] + (q - s_poff[lo]);
         int64_t row = -1;
         float ds = 0.f;
         if (pos < offsets[lo + 1]) {
