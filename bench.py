@@ -258,7 +258,8 @@ def summarize_pmc(fetch_csv, write_csv, bench):
 def summarize_mfma(path):
     """MfmaUtil (rocprofv3's derived counter: SQ_VALU_MFMA_BUSY_CYCLES over
     all SIMDs / (GRBM_GUI_ACTIVE x SIMDs)) per kernel of the forward steps,
-    the expert FFN loop and the backward loop, and of the register-only MFMA
+    the expert FFN loop, the backward loop and the fp8 expert FFN loop (when
+    the run has them), and of the register-only MFMA
     kernel; the clock is GRBM_GUI_ACTIVE (summed over the 8 XCDs) / 8 / the
     kernel's duration, given for kernels of 500 us or more."""
     ds = _pmc_dispatches(path)
@@ -266,7 +267,7 @@ def summarize_mfma(path):
     reg["peak"] = [a for a in ds if a["name"].startswith("mfma_peak_kernel")]
     reg["lib"] = [dict(a, name="vendor library GEMM (" + a["name"][:24] + "...)") for a in ds if "Cijk" in a["name"]]
     lines = []
-    for m, title in [(1, REGIONS[1]), (3, REGIONS[3]), (5, REGIONS[5]),
+    for m, title in [(1, REGIONS[1]), (3, REGIONS[3]), (5, REGIONS[5]), (7, REGIONS[7]),
                      ("peak", "register-operand MFMA kernel (moe_mfma_peak)"),
                      ("lib", "the vendor library's dense GEMM on the expert GEMMs' shapes (--library-gemm)")]:
         if not reg.get(m):
