@@ -338,6 +338,9 @@ __global__ __launch_bounds__(256) void bwd_dwr_kernel(const float* __restrict__ 
     if (c >= d) return;
     float acc = 0.f;
     const int b1 = poff[e + 1] / 64;
+    // (unrolled so that the loads of 8 blocks are in flight together; the
+    // sum stays in block order)
+#pragma unroll 8
     for (int b = poff[e] / 64; b < b1; ++b) acc += wr_part[static_cast<int64_t>(b) * d + c];
     dw_router[static_cast<int64_t>(e) * d + c] = __builtin_bit_cast(bf16_t, static_cast<__bf16>(acc));
 }
